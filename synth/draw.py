@@ -1,0 +1,133 @@
+"""Seeded Gaussian draws, rounded to nearest-even into the storage dtype.
+
+The rounding is written from the IEEE-754 definition: a finite x is snapped
+to the nearest multiple of the unit in the last place of its binade (never
+finer than the format's subnormal spacing), ties to the even multiple, and
+results beyond the largest finite value become +-inf. It is carried out in
+float64, where every step below is exact, so fp64 -> fp16 and fp64 -> bf16
+are each rounded once (no double rounding through fp32).
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+from .configs import Config
+
+# (stored mantissa bits, minimum normal exponent, largest finite value)
+_FORMATS = {
+    "f32": (23, -126, float(np.finfo(np.float32).max)),
+    "f16": (10, -14, 65504.0),
+    "bf16": (7, -126, float.fromhex("0x1.fep127")),
+}
+
+# NumPy container that holds the storage bits of each dtype.
+STORAGE_NUMPY = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+_CHUNK = 1 << 22
+
+
+def _round_chunk(x: np.ndarray, mant: int, emin: int, maxval: float) -> None:
+    _, e = np.frexp(x)                      # x = m * 2**e with 0.5 <= |m| < 1
+    q = np.maximum(e - 1, emin) - mant      # exponent of one ulp at x
+    r = np.ldexp(np.rint(np.ldexp(x, -q)), q)   # np.rint rounds half to even
+    over = np.abs(r) > maxval
+    if over.any():
+        r[over] = np.copysign(np.inf, x[over])
+    x[...] = r
+
+
+def round_to_storage(x, dtype: str, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Return float64 values of x rounded (RNE) to the storage dtype.
+
+    `out` may be x itself for in-place rounding of a float64 array.
+    """
+    mant, emin, maxval = _FORMATS[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    if out is None:
+        out = np.array(x, dtype=np.float64, copy=True)
+    elif out is not x:
+        out[...] = x
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, _CHUNK):
+        _round_chunk(flat[s:s + _CHUNK], mant, emin, maxval)
+    return out
+
+
+def storage_bits(r: np.ndarray, dtype: str) -> np.ndarray:
+    """Pack float64 values that are exact in `dtype` into its storage container.
+
+    f32 -> float32, f16 -> float16, bf16 -> uint16 (the top half of the fp32
+    bit pattern, which is exact for a bf16-representable value).
+    """
+    if dtype == "f32":
+        return r.astype(np.float32)
+    if dtype == "f16":
+        return r.astype(np.float16)
+    if dtype == "bf16":
+        return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+@dataclass
+class Inputs:
+    """One draw of the shard's operands, as float64 values exact in `dtype`.
+
+    A, b1 and B are either the full FFN weights (all_shards) or one rank's
+    blocks A_i [h, f], b1_i [f], B_i [f, h].
+    """
+    dtype: str
+    X: np.ndarray
+    A: np.ndarray
+    b1: np.ndarray
+    B: np.ndarray
+    dY: np.ndarray
+    tp: int = 1
+    full: bool = False
+    _bits: dict = field(default_factory=dict, repr=False)
+
+    def bits(self, name: str) -> np.ndarray:
+        if name not in self._bits:
+            self._bits[name] = storage_bits(getattr(self, name), self.dtype)
+        return self._bits[name]
+
+    @property
+    def tokens(self) -> int:
+        return self.X.shape[0]
+
+    @property
+    def hidden(self) -> int:
+        return self.X.shape[1]
+
+
+def _normal(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float64)
+    if sigma != 1.0:
+        x *= sigma
+    return round_to_storage(x, dtype, out=x)
+
+
+def draw_inputs(tokens: int, hidden: int, ffn: int, dtype: str, *, seed: int = 0,
+                sigma_x: float = 1.0, sigma_w: float = 0.02, sigma_b: float = 0.01,
+                sigma_dy: float = 0.01, tp: int = 1, full: bool = False) -> Inputs:
+    """Draw X [T,h], A [h,ffn], b1 [ffn], B [ffn,h], dY [T,h] in that order.
+
+    PCG64 seeded with `seed`; every tensor is i.i.d. N(0, sigma^2), drawn in
+    float64 and rounded to nearest-even into `dtype`. `ffn` is the width of
+    what is drawn: the full FFN when full=True (shards are sliced later),
+    otherwise the shard width f.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = _normal(rng, (tokens, hidden), sigma_x, dtype)
+    A = _normal(rng, (hidden, ffn), sigma_w, dtype)
+    b1 = _normal(rng, (ffn,), sigma_b, dtype)
+    B = _normal(rng, (ffn, hidden), sigma_w, dtype)
+    dY = _normal(rng, (tokens, hidden), sigma_dy, dtype)
+    return Inputs(dtype, X, A, b1, B, dY, tp=tp, full=full)
+
+
+def draw_config(cfg: Config) -> Inputs:
+    width = cfg.ffn if cfg.all_shards else cfg.ffn_shard
+    return draw_inputs(cfg.tokens, cfg.hidden, width, cfg.dtype, seed=cfg.seed,
+                       sigma_x=cfg.sigma_x, sigma_w=cfg.sigma_w, sigma_b=cfg.sigma_b,
+                       sigma_dy=cfg.sigma_dy, tp=cfg.tp, full=cfg.all_shards)
