@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's MLP forward + backward on one MI355X.
+
+A step is one pass of the whole path over one batch: tp_mlp_fwd (F1: X A_i
+with fused bias + GeLU, F2: H_i B_i) then tp_mlp_bwd (B1: dY B_i^T with fused
+gelu' and db1 partials, B5: db1 finish, B2: dB, B3: dA, B4: dXp). Inputs are
+seeded synthetic tensors resident in HBM before timing starts.
+
+Prints one JSON line: whole-step TFLOP/s (GEMM flops 12 T h f per step over
+wall-clock time between device synchronizations), the fraction of the dense
+16-bit MFMA peak, the dominant kernel's roofline (its algorithmic flops over
+its average duration from HIP events recorded on the launch stream), and the
+float64 CPU oracle timed on a bounded token sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + % MFMA peak, TP-shard MLP fwd+bwd (h=2560..10240), 1 MI355X"
+# Dense MFMA peaks of MI355X in TFLOP/s: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
+# for fp16/bf16; the fp32 figure is the vector (FMA) peak the fp32 path uses.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+FWD_STEPS = ["F1", "F2"]
+BWD_STEPS = ["B1", "B5", "B2", "B3", "B4"]
+GEMM_STEPS = ["F1", "F2", "B1", "B2", "B3", "B4"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_name(cfg):
+    return (f"{cfg.name}: one TP={cfg.tp} shard of an MLP with hidden {cfg.hidden}, FFN {cfg.ffn}; "
+            f"tokens {cfg.tokens} (micro-batch {cfg.micro_batch} x seq {cfg.seq_len}), shard width {cfg.ffn_shard}")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(inp, cfg, target_s):
+    """The float64 oracle (as it stands) on the first Ts tokens of the same
+    workload, Ts chosen so that the timed run takes roughly target_s."""
+    import oracle
+    h, f = inp.X.shape[1], inp.A.shape[1]
+
+    def run(ts):
+        t0 = time.perf_counter()
+        oracle.shard_forward(inp.X[:ts], inp.A, inp.b1, inp.B)
+        oracle.shard_backward(inp.X[:ts], inp.A, inp.b1, inp.B, inp.dY[:ts])
+        return time.perf_counter() - t0
+
+    probe = min(64, inp.X.shape[0])
+    dt = run(probe)
+    ts = int(probe * target_s / max(dt, 1e-3)) // 8 * 8
+    ts = max(probe, min(ts, inp.X.shape[0]))
+    log(f"cpu baseline: oracle on {ts} tokens (probe {probe} tokens took {dt:.2f} s)")
+    dt = run(ts)
+    flops = 12.0 * ts * h * f
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"float64 NumPy oracle, forward+backward of the same shard on the first {ts} of {cfg.tokens} "
+                  f"tokens (same weights), {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt_h10240")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share (one TP rank) only: the path has no cross-GPU step here. "
+              "Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import megatron_tensor_transformer_04_amd as tpmlp
+
+    tpmlp.load()
+    cfg = synth.get_config(args.config)
+    T, h, f = cfg.tokens, cfg.hidden, cfg.ffn_shard
+    log(f"drawing inputs for {cfg.name} (T={T} h={h} f={f} {cfg.dtype})")
+    inp = synth.draw_config(cfg)
+    if cfg.all_shards:  # bench one rank's share
+        import oracle
+        inp.A, inp.b1, inp.B = (x.copy() for x in oracle.shard_weights(inp.A, inp.b1, inp.B, cfg.tp, 0))
+        inp._bits.clear()
+    from tests.gpu_util import device_inputs, torch_dtype
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    X, A, b1, B, dY = device_inputs(inp)
+    td = torch_dtype(cfg.dtype)
+    e = lambda *s: torch.empty(s, dtype=td, device=dev)
+    Z, H, Yp = e(T, f), e(T, f), e(T, h)
+    dZ, dXp, dA, dB, db1 = e(T, f), e(T, h), e(h, f), e(f, h), e(f)
+    code = {"f32": tpmlp.TPMLP_F32, "f16": tpmlp.TPMLP_F16, "bf16": tpmlp.TPMLP_BF16}[cfg.dtype]
+    nws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(fe=None, be=None):
+        tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, events=fe)
+        tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(fev[k], bev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    per = {n: 0.0 for n in FWD_STEPS + BWD_STEPS}
+    for k in range(K):
+        for i, n in enumerate(FWD_STEPS):
+            per[n] += fev[k][i].elapsed_time(fev[k][i + 1])
+        for i, n in enumerate(BWD_STEPS):
+            per[n] += bev[k][i].elapsed_time(bev[k][i + 1])
+    per = {n: v / K for n, v in per.items()}
+    gpu_ms = fev[0][0].elapsed_time(bev[K - 1][5]) / K
+    ms = wall / K * 1e3
+    flops = 12.0 * T * h * f
+    value = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    gemm_flops = 2.0 * T * h * f
+    dom = max(GEMM_STEPS, key=lambda n: per[n])
+    achieved = gemm_flops / (per[dom] * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload_name(cfg), "tokens": T, "hidden": h, "ffn_shard": f, "tp": cfg.tp},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "peak_tflops": peak,
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in per.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma" if cfg.dtype != "f32" else "alu",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * tp_mlp.h - one tensor-parallel rank's share of a Transformer MLP block,
+ * forward and backward, on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation. The MLP block is Y = GeLU(X A + b1) B (+ b2). Tensor
+ * parallelism over P ranks splits the first linear by output columns and the
+ * second by input rows ("Understanding the Megatron-LM architecture: how 3D
+ * parallelism assigns roles", section 1, the column-split and row-split
+ * bullets; "Megatron-LM overview", section 2.2). Rank i holds
+ *   A_i  = A[:, i f : (i+1) f]   [hidden, f]
+ *   b1_i = b1[i f : (i+1) f]     [f]
+ *   B_i  = B[i f : (i+1) f, :]   [f, hidden]        with f = ffn / P,
+ * computes its columns of the first linear on its own, and produces a
+ * partial sum of the second linear that the caller reduces over ranks. The
+ * bias add and the GeLU are one fused step ("Training GPT-2 with
+ * Megatron-LM", section 6.2, fused_bias_gelu). GeLU is the tanh form
+ *   gelu(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+ *
+ * Forward (tp_mlp_fwd), with T = tokens:
+ *   Z_i  = X A_i + 1 b1_i^T        [T, f]   pre-activation, kept for backward
+ *   H_i  = gelu(Z_i)               [T, f]   optional output
+ *   Yp_i = H_i B_i                 [T, hidden] partial; sum over ranks (+ b2)
+ * Backward (tp_mlp_bwd), given dY [T, hidden] (identical on every rank):
+ *   dZ_i  = (dY B_i^T) * gelu'(Z_i)           [T, f]
+ *   db1_i = sum over tokens of dZ_i           [f]
+ *   dB_i  = H_i^T dY                          [f, hidden]
+ *   dA_i  = X^T dZ_i                          [hidden, f]
+ *   dXp_i = dZ_i A_i^T                        [T, hidden] partial; sum over ranks
+ * The cross-rank sums (of Yp and dXp) and the second bias b2 are the
+ * caller's; nothing here talks to another GPU.
+ *
+ * Conventions for every entry point below.
+ *   - Tensors are dense, row-major, in the shapes above, all in the storage
+ *     dtype of the shape (fp32, fp16 or bf16), inputs and outputs alike.
+ *     Products accumulate in fp32; every 16-bit result is rounded once to
+ *     nearest-even from its fp32 value.
+ *   - Tensor pointers are DEVICE pointers on the current HIP device, 16-byte
+ *     aligned. `stream` is a hipStream_t (NULL = the null stream). The
+ *     caller owns every buffer and the stream; the library allocates nothing
+ *     and keeps no per-call state, so calls from several threads are safe.
+ *   - Calls are asynchronous: TPMLP_OK means the work was enqueued on
+ *     `stream`. Outputs are fully overwritten (never accumulated into).
+ *   - Dimensions may be 0. A product over an empty dimension is 0 (e.g.
+ *     tokens == 0 gives dA = 0, dB = 0, db1 = 0); tensors with no elements
+ *     are not touched. Nonzero dimensions must be multiples of 8 for fp16 /
+ *     bf16 and of 4 for fp32, so that every row is 16-byte aligned.
+ *   - Validation failures return before anything is enqueued and leave every
+ *     output untouched. Outputs must not overlap each other or any input
+ *     (TPMLP_ERR_ALIAS). A failed kernel launch returns TPMLP_ERR_HIP; HIP's
+ *     sticky error state of the calling thread is read with hipGetLastError,
+ *     so an error left pending by earlier, unrelated work may surface here.
+ *   - Results are bitwise deterministic for a given shape, dtype and device:
+ *     no floating-point atomics are used and every cross-workgroup sum runs
+ *     in a fixed order.
+ */
+#ifndef TP_MLP_H
+#define TP_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPMLP_ABI_VERSION 1
+
+typedef enum {
+  TPMLP_F32 = 0,
+  TPMLP_F16 = 1,
+  TPMLP_BF16 = 2
+} tpmlp_dtype;
+
+typedef enum {
+  TPMLP_OK = 0,
+  TPMLP_ERR_NULL = 1,      /* a required pointer is NULL */
+  TPMLP_ERR_SHAPE = 2,     /* negative dimension, or a size beyond the supported range */
+  TPMLP_ERR_ALIGN = 3,     /* pointer not 16-byte aligned, or dimension not a multiple of 8 (4 for fp32) */
+  TPMLP_ERR_DTYPE = 4,     /* dtype not one of tpmlp_dtype */
+  TPMLP_ERR_WORKSPACE = 5, /* workspace smaller than tp_mlp_workspace_bytes() */
+  TPMLP_ERR_HIP = 6,       /* a HIP call or kernel launch failed */
+  TPMLP_ERR_ALIAS = 7      /* an output overlaps an input or another output */
+} tpmlp_status;
+
+/* Shape of one rank's share: X [tokens, hidden], A_i [hidden, ffn_shard]. */
+typedef struct {
+  int64_t tokens;
+  int64_t hidden;
+  int64_t ffn_shard;
+  int32_t dtype; /* tpmlp_dtype */
+} tpmlp_shape;
+
+/* TPMLP_ABI_VERSION of the built library. */
+int tp_mlp_abi_version(void);
+
+/* Static, human-readable name of a tpmlp_status value (never NULL). */
+const char* tp_mlp_status_string(int status);
+
+/*
+ * Bytes of device workspace tp_mlp_bwd needs for `shape` (0 if none; fp32
+ * per-tile column partials of dZ for db1, and split-K partials). With
+ * dz_in_workspace != 0 it also counts room for dZ_i, for callers that pass
+ * dZ = NULL to tp_mlp_bwd. Returns 0 and sets nothing on an invalid shape.
+ */
+size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, int dz_in_workspace);
+
+/*
+ * Forward of one rank (Z_i, optional H_i, partial Yp_i); see the top of this
+ * file for the operation and conventions.
+ *   X  [tokens, hidden]    in
+ *   A  [hidden, ffn_shard] in   (A_i)
+ *   b1 [ffn_shard]         in   (b1_i)
+ *   B  [ffn_shard, hidden] in   (B_i)
+ *   Z  [tokens, ffn_shard] out  pre-activation X A_i + b1_i (bias included)
+ *   H  [tokens, ffn_shard] out, may be NULL: gelu(Z_i). When NULL, the second
+ *                          GEMM applies the GeLU to Z_i while loading it.
+ *   Yp [tokens, hidden]    out  H_i B_i (partial over ranks, no b2)
+ *   events: NULL, or 3 hipEvent_t recorded on `stream` before the first
+ *           GEMM, between the two GEMMs and after the second (per-step
+ *           timing for profilers and benchmarks).
+ */
+int tp_mlp_fwd(const tpmlp_shape* shape,
+               const void* X, const void* A, const void* b1, const void* B,
+               void* Z, void* H, void* Yp,
+               void* stream, void* const* events);
+
+/*
+ * Backward of one rank; see the top of this file for the operation.
+ *   dY  [tokens, hidden]    in   output gradient (same on every rank)
+ *   X, A, B                 in   as in tp_mlp_fwd
+ *   Z   [tokens, ffn_shard] in   the forward's Z_i
+ *   H   [tokens, ffn_shard] in, may be NULL: the forward's H_i. When NULL,
+ *                           gelu(Z_i) is recomputed while loading Z_i.
+ *   dZ  [tokens, ffn_shard] out, may be NULL: dZ_i. When NULL it is kept in
+ *                           the workspace (size it with dz_in_workspace = 1).
+ *   dXp [tokens, hidden]    out  dZ_i A_i^T (partial over ranks)
+ *   dA  [hidden, ffn_shard] out  X^T dZ_i
+ *   dB  [ffn_shard, hidden] out  H_i^T dY
+ *   db1 [ffn_shard]         out  column sums of dZ_i
+ *   ws, ws_bytes            device workspace of at least
+ *                           tp_mlp_workspace_bytes(shape, dZ == NULL) bytes,
+ *                           16-byte aligned; may be NULL when that is 0. Its
+ *                           contents on entry are ignored.
+ *   events: NULL, or 6 hipEvent_t recorded on `stream` before the dZ GEMM
+ *           and after each of: dZ GEMM (with the db1 column partials),
+ *           db1 finish, dB GEMM, dA GEMM, dXp GEMM.
+ */
+int tp_mlp_bwd(const tpmlp_shape* shape,
+               const void* dY, const void* X, const void* A, const void* B,
+               const void* Z, const void* H,
+               void* dZ, void* dXp, void* dA, void* dB, void* db1,
+               void* ws, size_t ws_bytes,
+               void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_MLP_H */

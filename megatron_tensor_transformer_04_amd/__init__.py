@@ -1,0 +1,22 @@
+"""MI355X (gfx950) tensor-parallel MLP shard: forward and backward of one
+rank's share of a Transformer FFN block, as hand-written HIP kernels behind
+the C ABI in include/tp_mlp.h. This package is the ctypes binding to that
+library (libtpmlp.so, built in-tree by _build.build()).
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    STATUS,
+    TPMLP_BF16,
+    TPMLP_F16,
+    TPMLP_F32,
+    TpMlpError,
+    bwd,
+    fwd,
+    load,
+    tp_mlp_abi_version,
+    tp_mlp_bwd,
+    tp_mlp_fwd,
+    tp_mlp_status_string,
+    tp_mlp_workspace_bytes,
+)

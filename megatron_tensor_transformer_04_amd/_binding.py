@@ -1,0 +1,166 @@
+"""ctypes binding of libtpmlp.so (include/tp_mlp.h), same names as the C ABI.
+
+Argument marshalling only: tensors are torch device tensors whose data
+pointers are handed to the library together with torch's current HIP
+stream; every step of the computation runs in the library's kernels. There
+is no fallback: if the library is missing or was not built, loading fails
+with an error.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtpmlp.so")
+
+TPMLP_F32, TPMLP_F16, TPMLP_BF16 = 0, 1, 2
+STATUS = {
+    0: "TPMLP_OK",
+    1: "TPMLP_ERR_NULL",
+    2: "TPMLP_ERR_SHAPE",
+    3: "TPMLP_ERR_ALIGN",
+    4: "TPMLP_ERR_DTYPE",
+    5: "TPMLP_ERR_WORKSPACE",
+    6: "TPMLP_ERR_HIP",
+    7: "TPMLP_ERR_ALIAS",
+}
+EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd")
+
+
+class TpMlpError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class tpmlp_shape(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("ffn_shard", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library once; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.tp_mlp_abi_version.restype = ctypes.c_int
+    lib.tp_mlp_abi_version.argtypes = []
+    lib.tp_mlp_status_string.restype = ctypes.c_char_p
+    lib.tp_mlp_status_string.argtypes = [ctypes.c_int]
+    lib.tp_mlp_workspace_bytes.restype = sz
+    lib.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int]
+    lib.tp_mlp_fwd.restype = ctypes.c_int
+    lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_bwd.restype = ctypes.c_int
+    lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: TPMLP_F32, torch.float16: TPMLP_F16, torch.bfloat16: TPMLP_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous row-major")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _events(events):
+    if events is None:
+        return None
+    arr = (ctypes.c_void_p * len(events))()
+    for i, e in enumerate(events):
+        if hasattr(e, "cuda_event"):
+            if not e.cuda_event:  # torch creates its HIP event on first record
+                e.record()
+            arr[i] = e.cuda_event
+        else:
+            arr[i] = int(e)
+    return arr
+
+
+def _check(status: int):
+    if status != 0:
+        raise TpMlpError(status, load().tp_mlp_status_string(status).decode())
+
+
+def shape_of(tokens: int, hidden: int, ffn_shard: int, dtype: int) -> tpmlp_shape:
+    return tpmlp_shape(tokens, hidden, ffn_shard, dtype)
+
+
+def tp_mlp_abi_version() -> int:
+    return load().tp_mlp_abi_version()
+
+
+def tp_mlp_status_string(status: int) -> str:
+    return load().tp_mlp_status_string(status).decode()
+
+
+def tp_mlp_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int, dz_in_workspace: bool = False) -> int:
+    s = shape_of(tokens, hidden, ffn_shard, dtype)
+    return load().tp_mlp_workspace_bytes(ctypes.byref(s), int(bool(dz_in_workspace)))
+
+
+def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, *, stream=None, events=None) -> None:
+    """Forward of one TP rank into caller-allocated Z, H (or None) and Yp."""
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    ev = _events(events)
+    _check(load().tp_mlp_fwd(ctypes.byref(s), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),
+                             _stream(stream), ev))
+
+
+def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None) -> None:
+    """Backward of one TP rank into caller-allocated gradients and workspace."""
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ev = _events(events)
+    _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
+                             _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+# ---- convenience wrappers that allocate the outputs with torch ----
+
+def fwd(X, A, b1, B, keep_h: bool = True, stream=None, events=None):
+    import torch
+    T, f, h = X.shape[0], A.shape[1], X.shape[1]
+    Z = torch.empty((T, f), dtype=X.dtype, device=X.device)
+    H = torch.empty((T, f), dtype=X.dtype, device=X.device) if keep_h else None
+    Yp = torch.empty((T, h), dtype=X.dtype, device=X.device)
+    tp_mlp_fwd(X, A, b1, B, Z, H, Yp, stream=stream, events=events)
+    return Z, H, Yp
+
+
+def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, stream=None, events=None):
+    import torch
+    T, f, h = X.shape[0], A.shape[1], X.shape[1]
+    dev, dt = X.device, X.dtype
+    dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
+    dXp = torch.empty((T, h), dtype=dt, device=dev)
+    dA = torch.empty((h, f), dtype=dt, device=dev)
+    dB = torch.empty((f, h), dtype=dt, device=dev)
+    db1 = torch.empty((f,), dtype=dt, device=dev)
+    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), dz_in_workspace=not keep_dz)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
+    tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events)
+    return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}

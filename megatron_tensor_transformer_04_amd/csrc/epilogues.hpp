@@ -1,0 +1,71 @@
+// GEMM epilogues: what happens to each fp32 accumulator C[m][n] of a tile.
+//
+// Every epilogue exposes
+//   float apply(int64_t m, int64_t n, float acc)   store the result, return
+//                                                  the value that enters the
+//                                                  optional column sum;
+//   static constexpr bool kColSum                  whether the kernel also
+//                                                  reduces the tile's columns;
+//   void colsum(int tile_m, int64_t n, float s)    store one tile's sum.
+// apply() is only called for in-range (m, n).
+#pragma once
+
+#include "numerics.hpp"
+
+namespace tpmlp {
+
+// C = round(acc): the row-parallel partial Yp, dB, dA and dXp.
+template <class S>
+struct EpiStore {
+  typename S::T* out;
+  int64_t ld;
+  static constexpr bool kColSum = false;
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    out[m * ld + n] = S::from_f(acc);
+    return 0.0f;
+  }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
+// Fused bias + GeLU after the column-parallel GEMM:
+//   z = acc + b1[n];  Z[m][n] = round(z);  H[m][n] = round(gelu(z)).
+// Both outputs come from the one fp32 value z ("Training GPT-2 with
+// Megatron-LM", section 6.2, fused_bias_gelu).
+template <class S>
+struct EpiBiasGelu {
+  const typename S::T* bias;
+  typename S::T* z;
+  typename S::T* h;  // may be null: H not kept
+  int64_t ld;
+  static constexpr bool kColSum = false;
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    const float v = acc + S::to_f(bias[n]);
+    z[m * ld + n] = S::from_f(v);
+    if (h) h[m * ld + n] = S::from_f(gelu_tanh(v));
+    return 0.0f;
+  }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
+// Backward through the GeLU after the dH GEMM (dH = dY B_i^T):
+//   d = acc * gelu'(Z[m][n]);  dZ[m][n] = round(d);
+// and the fp32 column sums of d over the tile's rows, the per-tile partials
+// of db1 = sum over tokens of dZ.
+template <class S>
+struct EpiGeluGrad {
+  const typename S::T* zin;
+  typename S::T* dz;
+  float* partial;  // [tiles_m][ld]
+  int64_t ld;
+  static constexpr bool kColSum = true;
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    const float d = acc * gelu_tanh_grad(S::to_f(zin[m * ld + n]));
+    dz[m * ld + n] = S::from_f(d);
+    return d;
+  }
+  __device__ __forceinline__ void colsum(int tile_m, int64_t n, float s) const {
+    partial[(int64_t)tile_m * ld + n] = s;
+  }
+};
+
+}  // namespace tpmlp

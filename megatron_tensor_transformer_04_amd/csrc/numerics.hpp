@@ -1,0 +1,106 @@
+// Storage formats, fp32 <-> 16-bit conversions and the tanh-GeLU for gfx950.
+//
+// GeLU is the tanh approximation of Hendrycks & Gimpel, "Gaussian Error
+// Linear Units" (2016); the pages fuse it with the first linear's bias
+// ("Training GPT-2 with Megatron-LM", section 6.2, fused_bias_gelu) without
+// stating a formula. tanh(u) enters only through exp(2u), see tanh_parts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+
+// fp32 storage (the plain-FMA path)
+struct StoreF32 {
+  using T = float;
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+
+// IEEE binary16 storage; the hardware conversion rounds to nearest-even.
+struct StoreF16 {
+  using T = uint16_t;
+  static __device__ __forceinline__ float to_f(uint16_t v) {
+    return (float)__builtin_bit_cast(_Float16, v);
+  }
+  static __device__ __forceinline__ uint16_t from_f(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// bfloat16 storage: the top 16 bits of an fp32; rounded to nearest-even
+// (ties to even, NaN kept quiet) from the fp32 bit pattern.
+struct StoreBF16 {
+  using T = uint16_t;
+  static __device__ __forceinline__ float to_f(uint16_t v) {
+    return __builtin_bit_cast(float, (uint32_t)v << 16);
+  }
+  static __device__ __forceinline__ uint16_t from_f(float v) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+constexpr float kSqrt2OverPi = 0.7978845608028654f;
+constexpr float kGeluC = 0.044715f;
+
+// With t = tanh(u), e = exp(2u) and r = 1 / (e + 1):
+//   1 + t = 2 e r,   1 - t = 2 r,   1 - t^2 = 4 e r^2,
+// forms without the cancellation of 1 +- t near t = -+1. 2u is clamped to
+// [-80, 40]: there tanh is already +-1 to fp32 precision and exp stays finite.
+__device__ __forceinline__ void tanh_parts(float u, float& e, float& r) {
+  const float u2 = fminf(fmaxf(2.0f * u, -80.0f), 40.0f);
+  e = __expf(u2);
+  r = __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+// gelu(x) = x/2 (1 + tanh(u)) = x e r,  u = sqrt(2/pi) (x + c x^3)
+__device__ __forceinline__ float gelu_tanh(float x) {
+  float e, r;
+  tanh_parts(kSqrt2OverPi * (x + kGeluC * x * x * x), e, r);
+  return x * e * r;
+}
+
+// d/dx gelu(x) = (1 + t)/2 + x/2 (1 - t^2) sqrt(2/pi) (1 + 3 c x^2)
+//              = e r + 2 sqrt(2/pi) x (1 + 3 c x^2) e r^2
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+  const float x2 = x * x;
+  float e, r;
+  tanh_parts(kSqrt2OverPi * (x + kGeluC * x2 * x), e, r);
+  const float er = e * r;
+  return er + 2.0f * kSqrt2OverPi * x * (1.0f + 3.0f * kGeluC * x2) * er * r;
+}
+
+// Apply gelu to the eight 16-bit values packed in one 16-byte chunk.
+template <class S>
+__device__ __forceinline__ u32x4 gelu_chunk(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint16_t lo = (uint16_t)(v[w] & 0xffffu), hi = (uint16_t)(v[w] >> 16);
+    const uint16_t glo = S::from_f(gelu_tanh(S::to_f(lo)));
+    const uint16_t ghi = S::from_f(gelu_tanh(S::to_f(hi)));
+    r[w] = (uint32_t)glo | ((uint32_t)ghi << 16);
+  }
+  return r;
+}
+
+}  // namespace tpmlp

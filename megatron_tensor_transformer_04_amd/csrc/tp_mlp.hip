@@ -1,0 +1,319 @@
+// C ABI of the tensor-parallel MLP shard (declared in include/tp_mlp.h):
+// argument validation, tile planning and the launch sequences of the forward
+// (F1: X A_i with fused bias + GeLU, F2: H_i B_i) and backward (B1: dY B_i^T
+// with fused gelu' and db1 column partials, B5: db1 finish, B2: H_i^T dY,
+// B3: X^T dZ_i, B4: dZ_i A_i^T).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "tp_mlp.h"
+#include "epilogues.hpp"
+#include "gemm_mfma.hpp"
+#include "gemm_simt.hpp"
+
+namespace tpmlp {
+namespace {
+
+// Sum of the per-tile fp32 column partials in tile order, rounded once.
+template <class S>
+__global__ __launch_bounds__(256) void db1_finish_kernel(const float* partial, int tiles_m, int64_t f,
+                                                         typename S::T* db1) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= f) return;
+  float s = 0.0f;
+  for (int t = 0; t < tiles_m; ++t) s += partial[(int64_t)t * f + n];
+  db1[n] = S::from_f(s);
+}
+
+enum class Engine { Simt, Mfma128, Mfma256 };
+
+using Cfg128 = MfmaTile<128, 128, 2, 2>;
+using Cfg256 = MfmaTile<256, 256, 2, 4>;
+
+struct Plan {
+  Engine eng;
+  int bm, bn;
+  int tiles_m, tiles_n;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile choice for the 16-bit engine: 256x256 tiles once they give at least
+// two full waves over the 256 CUs, else 128x128. TPMLP_TILE=128 or 256 in
+// the environment forces one size (read on every call; for tuning and tests).
+bool use_big_tiles(int64_t M, int64_t N) {
+  if (const char* e = std::getenv("TPMLP_TILE")) {
+    if (!std::strcmp(e, "128")) return false;
+    if (!std::strcmp(e, "256")) return true;
+  }
+  return ceil_div(M, 256) * ceil_div(N, 256) >= 512;
+}
+
+Plan plan_gemm(int dtype, int64_t M, int64_t N) {
+  Plan p;
+  if (dtype == TPMLP_F32) {
+    p.eng = Engine::Simt;
+    p.bm = SimtTile::BM;
+    p.bn = SimtTile::BN;
+  } else if (use_big_tiles(M, N)) {
+    p.eng = Engine::Mfma256;
+    p.bm = Cfg256::BM;
+    p.bn = Cfg256::BN;
+  } else {
+    p.eng = Engine::Mfma128;
+    p.bm = Cfg128::BM;
+    p.bn = Cfg128::BN;
+  }
+  p.tiles_m = (int)ceil_div(M, p.bm);
+  p.tiles_n = (int)ceil_div(N, p.bn);
+  return p;
+}
+
+template <class Cfg, class S, bool PK, bool QK, bool GP, class Epi>
+void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q, int64_t ldq, const Epi& epi,
+                 hipStream_t st) {
+  const int nblk = sh.tiles_m * sh.tiles_n * sh.splits;
+  hipLaunchKernelGGL((gemm_mfma_kernel<Cfg, S, PK, QK, GP, Epi>), dim3(nblk), dim3(Cfg::THREADS), 0, st, sh,
+                     Operand{static_cast<const uint16_t*>(p), ldp}, Operand{static_cast<const uint16_t*>(q), ldq},
+                     epi);
+}
+
+// C[M][N] = sum_k P[m][k] Q[k][n] through epilogue `epi`; PK / QK select the
+// k-contiguous layout of P / Q, GP applies gelu to P as it is loaded.
+template <class S, bool PK, bool QK, bool GP, class Epi>
+hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q,
+                    int64_t ldq, const Epi& epi, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const Plan pl = plan_gemm(dtype, M, N);
+  GemmShape sh{M, N, K, pl.tiles_m, pl.tiles_n, 1, std::max<int64_t>(K, 1)};
+  if constexpr (std::is_same_v<S, StoreF32>) {
+    hipLaunchKernelGGL((gemm_simt_kernel<PK, QK, GP, Epi>), dim3(pl.tiles_m * pl.tiles_n), dim3(SimtTile::THREADS),
+                       0, st, sh, OperandF32{static_cast<const float*>(p), ldp},
+                       OperandF32{static_cast<const float*>(q), ldq}, epi);
+  } else {
+    if (pl.eng == Engine::Mfma256)
+      launch_mfma<Cfg256, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st);
+    else
+      launch_mfma<Cfg128, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st);
+  }
+  return hipGetLastError();
+}
+
+size_t elt_size(int dtype) { return dtype == TPMLP_F32 ? 4 : 2; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+int check_shape(const tpmlp_shape* s) {
+  if (!s) return TPMLP_ERR_NULL;
+  if (s->dtype != TPMLP_F32 && s->dtype != TPMLP_F16 && s->dtype != TPMLP_BF16) return TPMLP_ERR_DTYPE;
+  const int64_t d[3] = {s->tokens, s->hidden, s->ffn_shard};
+  const int64_t mult = s->dtype == TPMLP_F32 ? 4 : 8;
+  for (int64_t v : d) {
+    if (v < 0 || v > kMaxDim) return TPMLP_ERR_SHAPE;
+  }
+  // the smallest tiles (64) must give a grid that fits in 31 bits
+  if (ceil_div(s->tokens, 64) * ceil_div(std::max(s->hidden, s->ffn_shard), 64) > INT32_MAX / 2 ||
+      ceil_div(s->hidden, 64) * ceil_div(s->ffn_shard, 64) > INT32_MAX / 2)
+    return TPMLP_ERR_SHAPE;
+  for (int64_t v : d) {
+    if (v % mult) return TPMLP_ERR_ALIGN;
+  }
+  return TPMLP_OK;
+}
+
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Required pointers (non-empty tensors) must be non-null; every non-null
+// pointer must be 16-byte aligned; outputs may not overlap anything else.
+int check_buffers(const Span* in, int n_in, const bool* in_required, const Span* out, int n_out,
+                  const bool* out_required) {
+  for (int i = 0; i < n_in; ++i)
+    if (in_required[i] && in[i].bytes && !in[i].p) return TPMLP_ERR_NULL;
+  for (int i = 0; i < n_out; ++i)
+    if (out_required[i] && out[i].bytes && !out[i].p) return TPMLP_ERR_NULL;
+  for (int i = 0; i < n_in; ++i)
+    if (((uintptr_t)in[i].p & 15u) != 0) return TPMLP_ERR_ALIGN;
+  for (int i = 0; i < n_out; ++i)
+    if (((uintptr_t)out[i].p & 15u) != 0) return TPMLP_ERR_ALIGN;
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(out[i], in[j])) return TPMLP_ERR_ALIAS;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(out[i], out[j])) return TPMLP_ERR_ALIAS;
+  }
+  return TPMLP_OK;
+}
+
+int record(void* const* events, int i, hipStream_t st) {
+  if (!events) return TPMLP_OK;
+  return hipEventRecord(static_cast<hipEvent_t>(events[i]), st) == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
+}
+
+#define TPMLP_TRY(expr)              \
+  do {                               \
+    const int rc_ = (expr);          \
+    if (rc_ != TPMLP_OK) return rc_; \
+  } while (0)
+#define TPMLP_HIP(expr)                                 \
+  do {                                                  \
+    if ((expr) != hipSuccess) return TPMLP_ERR_HIP;     \
+  } while (0)
+
+struct WsLayout {
+  size_t dz_off, dz_bytes, part_off, part_bytes, total;
+  int part_tiles;
+};
+
+WsLayout ws_layout(const tpmlp_shape& s, bool dz_in_ws) {
+  WsLayout w{};
+  const Plan b1 = plan_gemm(s.dtype, s.tokens, s.ffn_shard);
+  w.part_tiles = (s.tokens > 0 && s.ffn_shard > 0) ? b1.tiles_m : 0;
+  w.dz_off = 0;
+  w.dz_bytes = dz_in_ws ? (size_t)(s.tokens * s.ffn_shard) * elt_size(s.dtype) : 0;
+  w.part_off = (w.dz_bytes + 255) / 256 * 256;
+  w.part_bytes = (size_t)w.part_tiles * (size_t)s.ffn_shard * sizeof(float);
+  w.total = w.part_bytes ? w.part_off + w.part_bytes : w.dz_bytes;
+  return w;
+}
+
+template <class S>
+int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1, const void* B, void* Z, void* H,
+             void* Yp, hipStream_t st, void* const* ev) {
+  using T = typename S::T;
+  const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
+  TPMLP_TRY(record(ev, 0, st));
+  // F1: Z = X A_i + b1 (and H = gelu(Z)); P = X [T,h] k-contiguous, Q = A_i [h,f] n-contiguous
+  TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, f, h, X, h, A, f,
+                                             EpiBiasGelu<S>{(const T*)b1, (T*)Z, (T*)H, f}, st)));
+  TPMLP_TRY(record(ev, 1, st));
+  // F2: Yp = H B_i (gelu(Z) on load when H is not kept); P [T,f] k-contiguous, Q = B_i [f,h] n-contiguous
+  if (H)
+    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, h, f, H, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
+  else
+    TPMLP_HIP((run_gemm<S, true, false, true>(s.dtype, Tn, h, f, Z, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
+  TPMLP_TRY(record(ev, 2, st));
+  return TPMLP_OK;
+}
+
+template <class S>
+int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A, const void* B, const void* Z,
+             const void* H, void* dZ, void* dXp, void* dA, void* dB, void* db1, const WsLayout& w, void* ws,
+             hipStream_t st, void* const* ev) {
+  using T = typename S::T;
+  const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
+  char* wsb = static_cast<char*>(ws);
+  if (!dZ && w.dz_bytes) dZ = wsb + w.dz_off;
+  float* part = w.part_bytes ? reinterpret_cast<float*>(wsb + w.part_off) : nullptr;
+
+  TPMLP_TRY(record(ev, 0, st));
+  // B1: dZ = (dY B_i^T) * gelu'(Z), plus per-tile column sums; Q[k][n] = B_i[n][k] is k-contiguous
+  TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, dY, h, B, h,
+                                            EpiGeluGrad<S>{(const T*)Z, (T*)dZ, part, f}, st)));
+  TPMLP_TRY(record(ev, 1, st));
+  // B5: db1 = sum of the column partials
+  if (f > 0) {
+    hipLaunchKernelGGL((db1_finish_kernel<S>), dim3((unsigned)ceil_div(f, 256)), dim3(256), 0, st, part,
+                       w.part_tiles, f, (T*)db1);
+    TPMLP_HIP(hipGetLastError());
+  }
+  TPMLP_TRY(record(ev, 2, st));
+  // B2: dB = H^T dY; P[m=f][k=T] = H[k][m] and Q = dY are both mn-contiguous
+  if (H)
+    TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
+  else
+    TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
+  TPMLP_TRY(record(ev, 3, st));
+  // B3: dA = X^T dZ; both operands mn-contiguous
+  TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, EpiStore<S>{(T*)dA, f}, st)));
+  TPMLP_TRY(record(ev, 4, st));
+  // B4: dXp = dZ A_i^T; Q[k=f][n=h] = A_i[n][k] is k-contiguous
+  TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, dZ, f, A, f, EpiStore<S>{(T*)dXp, h}, st)));
+  TPMLP_TRY(record(ev, 5, st));
+  return TPMLP_OK;
+}
+
+}  // namespace
+}  // namespace tpmlp
+
+using namespace tpmlp;
+
+extern "C" {
+
+int tp_mlp_abi_version(void) { return TPMLP_ABI_VERSION; }
+
+const char* tp_mlp_status_string(int status) {
+  switch (status) {
+    case TPMLP_OK: return "ok";
+    case TPMLP_ERR_NULL: return "a required pointer is NULL";
+    case TPMLP_ERR_SHAPE: return "invalid shape";
+    case TPMLP_ERR_ALIGN: return "pointer not 16-byte aligned or dimension not a multiple of 8 (4 for fp32)";
+    case TPMLP_ERR_DTYPE: return "unknown dtype";
+    case TPMLP_ERR_WORKSPACE: return "workspace too small";
+    case TPMLP_ERR_HIP: return "HIP error";
+    case TPMLP_ERR_ALIAS: return "an output overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, int dz_in_workspace) {
+  if (check_shape(shape) != TPMLP_OK) return 0;
+  return ws_layout(*shape, dz_in_workspace != 0).total;
+}
+
+int tp_mlp_fwd(const tpmlp_shape* shape, const void* X, const void* A, const void* b1, const void* B, void* Z,
+               void* H, void* Yp, void* stream, void* const* events) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  const size_t e = elt_size(s.dtype);
+  const size_t Th = (size_t)(s.tokens * s.hidden) * e, hf = (size_t)(s.hidden * s.ffn_shard) * e,
+               Tf = (size_t)(s.tokens * s.ffn_shard) * e, fb = (size_t)s.ffn_shard * e;
+  const Span in[4] = {{X, Th}, {A, hf}, {b1, fb}, {B, hf}};
+  const bool in_req[4] = {true, true, true, true};
+  const Span out[3] = {{Z, Tf}, {H, Tf}, {Yp, Th}};
+  const bool out_req[3] = {true, false, true};
+  TPMLP_TRY(check_buffers(in, 4, in_req, out, 3, out_req));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (s.dtype) {
+    case TPMLP_F32: return fwd_impl<StoreF32>(s, X, A, b1, B, Z, H, Yp, st, events);
+    case TPMLP_F16: return fwd_impl<StoreF16>(s, X, A, b1, B, Z, H, Yp, st, events);
+    default: return fwd_impl<StoreBF16>(s, X, A, b1, B, Z, H, Yp, st, events);
+  }
+}
+
+int tp_mlp_bwd(const tpmlp_shape* shape, const void* dY, const void* X, const void* A, const void* B,
+               const void* Z, const void* H, void* dZ, void* dXp, void* dA, void* dB, void* db1, void* ws,
+               size_t ws_bytes, void* stream, void* const* events) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  const size_t e = elt_size(s.dtype);
+  const size_t Th = (size_t)(s.tokens * s.hidden) * e, hf = (size_t)(s.hidden * s.ffn_shard) * e,
+               Tf = (size_t)(s.tokens * s.ffn_shard) * e, fb = (size_t)s.ffn_shard * e;
+  const WsLayout w = ws_layout(s, dZ == nullptr);
+  const Span in[6] = {{dY, Th}, {X, Th}, {A, hf}, {B, hf}, {Z, Tf}, {H, Tf}};
+  const bool in_req[6] = {true, true, true, true, true, false};
+  const Span out[6] = {{dZ, Tf}, {dXp, Th}, {dA, hf}, {dB, hf}, {db1, fb}, {ws, w.total}};
+  const bool out_req[6] = {false, true, true, true, true, true};
+  TPMLP_TRY(check_buffers(in, 6, in_req, out, 6, out_req));
+  if (ws_bytes < w.total) return TPMLP_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (s.dtype) {
+    case TPMLP_F32: return bwd_impl<StoreF32>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, st, events);
+    case TPMLP_F16: return bwd_impl<StoreF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, st, events);
+    default: return bwd_impl<StoreBF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, st, events);
+  }
+}
+
+}  // extern "C"

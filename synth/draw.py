@@ -7,6 +7,8 @@ results beyond the largest finite value become +-inf. It is carried out in
 float64, where every step below is exact, so fp64 -> fp16 and fp64 -> bf16
 are each rounded once (no double rounding through fp32).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -100,29 +102,60 @@ class Inputs:
         return self.X.shape[1]
 
 
-def _normal(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float64)
-    if sigma != 1.0:
-        x *= sigma
-    return round_to_storage(x, dtype, out=x)
+# Draws are made in chunks of DRAW_CHUNK consecutive (row-major) elements;
+# chunk c of tensor t comes from its own PCG64 stream seeded with the entropy
+# (seed, t, c), so chunks can be drawn in parallel and the values do not
+# depend on the number of threads.
+DRAW_CHUNK = 1 << 22
+TENSOR_IDS = {"X": 0, "A": 1, "b1": 2, "B": 3, "dY": 4}
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normal(seed: int, tensor: str, shape, sigma: float, dtype: str) -> np.ndarray:
+    out = np.empty(shape, dtype=np.float64)
+    flat = out.reshape(-1)
+    tid = TENSOR_IDS[tensor]
+
+    def fill(c: int) -> None:
+        seg = flat[c * DRAW_CHUNK:(c + 1) * DRAW_CHUNK]
+        rng = np.random.Generator(np.random.PCG64([seed, tid, c]))
+        rng.standard_normal(out=seg, dtype=np.float64)
+        if sigma != 1.0:
+            seg *= sigma
+        round_to_storage(seg, dtype, out=seg)
+
+    n_chunks = (flat.size + DRAW_CHUNK - 1) // DRAW_CHUNK
+    if n_chunks <= 1:
+        for c in range(n_chunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(fill, range(n_chunks)))
+    return out
 
 
 def draw_inputs(tokens: int, hidden: int, ffn: int, dtype: str, *, seed: int = 0,
                 sigma_x: float = 1.0, sigma_w: float = 0.02, sigma_b: float = 0.01,
                 sigma_dy: float = 0.01, tp: int = 1, full: bool = False) -> Inputs:
-    """Draw X [T,h], A [h,ffn], b1 [ffn], B [ffn,h], dY [T,h] in that order.
+    """Draw X [T,h], A [h,ffn], b1 [ffn], B [ffn,h], dY [T,h].
 
-    PCG64 seeded with `seed`; every tensor is i.i.d. N(0, sigma^2), drawn in
-    float64 and rounded to nearest-even into `dtype`. `ffn` is the width of
-    what is drawn: the full FFN when full=True (shards are sliced later),
-    otherwise the shard width f.
+    Every tensor is i.i.d. N(0, sigma^2), drawn in float64 from PCG64 streams
+    keyed by (seed, tensor, chunk) and rounded to nearest-even into `dtype`.
+    `ffn` is the width of what is drawn: the full FFN when full=True (shards
+    are sliced later), otherwise the shard width f.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
-    X = _normal(rng, (tokens, hidden), sigma_x, dtype)
-    A = _normal(rng, (hidden, ffn), sigma_w, dtype)
-    b1 = _normal(rng, (ffn,), sigma_b, dtype)
-    B = _normal(rng, (ffn, hidden), sigma_w, dtype)
-    dY = _normal(rng, (tokens, hidden), sigma_dy, dtype)
+    X = _normal(seed, "X", (tokens, hidden), sigma_x, dtype)
+    A = _normal(seed, "A", (hidden, ffn), sigma_w, dtype)
+    b1 = _normal(seed, "b1", (ffn,), sigma_b, dtype)
+    B = _normal(seed, "B", (ffn, hidden), sigma_w, dtype)
+    dY = _normal(seed, "dY", (tokens, hidden), sigma_dy, dtype)
     return Inputs(dtype, X, A, b1, B, dY, tp=tp, full=full)
 
 

@@ -116,10 +116,21 @@ def test_draws_are_seeded_and_ordered():
     for k in ("X", "A", "b1", "B", "dY"):
         assert np.array_equal(getattr(a, k), getattr(b, k))
     assert not np.array_equal(a.X, c.X)
-    # draw order X, A, b1, B, dY from one PCG64 stream
-    rng = np.random.Generator(np.random.PCG64(0))
-    X = rng.standard_normal((16, 8))
-    A = rng.standard_normal((8, 24)) * 0.02
+    # each tensor chunk comes from its own PCG64 stream keyed (seed, tensor, chunk)
+    X = np.random.Generator(np.random.PCG64([0, 0, 0])).standard_normal((16, 8))
+    A = np.random.Generator(np.random.PCG64([0, 1, 0])).standard_normal((8, 24)) * 0.02
     assert np.array_equal(a.X, round_to_storage(X, "bf16"))
     assert np.array_equal(a.A, round_to_storage(A, "bf16"))
     assert a.X.std() > 0.5 and a.A.std() < 0.05
+
+
+def test_chunked_draws_do_not_depend_on_threads(monkeypatch):
+    from synth import draw as d
+    monkeypatch.setattr(d, "DRAW_CHUNK", 64)
+    a = synth.draw_inputs(40, 16, 24, "f16", seed=3)
+    monkeypatch.setattr(d, "_threads", lambda: 1)
+    b = synth.draw_inputs(40, 16, 24, "f16", seed=3)
+    assert np.array_equal(a.X, b.X) and np.array_equal(a.dY, b.dY)
+    # chunk 1 of X is the second stream of the X tensor
+    x1 = np.random.Generator(np.random.PCG64([3, 0, 1])).standard_normal(64)
+    assert np.array_equal(a.X.reshape(-1)[64:128], round_to_storage(x1, "f16"))
