@@ -1,0 +1,367 @@
+// Direct-to-LDS MFMA GEMM engine for gfx950: C[M][N] = sum_k P[m][k] Q[k][n]
+// with 16-bit operands and fp32 accumulation in v_mfma_f32_32x32x16_{f16,bf16}.
+//
+// This is the engine for large tiles. Operand tiles travel from HBM/L2
+// straight into LDS with buffer_load_dwordx4 ... lds: no VGPRs hold staged
+// data, no ds_write is issued, and rows or k-chunks outside the matrix are
+// zero-filled by the buffer unit's range check (num_records) instead of by
+// branches.
+//
+// Operand layouts. Each operand is either k-contiguous ("KC": P[m][k] at
+// p[m*ld + k], Q[k][n] at q[n*ld + k]) or mn-contiguous ("MC": P[m][k] at
+// p[k*ld + m], Q[k][n] at q[k*ld + n]).
+//
+// LDS is a ring of STAGES k-tiles (BK deep); P's stages come first, then Q's:
+//   [P stage 0 .. P stage S-1][Q stage 0 .. Q stage S-1]
+//   KC tile: [rows][BK], rows of BK/8 16-byte chunks; chunk c of row r sits
+//            at c ^ sk(r): sk(r) = (r & 7) ^ ((r >> 3) & 1) for BK = 64,
+//            ((r >> 1) ^ (r >> 3)) & 3 for BK = 32.
+//   MC tile: [BK][R], k-rows of R/16 32-byte units; unit u of k-row k sits
+//            at u ^ sm(k), sm(k) = (k & 3) ^ ((k & 3) << 1) (mod 8).
+// A fragment read by 8 or 16 consecutive lanes (KC, ds_read_b128) and by 16
+// or 32 consecutive lanes (MC, ds_read_b64_tr_b16) touches distinct banks
+// under either swizzle, and both depend only on the lane, so every fragment
+// of a wave is addressed as a per-lane base register plus an immediate.
+//
+// A direct LDS load writes the 16 bytes of lane l at offset 16 l of a 1 KB
+// block, so the swizzle is applied on the global side: lane l fetches the
+// logical chunk that belongs at its fixed LDS slot.
+//
+// MFMA: v_mfma_f32_32x32x16_{bf16,f16}. Lane l supplies row (A) / column (B)
+// l % 32 and the eight k values 8 (l / 32) .. 8 (l / 32) + 7, and holds the
+// results C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15. A fragment
+// comes from a KC tile with one ds_read_b128 and from an MC tile with two
+// ds_read_b64_tr_b16 transposing reads. (The 16x16x32 form is avoided: the
+// compiler does not accumulate it in place, and copies every accumulator
+// once per use.)
+//
+// Pipeline. Tile t lives in stage t % S and is consumed in BK/16 substeps
+// (fragments double-buffered in registers). The prologue issues tiles
+// 0..S-1; iteration t then does
+//   read frags (t, 1)        | MFMAs (t, 0)
+//   ...
+//   read frags (t, last)     | MFMAs (t, last-1)
+//   -- wait until tile t+1 has landed (later tiles may still be in flight),
+//      barrier: every wave is done with stage t % S --
+//   load tile t+S into stage t % S
+//   read frags (t+1, 0)      | MFMAs (t, last)
+// so LDS reads overlap MFMAs and a tile's global loads have S-1 iterations
+// of MFMA work to land.
+//
+// Workgroup -> tile order: see map_tile (XCD-contiguous ranges, walked GROUP
+// tile-rows at a time).
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_mfma.hpp"
+
+namespace tpmlp {
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+struct DmaTile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M_ * WAVES_N_;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int LDS_P = BM * BK * 2, LDS_Q = BN * BK * 2;  // one stage
+  static constexpr int Q_OFF = STAGES * LDS_P;
+  static constexpr int LDS_BYTES = STAGES * (LDS_P + LDS_Q);
+  // direct loads (1 KB blocks) per wave per stage
+  static constexpr int LP = LDS_P / 1024 / WAVES, LQ = LDS_Q / 1024 / WAVES;
+  static constexpr int GROUP = 8;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(LP * WAVES * 1024 == LDS_P && LQ * WAVES * 1024 == LDS_Q, "tile not divisible into 1 KB blocks");
+  static_assert(BM >= 128 && BN >= 128 && BM <= 512 && BN <= 512, "MC tiles need 8..32 32-byte units per k-row");
+  static_assert(STAGES >= 2, "at least two stages");
+  static_assert(BK == 32 || BK == 64, "k-tiles of 32 or 64 (an even number of 16-wide substeps)");
+  static_assert(BK == 32 || WAVES % 2 == 0, "64-deep KC tiles need an even number of waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KB per workgroup");
+};
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most N vector
+// memory operations of this wave are outstanding: vmcnt in bits 3:0 and
+// 15:14, expcnt (bits 6:4) and lgkmcnt (bits 11:8) left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Offsets beyond every buffer's num_records: the load returns zeros.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+template <int BK>
+__device__ __forceinline__ int dsk(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+  return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+__device__ __forceinline__ int dsm(int k) { return ((k & 3) ^ ((k & 3) << 1)) & 7; }
+
+// Raw buffer resource (stride 0) over `bytes` bytes at `p`, built from
+// wave-uniform values so that it lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7fffffff ? bytes : 0x7fffffff));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+}
+
+// Source of the 16 bytes that lane `lane` writes in 1 KB block `blk` of an
+// operand tile: element offset from the tile origin at k = 0 (`rel`), the
+// tile-local row (KC) or column (MC) index `mn`, and the k offset `kk`.
+template <bool KC, int R, int BK>
+__device__ __forceinline__ void dma_slot(int blk, int lane, int64_t ld, int64_t& rel, int& mn, int& kk) {
+  if constexpr (KC) {
+    constexpr int CH = BK / 8;                // 16-byte chunks per row
+    const int r = blk * (64 / CH) + lane / CH;  // 1024 / (2 BK) rows per block
+    const int kc = (lane % CH) ^ dsk<BK>(r);
+    mn = r;
+    kk = kc * 8;
+    rel = (int64_t)r * ld + kk;
+  } else {
+    const int o = blk * 1024 + lane * 16;
+    const int kr = o / (R * 2), w = o % (R * 2);
+    const int u = (w >> 5) ^ dsm(kr);
+    const int c8 = 2 * u + ((w >> 4) & 1);
+    mn = c8 * 8;
+    kk = kr;
+    rel = (int64_t)kr * ld + mn;
+  }
+}
+
+// k offset of direct load c's chunk relative to load 0's (same lane). KC:
+// the chunk's k depends on the row only through r & 15, and load c's rows
+// are c * WAVES * 1024 / (2 BK) further on: a multiple of 16 (for BK = 64
+// because WAVES is even). MC: each load covers 1024 / (2R) k-rows.
+template <bool KC, int R, int WAVES>
+__host__ __device__ constexpr int dma_kstep(int c) {
+  return KC ? 0 : c * WAVES * (1024 / (2 * R));
+}
+
+// Per-lane LDS byte offsets of a wave's MFMA fragments (relative to the LDS
+// base; they start in stage 0 and step through the ring). NF fragments of
+// 32 rows (KC) or 32 columns (MC), the first at tile row / column `first`
+// (a multiple of 32).
+template <bool KC, int R, int BK, int NF>
+struct FragAddr {
+  static constexpr int NB = KC ? BK / 16 : NF;
+  uint32_t base[NB];
+
+  __device__ __forceinline__ void init(int lane, int region, int first) {
+    if constexpr (KC) {
+      // row first + 32 i + (l & 31); 16-byte chunk 2 ks + (l >> 5)
+      const int r = lane & 31;
+#pragma unroll
+      for (int ks = 0; ks < NB; ++ks)
+        base[ks] = (uint32_t)(region + (first + r) * (2 * BK) + (((2 * ks + (lane >> 5)) ^ dsk<BK>(r)) << 4));
+    } else {
+      // lanes 16 G .. 16 G + 15: 32-byte unit first/16 + 2 i + (G & 1),
+      // k-rows 16 ks + 8 (G >> 1) + 4 hh + (j >> 2), 8-byte piece j & 3
+      const int G = lane >> 4, j = lane & 15;
+      const int kr = 8 * (G >> 1) + (j >> 2);
+      const int u0 = first >> 4;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        base[i] = (uint32_t)(region + kr * (R * 2) + (((u0 + 2 * i + (G & 1)) ^ dsm(kr)) << 5) + ((j & 3) << 3));
+    }
+  }
+
+  // Move every base by `delta` bytes (to the next stage of the ring).
+  __device__ __forceinline__ void advance(uint32_t delta) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) base[i] += delta;
+  }
+
+  // Fragment I for k-substep KS (16 wide) of the stage the bases point at.
+  template <int I, int KS>
+  __device__ __forceinline__ u32x4 read(const char* lds) const {
+    if constexpr (KC) {
+      return *reinterpret_cast<const u32x4*>(lds + base[KS] + I * 32 * (2 * BK));
+    } else {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      u32x4 out;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(lds + base[I] + (KS * 16 + hh * 4) * (R * 2)));
+        const u32x2 w = __builtin_bit_cast(u32x2, v);
+        out[2 * hh] = w[0];
+        out[2 * hh + 1] = w[1];
+      }
+      return out;
+    }
+  }
+};
+
+template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi>
+__global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg::WAVES / 4, Cfg::WAVES / 4)))
+void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES;
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  int split, tm, tn;
+  map_tile<Cfg::GROUP>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t kbeg = (int64_t)split * sh.k_per;
+  const int64_t kend = min(sh.K, kbeg + sh.k_per);
+  const int kspan = kend > kbeg ? (int)(kend - kbeg) : 0;
+  const int nk = (kspan + BK - 1) / BK;
+
+  // Buffer resources based at the tile origin; num_records is the operand's
+  // extent from there, so any offset past the tensor reads zeros.
+  const int64_t pbase = P_KC ? m0 * P.ld : m0, qbase = Q_KC ? n0 * Q.ld : n0;
+  const __amdgpu_buffer_rsrc_t prs = uniform_rsrc(P.ptr + pbase, (p_extent - pbase) * 2);
+  const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(Q.ptr + qbase, (q_extent - qbase) * 2);
+
+  // Per-lane byte offsets from the tile origin at k = 0, loop-invariant;
+  // rows / columns outside the matrix get kOobOffset. The k advance of each
+  // tile goes in the instruction's scalar offset, so the K loop does no
+  // per-lane address arithmetic. pk0 / qk0: the k offset (within a tile) of
+  // load 0's chunk; load c's is that plus dma_kstep<>(c).
+  uint32_t pv[LP], qv[LQ];
+  int pk0 = 0, qk0 = 0;
+  static_for<0, LP>([&](auto c) {
+    int64_t rel;
+    int mn, kk;
+    dma_slot<P_KC, BM, BK>(c * Cfg::WAVES + wave, lane, P.ld, rel, mn, kk);
+    pv[c] = m0 + mn < sh.M ? (uint32_t)rel * 2u : kOobOffset;
+    if constexpr (c == 0) pk0 = kk;
+  });
+  static_for<0, LQ>([&](auto c) {
+    int64_t rel;
+    int mn, kk;
+    dma_slot<Q_KC, BN, BK>(c * Cfg::WAVES + wave, lane, Q.ld, rel, mn, kk);
+    qv[c] = n0 + mn < sh.N ? (uint32_t)rel * 2u : kOobOffset;
+    if constexpr (c == 0) qk0 = kk;
+  });
+
+  typedef __attribute__((address_space(3))) void lds_void;
+  // Direct loads of k-tile t into its stage. On a K-tail tile, chunks at or
+  // beyond kend take kOobOffset (one 32-bit compare per load).
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
+    const int stage = t % ST;
+    const int64_t k0 = kbeg + (int64_t)t * BK;
+    const int psoff = __builtin_amdgcn_readfirstlane((int)((P_KC ? k0 : k0 * P.ld) * 2));
+    const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
+    const int krem = kspan - t * BK;  // k extent left from this tile on
+    static_for<0, LP>([&](auto c) {
+      const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          prs, (lds_void*)(smem + stage * Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024), 16, off, psoff, 0, 0);
+    });
+    static_for<0, LQ>([&](auto c) {
+      const uint32_t off = qk0 + dma_kstep<Q_KC, BN, Cfg::WAVES>(c) < krem ? qv[c] : kOobOffset;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (lds_void*)(smem + Cfg::Q_OFF + stage * Cfg::LDS_Q + (c * Cfg::WAVES + wave) * 1024), 16, off,
+          qsoff, 0, 0);
+    });
+  };
+  // Wait until at most `tiles` k-tiles of this wave's loads are in flight.
+  auto wait_tiles = [&](int tiles) __attribute__((always_inline)) {
+    static_for<0, ST - 1>([&](auto a) {
+      if (tiles == a) wait_vmcnt<a * (LP + LQ)>();
+    });
+  };
+
+  FragAddr<P_KC, BM, BK, FM> pa;
+  FragAddr<Q_KC, BN, BK, FN> qa;
+  pa.init(lane, 0, wm * Cfg::WTM);
+  qa.init(lane, Cfg::Q_OFF, wn * Cfg::WTN);
+
+  f32x16 acc[FM][FN];
+  static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
+
+  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto read_frags = [&](u32x4(&fa)[FM], u32x4(&fb)[FN], auto ks_c) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks_c)::value;
+    static_for<0, FM>([&](auto i) { fa[i] = pa.template read<i, KS>(smem); });
+    static_for<0, FN>([&](auto j) { fb[j] = qa.template read<j, KS>(smem); });
+  };
+  auto mfmas = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN]) __attribute__((always_inline)) {
+    static_for<0, FM>([&](auto i) {
+      static_for<0, FN>([&](auto j) { acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]); });
+    });
+  };
+  constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
+
+  // One straight-line loop body (no branch touches the accumulators, so
+  // they keep their registers). The last iteration reads fragments of a
+  // stage nothing will use again: in bounds, and discarded.
+  if (nk > 0) {
+    for (int t = 0; t < ST && t < nk; ++t) issue_tile(t);
+    wait_tiles(min(ST, nk) - 1);
+    __syncthreads();
+    read_frags(fa0, fb0, std::integral_constant<int, 0>{});
+    for (int t = 0; t < nk; ++t) {
+      static_for<0, NKS - 1>([&](auto ks) {
+        if constexpr (ks % 2 == 0) {
+          read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+          mfmas(fa0, fb0);
+        } else {
+          read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+          mfmas(fa1, fb1);
+        }
+      });
+      // Tile t+1 must have landed; tiles t+2 .. min(t+S-1, nk-1) may still
+      // be in flight. The barrier also orders every wave's reads of stage
+      // t % S before the loads that refill it. (__syncthreads does not wait
+      // for direct-to-LDS loads by itself: the compiler sees them as global
+      // reads only.)
+      wait_tiles(max(0, min(ST - 2, nk - 2 - t)));
+      __syncthreads();
+      if (t + ST < nk) issue_tile(t + ST);
+      const bool wrap = (t + 1) % ST == 0;
+      pa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_P) : (uint32_t)Cfg::LDS_P);
+      qa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_Q) : (uint32_t)Cfg::LDS_Q);
+      read_frags(fa0, fb0, std::integral_constant<int, 0>{});
+      mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
+    }
+  }
+
+  // Epilogue. Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each
+  // 32x32 fragment, r = 0..15.
+  float cs[FN];
+  static_for<0, FN>([&](auto j) { cs[j] = 0.0f; });
+  static_for<0, FM>([&](auto i) {
+    static_for<0, FN>([&](auto j) {
+      const int64_t n = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+      static_for<0, 16>([&](auto r) {
+        const int64_t m = m0 + wm * Cfg::WTM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+        if (m < sh.M && n < sh.N) cs[j] += epi.apply(m, n, acc[i][j][(int)r]);
+      });
+    });
+  });
+  if constexpr (Epi::kColSum) {
+    // Column sums of this tile, in a fixed order: the two lane halves, then
+    // the waves along M.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);  // [WAVES_M][BN]
+    static_for<0, FN>([&](auto j) { cs[j] += __shfl_xor(cs[j], 32); });
+    if (lane < 32) static_for<0, FN>([&](auto j) { red[wm * BN + wn * Cfg::WTN + j * 32 + lane] = cs[j]; });
+    __syncthreads();
+    for (int c = tid; c < BN; c += Cfg::THREADS) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < Cfg::WAVES_M; ++w) s += red[w * BN + c];
+      if (n0 + c < sh.N) epi.colsum(tm, n0 + c, s);
+    }
+  }
+}
+
+}  // namespace tpmlp

@@ -12,6 +12,7 @@
 
 #include "tp_mlp.h"
 #include "epilogues.hpp"
+#include "gemm_dma.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_simt.hpp"
 
@@ -29,10 +30,11 @@ __global__ __launch_bounds__(256) void db1_finish_kernel(const float* partial, i
   db1[n] = S::from_f(s);
 }
 
-enum class Engine { Simt, Mfma128, Mfma256 };
+enum class Engine { Simt, Mfma128, Mfma256, Dma256 };
 
 using Cfg128 = MfmaTile<128, 128, 2, 2>;
 using Cfg256 = MfmaTile<256, 256, 2, 4>;
+using CfgD256 = DmaTile<256, 256, 2, 4, 64, 2>;
 
 struct Plan {
   Engine eng;
@@ -42,31 +44,36 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tile choice for the 16-bit engine: 256x256 tiles once they give at least
-// two full waves over the 256 CUs, else 128x128. TPMLP_TILE=128 or 256 in
-// the environment forces one size (read on every call; for tuning and tests).
-bool use_big_tiles(int64_t M, int64_t N) {
+// Largest operand (in elements) the direct-load engine addresses: byte
+// offsets within one operand stay below 2^31.
+constexpr int64_t kDmaMaxElems = (int64_t(1) << 30) - (int64_t(1) << 20);
+
+// Tile choice for the 16-bit engines. Large tiles (256x256) once they give
+// at least two full waves over the 256 CUs, else 128x128. Large tiles use the
+// direct-to-LDS engine unless P needs the GeLU applied on load (that engine
+// has no register stage to apply it in) or an operand is too large for its
+// 32-bit offsets. TPMLP_TILE=128, 256 (register-staged) or dma256 in the
+// environment forces one engine where it applies (read on every call; for
+// tuning and tests).
+Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p) {
+  const bool dma_fits = !gelu_p && M * K <= kDmaMaxElems && N * K <= kDmaMaxElems;
   if (const char* e = std::getenv("TPMLP_TILE")) {
-    if (!std::strcmp(e, "128")) return false;
-    if (!std::strcmp(e, "256")) return true;
+    if (!std::strcmp(e, "128")) return Engine::Mfma128;
+    if (!std::strcmp(e, "256")) return Engine::Mfma256;
+    if (!std::strcmp(e, "dma256")) return dma_fits ? Engine::Dma256 : Engine::Mfma256;
   }
-  return ceil_div(M, 256) * ceil_div(N, 256) >= 512;
+  if (ceil_div(M, 256) * ceil_div(N, 256) >= 512) return dma_fits ? Engine::Dma256 : Engine::Mfma256;
+  return Engine::Mfma128;
 }
 
-Plan plan_gemm(int dtype, int64_t M, int64_t N) {
+Plan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool gelu_p) {
   Plan p;
-  if (dtype == TPMLP_F32) {
-    p.eng = Engine::Simt;
-    p.bm = SimtTile::BM;
-    p.bn = SimtTile::BN;
-  } else if (use_big_tiles(M, N)) {
-    p.eng = Engine::Mfma256;
-    p.bm = Cfg256::BM;
-    p.bn = Cfg256::BN;
-  } else {
-    p.eng = Engine::Mfma128;
-    p.bm = Cfg128::BM;
-    p.bn = Cfg128::BN;
+  p.eng = dtype == TPMLP_F32 ? Engine::Simt : pick_engine(M, N, K, gelu_p);
+  switch (p.eng) {
+    case Engine::Simt: p.bm = SimtTile::BM; p.bn = SimtTile::BN; break;
+    case Engine::Mfma128: p.bm = Cfg128::BM; p.bn = Cfg128::BN; break;
+    case Engine::Mfma256: p.bm = Cfg256::BM; p.bn = Cfg256::BN; break;
+    case Engine::Dma256: p.bm = CfgD256::BM; p.bn = CfgD256::BN; break;
   }
   p.tiles_m = (int)ceil_div(M, p.bm);
   p.tiles_n = (int)ceil_div(N, p.bn);
@@ -82,23 +89,37 @@ void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q,
                      epi);
 }
 
+template <class Cfg, class S, bool PK, bool QK, class Epi>
+void launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const void* q, int64_t ldq, const Epi& epi,
+                hipStream_t st) {
+  const int nblk = sh.tiles_m * sh.tiles_n * sh.splits;
+  hipLaunchKernelGGL((gemm_dma_kernel<Cfg, S, PK, QK, Epi>), dim3(nblk), dim3(Cfg::THREADS), 0, st, sh,
+                     Operand{static_cast<const uint16_t*>(p), ldp}, sh.M * sh.K,
+                     Operand{static_cast<const uint16_t*>(q), ldq}, sh.N * sh.K, epi);
+}
+
 // C[M][N] = sum_k P[m][k] Q[k][n] through epilogue `epi`; PK / QK select the
-// k-contiguous layout of P / Q, GP applies gelu to P as it is loaded.
+// k-contiguous layout of P / Q, GP applies gelu to P as it is loaded. Every
+// operand is dense: its leading dimension is its contiguous extent (K for a
+// k-contiguous operand, M or N otherwise).
 template <class S, bool PK, bool QK, bool GP, class Epi>
 hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q,
                     int64_t ldq, const Epi& epi, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  const Plan pl = plan_gemm(dtype, M, N);
+  const Plan pl = plan_gemm(dtype, M, N, K, GP);
   GemmShape sh{M, N, K, pl.tiles_m, pl.tiles_n, 1, std::max<int64_t>(K, 1)};
   if constexpr (std::is_same_v<S, StoreF32>) {
     hipLaunchKernelGGL((gemm_simt_kernel<PK, QK, GP, Epi>), dim3(pl.tiles_m * pl.tiles_n), dim3(SimtTile::THREADS),
                        0, st, sh, OperandF32{static_cast<const float*>(p), ldp},
                        OperandF32{static_cast<const float*>(q), ldq}, epi);
   } else {
-    if (pl.eng == Engine::Mfma256)
-      launch_mfma<Cfg256, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st);
-    else
-      launch_mfma<Cfg128, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st);
+    switch (pl.eng) {
+      case Engine::Dma256:
+        if constexpr (!GP) launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, st);
+        break;
+      case Engine::Mfma256: launch_mfma<Cfg256, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st); break;
+      default: launch_mfma<Cfg128, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st); break;
+    }
   }
   return hipGetLastError();
 }
@@ -179,7 +200,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const tpmlp_shape& s, bool dz_in_ws) {
   WsLayout w{};
-  const Plan b1 = plan_gemm(s.dtype, s.tokens, s.ffn_shard);
+  const Plan b1 = plan_gemm(s.dtype, s.tokens, s.ffn_shard, s.hidden, false);
   w.part_tiles = (s.tokens > 0 && s.ffn_shard > 0) ? b1.tiles_m : 0;
   w.dz_off = 0;
   w.dz_bytes = dz_in_ws ? (size_t)(s.tokens * s.ffn_shard) * elt_size(s.dtype) : 0;

@@ -45,7 +45,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("tile", [128, 256], indirect=True)
+@pytest.mark.parametrize("tile", [128, 256, "dma256"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,h,f", RAGGED)
 def test_ragged_shapes_16bit(gpu_lib, tile, dtype, T, h, f):
@@ -65,7 +65,7 @@ def test_ragged_shapes_fp32(gpu_lib, T, h, f):
     compare(got, ref, TOL["f32"])
 
 
-@pytest.mark.parametrize("tile", [128, 256], indirect=True)
+@pytest.mark.parametrize("tile", [128, 256, "dma256"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_without_h_and_dz_buffers(gpu_lib, tile, dtype):
     """H not kept (GeLU applied to Z on load) and dZ kept in the workspace."""
@@ -173,7 +173,7 @@ def test_deterministic_bitwise(gpu_lib):
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
 
 
-@pytest.mark.parametrize("tile", [128, 256], indirect=True)
+@pytest.mark.parametrize("tile", [128, 256, "dma256"], indirect=True)
 def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile):
     """Each output lives between two poisoned guard regions, which must
     survive forward + backward unchanged."""
