@@ -29,6 +29,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 FWD_STEPS = ["F1", "F2"]
 BWD_STEPS = ["B1", "B5", "B2", "B3", "B4"]
 GEMM_STEPS = ["F1", "F2", "B1", "B2", "B3", "B4"]
+PROFILE_TAG = {"gpt_h10240": "h10240_bf16"}
 
 
 def log(*a):
@@ -38,6 +39,38 @@ def log(*a):
 def workload_name(cfg):
     return (f"{cfg.name}: one TP={cfg.tp} shard of an MLP with hidden {cfg.hidden}, FFN {cfg.ffn}; "
             f"tokens {cfg.tokens} (micro-batch {cfg.micro_batch} x seq {cfg.seq_len}), shard width {cfg.ffn_shard}")
+
+
+def source_hash():
+    """sha256 over the HIP sources (csrc/*), in name order."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(cfg_name, step):
+    """HBM bytes per launch of `step` (read + write) from the rocprofv3 counter
+    summary of this workload under profiles/, or None when there is none or
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm_dma_{PROFILE_TAG.get(cfg_name, cfg_name)}.md")
+    if not os.path.exists(path):
+        return None
+    want, vals = None, {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-source-sha256:"):
+                want = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic "):
+                parts = line.split()
+                kv = dict(x.split("=") for x in parts[2:])
+                vals[parts[1]] = int(kv["read_bytes"]) + int(kv["write_bytes"])
+    if want != source_hash() or step not in vals:
+        return None
+    return vals[step]
 
 
 def blas_threads():
@@ -88,6 +121,9 @@ def main():
     ap.add_argument("--config", default="gpt_h10240")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warm-up, run one plain device copy of this many MiB (a known-size kernel that "
+                         "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share (one TP rank) only: the path has no cross-GPU step here. "
@@ -123,6 +159,16 @@ def main():
     def step(fe=None, be=None):
         tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, events=fe)
         tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read and written by one copy kernel")
+        del src, dst
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -182,7 +228,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(cfg.name, dom),
         },
         "cpu_baseline": None,
     }
