@@ -26,8 +26,8 @@ METRIC = "TFLOP/s + % MFMA peak, TP-shard MLP fwd+bwd (h=2560..10240), 1 MI355X"
 # Dense MFMA peaks of MI355X in TFLOP/s: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
 # for fp16/bf16; the fp32 figure is the vector (FMA) peak the fp32 path uses.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
-FWD_STEPS = ["F1", "F2"]
-BWD_STEPS = ["B1", "B5", "B2", "B3", "B4"]
+FWD_STEPS = ["TA", "F1", "TB", "F2"]                               # what the 5 forward events bracket
+BWD_STEPS = ["B1", "B5", "TH", "TdY", "B2", "TX", "TdZ", "B3", "B4"]  # ... and the 10 backward events
 GEMM_STEPS = ["F1", "F2", "B1", "B2", "B3", "B4"]
 PROFILE_TAG = {"gpt_h10240": "h10240_bf16"}
 
@@ -154,10 +154,12 @@ def main():
     code = {"f32": tpmlp.TPMLP_F32, "f16": tpmlp.TPMLP_F16, "bf16": tpmlp.TPMLP_BF16}[cfg.dtype]
     nws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code)
     ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    nfws = tpmlp.tp_mlp_fwd_workspace_bytes(T, h, f, code)
+    fws = torch.empty((nfws,), dtype=torch.uint8, device=dev) if nfws else None
+    log(f"workspace: forward {nfws / 2**20:.0f} MiB, backward {nws / 2**20:.0f} MiB")
 
     def step(fe=None, be=None):
-        tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, events=fe)
+        tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe)
         tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be)
 
     if args.copy_probe_mib:
@@ -176,8 +178,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(FWD_STEPS) + 1)] for _ in range(K)]
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_STEPS) + 1)] for _ in range(K)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -194,7 +196,7 @@ def main():
         for i, n in enumerate(BWD_STEPS):
             per[n] += bev[k][i].elapsed_time(bev[k][i + 1])
     per = {n: v / K for n, v in per.items()}
-    gpu_ms = fev[0][0].elapsed_time(bev[K - 1][5]) / K
+    gpu_ms = fev[0][0].elapsed_time(bev[K - 1][len(BWD_STEPS)]) / K
     ms = wall / K * 1e3
     flops = 12.0 * T * h * f
     value = flops / (ms * 1e-3) / 1e12

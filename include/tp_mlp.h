@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 1
+#define TPMLP_ABI_VERSION 2
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -97,12 +97,30 @@ int tp_mlp_abi_version(void);
 const char* tp_mlp_status_string(int status);
 
 /*
- * Bytes of device workspace tp_mlp_bwd needs for `shape` (0 if none; fp32
- * per-tile column partials of dZ for db1, and split-K partials). With
- * dz_in_workspace != 0 it also counts room for dZ_i, for callers that pass
- * dZ = NULL to tp_mlp_bwd. Returns 0 and sets nothing on an invalid shape.
+ * Device workspace. The library allocates nothing; both passes take a
+ * caller-owned workspace (16-byte aligned, contents on entry ignored, not
+ * overlapping any tensor argument).
+ *
+ * tp_mlp_fwd_workspace_bytes: bytes with which tp_mlp_fwd stages
+ * k-contiguous copies of A_i and B_i for the GEMMs that read them faster
+ * that way (0 if no GEMM of this shape does). tp_mlp_fwd accepts any size:
+ * with less than this (or NULL) it reads the weights in place, slower.
+ *
+ * tp_mlp_workspace_bytes: bytes for tp_mlp_bwd. Flags:
+ *   TPMLP_WS_DZ       room for dZ_i as well, for callers that pass dZ = NULL;
+ *   TPMLP_WS_MINIMAL  only what tp_mlp_bwd requires (fp32 per-tile column
+ *                     partials of dZ for db1, and dZ if TPMLP_WS_DZ).
+ * Without TPMLP_WS_MINIMAL the size also holds k-contiguous copies of H_i,
+ * dY, X and dZ_i (each [rows][tokens]) for the weight-gradient GEMMs;
+ * tp_mlp_bwd uses them when ws_bytes reaches that size, and otherwise reads
+ * the operands in place (slower). A workspace below the minimal size is
+ * TPMLP_ERR_WORKSPACE.
+ * Both return 0 and set nothing on an invalid shape.
  */
-size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, int dz_in_workspace);
+#define TPMLP_WS_DZ 1u
+#define TPMLP_WS_MINIMAL 2u
+size_t tp_mlp_fwd_workspace_bytes(const tpmlp_shape* shape);
+size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags);
 
 /*
  * Forward of one rank (Z_i, optional H_i, partial Yp_i); see the top of this
@@ -115,13 +133,17 @@ size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, int dz_in_workspace);
  *   H  [tokens, ffn_shard] out, may be NULL: gelu(Z_i). When NULL, the second
  *                          GEMM applies the GeLU to Z_i while loading it.
  *   Yp [tokens, hidden]    out  H_i B_i (partial over ranks, no b2)
- *   events: NULL, or 3 hipEvent_t recorded on `stream` before the first
- *           GEMM, between the two GEMMs and after the second (per-step
- *           timing for profilers and benchmarks).
+ *   ws, ws_bytes           workspace (see tp_mlp_fwd_workspace_bytes); may
+ *                          be NULL / 0.
+ *   events: NULL, or 5 hipEvent_t recorded on `stream`: before the first
+ *           kernel and after each of: A_i transpose (TA), first GEMM (F1),
+ *           B_i transpose (TB), second GEMM (F2). A transpose that does not
+ *           run leaves its two events back to back.
  */
 int tp_mlp_fwd(const tpmlp_shape* shape,
                const void* X, const void* A, const void* b1, const void* B,
                void* Z, void* H, void* Yp,
+               void* ws, size_t ws_bytes,
                void* stream, void* const* events);
 
 /*
@@ -130,20 +152,23 @@ int tp_mlp_fwd(const tpmlp_shape* shape,
  *   X, A, B                 in   as in tp_mlp_fwd
  *   Z   [tokens, ffn_shard] in   the forward's Z_i
  *   H   [tokens, ffn_shard] in, may be NULL: the forward's H_i. When NULL,
- *                           gelu(Z_i) is recomputed while loading Z_i.
+ *                           gelu(Z_i) is recomputed from Z_i.
  *   dZ  [tokens, ffn_shard] out, may be NULL: dZ_i. When NULL it is kept in
- *                           the workspace (size it with dz_in_workspace = 1).
+ *                           the workspace (size it with TPMLP_WS_DZ).
  *   dXp [tokens, hidden]    out  dZ_i A_i^T (partial over ranks)
  *   dA  [hidden, ffn_shard] out  X^T dZ_i
  *   dB  [ffn_shard, hidden] out  H_i^T dY
  *   db1 [ffn_shard]         out  column sums of dZ_i
- *   ws, ws_bytes            device workspace of at least
- *                           tp_mlp_workspace_bytes(shape, dZ == NULL) bytes,
- *                           16-byte aligned; may be NULL when that is 0. Its
- *                           contents on entry are ignored.
- *   events: NULL, or 6 hipEvent_t recorded on `stream` before the dZ GEMM
- *           and after each of: dZ GEMM (with the db1 column partials),
- *           db1 finish, dB GEMM, dA GEMM, dXp GEMM.
+ *   ws, ws_bytes            workspace of at least
+ *                           tp_mlp_workspace_bytes(shape, TPMLP_WS_MINIMAL |
+ *                           (dZ == NULL ? TPMLP_WS_DZ : 0)) bytes; may be
+ *                           NULL when that is 0.
+ *   events: NULL, or 10 hipEvent_t recorded on `stream`: before the first
+ *           kernel and after each of: dZ GEMM with the db1 column partials
+ *           (B1), db1 finish (B5), H_i transpose (TH), dY transpose (TdY),
+ *           dB GEMM (B2), X transpose (TX), dZ_i transpose (TdZ), dA GEMM
+ *           (B3), dXp GEMM (B4). A transpose that does not run leaves its
+ *           two events back to back.
  */
 int tp_mlp_bwd(const tpmlp_shape* shape,
                const void* dY, const void* X, const void* A, const void* B,

@@ -4,12 +4,16 @@ the C ABI in include/tp_mlp.h. This package is the ctypes binding to that
 library (libtpmlp.so, built in-tree by _build.build()).
 """
 from ._binding import (  # noqa: F401
+    BWD_EVENTS,
     EXPORTS,
+    FWD_EVENTS,
     LIB_PATH,
     STATUS,
     TPMLP_BF16,
     TPMLP_F16,
     TPMLP_F32,
+    TPMLP_WS_DZ,
+    TPMLP_WS_MINIMAL,
     TpMlpError,
     bwd,
     fwd,
@@ -17,6 +21,7 @@ from ._binding import (  # noqa: F401
     tp_mlp_abi_version,
     tp_mlp_bwd,
     tp_mlp_fwd,
+    tp_mlp_fwd_workspace_bytes,
     tp_mlp_status_string,
     tp_mlp_workspace_bytes,
 )

@@ -23,7 +23,11 @@ STATUS = {
     6: "TPMLP_ERR_HIP",
     7: "TPMLP_ERR_ALIAS",
 }
-EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd")
+EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
+           "tp_mlp_fwd", "tp_mlp_bwd")
+TPMLP_WS_DZ, TPMLP_WS_MINIMAL = 1, 2
+FWD_EVENTS = ("TA", "F1", "TB", "F2")                                     # steps bracketed by the 5 events
+BWD_EVENTS = ("B1", "B5", "TH", "TdY", "B2", "TX", "TdZ", "B3", "B4")    # ... by the 10 events
 
 
 class TpMlpError(RuntimeError):
@@ -53,10 +57,12 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_abi_version.argtypes = []
     lib.tp_mlp_status_string.restype = ctypes.c_char_p
     lib.tp_mlp_status_string.argtypes = [ctypes.c_int]
+    lib.tp_mlp_fwd_workspace_bytes.restype = sz
+    lib.tp_mlp_fwd_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape)]
     lib.tp_mlp_workspace_bytes.restype = sz
-    lib.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int]
+    lib.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_uint]
     lib.tp_mlp_fwd.restype = ctypes.c_int
-    lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd.restype = ctypes.c_int
     lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
     _lib = lib
@@ -117,23 +123,32 @@ def tp_mlp_status_string(status: int) -> str:
     return load().tp_mlp_status_string(status).decode()
 
 
-def tp_mlp_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int, dz_in_workspace: bool = False) -> int:
+def tp_mlp_fwd_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int) -> int:
     s = shape_of(tokens, hidden, ffn_shard, dtype)
-    return load().tp_mlp_workspace_bytes(ctypes.byref(s), int(bool(dz_in_workspace)))
+    return load().tp_mlp_fwd_workspace_bytes(ctypes.byref(s))
 
 
-def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, *, stream=None, events=None) -> None:
+def tp_mlp_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int, flags: int = 0) -> int:
+    s = shape_of(tokens, hidden, ffn_shard, dtype)
+    return load().tp_mlp_workspace_bytes(ctypes.byref(s), int(flags))
+
+
+def _nbytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None) -> None:
     """Forward of one TP rank into caller-allocated Z, H (or None) and Yp."""
     s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
     ev = _events(events)
     _check(load().tp_mlp_fwd(ctypes.byref(s), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),
-                             _stream(stream), ev))
+                             _ptr(ws), _nbytes(ws), _stream(stream), ev))
 
 
 def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None) -> None:
     """Backward of one TP rank into caller-allocated gradients and workspace."""
     s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    nbytes = _nbytes(ws)
     ev = _events(events)
     _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
                              _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
@@ -141,17 +156,22 @@ def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, even
 
 # ---- convenience wrappers that allocate the outputs with torch ----
 
-def fwd(X, A, b1, B, keep_h: bool = True, stream=None, events=None):
+def fwd(X, A, b1, B, keep_h: bool = True, staged: bool = True, stream=None, events=None):
+    """Allocate the outputs (and, if `staged`, the workspace) with torch and run tp_mlp_fwd."""
     import torch
     T, f, h = X.shape[0], A.shape[1], X.shape[1]
     Z = torch.empty((T, f), dtype=X.dtype, device=X.device)
     H = torch.empty((T, f), dtype=X.dtype, device=X.device) if keep_h else None
     Yp = torch.empty((T, h), dtype=X.dtype, device=X.device)
-    tp_mlp_fwd(X, A, b1, B, Z, H, Yp, stream=stream, events=events)
+    nws = tp_mlp_fwd_workspace_bytes(T, h, f, _dtype_code(X)) if staged else 0
+    ws = torch.empty((nws,), dtype=torch.uint8, device=X.device) if nws else None
+    tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws, stream=stream, events=events)
     return Z, H, Yp
 
 
-def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, stream=None, events=None):
+def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, stream=None, events=None):
+    """Allocate the gradients and the workspace (the staged size, or the
+    minimal one when `staged` is False) with torch and run tp_mlp_bwd."""
     import torch
     T, f, h = X.shape[0], A.shape[1], X.shape[1]
     dev, dt = X.device, X.dtype
@@ -160,7 +180,8 @@ def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, stream=None, events=None):
     dA = torch.empty((h, f), dtype=dt, device=dev)
     dB = torch.empty((f, h), dtype=dt, device=dev)
     db1 = torch.empty((f,), dtype=dt, device=dev)
-    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), dz_in_workspace=not keep_dz)
+    flags = (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
+    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags)
     ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
     tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events)
     return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}

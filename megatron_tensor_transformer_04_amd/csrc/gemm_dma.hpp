@@ -48,8 +48,7 @@
 // so LDS reads overlap MFMAs and a tile's global loads have S-1 iterations
 // of MFMA work to land.
 //
-// Workgroup -> tile order: see map_tile (XCD-contiguous ranges, walked GROUP
-// tile-rows at a time).
+// Workgroup -> tile order: see map_tile_shared.
 #pragma once
 
 #include <type_traits>
@@ -107,6 +106,35 @@ __device__ __forceinline__ int dsk(int r) {
 }
 
 __device__ __forceinline__ int dsm(int k) { return ((k & 3) ^ ((k & 3) << 1)) & 7; }
+
+// Workgroup -> tile order for kernels that run one workgroup per CU. The
+// hardware hands workgroup b to XCD b % 8, and each XCD has its own L2;
+// all XCDs share the memory-side cache (MALL). Tiles are numbered GROUP
+// tile-rows at a time, column-major inside a group, and each "wave" of
+// 8 x PER consecutive tiles (PER = CUs per XCD) is split into 8 runs of PER,
+// one per XCD: the tiles in flight on one XCD form a compact GROUP x PER/GROUP
+// block (L2 reuse of both operand panels), and the eight XCDs work side by
+// side on the same row panels (MALL reuse across XCDs). A last partial wave
+// keeps the plain order.
+template <int GROUP, int PER>
+__device__ __forceinline__ void map_tile_shared(int b, int nblk, int tiles_m, int tiles_n, int& split, int& tm,
+                                                int& tn) {
+  constexpr int WAVE = 8 * PER;
+  int t = b;
+  if (b < nblk / WAVE * WAVE) {
+    const int x = b & 7, p = b >> 3;
+    t = (p / PER) * WAVE + x * PER + p % PER;
+  }
+  const int ntile = tiles_m * tiles_n;
+  split = t / ntile;
+  t -= split * ntile;
+  const int gid = t / (GROUP * tiles_n);
+  const int first = gid * GROUP;
+  const int gsz = min(tiles_m - first, GROUP);
+  const int in = t - gid * GROUP * tiles_n;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
 
 // Raw buffer resource (stride 0) over `bytes` bytes at `p`, built from
 // wave-uniform values so that it lives in SGPRs.
@@ -216,7 +244,11 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   int split, tm, tn;
+#ifdef EXP_OLDMAP
   map_tile<Cfg::GROUP>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
+#else
+  map_tile_shared<Cfg::GROUP, 32>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
+#endif
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kbeg = (int64_t)split * sh.k_per;
   const int64_t kend = min(sh.K, kbeg + sh.k_per);
@@ -253,13 +285,15 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
 
   typedef __attribute__((address_space(3))) void lds_void;
   // Direct loads of k-tile t into its stage. On a K-tail tile, chunks at or
-  // beyond kend take kOobOffset (one 32-bit compare per load).
+  // beyond kend take kOobOffset (one 32-bit compare per load); a tile past
+  // the end (t >= nk) is all kOobOffset and fills its stage with zeros that
+  // nothing reads, which keeps the loop body free of branches.
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const int stage = t % ST;
-    const int64_t k0 = kbeg + (int64_t)t * BK;
+    const int krem = kspan - t * BK;  // k extent left from this tile on
+    const int64_t k0 = krem > 0 ? kbeg + (int64_t)t * BK : 0;
     const int psoff = __builtin_amdgcn_readfirstlane((int)((P_KC ? k0 : k0 * P.ld) * 2));
     const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
-    const int krem = kspan - t * BK;  // k extent left from this tile on
     static_for<0, LP>([&](auto c) {
       const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -272,12 +306,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           qsoff, 0, 0);
     });
   };
-  // Wait until at most `tiles` k-tiles of this wave's loads are in flight.
-  auto wait_tiles = [&](int tiles) __attribute__((always_inline)) {
-    static_for<0, ST - 1>([&](auto a) {
-      if (tiles == a) wait_vmcnt<a * (LP + LQ)>();
-    });
-  };
+  constexpr int LOADS = LP + LQ;  // direct loads per wave per tile
 
   FragAddr<P_KC, BM, BK, FM> pa;
   FragAddr<Q_KC, BN, BK, FN> qa;
@@ -300,12 +329,13 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   };
   constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
 
-  // One straight-line loop body (no branch touches the accumulators, so
-  // they keep their registers). The last iteration reads fragments of a
-  // stage nothing will use again: in bounds, and discarded.
+  // One straight-line loop body: no branch at all, so the accumulators keep
+  // their registers and the scheduler can interleave the loads with the
+  // MFMAs. The last iterations load and read stages nothing uses again (in
+  // bounds; zeros or stale data, discarded).
   if (nk > 0) {
-    for (int t = 0; t < ST && t < nk; ++t) issue_tile(t);
-    wait_tiles(min(ST, nk) - 1);
+    static_for<0, ST>([&](auto t) { issue_tile(t); });
+    wait_vmcnt<(ST - 1) * LOADS>();  // tile 0 has landed
     __syncthreads();
     read_frags(fa0, fb0, std::integral_constant<int, 0>{});
     for (int t = 0; t < nk; ++t) {
@@ -318,20 +348,23 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           mfmas(fa1, fb1);
         }
       });
-      // Tile t+1 must have landed; tiles t+2 .. min(t+S-1, nk-1) may still
-      // be in flight. The barrier also orders every wave's reads of stage
-      // t % S before the loads that refill it. (__syncthreads does not wait
-      // for direct-to-LDS loads by itself: the compiler sees them as global
+      // Tile t+1 must have landed; tiles t+2 .. t+S-1 may still be in
+      // flight. The barrier also orders every wave's reads of stage t % S
+      // before the loads that refill it. (__syncthreads does not wait for
+      // direct-to-LDS loads by itself: the compiler sees them as global
       // reads only.)
-      wait_tiles(max(0, min(ST - 2, nk - 2 - t)));
+      wait_vmcnt<(ST - 2) * LOADS>();
       __syncthreads();
-      if (t + ST < nk) issue_tile(t + ST);
+      issue_tile(t + ST);
       const bool wrap = (t + 1) % ST == 0;
       pa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_P) : (uint32_t)Cfg::LDS_P);
       qa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_Q) : (uint32_t)Cfg::LDS_Q);
       read_frags(fa0, fb0, std::integral_constant<int, 0>{});
       mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
     }
+    // Drain the loads of the tiles past the end before LDS is reused (or
+    // released to the next workgroup).
+    wait_vmcnt<0>();
   }
 
   // Epilogue. Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each

@@ -3,6 +3,12 @@
 // (F1: X A_i with fused bias + GeLU, F2: H_i B_i) and backward (B1: dY B_i^T
 // with fused gelu' and db1 column partials, B5: db1 finish, B2: H_i^T dY,
 // B3: X^T dZ_i, B4: dZ_i A_i^T).
+//
+// GEMMs that run on the direct-to-LDS engine read an operand fastest when it
+// is k-contiguous. When the caller's workspace has room, the operands that
+// are stored mn-contiguous (A_i and B_i in the forward; X, dY, H and dZ for
+// the weight gradients) are first transposed into it by an HBM-bound kernel
+// (TA, TB; TH, TdY, TX, TdZ), so all six GEMMs read k-contiguous tiles.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -15,6 +21,7 @@
 #include "gemm_dma.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_simt.hpp"
+#include "transpose.hpp"
 
 namespace tpmlp {
 namespace {
@@ -193,51 +200,130 @@ int record(void* const* events, int i, hipStream_t st) {
     if ((expr) != hipSuccess) return TPMLP_ERR_HIP;     \
   } while (0)
 
-struct WsLayout {
-  size_t dz_off, dz_bytes, part_off, part_bytes, total;
-  int part_tiles;
+// Transpose a dense [R][C] 16-bit matrix into out [C][R] (gelu applied on the
+// way when GELU).
+template <class S, bool GELU>
+hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStream_t st) {
+  if (R == 0 || C == 0) return hipSuccess;
+  const int tiles_c = (int)ceil_div(C, kTrCols), tiles_r = (int)ceil_div(R, kTrWaveTile);
+  hipLaunchKernelGGL((transpose16_kernel<S, GELU>), dim3(tiles_r * tiles_c), dim3(64 * kTrWaves), 0, st,
+                     static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C, tiles_c);
+  return hipGetLastError();
+}
+
+// Does a GEMM of this shape run on the direct-to-LDS engine once all its
+// operands are k-contiguous? (Then staging transposed copies pays off.)
+bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
+  return dtype != TPMLP_F32 && M > 0 && N > 0 && K > 0 && pick_engine(M, N, K, false) == Engine::Dma256;
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Forward workspace: [A_i^T [f][h]] [B_i^T [h][f]], each only if its GEMM stages.
+struct FwdWs {
+  size_t at_off, bt_off, total;
+  bool at, bt;
 };
 
-WsLayout ws_layout(const tpmlp_shape& s, bool dz_in_ws) {
-  WsLayout w{};
+FwdWs fwd_ws(const tpmlp_shape& s) {
+  FwdWs w{};
+  const size_t hf = (size_t)(s.hidden * s.ffn_shard) * elt_size(s.dtype);
+  w.at = stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
+  w.bt = stages(s.dtype, s.tokens, s.hidden, s.ffn_shard);
+  w.at_off = 0;
+  w.bt_off = w.at ? align256(hf) : 0;
+  w.total = w.bt_off + (w.bt ? align256(hf) : 0);
+  return w;
+}
+
+// Backward workspace: [dZ (if kept here)] [db1 partials fp32 [tiles][f]]
+// then, when the weight-gradient GEMMs stage: [H^T][dY^T] for dB and
+// [X^T][dZ^T] for dA (each [rows][T]).
+struct BwdWs {
+  size_t dz_off, dz_bytes, part_off, part_bytes, minimal;
+  size_t ht_off, dyt_off, xt_off, dzt_off, total;
+  int part_tiles;
+  bool stage_b2, stage_b3;
+};
+
+BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
+  BwdWs w{};
+  const size_t e = elt_size(s.dtype);
   const Plan b1 = plan_gemm(s.dtype, s.tokens, s.ffn_shard, s.hidden, false);
   w.part_tiles = (s.tokens > 0 && s.ffn_shard > 0) ? b1.tiles_m : 0;
   w.dz_off = 0;
-  w.dz_bytes = dz_in_ws ? (size_t)(s.tokens * s.ffn_shard) * elt_size(s.dtype) : 0;
-  w.part_off = (w.dz_bytes + 255) / 256 * 256;
+  w.dz_bytes = dz_in_ws ? (size_t)(s.tokens * s.ffn_shard) * e : 0;
+  w.part_off = align256(w.dz_bytes);
   w.part_bytes = (size_t)w.part_tiles * (size_t)s.ffn_shard * sizeof(float);
-  w.total = w.part_bytes ? w.part_off + w.part_bytes : w.dz_bytes;
+  w.minimal = w.part_bytes ? w.part_off + w.part_bytes : w.dz_bytes;
+  w.stage_b2 = stages(s.dtype, s.ffn_shard, s.hidden, s.tokens);
+  w.stage_b3 = stages(s.dtype, s.hidden, s.ffn_shard, s.tokens);
+  const size_t tf = align256((size_t)(s.tokens * s.ffn_shard) * e), th = align256((size_t)(s.tokens * s.hidden) * e);
+  size_t at = align256(w.minimal);
+  if (w.stage_b2) {
+    w.ht_off = at;
+    w.dyt_off = at + tf;
+    at += tf + th;
+  }
+  if (w.stage_b3) {
+    w.xt_off = at;
+    w.dzt_off = at + th;
+    at += th + tf;
+  }
+  w.total = (w.stage_b2 || w.stage_b3) ? at : w.minimal;
   return w;
 }
 
 template <class S>
 int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1, const void* B, void* Z, void* H,
-             void* Yp, hipStream_t st, void* const* ev) {
+             void* Yp, void* ws, size_t ws_bytes, hipStream_t st, void* const* ev) {
   using T = typename S::T;
   const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
+  const FwdWs w = fwd_ws(s);
+  const bool room = ws && ws_bytes >= w.total;
+  char* wsb = static_cast<char*>(ws);
   TPMLP_TRY(record(ev, 0, st));
-  // F1: Z = X A_i + b1 (and H = gelu(Z)); P = X [T,h] k-contiguous, Q = A_i [h,f] n-contiguous
-  TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, f, h, X, h, A, f,
-                                             EpiBiasGelu<S>{(const T*)b1, (T*)Z, (T*)H, f}, st)));
-  TPMLP_TRY(record(ev, 1, st));
-  // F2: Yp = H B_i (gelu(Z) on load when H is not kept); P [T,f] k-contiguous, Q = B_i [f,h] n-contiguous
-  if (H)
-    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, h, f, H, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
-  else
-    TPMLP_HIP((run_gemm<S, true, false, true>(s.dtype, Tn, h, f, Z, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
+  // TA + F1: Z = X A_i + b1 (and H = gelu(Z)); P = X [T,h] k-contiguous,
+  // Q = A_i [h,f] (n-contiguous), or its transpose A_i^T [f,h] (k-contiguous)
+  if (room && w.at) {
+    TPMLP_HIP((run_transpose<S, false>(A, wsb + w.at_off, h, f, st)));
+    TPMLP_TRY(record(ev, 1, st));
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, X, h, wsb + w.at_off, h,
+                                              EpiBiasGelu<S>{(const T*)b1, (T*)Z, (T*)H, f}, st)));
+  } else {
+    TPMLP_TRY(record(ev, 1, st));
+    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, f, h, X, h, A, f,
+                                               EpiBiasGelu<S>{(const T*)b1, (T*)Z, (T*)H, f}, st)));
+  }
   TPMLP_TRY(record(ev, 2, st));
+  // TB + F2: Yp = H B_i (gelu(Z) on load when H is not kept); P [T,f]
+  // k-contiguous, Q = B_i [f,h] (n-contiguous) or B_i^T [h,f] (k-contiguous)
+  if (!H) {
+    TPMLP_TRY(record(ev, 3, st));
+    TPMLP_HIP((run_gemm<S, true, false, true>(s.dtype, Tn, h, f, Z, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
+  } else if (room && w.bt) {
+    TPMLP_HIP((run_transpose<S, false>(B, wsb + w.bt_off, f, h, st)));
+    TPMLP_TRY(record(ev, 3, st));
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, H, f, wsb + w.bt_off, f, EpiStore<S>{(T*)Yp, h},
+                                              st)));
+  } else {
+    TPMLP_TRY(record(ev, 3, st));
+    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, h, f, H, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
+  }
+  TPMLP_TRY(record(ev, 4, st));
   return TPMLP_OK;
 }
 
 template <class S>
 int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A, const void* B, const void* Z,
-             const void* H, void* dZ, void* dXp, void* dA, void* dB, void* db1, const WsLayout& w, void* ws,
-             hipStream_t st, void* const* ev) {
+             const void* H, void* dZ, void* dXp, void* dA, void* dB, void* db1, const BwdWs& w, void* ws,
+             size_t ws_bytes, hipStream_t st, void* const* ev) {
   using T = typename S::T;
   const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
   char* wsb = static_cast<char*>(ws);
   if (!dZ && w.dz_bytes) dZ = wsb + w.dz_off;
   float* part = w.part_bytes ? reinterpret_cast<float*>(wsb + w.part_off) : nullptr;
+  const bool room = ws_bytes >= w.total;
 
   TPMLP_TRY(record(ev, 0, st));
   // B1: dZ = (dY B_i^T) * gelu'(Z), plus per-tile column sums; Q[k][n] = B_i[n][k] is k-contiguous
@@ -251,18 +337,45 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_HIP(hipGetLastError());
   }
   TPMLP_TRY(record(ev, 2, st));
-  // B2: dB = H^T dY; P[m=f][k=T] = H[k][m] and Q = dY are both mn-contiguous
-  if (H)
-    TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
-  else
-    TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
-  TPMLP_TRY(record(ev, 3, st));
-  // B3: dA = X^T dZ; both operands mn-contiguous
-  TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, EpiStore<S>{(T*)dA, f}, st)));
-  TPMLP_TRY(record(ev, 4, st));
+  // TH, TdY + B2: dB = H^T dY. Staged: P = H^T [f,T] (gelu(Z)^T when H is
+  // not kept) and Q[k][n] = dY^T[n][k], both k-contiguous. In place: both
+  // operands mn-contiguous (and gelu applied to Z on load without H).
+  if (room && w.stage_b2) {
+    if (H)
+      TPMLP_HIP((run_transpose<S, false>(H, wsb + w.ht_off, Tn, f, st)));
+    else
+      TPMLP_HIP((run_transpose<S, true>(Z, wsb + w.ht_off, Tn, f, st)));
+    TPMLP_TRY(record(ev, 3, st));
+    TPMLP_HIP((run_transpose<S, false>(dY, wsb + w.dyt_off, Tn, h, st)));
+    TPMLP_TRY(record(ev, 4, st));
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, Tn, wsb + w.dyt_off, Tn,
+                                              EpiStore<S>{(T*)dB, h}, st)));
+  } else {
+    TPMLP_TRY(record(ev, 3, st));
+    TPMLP_TRY(record(ev, 4, st));
+    if (H)
+      TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
+    else
+      TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
+  }
+  TPMLP_TRY(record(ev, 5, st));
+  // TX, TdZ + B3: dA = X^T dZ. Staged: P = X^T [h,T], Q[k][n] = dZ^T[n][k].
+  if (room && w.stage_b3) {
+    TPMLP_HIP((run_transpose<S, false>(X, wsb + w.xt_off, Tn, h, st)));
+    TPMLP_TRY(record(ev, 6, st));
+    TPMLP_HIP((run_transpose<S, false>(dZ, wsb + w.dzt_off, Tn, f, st)));
+    TPMLP_TRY(record(ev, 7, st));
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, Tn, wsb + w.dzt_off, Tn,
+                                              EpiStore<S>{(T*)dA, f}, st)));
+  } else {
+    TPMLP_TRY(record(ev, 6, st));
+    TPMLP_TRY(record(ev, 7, st));
+    TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, EpiStore<S>{(T*)dA, f}, st)));
+  }
+  TPMLP_TRY(record(ev, 8, st));
   // B4: dXp = dZ A_i^T; Q[k=f][n=h] = A_i[n][k] is k-contiguous
   TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, dZ, f, A, f, EpiStore<S>{(T*)dXp, h}, st)));
-  TPMLP_TRY(record(ev, 5, st));
+  TPMLP_TRY(record(ev, 9, st));
   return TPMLP_OK;
 }
 
@@ -289,13 +402,19 @@ const char* tp_mlp_status_string(int status) {
   }
 }
 
-size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, int dz_in_workspace) {
+size_t tp_mlp_fwd_workspace_bytes(const tpmlp_shape* shape) {
   if (check_shape(shape) != TPMLP_OK) return 0;
-  return ws_layout(*shape, dz_in_workspace != 0).total;
+  return fwd_ws(*shape).total;
+}
+
+size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags) {
+  if (check_shape(shape) != TPMLP_OK) return 0;
+  const BwdWs w = bwd_ws(*shape, (flags & TPMLP_WS_DZ) != 0);
+  return (flags & TPMLP_WS_MINIMAL) ? w.minimal : w.total;
 }
 
 int tp_mlp_fwd(const tpmlp_shape* shape, const void* X, const void* A, const void* b1, const void* B, void* Z,
-               void* H, void* Yp, void* stream, void* const* events) {
+               void* H, void* Yp, void* ws, size_t ws_bytes, void* stream, void* const* events) {
   TPMLP_TRY(check_shape(shape));
   const tpmlp_shape& s = *shape;
   const size_t e = elt_size(s.dtype);
@@ -303,14 +422,14 @@ int tp_mlp_fwd(const tpmlp_shape* shape, const void* X, const void* A, const voi
                Tf = (size_t)(s.tokens * s.ffn_shard) * e, fb = (size_t)s.ffn_shard * e;
   const Span in[4] = {{X, Th}, {A, hf}, {b1, fb}, {B, hf}};
   const bool in_req[4] = {true, true, true, true};
-  const Span out[3] = {{Z, Tf}, {H, Tf}, {Yp, Th}};
-  const bool out_req[3] = {true, false, true};
-  TPMLP_TRY(check_buffers(in, 4, in_req, out, 3, out_req));
+  const Span out[4] = {{Z, Tf}, {H, Tf}, {Yp, Th}, {ws, ws ? ws_bytes : 0}};
+  const bool out_req[4] = {true, false, true, false};
+  TPMLP_TRY(check_buffers(in, 4, in_req, out, 4, out_req));
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (s.dtype) {
-    case TPMLP_F32: return fwd_impl<StoreF32>(s, X, A, b1, B, Z, H, Yp, st, events);
-    case TPMLP_F16: return fwd_impl<StoreF16>(s, X, A, b1, B, Z, H, Yp, st, events);
-    default: return fwd_impl<StoreBF16>(s, X, A, b1, B, Z, H, Yp, st, events);
+    case TPMLP_F32: return fwd_impl<StoreF32>(s, X, A, b1, B, Z, H, Yp, ws, ws_bytes, st, events);
+    case TPMLP_F16: return fwd_impl<StoreF16>(s, X, A, b1, B, Z, H, Yp, ws, ws_bytes, st, events);
+    default: return fwd_impl<StoreBF16>(s, X, A, b1, B, Z, H, Yp, ws, ws_bytes, st, events);
   }
 }
 
@@ -322,18 +441,22 @@ int tp_mlp_bwd(const tpmlp_shape* shape, const void* dY, const void* X, const vo
   const size_t e = elt_size(s.dtype);
   const size_t Th = (size_t)(s.tokens * s.hidden) * e, hf = (size_t)(s.hidden * s.ffn_shard) * e,
                Tf = (size_t)(s.tokens * s.ffn_shard) * e, fb = (size_t)s.ffn_shard * e;
-  const WsLayout w = ws_layout(s, dZ == nullptr);
+  const BwdWs w = bwd_ws(s, dZ == nullptr);
+  const size_t ws_used = ws_bytes >= w.total ? w.total : w.minimal;
   const Span in[6] = {{dY, Th}, {X, Th}, {A, hf}, {B, hf}, {Z, Tf}, {H, Tf}};
   const bool in_req[6] = {true, true, true, true, true, false};
-  const Span out[6] = {{dZ, Tf}, {dXp, Th}, {dA, hf}, {dB, hf}, {db1, fb}, {ws, w.total}};
+  const Span out[6] = {{dZ, Tf}, {dXp, Th}, {dA, hf}, {dB, hf}, {db1, fb}, {ws, ws_used}};
   const bool out_req[6] = {false, true, true, true, true, true};
   TPMLP_TRY(check_buffers(in, 6, in_req, out, 6, out_req));
-  if (ws_bytes < w.total) return TPMLP_ERR_WORKSPACE;
+  if (ws_bytes < w.minimal) return TPMLP_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (s.dtype) {
-    case TPMLP_F32: return bwd_impl<StoreF32>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, st, events);
-    case TPMLP_F16: return bwd_impl<StoreF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, st, events);
-    default: return bwd_impl<StoreBF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, st, events);
+    case TPMLP_F32:
+      return bwd_impl<StoreF32>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+    case TPMLP_F16:
+      return bwd_impl<StoreF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+    default:
+      return bwd_impl<StoreBF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
   }
 }
 

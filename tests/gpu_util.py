@@ -35,11 +35,13 @@ def device_inputs(inp, A=None, b1=None, B=None):
             to_device(inp.B if B is None else B, d), to_device(inp.dY, d))
 
 
-def run_shard(tpmlp, X, A, b1, B, dY, keep_h=True, keep_dz=True):
-    """Forward then backward of one rank; returns the device outputs."""
+def run_shard(tpmlp, X, A, b1, B, dY, keep_h=True, keep_dz=True, staged=True):
+    """Forward then backward of one rank; returns the device outputs.
+    staged=False gives the library the minimal workspaces (operands read in
+    place instead of through k-contiguous copies)."""
     import torch
-    Z, H, Yp = tpmlp.fwd(X, A, b1, B, keep_h=keep_h)
-    g = tpmlp.bwd(dY, X, A, B, Z, H, keep_dz=keep_dz)
+    Z, H, Yp = tpmlp.fwd(X, A, b1, B, keep_h=keep_h, staged=staged)
+    g = tpmlp.bwd(dY, X, A, B, Z, H, keep_dz=keep_dz, staged=staged)
     torch.cuda.synchronize()
     out = {"Z": Z, "Yp": Yp, **g}
     if H is not None:

@@ -56,6 +56,19 @@ def test_ragged_shapes_16bit(gpu_lib, tile, dtype, T, h, f):
     compare(got, ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("tile", ["dma256"], indirect=True)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,h,f", [(200, 136, 264), (520, 264, 392)])
+def test_operands_read_in_place(gpu_lib, tile, dtype, T, h, f):
+    """Minimal workspaces: the large-tile engine reads the mn-contiguous
+    operands in place (transposing LDS reads) instead of staged copies."""
+    print(f"case in-place dtype={dtype} T={T} h={h} f={f}", flush=True)
+    inp = synth.draw_inputs(T, h, f, dtype, seed=T + 3 * f, sigma_dy=1.0)
+    ref = _oracle_shard(inp)
+    got = run_shard(gpu_lib, *device_inputs(inp), staged=False)
+    compare(got, ref, TOL[dtype])
+
+
 @pytest.mark.parametrize("T,h,f", [(4, 4, 4), (200, 132, 268), (64, 128, 256)])
 def test_ragged_shapes_fp32(gpu_lib, T, h, f):
     print(f"case ragged dtype=f32 T={T} h={h} f={f}", flush=True)
@@ -191,7 +204,9 @@ def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile):
         return raw[G:G + n].view(*shape)
 
     Z, H, Yp = guarded(T, f), guarded(T, f), guarded(T, h)
-    gpu_lib.tp_mlp_fwd(X, A, b1, B, Z, H, Yp)
+    nfws = gpu_lib.tp_mlp_fwd_workspace_bytes(T, h, f, gpu_lib.TPMLP_BF16)
+    fws_raw = torch.full((nfws + 2 * G,), 0x5A, dtype=torch.uint8, device="cuda")
+    gpu_lib.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws_raw[G:G + nfws] if nfws else None)
     dZ, dXp, dA, dB, db1 = guarded(T, f), guarded(T, h), guarded(h, f), guarded(f, h), guarded(f)
     nws = gpu_lib.tp_mlp_workspace_bytes(T, h, f, gpu_lib.TPMLP_BF16)
     ws_raw = torch.full((nws + 2 * G,), 0x5A, dtype=torch.uint8, device="cuda")
@@ -202,6 +217,7 @@ def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile):
         assert torch.all(raw[:G] == -4096.0) and torch.all(raw[G + n:] == -4096.0)
         assert not torch.any(raw[G:G + n] == -4096.0)
     assert torch.all(ws_raw[:G] == 0x5A) and torch.all(ws_raw[G + nws:] == 0x5A)
+    assert torch.all(fws_raw[:G] == 0x5A) and torch.all(fws_raw[G + nfws:] == 0x5A)
     ref = _oracle_shard(inp)
     compare({"Z": Z, "H": H, "Yp": Yp, "dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}, ref, TOL["bf16"])
 
@@ -210,8 +226,8 @@ def test_events_bracket_each_step(gpu_lib):
     import torch
     inp = synth.draw_inputs(512, 256, 512, "f16", seed=6)
     X, A, b1, B, dY = device_inputs(inp)
-    fe = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    be = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    be = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
     Z, H, Yp = gpu_lib.fwd(X, A, b1, B, events=fe)
     gpu_lib.bwd(dY, X, A, B, Z, H, events=be)
     torch.cuda.synchronize()
