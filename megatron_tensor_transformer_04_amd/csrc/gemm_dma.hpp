@@ -65,9 +65,11 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+// OCC_: workgroups per CU the tile is built for (their waves share each
+// SIMD's registers and the CU's LDS).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1>
 struct DmaTile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M_ * WAVES_N_;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -84,7 +86,9 @@ struct DmaTile {
   static_assert(STAGES >= 2, "at least two stages");
   static_assert(BK == 32 || BK == 64, "k-tiles of 32 or 64 (an even number of 16-wide substeps)");
   static_assert(BK == 32 || WAVES % 2 == 0, "64-deep KC tiles need an even number of waves");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KB per workgroup");
+  static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS is 160 KB per CU");
+  static constexpr int WAVES_PER_SIMD = WAVES * OCC / 4;
+  static constexpr int PER_XCD = 32 * OCC;  // workgroups in flight per XCD
 };
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most N vector
@@ -94,6 +98,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations
+// (lgkmcnt 0), not for its direct-to-LDS loads. __syncthreads' fence would
+// also wait for every outstanding direct load (their LDS writes count as
+// prior stores), which removes the overlap the loads are issued early for;
+// callers wait for the loads they need with wait_vmcnt. The asm statement's
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0; vmcnt (63) and expcnt (7) at their maxima
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Offsets beyond every buffer's num_records: the load returns zeros.
@@ -234,7 +249,8 @@ struct FragAddr {
 };
 
 template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi>
-__global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg::WAVES / 4, Cfg::WAVES / 4)))
+__global__ __launch_bounds__(Cfg::THREADS)
+__attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
 void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES;
@@ -247,7 +263,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
 #ifdef EXP_OLDMAP
   map_tile<Cfg::GROUP>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
 #else
-  map_tile_shared<Cfg::GROUP, 32>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
+  map_tile_shared<Cfg::GROUP, Cfg::PER_XCD>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
 #endif
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kbeg = (int64_t)split * sh.k_per;
@@ -336,7 +352,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   if (nk > 0) {
     static_for<0, ST>([&](auto t) { issue_tile(t); });
     wait_vmcnt<(ST - 1) * LOADS>();  // tile 0 has landed
-    __syncthreads();
+    barrier_lds();
     read_frags(fa0, fb0, std::integral_constant<int, 0>{});
     for (int t = 0; t < nk; ++t) {
       static_for<0, NKS - 1>([&](auto ks) {
@@ -348,13 +364,11 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           mfmas(fa1, fb1);
         }
       });
-      // Tile t+1 must have landed; tiles t+2 .. t+S-1 may still be in
-      // flight. The barrier also orders every wave's reads of stage t % S
-      // before the loads that refill it. (__syncthreads does not wait for
-      // direct-to-LDS loads by itself: the compiler sees them as global
-      // reads only.)
+      // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight. The
+      // barrier also orders every wave's reads of stage t % S before the
+      // loads that refill it.
       wait_vmcnt<(ST - 2) * LOADS>();
-      __syncthreads();
+      barrier_lds();
       issue_tile(t + ST);
       const bool wrap = (t + 1) % ST == 0;
       pa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_P) : (uint32_t)Cfg::LDS_P);
