@@ -8,6 +8,19 @@
 //                                                  reduces the tile's columns;
 //   void colsum(int tile_m, int64_t n, float s)    store one tile's sum.
 // apply() is only called for in-range (m, n).
+//
+// For the tile-wise epilogue of the direct-to-LDS engine (which loads and
+// stores whole 16-byte row chunks) every epilogue also exposes
+//   static constexpr int kOuts                     16-bit outputs (1 or 2);
+//   static constexpr bool kInput                   whether it reads a [M][N]
+//                                                  16-bit input at (m, n);
+//   const T* input() / T* output(k) / int64_t ld   those tensors (an output
+//                                                  may be null: not kept);
+//   float colparam(int64_t n)                      a per-column value;
+//   float eval(float acc, float colp, float in, float (&o)[2])
+//                                                  the fp32 outputs before
+//                                                  rounding, and the value
+//                                                  that enters the column sum.
 #pragma once
 
 #include "numerics.hpp"
@@ -20,6 +33,15 @@ struct EpiStore {
   typename S::T* out;
   int64_t ld;
   static constexpr bool kColSum = false;
+  static constexpr int kOuts = 1;
+  static constexpr bool kInput = false;
+  __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
+  __device__ __forceinline__ typename S::T* output(int) const { return out; }
+  __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
+  __device__ __forceinline__ float eval(float acc, float, float, float (&o)[2]) const {
+    o[0] = acc;
+    return 0.0f;
+  }
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
     out[m * ld + n] = S::from_f(acc);
     return 0.0f;
@@ -38,6 +60,17 @@ struct EpiBiasGelu {
   typename S::T* h;  // may be null: H not kept
   int64_t ld;
   static constexpr bool kColSum = false;
+  static constexpr int kOuts = 2;
+  static constexpr bool kInput = false;
+  __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
+  __device__ __forceinline__ typename S::T* output(int k) const { return k ? h : z; }
+  __device__ __forceinline__ float colparam(int64_t n) const { return S::to_f(bias[n]); }
+  __device__ __forceinline__ float eval(float acc, float colp, float, float (&o)[2]) const {
+    const float v = acc + colp;
+    o[0] = v;
+    o[1] = gelu_tanh(v);
+    return 0.0f;
+  }
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
     const float v = acc + S::to_f(bias[n]);
     z[m * ld + n] = S::from_f(v);
@@ -58,6 +91,16 @@ struct EpiGeluGrad {
   float* partial;  // [tiles_m][ld]
   int64_t ld;
   static constexpr bool kColSum = true;
+  static constexpr int kOuts = 1;
+  static constexpr bool kInput = true;
+  __device__ __forceinline__ const typename S::T* input() const { return zin; }
+  __device__ __forceinline__ typename S::T* output(int) const { return dz; }
+  __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
+  __device__ __forceinline__ float eval(float acc, float, float zv, float (&o)[2]) const {
+    const float d = acc * gelu_tanh_grad(zv);
+    o[0] = d;
+    return d;
+  }
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
     const float d = acc * gelu_tanh_grad(S::to_f(zin[m * ld + n]));
     dz[m * ld + n] = S::from_f(d);

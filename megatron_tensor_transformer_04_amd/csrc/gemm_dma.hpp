@@ -381,17 +381,74 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     wait_vmcnt<0>();
   }
 
-  // Epilogue. Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each
-  // 32x32 fragment, r = 0..15.
+  // Epilogue, one 32-row block of the wave's tile at a time, staged through
+  // a private LDS region so that global memory sees whole 16-byte row chunks:
+  //   input (if any): 16-byte row chunks -> LDS -> per lane the fragment's
+  //                   values via ds_read_b64_tr_b16 (four rows of a column);
+  //   outputs:        fp32 -> 16-bit, written to LDS at (row, column), read
+  //                   back as 16-byte row chunks and stored.
+  // Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each 32x32
+  // fragment, r = 0..15. The barrier first makes sure no wave still reads
+  // fragments or receives direct loads (each drained its own above).
+  barrier_lds();
+  constexpr int CPR = Cfg::WTN / 8;            // 16-byte chunks per staged row
+  constexpr int RS = Cfg::WTN * 2 + 16;        // staged row stride (bytes)
+  constexpr int BLK = 32 * RS;                 // one staged 32-row block
+  constexpr int PASSES = 32 * CPR / 64;        // chunks per lane per block
+  static_assert(PASSES * 64 == 32 * CPR, "a 32-row block is a whole number of chunks per lane");
+  static_assert(Cfg::WAVES * Epi::kOuts * BLK <= Cfg::LDS_BYTES, "staging fits in the stage buffers");
+  char* const stg = smem + wave * (Epi::kOuts * BLK);
+  const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
+  const int G = lane >> 4, jj = lane & 15;
   float cs[FN];
   static_for<0, FN>([&](auto j) { cs[j] = 0.0f; });
   static_for<0, FM>([&](auto i) {
-    static_for<0, FN>([&](auto j) {
-      const int64_t n = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
-      static_for<0, 16>([&](auto r) {
-        const int64_t m = m0 + wm * Cfg::WTM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        if (m < sh.M && n < sh.N) cs[j] += epi.apply(m, n, acc[i][j][(int)r]);
+    const int64_t mb = mw + i * 32;
+    if constexpr (Epi::kInput) {
+      static_for<0, PASSES>([&](auto p) {
+        const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (mb + row < sh.M && nw + c8 * 8 < sh.N)
+          v = *reinterpret_cast<const u32x4*>(epi.input() + (mb + row) * epi.ld + nw + c8 * 8);
+        *reinterpret_cast<u32x4*>(stg + row * RS + c8 * 16) = v;
       });
+    }
+    static_for<0, FN>([&](auto j) {
+      const int64_t n = nw + j * 32 + (lane & 31);
+      const bool n_ok = n < sh.N;
+      const float colp = n_ok ? epi.colparam(n) : 0.0f;
+      static_for<0, 4>([&](auto g) {
+        float in[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (Epi::kInput) {
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(stg + (8 * g + 4 * (G >> 1) + (jj >> 2)) * RS + ((G & 1) * 16 + (jj & 3) * 4) * 2 +
+                           j * 64));
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) in[rr] = S::to_f((typename S::T)(uint16_t)t[rr]);
+        }
+        static_for<0, 4>([&](auto rr) {
+          const int row = 8 * g + 4 * (lane >> 5) + rr;  // within the block
+          float o[2];
+          const float c = epi.eval(acc[i][j][4 * g + rr], colp, in[rr], o);
+          if (n_ok && mb + row < sh.M) cs[j] += c;
+          static_for<0, Epi::kOuts>([&](auto k) {
+            *reinterpret_cast<typename S::T*>(stg + k * BLK + row * RS + (j * 32 + (lane & 31)) * 2) =
+                S::from_f(o[k]);
+          });
+        });
+      });
+    });
+    static_for<0, Epi::kOuts>([&](auto k) {
+      typename S::T* const out = epi.output(k);
+      if (out) {
+        static_for<0, PASSES>([&](auto p) {
+          const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + k * BLK + row * RS + c8 * 16);
+          if (mb + row < sh.M && nw + c8 * 8 < sh.N)
+            *reinterpret_cast<u32x4*>(out + (mb + row) * epi.ld + nw + c8 * 8) = v;
+        });
+      }
     });
   });
   if constexpr (Epi::kColSum) {

@@ -45,18 +45,15 @@ struct StoreF16 {
   }
 };
 
-// bfloat16 storage: the top 16 bits of an fp32; rounded to nearest-even
-// (ties to even, NaN kept quiet) from the fp32 bit pattern.
+// bfloat16 storage: the top 16 bits of an fp32. fp32 -> bf16 is gfx950's
+// v_cvt_pk_bf16_f32, which rounds to nearest-even (NaN stays NaN).
 struct StoreBF16 {
   using T = uint16_t;
   static __device__ __forceinline__ float to_f(uint16_t v) {
     return __builtin_bit_cast(float, (uint32_t)v << 16);
   }
   static __device__ __forceinline__ uint16_t from_f(float v) {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
   }
   static __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
