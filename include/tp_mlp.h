@@ -103,18 +103,27 @@ const char* tp_mlp_status_string(int status);
  *
  * tp_mlp_fwd_workspace_bytes: bytes with which tp_mlp_fwd stages
  * k-contiguous copies of A_i and B_i for the GEMMs that read them faster
- * that way (0 if no GEMM of this shape does). tp_mlp_fwd accepts any size:
- * with less than this (or NULL) it reads the weights in place, slower.
+ * that way, plus room for fp32 partial sums of a k-split last wave of
+ * output tiles (below) (0 if this shape needs neither). tp_mlp_fwd
+ * accepts any size: with less than this (or NULL) it reads the weights in
+ * place and splits nothing, slower.
+ *
+ * k-split last wave: when a GEMM's output tiles leave a last wave that
+ * would occupy at most half the compute units, each of those tiles is
+ * computed as up to four k-ranges whose fp32 sums are added in a fixed
+ * order (results stay deterministic, but differ in the last bits from an
+ * unsplit run). Only plain-store GEMMs (the second forward GEMM, dB, dA,
+ * dXp) split, and only with the full workspace.
  *
  * tp_mlp_workspace_bytes: bytes for tp_mlp_bwd. Flags:
  *   TPMLP_WS_DZ       room for dZ_i as well, for callers that pass dZ = NULL;
  *   TPMLP_WS_MINIMAL  only what tp_mlp_bwd requires (fp32 per-tile column
  *                     partials of dZ for db1, and dZ if TPMLP_WS_DZ).
  * Without TPMLP_WS_MINIMAL the size also holds k-contiguous copies of H_i,
- * dY, X and dZ_i (each [rows][tokens]) for the weight-gradient GEMMs;
- * tp_mlp_bwd uses them when ws_bytes reaches that size, and otherwise reads
- * the operands in place (slower). A workspace below the minimal size is
- * TPMLP_ERR_WORKSPACE.
+ * dY, X and dZ_i (each [rows][tokens]) for the weight-gradient GEMMs and
+ * the k-split partial sums; tp_mlp_bwd uses them when ws_bytes reaches that
+ * size, and otherwise reads the operands in place and splits nothing
+ * (slower). A workspace below the minimal size is TPMLP_ERR_WORKSPACE.
  * Both return 0 and set nothing on an invalid shape.
  */
 #define TPMLP_WS_DZ 1u

@@ -35,6 +35,7 @@ struct EpiStore {
   static constexpr bool kColSum = false;
   static constexpr int kOuts = 1;
   static constexpr bool kInput = false;
+  static constexpr bool kTailSplit = true;  // a plain store: k-split tail tiles may finish it elsewhere
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int) const { return out; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
@@ -62,6 +63,7 @@ struct EpiBiasGelu {
   static constexpr bool kColSum = false;
   static constexpr int kOuts = 2;
   static constexpr bool kInput = false;
+  static constexpr bool kTailSplit = false;
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int k) const { return k ? h : z; }
   __device__ __forceinline__ float colparam(int64_t n) const { return S::to_f(bias[n]); }
@@ -93,6 +95,7 @@ struct EpiGeluGrad {
   static constexpr bool kColSum = true;
   static constexpr int kOuts = 1;
   static constexpr bool kInput = true;
+  static constexpr bool kTailSplit = false;
   __device__ __forceinline__ const typename S::T* input() const { return zin; }
   __device__ __forceinline__ typename S::T* output(int) const { return dz; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }

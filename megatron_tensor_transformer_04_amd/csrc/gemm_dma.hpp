@@ -48,7 +48,7 @@
 // so LDS reads overlap MFMAs and a tile's global loads have S-1 iterations
 // of MFMA work to land.
 //
-// Workgroup -> tile order: see map_tile_shared.
+// Workgroup -> tile order: see map_work and tile_coords.
 #pragma once
 
 #include <type_traits>
@@ -122,27 +122,27 @@ __device__ __forceinline__ int dsk(int r) {
 
 __device__ __forceinline__ int dsm(int k) { return ((k & 3) ^ ((k & 3) << 1)) & 7; }
 
-// Workgroup -> tile order for kernels that run one workgroup per CU. The
+// Workgroup -> work order for kernels that run one workgroup per CU. The
 // hardware hands workgroup b to XCD b % 8, and each XCD has its own L2;
-// all XCDs share the memory-side cache (MALL). Tiles are numbered GROUP
-// tile-rows at a time, column-major inside a group, and each "wave" of
-// 8 x PER consecutive tiles (PER = CUs per XCD) is split into 8 runs of PER,
-// one per XCD: the tiles in flight on one XCD form a compact GROUP x PER/GROUP
-// block (L2 reuse of both operand panels), and the eight XCDs work side by
-// side on the same row panels (MALL reuse across XCDs). A last partial wave
-// keeps the plain order.
-template <int GROUP, int PER>
-__device__ __forceinline__ void map_tile_shared(int b, int nblk, int tiles_m, int tiles_n, int& split, int& tm,
-                                                int& tn) {
+// all XCDs share the memory-side cache (MALL). Each "wave" of 8 x PER
+// consecutive work items (PER = workgroups in flight per XCD) is split into
+// 8 runs of PER, one per XCD. Tiles are numbered GROUP tile-rows at a time,
+// column-major inside a group (tile_coords), so the tiles in flight on one
+// XCD form a compact GROUP x PER/GROUP block (L2 reuse of both operand
+// panels) and the eight XCDs work side by side on the same row panels (MALL
+// reuse across XCDs). A last partial wave keeps the plain order.
+template <int PER>
+__device__ __forceinline__ int map_work(int b, int nblk) {
   constexpr int WAVE = 8 * PER;
-  int t = b;
   if (b < nblk / WAVE * WAVE) {
     const int x = b & 7, p = b >> 3;
-    t = (p / PER) * WAVE + x * PER + p % PER;
+    return (p / PER) * WAVE + x * PER + p % PER;
   }
-  const int ntile = tiles_m * tiles_n;
-  split = t / ntile;
-  t -= split * ntile;
+  return b;
+}
+
+template <int GROUP>
+__host__ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int gid = t / (GROUP * tiles_n);
   const int first = gid * GROUP;
   const int gsz = min(tiles_m - first, GROUP);
@@ -150,6 +150,19 @@ __device__ __forceinline__ void map_tile_shared(int b, int nblk, int tiles_m, in
   tm = first + in % gsz;
   tn = in / gsz;
 }
+
+// Work items past the last full wave of tiles. With T tiles and W workgroups
+// per wave, a last wave of r = T % W tiles would leave most CUs idle; when
+// parts > 1 those r tiles are instead each split into `parts` k-ranges of
+// k_part (a multiple of the k-tile), one work item each, whose fp32 partial
+// sums go to `partial` ([r][parts][BM][BN]) and are added, in part order, by
+// tail_finish_kernel. Work item w < full is tile w over all of K.
+struct TailSplit {
+  int full;       // tiles computed whole
+  int parts;      // k-ranges per tail tile (1: no tail split)
+  int64_t k_part; // k elements per range
+  float* partial;
+};
 
 // Raw buffer resource (stride 0) over `bytes` bytes at `p`, built from
 // wave-uniform values so that it lives in SGPRs.
@@ -251,7 +264,8 @@ struct FragAddr {
 template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi>
 __global__ __launch_bounds__(Cfg::THREADS)
 __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
-void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi) {
+void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi,
+                     TailSplit tail) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES;
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
@@ -259,15 +273,17 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  int split, tm, tn;
-#ifdef EXP_OLDMAP
-  map_tile<Cfg::GROUP>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
-#else
-  map_tile_shared<Cfg::GROUP, Cfg::PER_XCD>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
-#endif
+  const int w = map_work<Cfg::PER_XCD>(blockIdx.x, gridDim.x);
+  int tile = w, part = -1;  // part >= 0: a k-range of a tail tile
+  if (w >= tail.full) {
+    tile = tail.full + (w - tail.full) / tail.parts;
+    part = (w - tail.full) % tail.parts;
+  }
+  int tm, tn;
+  tile_coords<Cfg::GROUP>(tile, sh.tiles_m, sh.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kbeg = (int64_t)split * sh.k_per;
-  const int64_t kend = min(sh.K, kbeg + sh.k_per);
+  const int64_t kbeg = part >= 0 ? (int64_t)part * tail.k_part : 0;
+  const int64_t kend = part >= 0 ? min(sh.K, kbeg + tail.k_part) : sh.K;
   const int kspan = kend > kbeg ? (int)(kend - kbeg) : 0;
   const int nk = (kspan + BK - 1) / BK;
 
@@ -390,6 +406,21 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each 32x32
   // fragment, r = 0..15. The barrier first makes sure no wave still reads
   // fragments or receives direct loads (each drained its own above).
+  if (part >= 0) {
+    // One k-range of a tail tile: the raw fp32 partial sums, in place of the
+    // epilogue (tail_finish_kernel applies it).
+    float* pt = tail.partial + ((int64_t)(tile - tail.full) * tail.parts + part) * (BM * BN);
+    static_for<0, FM>([&](auto i) {
+      static_for<0, FN>([&](auto j) {
+        const int c = wn * Cfg::WTN + j * 32 + (lane & 31);
+        static_for<0, 16>([&](auto r) {
+          const int row = wm * Cfg::WTM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+          pt[row * BN + c] = acc[i][j][(int)r];
+        });
+      });
+    });
+    return;
+  }
   barrier_lds();
   constexpr int CPR = Cfg::WTN / 8;            // 16-byte chunks per staged row
   constexpr int RS = Cfg::WTN * 2 + 16;        // staged row stride (bytes)
@@ -466,6 +497,40 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       if (n0 + c < sh.N) epi.colsum(tm, n0 + c, s);
     }
   }
+}
+
+// Epilogue of the tail tiles of a split launch: C = round(sum of the
+// parts' fp32 partials, in part order). One thread per 8 consecutive
+// columns of one row of one tail tile.
+template <class S, int GROUP, int BM, int BN>
+__global__ __launch_bounds__(256) void tail_finish_kernel(const float* partial, int full, int ntail, int parts,
+                                                          int tiles_m, int tiles_n, int64_t M, int64_t N,
+                                                          typename S::T* out, int64_t ld) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (tail tile, row, 8-column chunk)
+  constexpr int CH = BN / 8;
+  const int64_t per_tile = (int64_t)BM * CH;
+  const int q = (int)(idx / per_tile);
+  if (q >= ntail) return;
+  const int rem = (int)(idx % per_tile), row = rem / CH, c8 = rem % CH;
+  int tm, tn;
+  tile_coords<GROUP>(full + q, tiles_m, tiles_n, tm, tn);
+  const int64_t m = (int64_t)tm * BM + row, n = (int64_t)tn * BN + c8 * 8;
+  if (m >= M || n >= N) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < parts; ++p) {
+    const float* src = partial + ((int64_t)q * parts + p) * (BM * BN) + row * BN + c8 * 8;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += a[e];
+      acc[4 + e] += b[e];
+    }
+  }
+  u32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    v[e] = (uint32_t)S::from_f(acc[2 * e]) | ((uint32_t)S::from_f(acc[2 * e + 1]) << 16);
+  *reinterpret_cast<u32x4*>(out + m * ld + n) = v;
 }
 
 }  // namespace tpmlp

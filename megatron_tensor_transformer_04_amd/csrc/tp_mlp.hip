@@ -96,22 +96,64 @@ void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q,
                      epi);
 }
 
+// CUs of an MI355X: one wave of 256 x 256 tiles.
+constexpr int kCUs = 256;
+
+// Split of the last partial wave of a direct-load GEMM (see TailSplit): when
+// fewer than half the CUs would get a tile in the last wave, those tiles are
+// split into up to four k-ranges of at least 512. Only plain-store epilogues.
+// TPMLP_TAIL_CUS in the environment replaces the CU count of this plan (read
+// on every call; lets tests exercise tail splits at small sizes).
+TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
+  const int ntile = pl.tiles_m * pl.tiles_n;
+  TailSplit t{ntile, 1, K, nullptr};
+  int cus = kCUs;
+  if (const char* e = std::getenv("TPMLP_TAIL_CUS")) cus = std::max(1, std::atoi(e));
+  const int r = ntile % cus;
+  if (!allowed || pl.eng != Engine::Dma256 || ntile < cus || r == 0 || r > cus / 2) return t;
+  int parts = std::min(4, cus / r);
+  while (parts > 1 && K < (int64_t)parts * 128) --parts;
+  if (parts < 2) return t;
+  t.full = ntile - r;
+  t.k_part = ceil_div(ceil_div(K, parts), 64) * 64;
+  t.parts = (int)ceil_div(K, t.k_part);  // every range non-empty
+  if (t.parts < 2) return TailSplit{ntile, 1, K, nullptr};
+  return t;
+}
+
+size_t tail_bytes(const TailSplit& t, const Plan& pl) {
+  return t.parts > 1 ? (size_t)(pl.tiles_m * pl.tiles_n - t.full) * t.parts * pl.bm * pl.bn * sizeof(float) : 0;
+}
+
 template <class Cfg, class S, bool PK, bool QK, class Epi>
-void launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const void* q, int64_t ldq, const Epi& epi,
-                hipStream_t st) {
-  const int nblk = sh.tiles_m * sh.tiles_n * sh.splits;
+hipError_t launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const void* q, int64_t ldq, const Epi& epi,
+                      TailSplit tail, hipStream_t st) {
+  const int ntile = sh.tiles_m * sh.tiles_n;
+  const int nblk = tail.full + (ntile - tail.full) * tail.parts;
   hipLaunchKernelGGL((gemm_dma_kernel<Cfg, S, PK, QK, Epi>), dim3(nblk), dim3(Cfg::THREADS), 0, st, sh,
                      Operand{static_cast<const uint16_t*>(p), ldp}, sh.M * sh.K,
-                     Operand{static_cast<const uint16_t*>(q), ldq}, sh.N * sh.K, epi);
+                     Operand{static_cast<const uint16_t*>(q), ldq}, sh.N * sh.K, epi, tail);
+  if constexpr (Epi::kTailSplit) {
+    if (tail.parts > 1) {
+      const int ntail = ntile - tail.full;
+      const int64_t threads = (int64_t)ntail * Cfg::BM * (Cfg::BN / 8);
+      hipLaunchKernelGGL((tail_finish_kernel<S, Cfg::GROUP, Cfg::BM, Cfg::BN>), dim3((unsigned)ceil_div(threads, 256)),
+                         dim3(256), 0, st, tail.partial, tail.full, ntail, tail.parts, sh.tiles_m, sh.tiles_n, sh.M,
+                         sh.N, epi.out, epi.ld);
+    }
+  }
+  return hipGetLastError();
 }
 
 // C[M][N] = sum_k P[m][k] Q[k][n] through epilogue `epi`; PK / QK select the
 // k-contiguous layout of P / Q, GP applies gelu to P as it is loaded. Every
 // operand is dense: its leading dimension is its contiguous extent (K for a
-// k-contiguous operand, M or N otherwise).
+// k-contiguous operand, M or N otherwise). tail_ws: room for the partials of
+// a k-split last wave and its size in bytes; the split is taken only if
+// its partials (tail_bytes(plan_tail(...))) fit.
 template <class S, bool PK, bool QK, bool GP, class Epi>
 hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q,
-                    int64_t ldq, const Epi& epi, hipStream_t st) {
+                    int64_t ldq, const Epi& epi, hipStream_t st, float* tail_ws = nullptr, size_t tail_cap = 0) {
   if (M == 0 || N == 0) return hipSuccess;
   const Plan pl = plan_gemm(dtype, M, N, K, GP);
   GemmShape sh{M, N, K, pl.tiles_m, pl.tiles_n, 1, std::max<int64_t>(K, 1)};
@@ -122,13 +164,25 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
   } else {
     switch (pl.eng) {
       case Engine::Dma256:
-        if constexpr (!GP) launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, st);
+        if constexpr (!GP) {
+          TailSplit tail = plan_tail(pl, K, Epi::kTailSplit && tail_ws != nullptr);
+          if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
+          tail.partial = tail_ws;
+          return launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
+        }
         break;
       case Engine::Mfma256: launch_mfma<Cfg256, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st); break;
       default: launch_mfma<Cfg128, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st); break;
     }
   }
   return hipGetLastError();
+}
+
+// Bytes of tail partials a plain-store GEMM of this shape uses (0 if none).
+size_t gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
+  if (dtype == TPMLP_F32 || M == 0 || N == 0) return 0;
+  const Plan pl = plan_gemm(dtype, M, N, K, false);
+  return tail_bytes(plan_tail(pl, K, true), pl);
 }
 
 size_t elt_size(int dtype) { return dtype == TPMLP_F32 ? 4 : 2; }
@@ -219,9 +273,10 @@ bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Forward workspace: [A_i^T [f][h]] [B_i^T [h][f]], each only if its GEMM stages.
+// Forward workspace: [A_i^T [f][h]] [B_i^T [h][f]] (each only if its GEMM
+// stages) [tail partials of the second GEMM].
 struct FwdWs {
-  size_t at_off, bt_off, total;
+  size_t at_off, bt_off, tail_off, tail_bytes, total;
   bool at, bt;
 };
 
@@ -232,16 +287,19 @@ FwdWs fwd_ws(const tpmlp_shape& s) {
   w.bt = stages(s.dtype, s.tokens, s.hidden, s.ffn_shard);
   w.at_off = 0;
   w.bt_off = w.at ? align256(hf) : 0;
-  w.total = w.bt_off + (w.bt ? align256(hf) : 0);
+  w.tail_off = w.bt_off + (w.bt ? align256(hf) : 0);
+  w.tail_bytes = gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard);
+  w.total = w.tail_off + align256(w.tail_bytes);
   return w;
 }
 
 // Backward workspace: [dZ (if kept here)] [db1 partials fp32 [tiles][f]]
 // then, when the weight-gradient GEMMs stage: [H^T][dY^T] for dB and
-// [X^T][dZ^T] for dA (each [rows][T]).
+// [X^T][dZ^T] for dA (each [rows][T]); then the tail partials of the
+// plain-store GEMMs (dB, dA, dXp run one after another and share them).
 struct BwdWs {
   size_t dz_off, dz_bytes, part_off, part_bytes, minimal;
-  size_t ht_off, dyt_off, xt_off, dzt_off, total;
+  size_t ht_off, dyt_off, xt_off, dzt_off, tail_off, tail_bytes, total;
   int part_tiles;
   bool stage_b2, stage_b3;
 };
@@ -270,7 +328,12 @@ BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
     w.dzt_off = at + th;
     at += th + tf;
   }
-  w.total = (w.stage_b2 || w.stage_b3) ? at : w.minimal;
+  const size_t tail = std::max({gemm_tail_bytes(s.dtype, s.ffn_shard, s.hidden, s.tokens),
+                                 gemm_tail_bytes(s.dtype, s.hidden, s.ffn_shard, s.tokens),
+                                 gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard)});
+  w.tail_off = at;
+  w.tail_bytes = tail;
+  w.total = (w.stage_b2 || w.stage_b3 || tail) ? at + align256(tail) : w.minimal;
   return w;
 }
 
@@ -305,10 +368,12 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
     TPMLP_HIP((run_transpose<S, false>(B, wsb + w.bt_off, f, h, st)));
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, H, f, wsb + w.bt_off, f, EpiStore<S>{(T*)Yp, h},
-                                              st)));
+                                              st, reinterpret_cast<float*>(wsb + w.tail_off), w.tail_bytes)));
   } else {
     TPMLP_TRY(record(ev, 3, st));
-    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, h, f, H, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
+    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, h, f, H, f, B, h, EpiStore<S>{(T*)Yp, h}, st,
+                                               room ? reinterpret_cast<float*>(wsb + w.tail_off) : nullptr,
+                                               room ? w.tail_bytes : 0)));
   }
   TPMLP_TRY(record(ev, 4, st));
   return TPMLP_OK;
@@ -324,6 +389,8 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
   if (!dZ && w.dz_bytes) dZ = wsb + w.dz_off;
   float* part = w.part_bytes ? reinterpret_cast<float*>(wsb + w.part_off) : nullptr;
   const bool room = ws_bytes >= w.total;
+  float* const tail = room ? reinterpret_cast<float*>(wsb + w.tail_off) : nullptr;
+  const size_t tcap = room ? w.tail_bytes : 0;
 
   TPMLP_TRY(record(ev, 0, st));
   // B1: dZ = (dY B_i^T) * gelu'(Z), plus per-tile column sums; Q[k][n] = B_i[n][k] is k-contiguous
@@ -349,12 +416,13 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_HIP((run_transpose<S, false>(dY, wsb + w.dyt_off, Tn, h, st)));
     TPMLP_TRY(record(ev, 4, st));
     TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, Tn, wsb + w.dyt_off, Tn,
-                                              EpiStore<S>{(T*)dB, h}, st)));
+                                              EpiStore<S>{(T*)dB, h}, st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_TRY(record(ev, 4, st));
     if (H)
-      TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
+      TPMLP_HIP(
+          (run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, EpiStore<S>{(T*)dB, h}, st, tail, tcap)));
     else
       TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
   }
@@ -366,15 +434,16 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_HIP((run_transpose<S, false>(dZ, wsb + w.dzt_off, Tn, f, st)));
     TPMLP_TRY(record(ev, 7, st));
     TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, Tn, wsb + w.dzt_off, Tn,
-                                              EpiStore<S>{(T*)dA, f}, st)));
+                                              EpiStore<S>{(T*)dA, f}, st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 6, st));
     TPMLP_TRY(record(ev, 7, st));
-    TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, EpiStore<S>{(T*)dA, f}, st)));
+    TPMLP_HIP(
+        (run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, EpiStore<S>{(T*)dA, f}, st, tail, tcap)));
   }
   TPMLP_TRY(record(ev, 8, st));
   // B4: dXp = dZ A_i^T; Q[k=f][n=h] = A_i[n][k] is k-contiguous
-  TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, dZ, f, A, f, EpiStore<S>{(T*)dXp, h}, st)));
+  TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, dZ, f, A, f, EpiStore<S>{(T*)dXp, h}, st, tail, tcap)));
   TPMLP_TRY(record(ev, 9, st));
   return TPMLP_OK;
 }

@@ -81,12 +81,21 @@ def test_workspace_bytes(lib):
     assert ws(16384, 10240, 10240, 2, MINIMAL) == part
     assert ws(4096, 768, 3072, 1, MINIMAL) == (4096 // 128) * 3072 * 4
     # large shards stage k-contiguous copies of H, dY, X and dZ for the
-    # weight-gradient GEMMs (each [rows][T] in 16 bits), after the minimal part
+    # weight-gradient GEMMs (each [rows][T] in 16 bits), after the minimal
+    # part, then the fp32 partials of k-split last waves: dB and dA have
+    # 40 x 40 = 1600 tiles of 256 x 256, 6 full waves on 256 CUs and 64 tiles
+    # left, each split into 4 k-ranges; dXp has 2560 tiles (no tail)
     t = 16384 * 10240 * 2
-    assert ws(16384, 10240, 10240, 2) == part + 4 * t
-    assert ws(16384, 10240, 10240, 2, DZ) == t + part + 4 * t
-    # ... and the forward stages A_i^T and B_i^T
+    tail = 64 * 4 * 256 * 256 * 4
+    assert ws(16384, 10240, 10240, 2) == part + 4 * t + tail
+    assert ws(16384, 10240, 10240, 2, DZ) == t + part + 4 * t + tail
+    # ... and the forward stages A_i^T and B_i^T (Yp: 2560 tiles, no tail)
     assert fws(16384, 10240, 10240, 2) == 2 * 10240 * 10240 * 2
+    # h = 8192 (TP = 4 of a 32768-wide FFN): Yp and dXp have 64 x 32 tiles,
+    # dB and dA 32 x 32 = 1024: no tails
+    t8 = 16384 * 8192 * 2
+    assert fws(16384, 8192, 8192, 2) == 2 * 8192 * 8192 * 2
+    assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240 + 4 * t8
     # small shapes and fp32 stage nothing
     assert ws(4096, 768, 3072, 1) == ws(4096, 768, 3072, 1, MINIMAL)
     assert fws(4096, 768, 3072, 1) == 0 and fws(64, 128, 256, 0) == 0
@@ -97,6 +106,33 @@ def test_workspace_bytes(lib):
     assert ws(-8, 128, 256, 2) == 0 and fws(-8, 128, 256, 2) == 0
     assert ws(64, 12, 256, 2) == 0
     assert ws(64, 128, 256, 7) == 0
+
+
+def test_k_split_tail_workspace(lib, monkeypatch):
+    """The k-split plan (as if the chip had `cus` CUs) sizes the partials:
+    [tail tiles][parts][256][256] fp32, the largest over dB, dA and dXp."""
+    ws = lambda T, h, f: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)), 0)
+    fws = lambda T, h, f: lib.tp_mlp_fwd_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)))
+    monkeypatch.setenv("TPMLP_TILE", "dma256")
+    base, fbase = ws(520, 264, 392), fws(520, 264, 392)
+    short = fws(520, 264, 200)
+    tile = 256 * 256 * 4
+    # 3 CUs: dB and dA have 2 x 2 tiles, one left over, split into
+    # ceil(520 / round_up(ceil(520 / 3), 64)) = 3 ranges; Yp / dXp (3 x 2) none
+    monkeypatch.setenv("TPMLP_TAIL_CUS", "3")
+    assert ws(520, 264, 392) == base + 1 * 3 * tile
+    assert fws(520, 264, 392) == fbase
+    # 4 CUs: Yp / dXp keep 2 of 6 tiles for the last wave, 2 ranges of K = 392
+    monkeypatch.setenv("TPMLP_TAIL_CUS", "4")
+    assert ws(520, 264, 392) == base + 2 * 2 * tile
+    assert fws(520, 264, 392) == fbase + 2 * 2 * tile
+    # ... unless K is too short for two ranges of at least 128
+    assert fws(520, 264, 200) == short
+    # 5 CUs: Yp / dXp leave 1 of 6 tiles; 4 ranges would be shorter than 128,
+    # 3 of round_up(ceil(392 / 3), 64) = 192; dB and dA (4 tiles) fill no wave
+    monkeypatch.setenv("TPMLP_TAIL_CUS", "5")
+    assert ws(520, 264, 392) == base + 1 * 3 * tile
+    assert fws(520, 264, 392) == fbase + 1 * 3 * tile
 
 
 BASE = 1 << 40  # fake, 16-byte aligned addresses that validation never dereferences

@@ -69,6 +69,27 @@ def test_operands_read_in_place(gpu_lib, tile, dtype, T, h, f):
     compare(got, ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("tile", ["dma256"], indirect=True)
+@pytest.mark.parametrize("cus", [3, 4, 5])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,h,f", [(520, 264, 392), (1000, 264, 392)])
+def test_k_split_last_wave(gpu_lib, tile, monkeypatch, cus, dtype, T, h, f):
+    """Tail tiles computed as k-ranges plus an ordered fp32 sum, planned as
+    if the chip had `cus` CUs so that small shapes split (3 CUs: dB and dA
+    split their one leftover tile into 3 ranges; 4 and 5: Yp and dXp split
+    ragged K = 392 into 2 or 3)."""
+    monkeypatch.setenv("TPMLP_TAIL_CUS", str(cus))
+    print(f"case k-split cus={cus} dtype={dtype} T={T} h={h} f={f}", flush=True)
+    inp = synth.draw_inputs(T, h, f, dtype, seed=T + cus, sigma_dy=1.0)
+    ref = _oracle_shard(inp)
+    got = run_shard(gpu_lib, *device_inputs(inp))
+    compare(got, ref, TOL[dtype])
+    again = run_shard(gpu_lib, *device_inputs(inp))
+    import torch
+    for k in got:
+        assert torch.equal(got[k].view(torch.int16), again[k].view(torch.int16)), k
+
+
 @pytest.mark.parametrize("T,h,f", [(4, 4, 4), (200, 132, 268), (64, 128, 256)])
 def test_ragged_shapes_fp32(gpu_lib, T, h, f):
     print(f"case ragged dtype=f32 T={T} h={h} f={f}", flush=True)
@@ -186,12 +207,16 @@ def test_deterministic_bitwise(gpu_lib):
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
 
 
-@pytest.mark.parametrize("tile", [128, 256, "dma256"], indirect=True)
-def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile):
+@pytest.mark.parametrize("tile,cus", [(128, None), (256, None), ("dma256", None), ("dma256", 4)],
+                         indirect=["tile"])
+def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, monkeypatch):
     """Each output lives between two poisoned guard regions, which must
-    survive forward + backward unchanged."""
+    survive forward + backward unchanged (cus: k-split tails planned as if
+    the chip had that many CUs, so that the partials use the workspace)."""
     import torch
-    T, h, f = 200, 136, 264
+    if cus is not None:
+        monkeypatch.setenv("TPMLP_TAIL_CUS", str(cus))
+    T, h, f = (520, 264, 392) if cus else (200, 136, 264)
     inp = synth.draw_inputs(T, h, f, "bf16", seed=4, sigma_dy=1.0)
     X, A, b1, B, dY = device_inputs(inp)
     G = 4096  # guard elements on each side (keeps 16-byte alignment)
