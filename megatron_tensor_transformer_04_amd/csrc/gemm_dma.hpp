@@ -46,7 +46,9 @@
 //   load tile t+S into stage t % S
 //   read frags (t+1, 0)      | MFMAs (t, last)
 // so LDS reads overlap MFMAs and a tile's global loads have S-1 iterations
-// of MFMA work to land.
+// of MFMA work to land. Scheduling constraints hold this order (the
+// compiler's own schedule serialises each read with its first use), and
+// after the barrier the loads and reads are interleaved with the MFMAs.
 //
 // Workgroup -> tile order: see map_work and tile_coords.
 #pragma once
@@ -109,6 +111,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0; vmcnt (63) and expcnt (7) at their maxima
   asm volatile("s_barrier" ::: "memory");
+}
+
+// Instruction-order constraints for the machine scheduler (AMDGPU
+// sched_barrier / sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read,
+// 0x100 DS read). sched_fence: nothing moves across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// The region just ended issues MF MFMAs, VM vector-memory reads and DS DS
+// reads: order them as MFMA, VMEM, DS, DS.., MFMA, VMEM, DS.. (one VMEM and
+// up to ceil(DS / MF) DS reads after each MFMA) and close the region.
+template <int MF, int VM, int DS>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int DPER = (DS + MF - 1) / MF;
+  static_for<0, MF>([&](auto i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (i < VM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    constexpr int d = DS - i * DPER < DPER ? DS - i * DPER : DPER;
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
+  });
+  sched_fence();
 }
 
 // Offsets beyond every buffer's num_records: the load returns zeros.
@@ -361,10 +383,20 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   };
   constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
 
+  // DS read instructions per substep (a transposing read moves half a
+  // fragment).
+  constexpr int DSR = (P_KC ? 1 : 2) * FM + (Q_KC ? 1 : 2) * FN;
+
   // One straight-line loop body: no branch at all, so the accumulators keep
-  // their registers and the scheduler can interleave the loads with the
-  // MFMAs. The last iterations load and read stages nothing uses again (in
-  // bounds; zeros or stale data, discarded).
+  // their registers. The last iterations load and read stages nothing uses
+  // again (in bounds; zeros or stale data, discarded).
+  //
+  // Software pipeline, pinned with scheduling constraints (left alone, the
+  // compiler sinks each fragment read to just before its first MFMA and
+  // exposes the full LDS latency on every read): substep s issues all reads
+  // of substep s+1, then its own MFMAs. After the barrier, the direct loads
+  // that refill the freed stage and the reads of the next tile's first
+  // substep are interleaved one by one with the MFMAs of the last substep.
   if (nk > 0) {
     static_for<0, ST>([&](auto t) { issue_tile(t); });
     wait_vmcnt<(ST - 1) * LOADS>();  // tile 0 has landed
@@ -374,23 +406,28 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       static_for<0, NKS - 1>([&](auto ks) {
         if constexpr (ks % 2 == 0) {
           read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+          sched_fence();
           mfmas(fa0, fb0);
         } else {
           read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+          sched_fence();
           mfmas(fa1, fb1);
         }
+        sched_fence();
       });
       // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight. The
       // barrier also orders every wave's reads of stage t % S before the
       // loads that refill it.
       wait_vmcnt<(ST - 2) * LOADS>();
       barrier_lds();
+      sched_fence();
       issue_tile(t + ST);
       const bool wrap = (t + 1) % ST == 0;
       pa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_P) : (uint32_t)Cfg::LDS_P);
       qa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_Q) : (uint32_t)Cfg::LDS_Q);
       read_frags(fa0, fb0, std::integral_constant<int, 0>{});
       mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
+      sched_interleave<FM * FN, LOADS, DSR>();
     }
     // Drain the loads of the tiles past the end before LDS is reused (or
     // released to the next workgroup).
