@@ -290,6 +290,8 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
                      TailSplit tail) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES;
+  static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
+                "an mn-contiguous operand needs a power-of-two tile extent (swizzle, loads per k-row)");
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -434,8 +436,9 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     wait_vmcnt<0>();
   }
 
-  // Epilogue, one 32-row block of the wave's tile at a time, staged through
-  // a private LDS region so that global memory sees whole 16-byte row chunks:
+  // Epilogue, one block of 32 (or 16) rows of the wave's tile at a time,
+  // staged through a private LDS region so that global memory sees whole
+  // 16-byte row chunks:
   //   input (if any): 16-byte row chunks -> LDS -> per lane the fragment's
   //                   values via ds_read_b64_tr_b16 (four rows of a column);
   //   outputs:        fp32 -> 16-bit, written to LDS at (row, column), read
@@ -461,17 +464,22 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   barrier_lds();
   constexpr int CPR = Cfg::WTN / 8;            // 16-byte chunks per staged row
   constexpr int RS = Cfg::WTN * 2 + 16;        // staged row stride (bytes)
-  constexpr int BLK = 32 * RS;                 // one staged 32-row block
-  constexpr int PASSES = 32 * CPR / 64;        // chunks per lane per block
-  static_assert(PASSES * 64 == 32 * CPR, "a 32-row block is a whole number of chunks per lane");
+  // Rows per staged block: 32 (a whole fragment row) when every wave's
+  // blocks fit in LDS, else 16 (two halves per fragment row).
+  constexpr int HB = Cfg::WAVES * Epi::kOuts * 32 * RS <= Cfg::LDS_BYTES ? 32 : 16;
+  constexpr int BLK = HB * RS;                 // one staged block
+  constexpr int PASSES = HB * CPR / 64;        // chunks per lane per block
+  static_assert(PASSES * 64 == HB * CPR, "a staged block is a whole number of chunks per lane");
   static_assert(Cfg::WAVES * Epi::kOuts * BLK <= Cfg::LDS_BYTES, "staging fits in the stage buffers");
   char* const stg = smem + wave * (Epi::kOuts * BLK);
   const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
   const int G = lane >> 4, jj = lane & 15;
   float cs[FN];
   static_for<0, FN>([&](auto j) { cs[j] = 0.0f; });
-  static_for<0, FM>([&](auto i) {
-    const int64_t mb = mw + i * 32;
+  static_for<0, FM * (32 / HB)>([&](auto ib) {
+    constexpr int i = ib / (32 / HB);            // fragment row
+    constexpr int g0 = (ib % (32 / HB)) * (HB / 8);  // first 8-row group of the block
+    const int64_t mb = mw + i * 32 + g0 * 8;
     if constexpr (Epi::kInput) {
       static_for<0, PASSES>([&](auto p) {
         const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
@@ -485,7 +493,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       const int64_t n = nw + j * 32 + (lane & 31);
       const bool n_ok = n < sh.N;
       const float colp = n_ok ? epi.colparam(n) : 0.0f;
-      static_for<0, 4>([&](auto g) {
+      static_for<0, HB / 8>([&](auto g) {
         float in[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (Epi::kInput) {
           typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -498,7 +506,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
         static_for<0, 4>([&](auto rr) {
           const int row = 8 * g + 4 * (lane >> 5) + rr;  // within the block
           float o[2];
-          const float c = epi.eval(acc[i][j][4 * g + rr], colp, in[rr], o);
+          const float c = epi.eval(acc[i][j][4 * (g0 + g) + rr], colp, in[rr], o);
           if (n_ok && mb + row < sh.M) cs[j] += c;
           static_for<0, Epi::kOuts>([&](auto k) {
             *reinterpret_cast<typename S::T*>(stg + k * BLK + row * RS + (j * 32 + (lane & 31)) * 2) =

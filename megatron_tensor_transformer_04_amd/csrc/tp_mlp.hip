@@ -37,11 +37,15 @@ __global__ __launch_bounds__(256) void db1_finish_kernel(const float* partial, i
   db1[n] = S::from_f(s);
 }
 
-enum class Engine { Simt, Mfma128, Mfma256, Dma256 };
+enum class Engine { Simt, Mfma128, Mfma256, Dma256, Dma320 };
 
 using Cfg128 = MfmaTile<128, 128, 2, 2>;
 using Cfg256 = MfmaTile<256, 256, 2, 4>;
 using CfgD256 = DmaTile<256, 256, 2, 4, 64, 2>;
+// 256 x 320 tiles (8 waves of 64 x 160): 10% fewer operand bytes per flop
+// through L2 and LDS than 256 x 256; k-contiguous operands only (the
+// mn-contiguous LDS swizzle assumes a power-of-two row of units).
+using CfgD320 = DmaTile<256, 320, 4, 2, 64, 2>;
 
 struct Plan {
   Engine eng;
@@ -55,32 +59,48 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // offsets within one operand stay below 2^31.
 constexpr int64_t kDmaMaxElems = (int64_t(1) << 30) - (int64_t(1) << 20);
 
+// CUs of an MI355X: one wave of 256 x 256 tiles.
+constexpr int kCUs = 256;
+
+// Tile work of a launch counted in whole waves over the CUs (a last partial
+// wave costs as much as a full one).
+int64_t wave_cost(int64_t M, int64_t N, int bm, int bn) {
+  return ceil_div(ceil_div(M, bm) * ceil_div(N, bn), kCUs) * bm * bn;
+}
+
 // Tile choice for the 16-bit engines. Large tiles (256x256) once they give
 // at least two full waves over the 256 CUs, else 128x128. Large tiles use the
 // direct-to-LDS engine unless P needs the GeLU applied on load (that engine
 // has no register stage to apply it in) or an operand is too large for its
-// 32-bit offsets. TPMLP_TILE=128, 256 (register-staged) or dma256 in the
-// environment forces one engine where it applies (read on every call; for
-// tuning and tests).
-Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p) {
+// 32-bit offsets; with both operands k-contiguous (kc) it takes 256x320
+// tiles unless they cost more whole waves. TPMLP_TILE=128, 256
+// (register-staged), dma256 or dma320 (kc only) in the environment forces
+// one engine where it applies (read on every call; for tuning and tests).
+Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
   const bool dma_fits = !gelu_p && M * K <= kDmaMaxElems && N * K <= kDmaMaxElems;
   if (const char* e = std::getenv("TPMLP_TILE")) {
     if (!std::strcmp(e, "128")) return Engine::Mfma128;
     if (!std::strcmp(e, "256")) return Engine::Mfma256;
     if (!std::strcmp(e, "dma256")) return dma_fits ? Engine::Dma256 : Engine::Mfma256;
+    if (!std::strcmp(e, "dma320")) return !dma_fits ? Engine::Mfma256 : kc ? Engine::Dma320 : Engine::Dma256;
   }
-  if (ceil_div(M, 256) * ceil_div(N, 256) >= 512) return dma_fits ? Engine::Dma256 : Engine::Mfma256;
-  return Engine::Mfma128;
+  if (ceil_div(M, 256) * ceil_div(N, 256) < 512) return Engine::Mfma128;
+  if (!dma_fits) return Engine::Mfma256;
+  if (kc && wave_cost(M, N, CfgD320::BM, CfgD320::BN) <= wave_cost(M, N, CfgD256::BM, CfgD256::BN))
+    return Engine::Dma320;
+  return Engine::Dma256;
 }
 
-Plan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool gelu_p) {
+// kc: both operands k-contiguous.
+Plan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
   Plan p;
-  p.eng = dtype == TPMLP_F32 ? Engine::Simt : pick_engine(M, N, K, gelu_p);
+  p.eng = dtype == TPMLP_F32 ? Engine::Simt : pick_engine(M, N, K, gelu_p, kc);
   switch (p.eng) {
     case Engine::Simt: p.bm = SimtTile::BM; p.bn = SimtTile::BN; break;
     case Engine::Mfma128: p.bm = Cfg128::BM; p.bn = Cfg128::BN; break;
     case Engine::Mfma256: p.bm = Cfg256::BM; p.bn = Cfg256::BN; break;
     case Engine::Dma256: p.bm = CfgD256::BM; p.bn = CfgD256::BN; break;
+    case Engine::Dma320: p.bm = CfgD320::BM; p.bn = CfgD320::BN; break;
   }
   p.tiles_m = (int)ceil_div(M, p.bm);
   p.tiles_n = (int)ceil_div(N, p.bn);
@@ -96,9 +116,6 @@ void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q,
                      epi);
 }
 
-// CUs of an MI355X: one wave of 256 x 256 tiles.
-constexpr int kCUs = 256;
-
 // Split of the last partial wave of a direct-load GEMM (see TailSplit): when
 // fewer than half the CUs would get a tile in the last wave, those tiles are
 // split into up to four k-ranges of at least 512. Only plain-store epilogues.
@@ -110,7 +127,8 @@ TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
   int cus = kCUs;
   if (const char* e = std::getenv("TPMLP_TAIL_CUS")) cus = std::max(1, std::atoi(e));
   const int r = ntile % cus;
-  if (!allowed || pl.eng != Engine::Dma256 || ntile < cus || r == 0 || r > cus / 2) return t;
+  const bool dma = pl.eng == Engine::Dma256 || pl.eng == Engine::Dma320;
+  if (!allowed || !dma || ntile < cus || r == 0 || r > cus / 2) return t;
   int parts = std::min(4, cus / r);
   while (parts > 1 && K < (int64_t)parts * 128) --parts;
   if (parts < 2) return t;
@@ -155,7 +173,7 @@ template <class S, bool PK, bool QK, bool GP, class Epi>
 hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q,
                     int64_t ldq, const Epi& epi, hipStream_t st, float* tail_ws = nullptr, size_t tail_cap = 0) {
   if (M == 0 || N == 0) return hipSuccess;
-  const Plan pl = plan_gemm(dtype, M, N, K, GP);
+  const Plan pl = plan_gemm(dtype, M, N, K, GP, PK && QK);
   GemmShape sh{M, N, K, pl.tiles_m, pl.tiles_n, 1, std::max<int64_t>(K, 1)};
   if constexpr (std::is_same_v<S, StoreF32>) {
     hipLaunchKernelGGL((gemm_simt_kernel<PK, QK, GP, Epi>), dim3(pl.tiles_m * pl.tiles_n), dim3(SimtTile::THREADS),
@@ -171,6 +189,14 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
           return launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
         }
         break;
+      case Engine::Dma320:
+        if constexpr (!GP && PK && QK) {
+          TailSplit tail = plan_tail(pl, K, Epi::kTailSplit && tail_ws != nullptr);
+          if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
+          tail.partial = tail_ws;
+          return launch_dma<CfgD320, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
+        }
+        break;
       case Engine::Mfma256: launch_mfma<Cfg256, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st); break;
       default: launch_mfma<Cfg128, S, PK, QK, GP>(sh, p, ldp, q, ldq, epi, st); break;
     }
@@ -178,10 +204,11 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
   return hipGetLastError();
 }
 
-// Bytes of tail partials a plain-store GEMM of this shape uses (0 if none).
-size_t gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
+// Bytes of tail partials a plain-store GEMM of this shape uses (0 if none);
+// kc: both operands k-contiguous.
+size_t gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K, bool kc) {
   if (dtype == TPMLP_F32 || M == 0 || N == 0) return 0;
-  const Plan pl = plan_gemm(dtype, M, N, K, false);
+  const Plan pl = plan_gemm(dtype, M, N, K, false, kc);
   return tail_bytes(plan_tail(pl, K, true), pl);
 }
 
@@ -268,7 +295,9 @@ hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStr
 // Does a GEMM of this shape run on the direct-to-LDS engine once all its
 // operands are k-contiguous? (Then staging transposed copies pays off.)
 bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
-  return dtype != TPMLP_F32 && M > 0 && N > 0 && K > 0 && pick_engine(M, N, K, false) == Engine::Dma256;
+  if (dtype == TPMLP_F32 || M <= 0 || N <= 0 || K <= 0) return false;
+  const Engine e = pick_engine(M, N, K, false, true);
+  return e == Engine::Dma256 || e == Engine::Dma320;
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -288,7 +317,7 @@ FwdWs fwd_ws(const tpmlp_shape& s) {
   w.at_off = 0;
   w.bt_off = w.at ? align256(hf) : 0;
   w.tail_off = w.bt_off + (w.bt ? align256(hf) : 0);
-  w.tail_bytes = gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard);
+  w.tail_bytes = gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard, w.bt);
   w.total = w.tail_off + align256(w.tail_bytes);
   return w;
 }
@@ -307,7 +336,7 @@ struct BwdWs {
 BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
   BwdWs w{};
   const size_t e = elt_size(s.dtype);
-  const Plan b1 = plan_gemm(s.dtype, s.tokens, s.ffn_shard, s.hidden, false);
+  const Plan b1 = plan_gemm(s.dtype, s.tokens, s.ffn_shard, s.hidden, false, true);
   w.part_tiles = (s.tokens > 0 && s.ffn_shard > 0) ? b1.tiles_m : 0;
   w.dz_off = 0;
   w.dz_bytes = dz_in_ws ? (size_t)(s.tokens * s.ffn_shard) * e : 0;
@@ -328,9 +357,9 @@ BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
     w.dzt_off = at + th;
     at += th + tf;
   }
-  const size_t tail = std::max({gemm_tail_bytes(s.dtype, s.ffn_shard, s.hidden, s.tokens),
-                                 gemm_tail_bytes(s.dtype, s.hidden, s.ffn_shard, s.tokens),
-                                 gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard)});
+  const size_t tail = std::max({gemm_tail_bytes(s.dtype, s.ffn_shard, s.hidden, s.tokens, w.stage_b2),
+                                 gemm_tail_bytes(s.dtype, s.hidden, s.ffn_shard, s.tokens, w.stage_b3),
+                                 gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard, true)});
   w.tail_off = at;
   w.tail_bytes = tail;
   w.total = (w.stage_b2 || w.stage_b3 || tail) ? at + align256(tail) : w.minimal;

@@ -82,13 +82,12 @@ def test_workspace_bytes(lib):
     assert ws(4096, 768, 3072, 1, MINIMAL) == (4096 // 128) * 3072 * 4
     # large shards stage k-contiguous copies of H, dY, X and dZ for the
     # weight-gradient GEMMs (each [rows][T] in 16 bits), after the minimal
-    # part, then the fp32 partials of k-split last waves: dB and dA have
-    # 40 x 40 = 1600 tiles of 256 x 256, 6 full waves on 256 CUs and 64 tiles
-    # left, each split into 4 k-ranges; dXp has 2560 tiles (no tail)
+    # part. Their GEMMs then run on 256 x 320 tiles: dB and dA have
+    # 40 x 32 = 1280 tiles, five full waves on 256 CUs, dXp 64 x 32: no
+    # k-split tails
     t = 16384 * 10240 * 2
-    tail = 64 * 4 * 256 * 256 * 4
-    assert ws(16384, 10240, 10240, 2) == part + 4 * t + tail
-    assert ws(16384, 10240, 10240, 2, DZ) == t + part + 4 * t + tail
+    assert ws(16384, 10240, 10240, 2) == part + 4 * t
+    assert ws(16384, 10240, 10240, 2, DZ) == t + part + 4 * t
     # ... and the forward stages A_i^T and B_i^T (Yp: 2560 tiles, no tail)
     assert fws(16384, 10240, 10240, 2) == 2 * 10240 * 10240 * 2
     # h = 8192 (TP = 4 of a 32768-wide FFN): Yp and dXp have 64 x 32 tiles,
@@ -106,6 +105,17 @@ def test_workspace_bytes(lib):
     assert ws(-8, 128, 256, 2) == 0 and fws(-8, 128, 256, 2) == 0
     assert ws(64, 12, 256, 2) == 0
     assert ws(64, 128, 256, 7) == 0
+
+
+def test_k_split_tail_workspace_full_shard(lib, monkeypatch):
+    """With 256 x 256 tiles forced, dB and dA of the h = 10240 shard have
+    40 x 40 = 1600 tiles: six full waves and 64 tiles left, each split into
+    4 k-ranges of fp32 partials; dXp (2560 tiles) splits nothing."""
+    ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
+    monkeypatch.setenv("TPMLP_TILE", "dma256")
+    part = (16384 // 256) * 10240 * 4
+    t = 16384 * 10240 * 2
+    assert ws() == part + 4 * t + 64 * 4 * 256 * 256 * 4
 
 
 def test_k_split_tail_workspace(lib, monkeypatch):

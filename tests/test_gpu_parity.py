@@ -45,7 +45,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("tile", [128, 256, "dma256"], indirect=True)
+@pytest.mark.parametrize("tile", [128, 256, "dma256", "dma320"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,h,f", RAGGED)
 def test_ragged_shapes_16bit(gpu_lib, tile, dtype, T, h, f):
@@ -69,7 +69,7 @@ def test_operands_read_in_place(gpu_lib, tile, dtype, T, h, f):
     compare(got, ref, TOL[dtype])
 
 
-@pytest.mark.parametrize("tile", ["dma256"], indirect=True)
+@pytest.mark.parametrize("tile", ["dma256", "dma320"], indirect=True)
 @pytest.mark.parametrize("cus", [3, 4, 5])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,h,f", [(520, 264, 392), (1000, 264, 392)])
@@ -99,7 +99,7 @@ def test_ragged_shapes_fp32(gpu_lib, T, h, f):
     compare(got, ref, TOL["f32"])
 
 
-@pytest.mark.parametrize("tile", [128, 256, "dma256"], indirect=True)
+@pytest.mark.parametrize("tile", [128, 256, "dma256", "dma320"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_without_h_and_dz_buffers(gpu_lib, tile, dtype):
     """H not kept (GeLU applied to Z on load) and dZ kept in the workspace."""
@@ -207,7 +207,8 @@ def test_deterministic_bitwise(gpu_lib):
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
 
 
-@pytest.mark.parametrize("tile,cus", [(128, None), (256, None), ("dma256", None), ("dma256", 4)],
+@pytest.mark.parametrize("tile,cus", [(128, None), (256, None), ("dma256", None), ("dma256", 4),
+                                      ("dma320", None), ("dma320", 2)],
                          indirect=["tile"])
 def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, monkeypatch):
     """Each output lives between two poisoned guard regions, which must
