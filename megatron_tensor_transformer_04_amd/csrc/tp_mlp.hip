@@ -59,6 +59,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // offsets within one operand stay below 2^31.
 constexpr int64_t kDmaMaxElems = (int64_t(1) << 30) - (int64_t(1) << 20);
 
+// Row pitch of the transposed copies staged in the workspace: R + 256
+// elements. A pitch that is a multiple of a large power of two (T = 16384
+// tokens: 32 KB) sends the rows a GEMM tile reads together to few L2
+// channels and sets; 512 bytes of padding per row spread them (measured on
+// MI355X: 128 bytes do as much for the GEMMs but slow the transposes'
+// stores by a sixth, 512 bytes do not).
+constexpr int64_t kStagePad = 256;
+int64_t staged_ld(int64_t R) { return R + kStagePad; }
+
 // CUs of an MI355X: one wave of 256 x 256 tiles.
 constexpr int kCUs = 256;
 
@@ -77,7 +86,7 @@ int64_t wave_cost(int64_t M, int64_t N, int bm, int bn) {
 // (register-staged), dma256 or dma320 (kc only) in the environment forces
 // one engine where it applies (read on every call; for tuning and tests).
 Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
-  const bool dma_fits = !gelu_p && M * K <= kDmaMaxElems && N * K <= kDmaMaxElems;
+  const bool dma_fits = !gelu_p && M * (K + kStagePad) <= kDmaMaxElems && N * (K + kStagePad) <= kDmaMaxElems;
   if (const char* e = std::getenv("TPMLP_TILE")) {
     if (!std::strcmp(e, "128")) return Engine::Mfma128;
     if (!std::strcmp(e, "256")) return Engine::Mfma256;
@@ -148,9 +157,10 @@ hipError_t launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const voi
                       TailSplit tail, hipStream_t st) {
   const int ntile = sh.tiles_m * sh.tiles_n;
   const int nblk = tail.full + (ntile - tail.full) * tail.parts;
+  // operand extents in elements: rows (KC) or k-rows (MC) times the pitch
   hipLaunchKernelGGL((gemm_dma_kernel<Cfg, S, PK, QK, Epi>), dim3(nblk), dim3(Cfg::THREADS), 0, st, sh,
-                     Operand{static_cast<const uint16_t*>(p), ldp}, sh.M * sh.K,
-                     Operand{static_cast<const uint16_t*>(q), ldq}, sh.N * sh.K, epi, tail);
+                     Operand{static_cast<const uint16_t*>(p), ldp}, (PK ? sh.M : sh.K) * ldp,
+                     Operand{static_cast<const uint16_t*>(q), ldq}, (QK ? sh.N : sh.K) * ldq, epi, tail);
   if constexpr (Epi::kTailSplit) {
     if (tail.parts > 1) {
       const int ntail = ntile - tail.full;
@@ -164,9 +174,10 @@ hipError_t launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const voi
 }
 
 // C[M][N] = sum_k P[m][k] Q[k][n] through epilogue `epi`; PK / QK select the
-// k-contiguous layout of P / Q, GP applies gelu to P as it is loaded. Every
-// operand is dense: its leading dimension is its contiguous extent (K for a
-// k-contiguous operand, M or N otherwise). tail_ws: room for the partials of
+// k-contiguous layout of P / Q, GP applies gelu to P as it is loaded. ldp /
+// ldq: row pitch in elements, at least the contiguous extent (K for a
+// k-contiguous operand, M or N otherwise; larger only for the padded staged
+// copies, which the direct-load engines read). tail_ws: room for the partials of
 // a k-split last wave and its size in bytes; the split is taken only if
 // its partials (tail_bytes(plan_tail(...))) fit.
 template <class S, bool PK, bool QK, bool GP, class Epi>
@@ -281,14 +292,14 @@ int record(void* const* events, int i, hipStream_t st) {
     if ((expr) != hipSuccess) return TPMLP_ERR_HIP;     \
   } while (0)
 
-// Transpose a dense [R][C] 16-bit matrix into out [C][R] (gelu applied on the
-// way when GELU).
+// Transpose a dense [R][C] 16-bit matrix into out [C][staged_ld(R)] (gelu
+// applied on the way when GELU).
 template <class S, bool GELU>
 hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStream_t st) {
   if (R == 0 || C == 0) return hipSuccess;
   const int tiles_c = (int)ceil_div(C, kTrCols), tiles_r = (int)ceil_div(R, kTrWaveTile);
   hipLaunchKernelGGL((transpose16_kernel<S, GELU>), dim3(tiles_r * tiles_c), dim3(64 * kTrWaves), 0, st,
-                     static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C, tiles_c);
+                     static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C, staged_ld(R), tiles_c);
   return hipGetLastError();
 }
 
@@ -302,8 +313,8 @@ bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Forward workspace: [A_i^T [f][h]] [B_i^T [h][f]] (each only if its GEMM
-// stages) [tail partials of the second GEMM].
+// Forward workspace: [A_i^T [f][h + pad]] [B_i^T [h][f + pad]] (each only
+// if its GEMM stages) [tail partials of the second GEMM].
 struct FwdWs {
   size_t at_off, bt_off, tail_off, tail_bytes, total;
   bool at, bt;
@@ -311,12 +322,13 @@ struct FwdWs {
 
 FwdWs fwd_ws(const tpmlp_shape& s) {
   FwdWs w{};
-  const size_t hf = (size_t)(s.hidden * s.ffn_shard) * elt_size(s.dtype);
+  const size_t e = elt_size(s.dtype);
+  const size_t at_b = (size_t)(s.ffn_shard * staged_ld(s.hidden)) * e, bt_b = (size_t)(s.hidden * staged_ld(s.ffn_shard)) * e;
   w.at = stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
   w.bt = stages(s.dtype, s.tokens, s.hidden, s.ffn_shard);
   w.at_off = 0;
-  w.bt_off = w.at ? align256(hf) : 0;
-  w.tail_off = w.bt_off + (w.bt ? align256(hf) : 0);
+  w.bt_off = w.at ? align256(at_b) : 0;
+  w.tail_off = w.bt_off + (w.bt ? align256(bt_b) : 0);
   w.tail_bytes = gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard, w.bt);
   w.total = w.tail_off + align256(w.tail_bytes);
   return w;
@@ -324,7 +336,7 @@ FwdWs fwd_ws(const tpmlp_shape& s) {
 
 // Backward workspace: [dZ (if kept here)] [db1 partials fp32 [tiles][f]]
 // then, when the weight-gradient GEMMs stage: [H^T][dY^T] for dB and
-// [X^T][dZ^T] for dA (each [rows][T]); then the tail partials of the
+// [X^T][dZ^T] for dA (each [rows][T + pad]); then the tail partials of the
 // plain-store GEMMs (dB, dA, dXp run one after another and share them).
 struct BwdWs {
   size_t dz_off, dz_bytes, part_off, part_bytes, minimal;
@@ -345,7 +357,8 @@ BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
   w.minimal = w.part_bytes ? w.part_off + w.part_bytes : w.dz_bytes;
   w.stage_b2 = stages(s.dtype, s.ffn_shard, s.hidden, s.tokens);
   w.stage_b3 = stages(s.dtype, s.hidden, s.ffn_shard, s.tokens);
-  const size_t tf = align256((size_t)(s.tokens * s.ffn_shard) * e), th = align256((size_t)(s.tokens * s.hidden) * e);
+  const size_t tf = align256((size_t)(staged_ld(s.tokens) * s.ffn_shard) * e),
+               th = align256((size_t)(staged_ld(s.tokens) * s.hidden) * e);
   size_t at = align256(w.minimal);
   if (w.stage_b2) {
     w.ht_off = at;
@@ -380,7 +393,7 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
   if (room && w.at) {
     TPMLP_HIP((run_transpose<S, false>(A, wsb + w.at_off, h, f, st)));
     TPMLP_TRY(record(ev, 1, st));
-    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, X, h, wsb + w.at_off, h,
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, X, h, wsb + w.at_off, staged_ld(h),
                                               EpiBiasGelu<S>{(const T*)b1, (T*)Z, (T*)H, f}, st)));
   } else {
     TPMLP_TRY(record(ev, 1, st));
@@ -396,7 +409,8 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
   } else if (room && w.bt) {
     TPMLP_HIP((run_transpose<S, false>(B, wsb + w.bt_off, f, h, st)));
     TPMLP_TRY(record(ev, 3, st));
-    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, H, f, wsb + w.bt_off, f, EpiStore<S>{(T*)Yp, h},
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, H, f, wsb + w.bt_off, staged_ld(f),
+                                              EpiStore<S>{(T*)Yp, h},
                                               st, reinterpret_cast<float*>(wsb + w.tail_off), w.tail_bytes)));
   } else {
     TPMLP_TRY(record(ev, 3, st));
@@ -444,7 +458,8 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_HIP((run_transpose<S, false>(dY, wsb + w.dyt_off, Tn, h, st)));
     TPMLP_TRY(record(ev, 4, st));
-    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, Tn, wsb + w.dyt_off, Tn,
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, staged_ld(Tn), wsb + w.dyt_off,
+                                              staged_ld(Tn),
                                               EpiStore<S>{(T*)dB, h}, st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 3, st));
@@ -462,7 +477,8 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_TRY(record(ev, 6, st));
     TPMLP_HIP((run_transpose<S, false>(dZ, wsb + w.dzt_off, Tn, f, st)));
     TPMLP_TRY(record(ev, 7, st));
-    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, Tn, wsb + w.dzt_off, Tn,
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, staged_ld(Tn), wsb + w.dzt_off,
+                                              staged_ld(Tn),
                                               EpiStore<S>{(T*)dA, f}, st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 6, st));

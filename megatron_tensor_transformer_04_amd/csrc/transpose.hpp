@@ -1,5 +1,6 @@
 // out[c][r] = in[r][c] for a dense row-major [R][C] matrix of 16-bit values
-// (R and C multiples of 8).
+// (R and C multiples of 8); out rows are ldo >= R elements apart (ldo a
+// multiple of 8; columns R..ldo-1 are not written).
 //
 // The large-tile GEMM engine reads k-contiguous operands fastest (one
 // ds_read_b128 per fragment; an mn-contiguous operand needs two transposing
@@ -29,7 +30,7 @@ constexpr int kTrCols = kTrWaveTile * kTrWaves;
 template <class S, bool GELU>
 __global__ __launch_bounds__(64 * kTrWaves) void transpose16_kernel(const uint16_t* __restrict__ in,
                                                                     uint16_t* __restrict__ out, int64_t R, int64_t C,
-                                                                    int tiles_c) {
+                                                                    int64_t ldo, int tiles_c) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
   const int64_t r = (int64_t)tr * kTrWaveTile + (lane >> 3) * 8;                 // first row of the block
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(64 * kTrWaves) void transpose16_kernel(const uint16
     u32x4 o;
 #pragma unroll
     for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(v[2 * w + 1][j >> 1], v[2 * w][j >> 1], sel);
-    *reinterpret_cast<u32x4*>(out + (c + j) * R + r) = o;
+    *reinterpret_cast<u32x4*>(out + (c + j) * ldo + r) = o;
   }
 }
 

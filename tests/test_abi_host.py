@@ -82,18 +82,19 @@ def test_workspace_bytes(lib):
     assert ws(4096, 768, 3072, 1, MINIMAL) == (4096 // 128) * 3072 * 4
     # large shards stage k-contiguous copies of H, dY, X and dZ for the
     # weight-gradient GEMMs (each [rows][T] in 16 bits), after the minimal
-    # part. Their GEMMs then run on 256 x 320 tiles: dB and dA have
-    # 40 x 32 = 1280 tiles, five full waves on 256 CUs, dXp 64 x 32: no
-    # k-split tails
-    t = 16384 * 10240 * 2
+    # part, each row padded by 256 elements. Their GEMMs then run on 256 x 320
+    # tiles: dB and dA have 40 x 32 = 1280 tiles, five full waves on 256 CUs,
+    # dXp 64 x 32: no k-split tails
+    t = 10240 * (16384 + 256) * 2
     assert ws(16384, 10240, 10240, 2) == part + 4 * t
-    assert ws(16384, 10240, 10240, 2, DZ) == t + part + 4 * t
-    # ... and the forward stages A_i^T and B_i^T (Yp: 2560 tiles, no tail)
-    assert fws(16384, 10240, 10240, 2) == 2 * 10240 * 10240 * 2
+    assert ws(16384, 10240, 10240, 2, DZ) == 16384 * 10240 * 2 + part + 4 * t
+    # ... and the forward stages A_i^T and B_i^T, rows padded likewise (Yp:
+    # 2048 tiles of 256 x 320, no tail)
+    assert fws(16384, 10240, 10240, 2) == 2 * 10240 * (10240 + 256) * 2
     # h = 8192 (TP = 4 of a 32768-wide FFN): Yp and dXp have 64 x 32 tiles,
     # dB and dA 32 x 32 = 1024: no tails
-    t8 = 16384 * 8192 * 2
-    assert fws(16384, 8192, 8192, 2) == 2 * 8192 * 8192 * 2
+    t8 = 8192 * (16384 + 256) * 2
+    assert fws(16384, 8192, 8192, 2) == 2 * 8192 * (8192 + 256) * 2
     assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240 + 4 * t8
     # small shapes and fp32 stage nothing
     assert ws(4096, 768, 3072, 1) == ws(4096, 768, 3072, 1, MINIMAL)
@@ -114,7 +115,7 @@ def test_k_split_tail_workspace_full_shard(lib, monkeypatch):
     ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
     monkeypatch.setenv("TPMLP_TILE", "dma256")
     part = (16384 // 256) * 10240 * 4
-    t = 16384 * 10240 * 2
+    t = 10240 * (16384 + 256) * 2
     assert ws() == part + 4 * t + 64 * 4 * 256 * 256 * 4
 
 
