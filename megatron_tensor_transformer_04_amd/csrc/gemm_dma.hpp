@@ -76,9 +76,9 @@ struct DmaTile {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int LDS_P = BM * BK * 2, LDS_Q = BN * BK * 2;  // one stage
-  static constexpr int Q_OFF = STAGES * LDS_P;
-  static constexpr int LDS_BYTES = STAGES * (LDS_P + LDS_Q);
+  static constexpr int LDS_P = BM * BK * 2, LDS_Q = BN * BK * 2;  // one stage of P / Q
+  static constexpr int STG = LDS_P + LDS_Q;                       // one stage (P, then Q)
+  static constexpr int LDS_BYTES = STAGES * STG;
   // direct loads (1 KB blocks) per wave per stage
   static constexpr int LP = LDS_P / 1024 / WAVES, LQ = LDS_Q / 1024 / WAVES;
   static constexpr int GROUP = 8;
@@ -131,6 +131,22 @@ __device__ __forceinline__ void sched_interleave() {
     if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
   });
   sched_fence();
+}
+
+// Opaque copies: the compiler can neither hoist out of a loop nor merge what
+// is computed from the result. The constraints are AMDGPU register classes
+// (v: VGPR, s: SGPR), so the statements exist in the device pass only.
+__device__ __forceinline__ int opaque_v(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+  return x;
+}
+__device__ __forceinline__ int opaque_s(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+s"(x));
+#endif
+  return x;
 }
 
 // Offsets beyond every buffer's num_records: the load returns zeros.
@@ -283,95 +299,122 @@ struct FragAddr {
   }
 };
 
+// One workgroup per CU, each looping over work items v = blockIdx.x,
+// blockIdx.x + gridDim.x, ... (nwork items: the tiles, with the tail tiles
+// split into k-ranges, see TailSplit). Between two items the first k-tile
+// of the next item is loaded into the free stage while the epilogue of the
+// current one runs out of the other stage, so that its load latency hides
+// behind the epilogue instead of stalling a freshly started workgroup.
 template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi>
 __global__ __launch_bounds__(Cfg::THREADS)
 __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
 void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi,
-                     TailSplit tail) {
+                     TailSplit tail, int nwork) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
-  constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES, STG = Cfg::STG;
   static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
                 "an mn-contiguous operand needs a power-of-two tile extent (swizzle, loads per k-row)");
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
+  int lane = tid & 63;  // made opaque at the top of every work item (see below)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  const int w = map_work<Cfg::PER_XCD>(blockIdx.x, gridDim.x);
-  int tile = w, part = -1;  // part >= 0: a k-range of a tail tile
-  if (w >= tail.full) {
-    tile = tail.full + (w - tail.full) / tail.parts;
-    part = (w - tail.full) % tail.parts;
-  }
-  int tm, tn;
-  tile_coords<Cfg::GROUP>(tile, sh.tiles_m, sh.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kbeg = part >= 0 ? (int64_t)part * tail.k_part : 0;
-  const int64_t kend = part >= 0 ? min(sh.K, kbeg + tail.k_part) : sh.K;
-  const int kspan = kend > kbeg ? (int)(kend - kbeg) : 0;
-  const int nk = (kspan + BK - 1) / BK;
 
-  // Buffer resources based at the tile origin; num_records is the operand's
-  // extent from there, so any offset past the tensor reads zeros.
-  const int64_t pbase = P_KC ? m0 * P.ld : m0, qbase = Q_KC ? n0 * Q.ld : n0;
-  const __amdgpu_buffer_rsrc_t prs = uniform_rsrc(P.ptr + pbase, (p_extent - pbase) * 2);
-  const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(Q.ptr + qbase, (q_extent - qbase) * 2);
+  // A work item: its output tile and k-range.
+  struct Item {
+    int tile, part;  // part >= 0: a k-range of a tail tile
+    int tm, tn;
+    int64_t m0, n0, kbeg;
+    int kspan, nk;
+  };
+  auto decode = [&](int v) __attribute__((always_inline)) {
+    Item it;
+    const int w = map_work<Cfg::PER_XCD>(v, nwork);
+    it.tile = w;
+    it.part = -1;
+    if (w >= tail.full) {
+      it.tile = tail.full + (w - tail.full) / tail.parts;
+      it.part = (w - tail.full) % tail.parts;
+    }
+    tile_coords<Cfg::GROUP>(it.tile, sh.tiles_m, sh.tiles_n, it.tm, it.tn);
+    it.m0 = (int64_t)it.tm * BM;
+    it.n0 = (int64_t)it.tn * BN;
+    it.kbeg = it.part >= 0 ? (int64_t)it.part * tail.k_part : 0;
+    const int64_t kend = it.part >= 0 ? min(sh.K, it.kbeg + tail.k_part) : sh.K;
+    it.kspan = kend > it.kbeg ? (int)(kend - it.kbeg) : 0;
+    it.nk = (it.kspan + BK - 1) / BK;
+    return it;
+  };
+  // Buffer resources of an item's operand tiles, based at the tile origin
+  // with num_records = the operand's extent from there, so any offset past
+  // the tensor reads zeros.
+  auto p_rsrc = [&](const Item& it) __attribute__((always_inline)) {
+    const int64_t base = P_KC ? it.m0 * P.ld : it.m0;
+    return uniform_rsrc(P.ptr + base, (p_extent - base) * 2);
+  };
+  auto q_rsrc = [&](const Item& it) __attribute__((always_inline)) {
+    const int64_t base = Q_KC ? it.n0 * Q.ld : it.n0;
+    return uniform_rsrc(Q.ptr + base, (q_extent - base) * 2);
+  };
 
-  // Per-lane byte offsets from the tile origin at k = 0, loop-invariant;
-  // rows / columns outside the matrix get kOobOffset. The k advance of each
-  // tile goes in the instruction's scalar offset, so the K loop does no
-  // per-lane address arithmetic. pk0 / qk0: the k offset (within a tile) of
-  // load 0's chunk; load c's is that plus dma_kstep<>(c).
-  uint32_t pv[LP], qv[LQ];
+  // Per-lane byte offsets from the tile origin at k = 0; rows / columns
+  // outside the matrix get kOobOffset. The k advance of each tile goes in
+  // the instruction's scalar offset, so the K loop does no per-lane address
+  // arithmetic. pk0 / qk0: the k offset (within a tile) of load 0's chunk
+  // (the same for every item); load c's is that plus dma_kstep<>(c).
   int pk0 = 0, qk0 = 0;
-  static_for<0, LP>([&](auto c) {
-    int64_t rel;
-    int mn, kk;
-    dma_slot<P_KC, BM, BK>(c * Cfg::WAVES + wave, lane, P.ld, rel, mn, kk);
-    pv[c] = m0 + mn < sh.M ? (uint32_t)rel * 2u : kOobOffset;
-    if constexpr (c == 0) pk0 = kk;
-  });
-  static_for<0, LQ>([&](auto c) {
-    int64_t rel;
-    int mn, kk;
-    dma_slot<Q_KC, BN, BK>(c * Cfg::WAVES + wave, lane, Q.ld, rel, mn, kk);
-    qv[c] = n0 + mn < sh.N ? (uint32_t)rel * 2u : kOobOffset;
-    if constexpr (c == 0) qk0 = kk;
-  });
+  auto offsets = [&](const Item& it, uint32_t(&pv)[LP], uint32_t(&qv)[LQ]) __attribute__((always_inline)) {
+    // Recomputed per item from an opaque copy of the lane index: hoisting
+    // the item-independent 64-bit parts out of the item loop would keep
+    // them live across the K loop.
+    const int ln = opaque_v(lane);
+    static_for<0, LP>([&](auto c) {
+      int64_t rel;
+      int mn, kk;
+      dma_slot<P_KC, BM, BK>(c * Cfg::WAVES + wave, ln, P.ld, rel, mn, kk);
+      pv[c] = it.m0 + mn < sh.M ? (uint32_t)rel * 2u : kOobOffset;
+      if constexpr (c == 0) pk0 = kk;
+    });
+    static_for<0, LQ>([&](auto c) {
+      int64_t rel;
+      int mn, kk;
+      dma_slot<Q_KC, BN, BK>(c * Cfg::WAVES + wave, ln, Q.ld, rel, mn, kk);
+      qv[c] = it.n0 + mn < sh.N ? (uint32_t)rel * 2u : kOobOffset;
+      if constexpr (c == 0) qk0 = kk;
+    });
+  };
 
   typedef __attribute__((address_space(3))) void lds_void;
-  // Direct loads of k-tile t into its stage. On a K-tail tile, chunks at or
-  // beyond kend take kOobOffset (one 32-bit compare per load); a tile past
-  // the end (t >= nk) is all kOobOffset and fills its stage with zeros that
-  // nothing reads, which keeps the loop body free of branches.
-  auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    const int stage = t % ST;
-    const int krem = kspan - t * BK;  // k extent left from this tile on
-    const int64_t k0 = krem > 0 ? kbeg + (int64_t)t * BK : 0;
+  // Direct loads of k-tile t of item `it` into stage `stage`. On a K-tail
+  // tile, chunks at or beyond the item's k-range take kOobOffset (one 32-bit
+  // compare per load); a tile past the end (t >= nk) is all kOobOffset and
+  // fills its stage with zeros that nothing reads, which keeps the loop body
+  // free of branches.
+  auto issue_tile = [&](const Item& it, __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs,
+                        const uint32_t(&pv)[LP], const uint32_t(&qv)[LQ], int t, int stage)
+      __attribute__((always_inline)) {
+    const int krem = it.kspan - t * BK;  // k extent left from this tile on
+    const int64_t k0 = krem > 0 ? it.kbeg + (int64_t)t * BK : 0;
     const int psoff = __builtin_amdgcn_readfirstlane((int)((P_KC ? k0 : k0 * P.ld) * 2));
     const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
+    char* const sp = smem + stage * STG;
     static_for<0, LP>([&](auto c) {
       const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          prs, (lds_void*)(smem + stage * Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024), 16, off, psoff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + (c * Cfg::WAVES + wave) * 1024), 16, off,
+                                               psoff, 0, 0);
     });
     static_for<0, LQ>([&](auto c) {
       const uint32_t off = qk0 + dma_kstep<Q_KC, BN, Cfg::WAVES>(c) < krem ? qv[c] : kOobOffset;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qrs, (lds_void*)(smem + Cfg::Q_OFF + stage * Cfg::LDS_Q + (c * Cfg::WAVES + wave) * 1024), 16, off,
-          qsoff, 0, 0);
+          qrs, (lds_void*)(sp + Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024), 16, off, qsoff, 0, 0);
     });
   };
   constexpr int LOADS = LP + LQ;  // direct loads per wave per tile
 
   FragAddr<P_KC, BM, BK, FM> pa;
   FragAddr<Q_KC, BN, BK, FN> qa;
-  pa.init(lane, 0, wm * Cfg::WTM);
-  qa.init(lane, Cfg::Q_OFF, wn * Cfg::WTN);
-
   f32x16 acc[FM][FN];
-  static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
-
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto read_frags = [&](u32x4(&fa)[FM], u32x4(&fb)[FN], auto ks_c) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks_c)::value;
@@ -384,163 +427,216 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     });
   };
   constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
-
   // DS read instructions per substep (a transposing read moves half a
   // fragment).
   constexpr int DSR = (P_KC ? 1 : 2) * FM + (Q_KC ? 1 : 2) * FN;
 
-  // One straight-line loop body: no branch at all, so the accumulators keep
-  // their registers. The last iterations load and read stages nothing uses
-  // again (in bounds; zeros or stale data, discarded).
-  //
-  // Software pipeline, pinned with scheduling constraints (left alone, the
-  // compiler sinks each fragment read to just before its first MFMA and
-  // exposes the full LDS latency on every read): substep s issues all reads
-  // of substep s+1, then its own MFMAs. After the barrier, the direct loads
-  // that refill the freed stage and the reads of the next tile's first
-  // substep are interleaved one by one with the MFMAs of the last substep.
-  if (nk > 0) {
-    static_for<0, ST>([&](auto t) { issue_tile(t); });
-    wait_vmcnt<(ST - 1) * LOADS>();  // tile 0 has landed
-    barrier_lds();
-    read_frags(fa0, fb0, std::integral_constant<int, 0>{});
-    for (int t = 0; t < nk; ++t) {
-      static_for<0, NKS - 1>([&](auto ks) {
-        if constexpr (ks % 2 == 0) {
-          read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
-          sched_fence();
-          mfmas(fa0, fb0);
-        } else {
-          read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
-          sched_fence();
-          mfmas(fa1, fb1);
-        }
-        sched_fence();
-      });
-      // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight. The
-      // barrier also orders every wave's reads of stage t % S before the
-      // loads that refill it.
-      wait_vmcnt<(ST - 2) * LOADS>();
-      barrier_lds();
-      sched_fence();
-      issue_tile(t + ST);
-      const bool wrap = (t + 1) % ST == 0;
-      pa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_P) : (uint32_t)Cfg::LDS_P);
-      qa.advance(wrap ? (uint32_t)(-(ST - 1) * Cfg::LDS_Q) : (uint32_t)Cfg::LDS_Q);
-      read_frags(fa0, fb0, std::integral_constant<int, 0>{});
-      mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
-      sched_interleave<FM * FN, LOADS, DSR>();
-    }
-    // Drain the loads of the tiles past the end before LDS is reused (or
-    // released to the next workgroup).
-    wait_vmcnt<0>();
+  // Work item state is decoded again where it is needed rather than kept
+  // live across the K loop (scalar registers are the scarce resource);
+  // opaque_s() hides the work index from common-subexpression elimination.
+  int v = blockIdx.x;
+  int s0 = 0;  // stage of the current item's k-tile 0
+  {
+    const Item first = decode(v);
+    uint32_t pv[LP], qv[LQ];
+    offsets(first, pv, qv);
+    issue_tile(first, p_rsrc(first), q_rsrc(first), pv, qv, 0, 0);
   }
+  while (true) {
+    // Everything derived from the lane index is recomputed per item: hoisted
+    // out of the item loop it would stay live across the K loop and the
+    // epilogue and push the accumulators out of registers.
+    lane = opaque_v(lane);
+    const Item cur = decode(opaque_s(v));
+    const __amdgpu_buffer_rsrc_t prs = p_rsrc(cur), qrs = q_rsrc(cur);
+    uint32_t pv[LP], qv[LQ];
+    offsets(cur, pv, qv);
+    static_for<1, ST>([&](auto t) { issue_tile(cur, prs, qrs, pv, qv, t, (t + s0) % ST); });
+    static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
+    pa.init(lane, s0 * STG, wm * Cfg::WTM);
+    qa.init(lane, s0 * STG + Cfg::LDS_P, wn * Cfg::WTN);
 
-  // Epilogue, one block of 32 (or 16) rows of the wave's tile at a time,
-  // staged through a private LDS region so that global memory sees whole
-  // 16-byte row chunks:
-  //   input (if any): 16-byte row chunks -> LDS -> per lane the fragment's
-  //                   values via ds_read_b64_tr_b16 (four rows of a column);
-  //   outputs:        fp32 -> 16-bit, written to LDS at (row, column), read
-  //                   back as 16-byte row chunks and stored.
-  // Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each 32x32
-  // fragment, r = 0..15. The barrier first makes sure no wave still reads
-  // fragments or receives direct loads (each drained its own above).
-  if (part >= 0) {
-    // One k-range of a tail tile: the raw fp32 partial sums, in place of the
-    // epilogue (tail_finish_kernel applies it).
-    float* pt = tail.partial + ((int64_t)(tile - tail.full) * tail.parts + part) * (BM * BN);
-    static_for<0, FM>([&](auto i) {
-      static_for<0, FN>([&](auto j) {
-        const int c = wn * Cfg::WTN + j * 32 + (lane & 31);
-        static_for<0, 16>([&](auto r) {
-          const int row = wm * Cfg::WTM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-          pt[row * BN + c] = acc[i][j][(int)r];
+    // One straight-line loop body: no branch at all, so the accumulators
+    // keep their registers. The last iterations load and read stages
+    // nothing uses again (in bounds; zeros or stale data, discarded).
+    //
+    // Software pipeline, pinned with scheduling constraints (left alone, the
+    // compiler sinks each fragment read to just before its first MFMA and
+    // exposes the full LDS latency on every read): substep s issues all
+    // reads of substep s+1, then its own MFMAs. After the barrier, the
+    // direct loads that refill the freed stage and the reads of the next
+    // tile's first substep are interleaved one by one with the MFMAs of the
+    // last substep.
+    if (cur.nk > 0) {
+      wait_vmcnt<(ST - 1) * LOADS>();  // k-tile 0 has landed
+      barrier_lds();
+      read_frags(fa0, fb0, std::integral_constant<int, 0>{});
+      for (int t = 0; t < cur.nk; ++t) {
+        static_for<0, NKS - 1>([&](auto ks) {
+          if constexpr (ks % 2 == 0) {
+            read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+            sched_fence();
+            mfmas(fa0, fb0);
+          } else {
+            read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+            sched_fence();
+            mfmas(fa1, fb1);
+          }
+          sched_fence();
         });
-      });
-    });
-    return;
-  }
-  barrier_lds();
-  constexpr int CPR = Cfg::WTN / 8;            // 16-byte chunks per staged row
-  constexpr int RS = Cfg::WTN * 2 + 16;        // staged row stride (bytes)
-  // Rows per staged block: 32 (a whole fragment row) when every wave's
-  // blocks fit in LDS, else 16 (two halves per fragment row).
-  constexpr int HB = Cfg::WAVES * Epi::kOuts * 32 * RS <= Cfg::LDS_BYTES ? 32 : 16;
-  constexpr int BLK = HB * RS;                 // one staged block
-  constexpr int PASSES = HB * CPR / 64;        // chunks per lane per block
-  static_assert(PASSES * 64 == HB * CPR, "a staged block is a whole number of chunks per lane");
-  static_assert(Cfg::WAVES * Epi::kOuts * BLK <= Cfg::LDS_BYTES, "staging fits in the stage buffers");
-  char* const stg = smem + wave * (Epi::kOuts * BLK);
-  const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
-  const int G = lane >> 4, jj = lane & 15;
-  float cs[FN];
-  static_for<0, FN>([&](auto j) { cs[j] = 0.0f; });
-  static_for<0, FM * (32 / HB)>([&](auto ib) {
-    constexpr int i = ib / (32 / HB);            // fragment row
-    constexpr int g0 = (ib % (32 / HB)) * (HB / 8);  // first 8-row group of the block
-    const int64_t mb = mw + i * 32 + g0 * 8;
-    if constexpr (Epi::kInput) {
-      static_for<0, PASSES>([&](auto p) {
-        const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (mb + row < sh.M && nw + c8 * 8 < sh.N)
-          v = *reinterpret_cast<const u32x4*>(epi.input() + (mb + row) * epi.ld + nw + c8 * 8);
-        *reinterpret_cast<u32x4*>(stg + row * RS + c8 * 16) = v;
-      });
+        // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight. The
+        // barrier also orders every wave's reads of tile t's stage before
+        // the loads that refill it.
+        wait_vmcnt<(ST - 2) * LOADS>();
+        barrier_lds();
+        sched_fence();
+        const int st_t = (t + s0) % ST;
+        issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t);
+        const bool wrap = st_t == ST - 1;  // tile t+1 sits in stage 0
+        pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+        qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+        read_frags(fa0, fb0, std::integral_constant<int, 0>{});
+        mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
+        sched_interleave<FM * FN, LOADS, DSR>();
+      }
     }
-    static_for<0, FN>([&](auto j) {
-      const int64_t n = nw + j * 32 + (lane & 31);
-      const bool n_ok = n < sh.N;
-      const float colp = n_ok ? epi.colparam(n) : 0.0f;
-      static_for<0, HB / 8>([&](auto g) {
-        float in[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (Epi::kInput) {
-          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(stg + (8 * g + 4 * (G >> 1) + (jj >> 2)) * RS + ((G & 1) * 16 + (jj & 3) * 4) * 2 +
-                           j * 64));
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) in[rr] = S::to_f((typename S::T)(uint16_t)t[rr]);
-        }
-        static_for<0, 4>([&](auto rr) {
-          const int row = 8 * g + 4 * (lane >> 5) + rr;  // within the block
-          float o[2];
-          const float c = epi.eval(acc[i][j][4 * (g0 + g) + rr], colp, in[rr], o);
-          if (n_ok && mb + row < sh.M) cs[j] += c;
-          static_for<0, Epi::kOuts>([&](auto k) {
-            *reinterpret_cast<typename S::T*>(stg + k * BLK + row * RS + (j * 32 + (lane & 31)) * 2) =
-                S::from_f(o[k]);
+    // Drain this wave's loads of the tiles past the end (they write LDS).
+    wait_vmcnt<0>();
+
+    // Stages: the next item's k-tile 0 goes to the stage after the last
+    // tile this item issued (free: its last reader passed a barrier above,
+    // and this wave's own loads into it have drained); the epilogue stages
+    // its output through the stage the next item's k-tile ST-1 will use.
+    const int s_next = (cur.nk + s0) % ST;
+    const int s_epi = (cur.nk + s0 + ST - 1) % ST;
+    const int v_next = v + (int)gridDim.x;
+    const bool has_next = v_next < nwork;
+    if (has_next) {
+      const Item nxt = decode(opaque_s(v_next));
+      uint32_t pv2[LP], qv2[LQ];
+      offsets(nxt, pv2, qv2);
+      const __amdgpu_buffer_rsrc_t prs2 = p_rsrc(nxt), qrs2 = q_rsrc(nxt);
+      static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST); });
+    }
+
+    const Item done = decode(opaque_s(v));
+    const int64_t m0 = done.m0, n0 = done.n0;
+    if (done.part >= 0) {
+      // One k-range of a tail tile: the raw fp32 partial sums, in place of
+      // the epilogue (tail_finish_kernel applies it).
+      float* pt = tail.partial + ((int64_t)(done.tile - tail.full) * tail.parts + done.part) * (BM * BN);
+      static_for<0, FM>([&](auto i) {
+        static_for<0, FN>([&](auto j) {
+          const int c = wn * Cfg::WTN + j * 32 + (lane & 31);
+          static_for<0, 16>([&](auto r) {
+            const int row = wm * Cfg::WTM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            pt[row * BN + c] = acc[i][j][(int)r];
           });
         });
       });
-    });
-    static_for<0, Epi::kOuts>([&](auto k) {
-      typename S::T* const out = epi.output(k);
-      if (out) {
-        static_for<0, PASSES>([&](auto p) {
-          const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + k * BLK + row * RS + c8 * 16);
-          if (mb + row < sh.M && nw + c8 * 8 < sh.N)
-            *reinterpret_cast<u32x4*>(out + (mb + row) * epi.ld + nw + c8 * 8) = v;
-        });
-      }
-    });
-  });
-  if constexpr (Epi::kColSum) {
-    // Column sums of this tile, in a fixed order: the two lane halves, then
-    // the waves along M.
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(smem);  // [WAVES_M][BN]
-    static_for<0, FN>([&](auto j) { cs[j] += __shfl_xor(cs[j], 32); });
-    if (lane < 32) static_for<0, FN>([&](auto j) { red[wm * BN + wn * Cfg::WTN + j * 32 + lane] = cs[j]; });
-    __syncthreads();
-    for (int c = tid; c < BN; c += Cfg::THREADS) {
-      float s = 0.0f;
+    } else {
+      // Epilogue, one block of 32, 16 or 8 rows of the wave's tile at a
+      // time, staged through a private region of stage s_epi so that global
+      // memory sees whole 16-byte row chunks:
+      //   input (if any): 16-byte row chunks -> LDS -> per lane the
+      //                   fragment's values via ds_read_b64_tr_b16 (four
+      //                   rows of a column);
+      //   outputs:        fp32 -> 16-bit, written to LDS at (row, column),
+      //                   read back as 16-byte row chunks and stored.
+      // Lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] of each 32x32
+      // fragment, r = 0..15. The barrier first makes sure no wave still
+      // reads fragments of that stage.
+      barrier_lds();
+      char* const epi_lds = smem + s_epi * STG;
+      constexpr int CPR = Cfg::WTN / 8;      // 16-byte chunks per staged row
+      constexpr int RS = Cfg::WTN * 2 + 16;  // staged row stride (bytes)
+      // Rows per staged block: as many (32, 16 or 8) as fit in one stage.
+      constexpr int HB = Cfg::WAVES * Epi::kOuts * 32 * RS <= STG   ? 32
+                         : Cfg::WAVES * Epi::kOuts * 16 * RS <= STG ? 16
+                                                                    : 8;
+      constexpr int BLK = HB * RS;                    // one staged block
+      constexpr int PASSES = (HB * CPR + 63) / 64;    // chunks per lane per block (the last pass may be partial)
+      constexpr bool PART = PASSES * 64 != HB * CPR;
+      static_assert(Cfg::WAVES * Epi::kOuts * BLK <= STG, "staging fits in one stage");
+      char* const stg = epi_lds + wave * (Epi::kOuts * BLK);
+      const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
+      const int G = lane >> 4, jj = lane & 15;
+      float cs[FN];
+      static_for<0, FN>([&](auto j) { cs[j] = 0.0f; });
+      static_for<0, FM * (32 / HB)>([&](auto ib) {
+        constexpr int i = ib / (32 / HB);                // fragment row
+        constexpr int g0 = (ib % (32 / HB)) * (HB / 8);  // first 8-row group of the block
+        const int64_t mb = mw + i * 32 + g0 * 8;
+        if constexpr (Epi::kInput) {
+          static_for<0, PASSES>([&](auto p) {
+            const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
+            if (PART && p == PASSES - 1 && q >= HB * CPR) return;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (mb + row < sh.M && nw + c8 * 8 < sh.N)
+              x = *reinterpret_cast<const u32x4*>(epi.input() + (mb + row) * epi.ld + nw + c8 * 8);
+            *reinterpret_cast<u32x4*>(stg + row * RS + c8 * 16) = x;
+          });
+        }
+        static_for<0, FN>([&](auto j) {
+          const int64_t n = nw + j * 32 + (lane & 31);
+          const bool n_ok = n < sh.N;
+          const float colp = n_ok ? epi.colparam(n) : 0.0f;
+          static_for<0, HB / 8>([&](auto g) {
+            float in[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (Epi::kInput) {
+              typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+              const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(stg + (8 * g + 4 * (G >> 1) + (jj >> 2)) * RS + ((G & 1) * 16 + (jj & 3) * 4) * 2 +
+                               j * 64));
 #pragma unroll
-      for (int w = 0; w < Cfg::WAVES_M; ++w) s += red[w * BN + c];
-      if (n0 + c < sh.N) epi.colsum(tm, n0 + c, s);
+              for (int rr = 0; rr < 4; ++rr) in[rr] = S::to_f((typename S::T)(uint16_t)x[rr]);
+            }
+            static_for<0, 4>([&](auto rr) {
+              const int row = 8 * g + 4 * (lane >> 5) + rr;  // within the block
+              float o[2];
+              const float c = epi.eval(acc[i][j][4 * (g0 + g) + rr], colp, in[rr], o);
+              if (n_ok && mb + row < sh.M) cs[j] += c;
+              static_for<0, Epi::kOuts>([&](auto k) {
+                *reinterpret_cast<typename S::T*>(stg + k * BLK + row * RS + (j * 32 + (lane & 31)) * 2) =
+                    S::from_f(o[k]);
+              });
+            });
+          });
+        });
+        static_for<0, Epi::kOuts>([&](auto k) {
+          typename S::T* const out = epi.output(k);
+          if (out) {
+            static_for<0, PASSES>([&](auto p) {
+              const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
+              if (PART && p == PASSES - 1 && q >= HB * CPR) return;
+              const u32x4 x = *reinterpret_cast<const u32x4*>(stg + k * BLK + row * RS + c8 * 16);
+              if (mb + row < sh.M && nw + c8 * 8 < sh.N)
+                *reinterpret_cast<u32x4*>(out + (mb + row) * epi.ld + nw + c8 * 8) = x;
+            });
+          }
+        });
+      });
+      if constexpr (Epi::kColSum) {
+        // Column sums of this tile, in a fixed order: the two lane halves,
+        // then the waves along M.
+        __syncthreads();
+        float* red = reinterpret_cast<float*>(epi_lds);  // [WAVES_M][BN]
+        static_for<0, FN>([&](auto j) { cs[j] += __shfl_xor(cs[j], 32); });
+        if (lane < 32) static_for<0, FN>([&](auto j) { red[wm * BN + wn * Cfg::WTN + j * 32 + lane] = cs[j]; });
+        __syncthreads();
+        for (int c = tid; c < BN; c += Cfg::THREADS) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int w = 0; w < Cfg::WAVES_M; ++w) sum += red[w * BN + c];
+          if (n0 + c < sh.N) epi.colsum(done.tm, n0 + c, sum);
+        }
+      }
     }
+    if (!has_next) break;
+    // Every wave is done with stage s_epi before the next item loads it.
+    barrier_lds();
+    v = v_next;
+    s0 = s_next;
   }
 }
 

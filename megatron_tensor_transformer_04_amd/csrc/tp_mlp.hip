@@ -156,11 +156,13 @@ template <class Cfg, class S, bool PK, bool QK, class Epi>
 hipError_t launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const void* q, int64_t ldq, const Epi& epi,
                       TailSplit tail, hipStream_t st) {
   const int ntile = sh.tiles_m * sh.tiles_n;
-  const int nblk = tail.full + (ntile - tail.full) * tail.parts;
+  const int nwork = tail.full + (ntile - tail.full) * tail.parts;
+  // one workgroup per CU, looping over the work items
+  const int nblk = std::min(nwork, kCUs * Cfg::OCC);
   // operand extents in elements: rows (KC) or k-rows (MC) times the pitch
   hipLaunchKernelGGL((gemm_dma_kernel<Cfg, S, PK, QK, Epi>), dim3(nblk), dim3(Cfg::THREADS), 0, st, sh,
                      Operand{static_cast<const uint16_t*>(p), ldp}, (PK ? sh.M : sh.K) * ldp,
-                     Operand{static_cast<const uint16_t*>(q), ldq}, (QK ? sh.N : sh.K) * ldq, epi, tail);
+                     Operand{static_cast<const uint16_t*>(q), ldq}, (QK ? sh.N : sh.K) * ldq, epi, tail, nwork);
   if constexpr (Epi::kTailSplit) {
     if (tail.parts > 1) {
       const int ntail = ntile - tail.full;
