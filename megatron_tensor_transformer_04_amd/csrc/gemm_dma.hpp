@@ -11,8 +11,8 @@
 // p[m*ld + k], Q[k][n] at q[n*ld + k]) or mn-contiguous ("MC": P[m][k] at
 // p[k*ld + m], Q[k][n] at q[k*ld + n]).
 //
-// LDS is a ring of STAGES k-tiles (BK deep); P's stages come first, then Q's:
-//   [P stage 0 .. P stage S-1][Q stage 0 .. Q stage S-1]
+// LDS is a ring of STAGES k-tiles (BK deep), each stage P's tile then Q's:
+//   [P stage 0][Q stage 0] .. [P stage S-1][Q stage S-1]
 //   KC tile: [rows][BK], rows of BK/8 16-byte chunks; chunk c of row r sits
 //            at c ^ sk(r): sk(r) = (r & 7) ^ ((r >> 3) & 1) for BK = 64,
 //            ((r >> 1) ^ (r >> 3)) & 3 for BK = 32.
@@ -35,9 +35,9 @@
 // compiler does not accumulate it in place, and copies every accumulator
 // once per use.)
 //
-// Pipeline. Tile t lives in stage t % S and is consumed in BK/16 substeps
-// (fragments double-buffered in registers). The prologue issues tiles
-// 0..S-1; iteration t then does
+// Pipeline. Within one output tile, k-tile t lives in stage (t + s0) % S
+// and is consumed in BK/16 substeps (fragments double-buffered in
+// registers). Tiles 0..S-1 are issued first; iteration t then does
 //   read frags (t, 1)        | MFMAs (t, 0)
 //   ...
 //   read frags (t, last)     | MFMAs (t, last-1)
@@ -49,6 +49,8 @@
 // of MFMA work to land. Scheduling constraints hold this order (the
 // compiler's own schedule serialises each read with its first use), and
 // after the barrier the loads and reads are interleaved with the MFMAs.
+// Workgroups are persistent (see gemm_dma_kernel): the next output tile's
+// k-tile 0 is issued before the current tile's epilogue.
 //
 // Workgroup -> tile order: see map_work and tile_coords.
 #pragma once
