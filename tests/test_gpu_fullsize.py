@@ -96,3 +96,18 @@ def test_four_shards_of_the_2p4b_mlp_sum_to_the_unsharded_result(gpu_lib):
     _check("db1[cols]", db1, rc["db1"], tol, errs)
     _check("dB[cols,:]", dB, rc["dB"], tol, errs)
     print("errors", errs, flush=True)
+
+
+def test_operands_beyond_the_direct_load_offset_range(gpu_lib):
+    """X and dY of 131072 x 8192 bf16 (2 GiB each, more than 2^30 elements):
+    the first GEMM and the dZ GEMM (512 tiles of 256 x 256 each) exceed the
+    32-bit byte offsets of the direct-load engine and run on the
+    register-staged 256 x 256 engine with 64-bit addressing; Yp and dXp still
+    use direct loads, and the weight gradients (32 tiles each) the 128 x 128
+    engine. Checked on sampled rows and columns."""
+    T, h, f = 131072, 8192, 256
+    print(f"case large operands T={T} h={h} f={f} bf16", flush=True)
+    inp = synth.draw_inputs(T, h, f, "bf16", seed=21, sigma_dy=1.0)
+    out = run_shard(gpu_lib, *device_inputs(inp))
+    errs = _sampled_parity(inp, out, inp.A, inp.b1, inp.B, TOL["bf16"], seed=3)
+    print("errors", errs, flush=True)
