@@ -113,6 +113,31 @@ def cpu_baseline(inp, cfg, target_s):
     }
 
 
+def reduce_partials_rate(tpmlp, Yp, cfg, dev, reps=10):
+    """HBM rate of tp_mlp_reduce_partials on the TP group's partials of this
+    workload: tp partials [T, h] (+ b2) -> Y [T, h], timed with HIP events
+    on the launch stream. Not part of a step (the sum over ranks is the
+    caller's); reported beside it."""
+    import torch
+    T, h = Yp.shape
+    parts = [Yp] + [torch.empty_like(Yp).copy_(Yp) for _ in range(cfg.tp - 1)]
+    b2 = torch.zeros((h,), dtype=Yp.dtype, device=dev)
+    out = torch.empty_like(Yp)
+    for _ in range(2):
+        tpmlp.tp_mlp_reduce_partials(parts, b2, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tpmlp.tp_mlp_reduce_partials(parts, b2, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = (cfg.tp + 1) * T * h * Yp.element_size() + h * Yp.element_size()
+    del parts, out
+    return {"parts": cfg.tp, "ms": round(ms, 4), "bytes": nbytes, "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / 8000.0, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +146,8 @@ def main():
     ap.add_argument("--config", default="gpt_h10240")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reduce", action="store_true",
+                    help="skip timing tp_mlp_reduce_partials (the TP group's sum of partials, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run one plain device copy of this many MiB (a known-size kernel that "
                          "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
@@ -205,6 +232,8 @@ def main():
     dom = max(GEMM_STEPS, key=lambda n: per[n])
     achieved = gemm_flops / (per[dom] * 1e-3) / 1e12
 
+    reduce_line = None if args.no_reduce else reduce_partials_rate(tpmlp, Yp, cfg, dev)
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -233,6 +262,7 @@ def main():
             "traffic": profiled_traffic(cfg.name, dom),
         },
         "cpu_baseline": None,
+        "reduce_partials": reduce_line,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)

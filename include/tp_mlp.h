@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 2
+#define TPMLP_ABI_VERSION 3
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -185,6 +185,34 @@ int tp_mlp_bwd(const tpmlp_shape* shape,
                void* dZ, void* dXp, void* dA, void* dB, void* db1,
                void* ws, size_t ws_bytes,
                void* stream, void* const* events);
+
+/*
+ * Sum over ranks of the row-parallel partials, for P ranks whose partials
+ * sit on this device: the arithmetic of the all-reduce that follows the
+ * second linear ("Understanding the Megatron-LM architecture: how 3D
+ * parallelism assigns roles", section 1, the row-split item), and, over one
+ * rank's slice of rows, of the reduce-scatter that replaces it when the
+ * sequence dimension is split as well ("Training GPT-2 with Megatron-LM",
+ * section 5.1, the --sequence-parallel switch). For rows r in
+ * [row_begin, row_end):
+ *   out[r - row_begin][c] = round( sum_{i < nparts} parts[i][r][c] (+ bias[c]) )
+ * with fp32 sums in the order i = 0, 1, ..., the bias added last and one
+ * rounding to the storage dtype.
+ *   shape       tokens (rows of each partial), hidden (columns) and dtype;
+ *               ffn_shard is not used but must be valid
+ *   nparts      1 .. 16 (TPMLP_ERR_SHAPE otherwise)
+ *   parts       HOST array of nparts DEVICE pointers, each [tokens, hidden]
+ *               (the forward's Yp or the backward's dXp of each rank)
+ *   bias        [hidden] (b2 after the forward), or NULL for none
+ *   row_begin, row_end   0 <= row_begin <= row_end <= tokens
+ *               (TPMLP_ERR_SHAPE otherwise); all rows: 0, tokens
+ *   out         [row_end - row_begin, hidden]; must not overlap any part or
+ *               the bias (TPMLP_ERR_ALIAS: no in-place form)
+ * Asynchronous on `stream` like the other calls; bitwise deterministic.
+ */
+#define TPMLP_MAX_PARTS 16
+int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* const* parts, const void* bias,
+                           int64_t row_begin, int64_t row_end, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     TPMLP_BF16,
     TPMLP_F16,
     TPMLP_F32,
+    TPMLP_MAX_PARTS,
     TPMLP_WS_DZ,
     TPMLP_WS_MINIMAL,
     TpMlpError,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     tp_mlp_bwd,
     tp_mlp_fwd,
     tp_mlp_fwd_workspace_bytes,
+    tp_mlp_reduce_partials,
     tp_mlp_status_string,
     tp_mlp_workspace_bytes,
 )

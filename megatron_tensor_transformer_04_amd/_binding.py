@@ -24,7 +24,8 @@ STATUS = {
     7: "TPMLP_ERR_ALIAS",
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
-           "tp_mlp_fwd", "tp_mlp_bwd")
+           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_reduce_partials")
+TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL = 1, 2
 FWD_EVENTS = ("TA", "F1", "TB", "F2")                                     # steps bracketed by the 5 events
 BWD_EVENTS = ("B1", "B5", "TH", "TdY", "B2", "TX", "TdZ", "B3", "B4")    # ... by the 10 events
@@ -65,6 +66,9 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd.restype = ctypes.c_int
     lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_reduce_partials.restype = ctypes.c_int
+    lib.tp_mlp_reduce_partials.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int, ctypes.POINTER(vp), vp,
+                                           ctypes.c_int64, ctypes.c_int64, vp, vp]
     _lib = lib
     return lib
 
@@ -152,6 +156,18 @@ def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, even
     ev = _events(events)
     _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
                              _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def tp_mlp_reduce_partials(parts, bias, out, row_begin: int = 0, row_end=None, *, stream=None) -> None:
+    """out = sum of the [T, h] partials `parts` (one per rank, summed in list
+    order in fp32) plus `bias` (or None), over rows [row_begin, row_end)."""
+    T, h = parts[0].shape
+    if row_end is None:
+        row_end = T
+    s = shape_of(T, h, 0, _dtype_code(parts[0]))
+    arr = (ctypes.c_void_p * max(len(parts), 1))(*[_ptr(p) for p in parts])
+    _check(load().tp_mlp_reduce_partials(ctypes.byref(s), len(parts), arr, _ptr(bias), int(row_begin), int(row_end),
+                                         _ptr(out), _stream(stream)))
 
 
 # ---- convenience wrappers that allocate the outputs with torch ----

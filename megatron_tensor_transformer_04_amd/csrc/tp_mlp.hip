@@ -9,6 +9,9 @@
 // are stored mn-contiguous (A_i and B_i in the forward; X, dY, H and dZ for
 // the weight gradients) are first transposed into it by an HBM-bound kernel
 // (TA, TB; TH, TdY, TX, TdZ), so all six GEMMs read k-contiguous tiles.
+//
+// tp_mlp_reduce_partials sums the row-parallel partials of P ranks held on
+// this device (plus b2), over all rows or one rank's slice of rows.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,6 +24,7 @@
 #include "gemm_dma.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_simt.hpp"
+#include "reduce.hpp"
 #include "transpose.hpp"
 
 namespace tpmlp {
@@ -574,6 +578,50 @@ int tp_mlp_bwd(const tpmlp_shape* shape, const void* dY, const void* X, const vo
     default:
       return bwd_impl<StoreBF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
   }
+}
+
+int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* const* parts, const void* bias,
+                           int64_t row_begin, int64_t row_end, void* out, void* stream) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  if (nparts < 1 || nparts > kMaxParts) return TPMLP_ERR_SHAPE;
+  if (!parts) return TPMLP_ERR_NULL;
+  if (row_begin < 0 || row_end < row_begin || row_end > s.tokens) return TPMLP_ERR_SHAPE;
+  const size_t e = elt_size(s.dtype);
+  const int64_t rows = row_end - row_begin;
+  const size_t Th = (size_t)(s.tokens * s.hidden) * e, hb = (size_t)s.hidden * e, ob = (size_t)(rows * s.hidden) * e;
+  Span in[kMaxParts + 1];
+  bool in_req[kMaxParts + 1];
+  for (int i = 0; i < nparts; ++i) {
+    in[i] = Span{parts[i], Th};
+    in_req[i] = true;
+  }
+  in[nparts] = Span{bias, hb};
+  in_req[nparts] = false;
+  const Span outs[1] = {{out, ob}};
+  const bool out_req[1] = {true};
+  TPMLP_TRY(check_buffers(in, nparts + 1, in_req, outs, 1, out_req));
+  if (ob == 0) return TPMLP_OK;
+  PartList pl{};
+  for (int i = 0; i < nparts; ++i) pl.p[i] = parts[i];
+  const int64_t chunks = rows * s.hidden / (16 / (int64_t)e);
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(chunks, 256), int64_t(1) << 20);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (s.dtype) {
+    case TPMLP_F32:
+      hipLaunchKernelGGL(reduce_partials_kernel<StoreF32>, dim3(grid), dim3(256), 0, st, pl, nparts,
+                         static_cast<const float*>(bias), row_begin, rows, s.hidden, static_cast<float*>(out));
+      break;
+    case TPMLP_F16:
+      hipLaunchKernelGGL(reduce_partials_kernel<StoreF16>, dim3(grid), dim3(256), 0, st, pl, nparts,
+                         static_cast<const uint16_t*>(bias), row_begin, rows, s.hidden, static_cast<uint16_t*>(out));
+      break;
+    default:
+      hipLaunchKernelGGL(reduce_partials_kernel<StoreBF16>, dim3(grid), dim3(256), 0, st, pl, nparts,
+                         static_cast<const uint16_t*>(bias), row_begin, rows, s.hidden, static_cast<uint16_t*>(out));
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@ from .mlp import (
     shard_weights,
     shard_forward,
     shard_backward,
+    reduce_partials,
     sampled_rows,
     sampled_cols,
     rel_err,
@@ -34,6 +35,7 @@ __all__ = [
     "shard_weights",
     "shard_forward",
     "shard_backward",
+    "reduce_partials",
     "sampled_rows",
     "sampled_cols",
     "rel_err",

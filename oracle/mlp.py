@@ -108,6 +108,27 @@ def shard_backward(X, A_i, b1_i, B_i, dY, Z_i=None):
     return {"dZ": g["dZ"], "dA": g["dA"], "db1": g["db1"], "dB": g["dB"], "dXp": g["dX"]}
 
 
+def reduce_partials(parts, bias=None, row_begin=0, row_end=None):
+    """Sum over ranks of the row-parallel partials, plus the second bias.
+
+    The result of a row split is all-reduced ("Understanding the Megatron-LM
+    architecture: how 3D parallelism assigns roles", section 1, the
+    row-split item): Y = sum_i Y_p,i + b2 forward, dX = sum_i dX_p,i
+    backward. With the sequence dimension split as well ("Training GPT-2 with
+    Megatron-LM", section 5.1, --sequence-parallel) the all-reduce becomes a
+    reduce-scatter: rank r keeps only its slice of token rows of the same
+    sum, here rows [row_begin, row_end). float64, exact up to rounding.
+    """
+    T = np.asarray(parts[0]).shape[0]
+    row_end = T if row_end is None else row_end
+    acc = np.zeros_like(np.asarray(parts[0][row_begin:row_end], dtype=np.float64))
+    for p in parts:
+        acc = acc + np.asarray(p[row_begin:row_end], dtype=np.float64)
+    if bias is not None:
+        acc = acc + np.asarray(bias, dtype=np.float64)[None, :]
+    return acc
+
+
 def sampled_rows(X, A_i, b1_i, B_i, dY, rows):
     """Shard outputs restricted to token rows `rows`.
 

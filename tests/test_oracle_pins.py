@@ -175,6 +175,52 @@ def test_split_identities(tp):
         assert oracle.rel_err(fw[0]["Yp"] + b2[None, :], full["Y"]) > 1e-3
 
 
+# ------------------------------------- reduction of the row-split partials ----
+
+def test_reduce_partials_matches_scalar_loops():
+    rng = np.random.default_rng(51)
+    P, T, h = 3, 5, 4
+    parts = [_rand(rng, T, h) for _ in range(P)]
+    bias = _rand(rng, h)
+    for rb, re_ in ((0, T), (1, 4), (2, 2)):
+        got = oracle.reduce_partials(parts, bias, rb, re_)
+        assert got.shape == (re_ - rb, h)
+        for r in range(rb, re_):
+            for c in range(h):
+                s = 0.0
+                for i in range(P):
+                    s += parts[i][r][c]
+                s += bias[c]
+                assert got[r - rb][c] == pytest.approx(s, rel=1e-15, abs=1e-15)
+    # without a bias: the plain sum
+    got = oracle.reduce_partials(parts)
+    assert got[4][3] == pytest.approx(parts[0][4][3] + parts[1][4][3] + parts[2][4][3], rel=1e-15)
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4])
+def test_reduced_partials_give_the_unsharded_mlp(tp):
+    """The all-reduce of the shards' partials (plus b2) is the unsharded
+    output and input gradient; the reduce-scatter slices, stacked, are the
+    same sum."""
+    rng = np.random.default_rng(60 + tp)
+    T, h, F = 8, 8, 16
+    X, A, b1, B, dY, b2 = (_rand(rng, T, h), _rand(rng, h, F, scale=0.3), _rand(rng, F, scale=0.1),
+                           _rand(rng, F, h, scale=0.3), _rand(rng, T, h), _rand(rng, h, scale=0.1))
+    full = oracle.mlp_forward(X, A, b1, B, b2)
+    g = oracle.mlp_backward(X, A, b1, B, dY)
+    yps = [oracle.shard_forward(X, *oracle.shard_weights(A, b1, B, tp, r))["Yp"] for r in range(tp)]
+    dxps = [oracle.shard_backward(X, *oracle.shard_weights(A, b1, B, tp, r), dY)["dXp"] for r in range(tp)]
+    assert oracle.rel_err(oracle.reduce_partials(yps, b2), full["Y"]) <= 1e-12
+    assert oracle.rel_err(oracle.reduce_partials(dxps), g["dX"]) <= 1e-12
+    rows = T // tp
+    scattered = [oracle.reduce_partials(yps, b2, r * rows, (r + 1) * rows) for r in range(tp)]
+    assert oracle.rel_err(np.concatenate(scattered, axis=0), full["Y"]) <= 1e-12
+    if tp > 1:
+        # leaving out a rank, or the bias, gives a different answer
+        assert oracle.rel_err(oracle.reduce_partials(yps[1:], b2), full["Y"]) > 1e-3
+        assert oracle.rel_err(oracle.reduce_partials(yps), full["Y"]) > 1e-3
+
+
 def test_adjoint_invariants():
     rng = np.random.default_rng(31)
     T, h, f = 7, 8, 12
