@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--config", default="gpt_h10240")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--main-grad", action="store_true",
+                    help="run the backward as tp_mlp_bwd_main_grad (dA, dB, db1 added to fp32 main gradients)")
     ap.add_argument("--no-reduce", action="store_true",
                     help="skip timing tp_mlp_reduce_partials (the TP group's sum of partials, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -185,9 +187,16 @@ def main():
     fws = torch.empty((nfws,), dtype=torch.uint8, device=dev) if nfws else None
     log(f"workspace: forward {nfws / 2**20:.0f} MiB, backward {nws / 2**20:.0f} MiB")
 
+    if args.main_grad:
+        f32 = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)
+        dA_main, dB_main, db1_main = f32(h, f), f32(f, h), f32(f)
+
     def step(fe=None, be=None):
         tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe)
-        tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be)
+        if args.main_grad:
+            tpmlp.tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, events=be)
+        else:
+            tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -247,7 +256,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_name(cfg), "tokens": T, "hidden": h, "ffn_shard": f, "tp": cfg.tp},
+        "config": {"workload": workload_name(cfg) + ("; fp32 main-gradient accumulation" if args.main_grad else ""),
+                   "tokens": T, "hidden": h, "ffn_shard": f, "tp": cfg.tp},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "peak_tflops": peak,
         "gpu_ms_per_step": round(gpu_ms, 4),

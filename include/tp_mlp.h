@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 3
+#define TPMLP_ABI_VERSION 4
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -185,6 +185,29 @@ int tp_mlp_bwd(const tpmlp_shape* shape,
                void* dZ, void* dXp, void* dA, void* dB, void* db1,
                void* ws, size_t ws_bytes,
                void* stream, void* const* events);
+
+/*
+ * Backward with gradient accumulation into fp32 main gradients: as
+ * tp_mlp_bwd, except that the weight gradients of this micro-batch are
+ * ADDED (beta = 1) to fp32 buffers the caller keeps across micro-batches,
+ * without a rounding to the storage dtype on the way:
+ *   dA_main  [hidden, ffn_shard] fp32   += X^T dZ_i
+ *   dB_main  [ffn_shard, hidden] fp32   += H_i^T dY
+ *   db1_main [ffn_shard]         fp32   += sum over tokens of dZ_i
+ * (the pages train with fp16 products and fp32 master weights, "Megatron-LM
+ * overview", section 3.1, and accumulate gradients over micro-batches,
+ * "Training GPT-2 with Megatron-LM", section 4.3). dZ, dXp, the workspace
+ * (sized with tp_mlp_workspace_bytes) and the 10 events are exactly as in
+ * tp_mlp_bwd. The main gradients are read and written, never just written;
+ * like the other outputs they must not overlap any input or each other.
+ * For fp32 storage the products are the same fp32 FMAs as in tp_mlp_bwd.
+ */
+int tp_mlp_bwd_main_grad(const tpmlp_shape* shape,
+                         const void* dY, const void* X, const void* A, const void* B,
+                         const void* Z, const void* H,
+                         void* dZ, void* dXp, float* dA_main, float* dB_main, float* db1_main,
+                         void* ws, size_t ws_bytes,
+                         void* stream, void* const* events);
 
 /*
  * Sum over ranks of the row-parallel partials, for P ranks whose partials

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     load,
     tp_mlp_abi_version,
     tp_mlp_bwd,
+    tp_mlp_bwd_main_grad,
     tp_mlp_fwd,
     tp_mlp_fwd_workspace_bytes,
     tp_mlp_reduce_partials,

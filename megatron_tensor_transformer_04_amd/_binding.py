@@ -24,7 +24,7 @@ STATUS = {
     7: "TPMLP_ERR_ALIAS",
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
-           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_reduce_partials")
+           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials")
 TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL = 1, 2
 FWD_EVENTS = ("TA", "F1", "TB", "F2")                                     # steps bracketed by the 5 events
@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd.restype = ctypes.c_int
     lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_bwd_main_grad.restype = ctypes.c_int
+    lib.tp_mlp_bwd_main_grad.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_reduce_partials.restype = ctypes.c_int
     lib.tp_mlp_reduce_partials.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int, ctypes.POINTER(vp), vp,
                                            ctypes.c_int64, ctypes.c_int64, vp, vp]
@@ -156,6 +158,21 @@ def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, even
     ev = _events(events)
     _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
                              _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, *, stream=None,
+                         events=None) -> None:
+    """Backward of one TP rank that adds the weight gradients to fp32 main
+    gradients (dA_main [h, f], dB_main [f, h], db1_main [f], float32)."""
+    import torch
+    for t in (dA_main, dB_main, db1_main):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("main gradients are float32")
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    ev = _events(events)
+    _check(load().tp_mlp_bwd_main_grad(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H),
+                                       _ptr(dZ), _ptr(dXp), _ptr(dA_main), _ptr(dB_main), _ptr(db1_main), _ptr(ws),
+                                       _nbytes(ws), _stream(stream), ev))
 
 
 def tp_mlp_reduce_partials(parts, bias, out, row_begin: int = 0, row_end=None, *, stream=None) -> None:

@@ -36,6 +36,7 @@ struct EpiStore {
   static constexpr int kOuts = 1;
   static constexpr bool kInput = false;
   static constexpr bool kTailSplit = true;  // a plain store: k-split tail tiles may finish it elsewhere
+  static constexpr bool kDirectF32 = false;
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int) const { return out; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
@@ -64,6 +65,7 @@ struct EpiBiasGelu {
   static constexpr int kOuts = 2;
   static constexpr bool kInput = false;
   static constexpr bool kTailSplit = false;
+  static constexpr bool kDirectF32 = false;
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int k) const { return k ? h : z; }
   __device__ __forceinline__ float colparam(int64_t n) const { return S::to_f(bias[n]); }
@@ -96,6 +98,7 @@ struct EpiGeluGrad {
   static constexpr int kOuts = 1;
   static constexpr bool kInput = true;
   static constexpr bool kTailSplit = false;
+  static constexpr bool kDirectF32 = false;
   __device__ __forceinline__ const typename S::T* input() const { return zin; }
   __device__ __forceinline__ typename S::T* output(int) const { return dz; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
@@ -112,6 +115,38 @@ struct EpiGeluGrad {
   __device__ __forceinline__ void colsum(int tile_m, int64_t n, float s) const {
     partial[(int64_t)tile_m * ld + n] = s;
   }
+};
+
+// Gradient accumulation into fp32 main gradients (beta = 1): the weight
+// gradient of this micro-batch is added to an fp32 buffer that the caller
+// keeps across micro-batches, main[m][n] += acc, without an intermediate
+// rounding to the storage dtype. The pages train with fp16 products and fp32
+// master weights ("Megatron-LM overview", section 3.1) and accumulate
+// gradients over micro-batches ("Training GPT-2 with Megatron-LM",
+// section 4.3, --gradient-accumulation-steps). kDirectF32: the
+// direct-to-LDS engine reads and writes the fp32 rows straight from its
+// accumulators (no 16-bit staging).
+template <class S>
+struct EpiAccumF32 {
+  float* main;
+  int64_t ld;
+  static constexpr bool kColSum = false;
+  static constexpr int kOuts = 1;
+  static constexpr bool kInput = false;
+  static constexpr bool kTailSplit = false;
+  static constexpr bool kDirectF32 = true;
+  __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
+  __device__ __forceinline__ typename S::T* output(int) const { return nullptr; }
+  __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
+  __device__ __forceinline__ float eval(float acc, float, float, float (&o)[2]) const {
+    o[0] = acc;
+    return 0.0f;
+  }
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    main[m * ld + n] += acc;
+    return 0.0f;
+  }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
 };
 
 }  // namespace tpmlp

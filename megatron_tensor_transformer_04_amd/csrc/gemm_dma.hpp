@@ -523,7 +523,29 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
 
     const Item done = decode(opaque_s(v));
     const int64_t m0 = done.m0, n0 = done.n0;
-    if (done.part >= 0) {
+    if constexpr (Epi::kDirectF32) {
+      // fp32 read-modify-write straight from the accumulators: lanes 0-31
+      // and 32-63 each cover 32 consecutive columns (128 bytes) of one row.
+      // All 16 loads of a fragment are issued before its stores (written
+      // out so: the compiler cannot tell the addresses apart and would
+      // otherwise wait for each load in turn).
+      static_for<0, FM>([&](auto i) {
+        static_for<0, FN>([&](auto j) {
+          const int64_t n = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+          const int64_t mf = m0 + wm * Cfg::WTM + i * 32 + 4 * (lane >> 5);
+          float* const base = epi.main + mf * epi.ld + n;
+          float old[16];
+          static_for<0, 16>([&](auto r) {
+            const int64_t m = mf + 8 * (r / 4) + (r % 4);
+            old[(int)r] = (m < sh.M && n < sh.N) ? base[(8 * (r / 4) + (r % 4)) * epi.ld] : 0.0f;
+          });
+          static_for<0, 16>([&](auto r) {
+            const int64_t m = mf + 8 * (r / 4) + (r % 4);
+            if (m < sh.M && n < sh.N) base[(8 * (r / 4) + (r % 4)) * epi.ld] = old[(int)r] + acc[i][j][(int)r];
+          });
+        });
+      });
+    } else if (done.part >= 0) {
       // One k-range of a tail tile: the raw fp32 partial sums, in place of
       // the epilogue (tail_finish_kernel applies it).
       float* pt = tail.partial + ((int64_t)(done.tile - tail.full) * tail.parts + done.part) * (BM * BN);

@@ -41,6 +41,16 @@ __global__ __launch_bounds__(256) void db1_finish_kernel(const float* partial, i
   db1[n] = S::from_f(s);
 }
 
+// The same sum, added to an fp32 main gradient (beta = 1).
+__global__ __launch_bounds__(256) void db1_accum_kernel(const float* partial, int tiles_m, int64_t f,
+                                                        float* db1_main) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= f) return;
+  float s = 0.0f;
+  for (int t = 0; t < tiles_m; ++t) s += partial[(int64_t)t * f + n];
+  db1_main[n] += s;
+}
+
 enum class Engine { Simt, Mfma128, Mfma256, Dma256, Dma320 };
 
 using Cfg128 = MfmaTile<128, 128, 2, 2>;
@@ -428,12 +438,22 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
   return TPMLP_OK;
 }
 
-template <class S>
+// ACC: dA, dB and db1 are fp32 main gradients that the weight gradients are
+// added to (beta = 1) instead of storage-dtype outputs.
+template <class S, bool ACC>
 int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A, const void* B, const void* Z,
              const void* H, void* dZ, void* dXp, void* dA, void* dB, void* db1, const BwdWs& w, void* ws,
              size_t ws_bytes, hipStream_t st, void* const* ev) {
   using T = typename S::T;
   const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
+  auto epi_dB = [&]() {
+    if constexpr (ACC) return EpiAccumF32<S>{static_cast<float*>(dB), h};
+    else return EpiStore<S>{static_cast<T*>(dB), h};
+  };
+  auto epi_dA = [&]() {
+    if constexpr (ACC) return EpiAccumF32<S>{static_cast<float*>(dA), f};
+    else return EpiStore<S>{static_cast<T*>(dA), f};
+  };
   char* wsb = static_cast<char*>(ws);
   if (!dZ && w.dz_bytes) dZ = wsb + w.dz_off;
   float* part = w.part_bytes ? reinterpret_cast<float*>(wsb + w.part_off) : nullptr;
@@ -448,8 +468,12 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
   TPMLP_TRY(record(ev, 1, st));
   // B5: db1 = sum of the column partials
   if (f > 0) {
-    hipLaunchKernelGGL((db1_finish_kernel<S>), dim3((unsigned)ceil_div(f, 256)), dim3(256), 0, st, part,
-                       w.part_tiles, f, (T*)db1);
+    if constexpr (ACC)
+      hipLaunchKernelGGL(db1_accum_kernel, dim3((unsigned)ceil_div(f, 256)), dim3(256), 0, st, part, w.part_tiles,
+                         f, static_cast<float*>(db1));
+    else
+      hipLaunchKernelGGL((db1_finish_kernel<S>), dim3((unsigned)ceil_div(f, 256)), dim3(256), 0, st, part,
+                         w.part_tiles, f, (T*)db1);
     TPMLP_HIP(hipGetLastError());
   }
   TPMLP_TRY(record(ev, 2, st));
@@ -466,15 +490,15 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_TRY(record(ev, 4, st));
     TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, staged_ld(Tn), wsb + w.dyt_off,
                                               staged_ld(Tn),
-                                              EpiStore<S>{(T*)dB, h}, st, tail, tcap)));
+                                              epi_dB(), st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_TRY(record(ev, 4, st));
     if (H)
       TPMLP_HIP(
-          (run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, EpiStore<S>{(T*)dB, h}, st, tail, tcap)));
+          (run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, epi_dB(), st, tail, tcap)));
     else
-      TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, EpiStore<S>{(T*)dB, h}, st)));
+      TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, epi_dB(), st)));
   }
   TPMLP_TRY(record(ev, 5, st));
   // TX, TdZ + B3: dA = X^T dZ. Staged: P = X^T [h,T], Q[k][n] = dZ^T[n][k].
@@ -485,12 +509,12 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_TRY(record(ev, 7, st));
     TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, staged_ld(Tn), wsb + w.dzt_off,
                                               staged_ld(Tn),
-                                              EpiStore<S>{(T*)dA, f}, st, tail, tcap)));
+                                              epi_dA(), st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 6, st));
     TPMLP_TRY(record(ev, 7, st));
     TPMLP_HIP(
-        (run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, EpiStore<S>{(T*)dA, f}, st, tail, tcap)));
+        (run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, epi_dA(), st, tail, tcap)));
   }
   TPMLP_TRY(record(ev, 8, st));
   // B4: dXp = dZ A_i^T; Q[k=f][n=h] = A_i[n][k] is k-contiguous
@@ -572,11 +596,42 @@ int tp_mlp_bwd(const tpmlp_shape* shape, const void* dY, const void* X, const vo
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (s.dtype) {
     case TPMLP_F32:
-      return bwd_impl<StoreF32>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+      return bwd_impl<StoreF32, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
     case TPMLP_F16:
-      return bwd_impl<StoreF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+      return bwd_impl<StoreF16, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
     default:
-      return bwd_impl<StoreBF16>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+      return bwd_impl<StoreBF16, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+  }
+}
+
+int tp_mlp_bwd_main_grad(const tpmlp_shape* shape, const void* dY, const void* X, const void* A, const void* B,
+                         const void* Z, const void* H, void* dZ, void* dXp, float* dA_main, float* dB_main,
+                         float* db1_main, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  const size_t e = elt_size(s.dtype);
+  const size_t Th = (size_t)(s.tokens * s.hidden) * e, hf = (size_t)(s.hidden * s.ffn_shard) * e,
+               Tf = (size_t)(s.tokens * s.ffn_shard) * e;
+  const size_t hf4 = (size_t)(s.hidden * s.ffn_shard) * 4, f4 = (size_t)s.ffn_shard * 4;
+  const BwdWs w = bwd_ws(s, dZ == nullptr);
+  const size_t ws_used = ws_bytes >= w.total ? w.total : w.minimal;
+  const Span in[6] = {{dY, Th}, {X, Th}, {A, hf}, {B, hf}, {Z, Tf}, {H, Tf}};
+  const bool in_req[6] = {true, true, true, true, true, false};
+  const Span out[6] = {{dZ, Tf}, {dXp, Th}, {dA_main, hf4}, {dB_main, hf4}, {db1_main, f4}, {ws, ws_used}};
+  const bool out_req[6] = {false, true, true, true, true, true};
+  TPMLP_TRY(check_buffers(in, 6, in_req, out, 6, out_req));
+  if (ws_bytes < w.minimal) return TPMLP_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (s.dtype) {
+    case TPMLP_F32:
+      return bwd_impl<StoreF32, true>(s, dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, w, ws, ws_bytes, st,
+                                      events);
+    case TPMLP_F16:
+      return bwd_impl<StoreF16, true>(s, dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, w, ws, ws_bytes, st,
+                                      events);
+    default:
+      return bwd_impl<StoreBF16, true>(s, dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, w, ws, ws_bytes,
+                                       st, events);
   }
 }
 

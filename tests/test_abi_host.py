@@ -38,7 +38,8 @@ def _header_enum(name):
 def test_exports_every_declared_function(lib):
     declared = _declared_functions()
     assert set(declared) == {"tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes",
-                             "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_reduce_partials"}
+                             "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad",
+                             "tp_mlp_reduce_partials"}
     raw = ctypes.CDLL(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "libtpmlp.so"))
     for name in declared:
         assert hasattr(raw, name), name
@@ -203,6 +204,29 @@ def test_bwd_validation_errors(lib):
     assert _bwd(lib, ok, dB=BASE + 32) == 7                     # dB inside dY
     assert _bwd(lib, ok, ws=BASE + (10 << 32) + 16) == 7        # workspace inside db1
     assert _bwd(lib, _shape(64, 128, 256, -1)) == 4
+
+
+def _bwd_main(lib, shape, ws_bytes=1 << 30, **kw):
+    p = dict(dY=BASE, X=BASE + (1 << 32), A=BASE + (2 << 32), B=BASE + (3 << 32), Z=BASE + (4 << 32),
+             H=BASE + (5 << 32), dZ=BASE + (6 << 32), dXp=BASE + (7 << 32), dA=BASE + (8 << 32),
+             dB=BASE + (9 << 32), db1=BASE + (10 << 32), ws=BASE + (11 << 32))
+    p.update(kw)
+    return lib.tp_mlp_bwd_main_grad(ctypes.byref(shape), p["dY"], p["X"], p["A"], p["B"], p["Z"], p["H"], p["dZ"],
+                                    p["dXp"], p["dA"], p["dB"], p["db1"], p["ws"], ws_bytes, None, None)
+
+
+def test_bwd_main_grad_validation_errors(lib):
+    ok = _shape(64, 128, 256, 2)
+    need = lib.tp_mlp_workspace_bytes(ctypes.byref(ok), MINIMAL)
+    assert _bwd_main(lib, ok, ws_bytes=need - 1) == 5
+    assert _bwd_main(lib, ok, dA=None) == 1
+    assert _bwd_main(lib, ok, db1=None) == 1
+    assert _bwd_main(lib, ok, dB=BASE + (9 << 32) + 8) == 3
+    # the fp32 main gradients are twice the storage size: dA_main [128, 256] fp32 is 128 KiB, so a dB_main
+    # starting 64 KiB after it overlaps it
+    assert _bwd_main(lib, ok, dB=BASE + (8 << 32) + (64 << 10)) == 7
+    assert _bwd_main(lib, ok, db1=BASE + 16) == 7                # db1_main inside dY
+    assert _bwd_main(lib, _shape(64, 128, 256, 7)) == 4
 
 
 def _reduce(lib, shape, parts, bias=None, rb=0, re_=None, out=BASE + (20 << 32)):
