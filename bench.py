@@ -148,6 +148,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-grad", action="store_true",
                     help="run the backward as tp_mlp_bwd_main_grad (dA, dB, db1 added to fp32 main gradients)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="selective recomputation: the backward is tp_mlp_bwd_recompute (Z recomputed from X, the "
+                         "forward's Z and H only scratch); value still counts the 12 T h f model flops")
     ap.add_argument("--no-reduce", action="store_true",
                     help="skip timing tp_mlp_reduce_partials (the TP group's sum of partials, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -191,7 +194,18 @@ def main():
         f32 = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)
         dA_main, dB_main, db1_main = f32(h, f), f32(f, h), f32(f)
 
+    if args.recompute:
+        if args.main_grad:
+            sys.exit("--recompute and --main-grad are separate entry points; pick one")
+        nrws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code, tpmlp.TPMLP_WS_RECOMPUTE)
+        rws = torch.empty((max(nrws, 1),), dtype=torch.uint8, device=dev)
+
     def step(fe=None, be=None):
+        if args.recompute:
+            # Z and H are scratch here (not kept for the backward, which recomputes them)
+            tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe)
+            tpmlp.tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, rws, events=be)
+            return
         tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe)
         if args.main_grad:
             tpmlp.tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, events=be)
@@ -215,7 +229,8 @@ def main():
 
     K = args.steps
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(FWD_STEPS) + 1)] for _ in range(K)]
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_STEPS) + 1)] for _ in range(K)]
+    bwd_steps = (["rTA", "rF1"] + BWD_STEPS) if args.recompute else BWD_STEPS
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bwd_steps) + 1)] for _ in range(K)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -225,14 +240,14 @@ def main():
     wall = time.perf_counter() - t0
     log("timed region done")
 
-    per = {n: 0.0 for n in FWD_STEPS + BWD_STEPS}
+    per = {n: 0.0 for n in FWD_STEPS + bwd_steps}
     for k in range(K):
         for i, n in enumerate(FWD_STEPS):
             per[n] += fev[k][i].elapsed_time(fev[k][i + 1])
-        for i, n in enumerate(BWD_STEPS):
+        for i, n in enumerate(bwd_steps):
             per[n] += bev[k][i].elapsed_time(bev[k][i + 1])
     per = {n: v / K for n, v in per.items()}
-    gpu_ms = fev[0][0].elapsed_time(bev[K - 1][len(BWD_STEPS)]) / K
+    gpu_ms = fev[0][0].elapsed_time(bev[K - 1][len(bwd_steps)]) / K
     ms = wall / K * 1e3
     flops = 12.0 * T * h * f
     value = flops / (ms * 1e-3) / 1e12
@@ -256,7 +271,9 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_name(cfg) + ("; fp32 main-gradient accumulation" if args.main_grad else ""),
+        "config": {"workload": workload_name(cfg) + ("; fp32 main-gradient accumulation" if args.main_grad else "")
+                   + ("; Z recomputed in the backward (value counts the 12 T h f model flops)" if args.recompute
+                      else ""),
                    "tokens": T, "hidden": h, "ffn_shard": f, "tp": cfg.tp},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "peak_tflops": peak,

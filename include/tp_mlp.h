@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 4
+#define TPMLP_ABI_VERSION 5
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -118,7 +118,10 @@ const char* tp_mlp_status_string(int status);
  * tp_mlp_workspace_bytes: bytes for tp_mlp_bwd. Flags:
  *   TPMLP_WS_DZ       room for dZ_i as well, for callers that pass dZ = NULL;
  *   TPMLP_WS_MINIMAL  only what tp_mlp_bwd requires (fp32 per-tile column
- *                     partials of dZ for db1, and dZ if TPMLP_WS_DZ).
+ *                     partials of dZ for db1, and dZ if TPMLP_WS_DZ);
+ *   TPMLP_WS_RECOMPUTE the size for tp_mlp_bwd_recompute: room for the
+ *                     recomputed Z_i (and a staged A_i^T) in front of
+ *                     what the other flags ask for.
  * Without TPMLP_WS_MINIMAL the size also holds k-contiguous copies of H_i,
  * dY, X and dZ_i (each [rows][tokens]) for the weight-gradient GEMMs and
  * the k-split partial sums; tp_mlp_bwd uses them when ws_bytes reaches that
@@ -128,6 +131,7 @@ const char* tp_mlp_status_string(int status);
  */
 #define TPMLP_WS_DZ 1u
 #define TPMLP_WS_MINIMAL 2u
+#define TPMLP_WS_RECOMPUTE 4u
 size_t tp_mlp_fwd_workspace_bytes(const tpmlp_shape* shape);
 size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags);
 
@@ -185,6 +189,28 @@ int tp_mlp_bwd(const tpmlp_shape* shape,
                void* dZ, void* dXp, void* dA, void* dB, void* db1,
                void* ws, size_t ws_bytes,
                void* stream, void* const* events);
+
+/*
+ * Backward with selective recomputation: the forward's Z_i and H_i are not
+ * kept; Z_i = X A_i + b1_i is recomputed here first (the forward's first
+ * step, "Megatron-LM overview", section 3.3, activation checkpointing),
+ * into the front of the workspace, and H_i is taken as gelu(Z_i) where it
+ * is needed. Arguments as in tp_mlp_bwd, plus b1 [ffn_shard] in, minus Z
+ * and H. ws: at least tp_mlp_workspace_bytes(shape, TPMLP_WS_RECOMPUTE |
+ * TPMLP_WS_MINIMAL | (dZ == NULL ? TPMLP_WS_DZ : 0)) bytes (never NULL for
+ * a nonempty shape); with TPMLP_WS_RECOMPUTE alone the transposed copies
+ * are staged as in tp_mlp_bwd.
+ *   events: NULL, or 12 hipEvent_t recorded on `stream`: before the first
+ *           kernel, after the A_i transpose (TA), after the recomputing
+ *           GEMM (F1), then as tp_mlp_bwd's events 1-9.
+ * Results are bitwise those of tp_mlp_fwd (H not kept) followed by
+ * tp_mlp_bwd with H = NULL.
+ */
+int tp_mlp_bwd_recompute(const tpmlp_shape* shape,
+                         const void* dY, const void* X, const void* A, const void* b1, const void* B,
+                         void* dZ, void* dXp, void* dA, void* dB, void* db1,
+                         void* ws, size_t ws_bytes,
+                         void* stream, void* const* events);
 
 /*
  * Backward with gradient accumulation into fp32 main gradients: as

@@ -7,6 +7,7 @@ from ._binding import (  # noqa: F401
     BWD_EVENTS,
     EXPORTS,
     FWD_EVENTS,
+    RECOMPUTE_EVENTS,
     LIB_PATH,
     STATUS,
     TPMLP_BF16,
@@ -15,13 +16,16 @@ from ._binding import (  # noqa: F401
     TPMLP_MAX_PARTS,
     TPMLP_WS_DZ,
     TPMLP_WS_MINIMAL,
+    TPMLP_WS_RECOMPUTE,
     TpMlpError,
     bwd,
+    bwd_recompute,
     fwd,
     load,
     tp_mlp_abi_version,
     tp_mlp_bwd,
     tp_mlp_bwd_main_grad,
+    tp_mlp_bwd_recompute,
     tp_mlp_fwd,
     tp_mlp_fwd_workspace_bytes,
     tp_mlp_reduce_partials,

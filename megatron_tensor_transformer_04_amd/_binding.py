@@ -24,11 +24,12 @@ STATUS = {
     7: "TPMLP_ERR_ALIAS",
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
-           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials")
+           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials")
 TPMLP_MAX_PARTS = 16
-TPMLP_WS_DZ, TPMLP_WS_MINIMAL = 1, 2
+TPMLP_WS_DZ, TPMLP_WS_MINIMAL, TPMLP_WS_RECOMPUTE = 1, 2, 4
 FWD_EVENTS = ("TA", "F1", "TB", "F2")                                     # steps bracketed by the 5 events
 BWD_EVENTS = ("B1", "B5", "TH", "TdY", "B2", "TX", "TdZ", "B3", "B4")    # ... by the 10 events
+RECOMPUTE_EVENTS = ("TA", "F1") + BWD_EVENTS                              # ... by the 12 events
 
 
 class TpMlpError(RuntimeError):
@@ -66,6 +67,8 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd.restype = ctypes.c_int
     lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_bwd_recompute.restype = ctypes.c_int
+    lib.tp_mlp_bwd_recompute.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 10 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd_main_grad.restype = ctypes.c_int
     lib.tp_mlp_bwd_main_grad.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_reduce_partials.restype = ctypes.c_int
@@ -158,6 +161,33 @@ def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, even
     ev = _events(events)
     _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
                              _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None) -> None:
+    """Backward of one TP rank that recomputes Z (and gelu(Z)) from X first."""
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    ev = _events(events)
+    _check(load().tp_mlp_bwd_recompute(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(dZ),
+                                       _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), _nbytes(ws),
+                                       _stream(stream), ev))
+
+
+def bwd_recompute(dY, X, A, b1, B, keep_dz: bool = True, staged: bool = True, stream=None, events=None):
+    """Allocate the gradients and the workspace with torch and run
+    tp_mlp_bwd_recompute."""
+    import torch
+    T, f, h = X.shape[0], A.shape[1], X.shape[1]
+    dev, dt = X.device, X.dtype
+    dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
+    dXp = torch.empty((T, h), dtype=dt, device=dev)
+    dA = torch.empty((h, f), dtype=dt, device=dev)
+    dB = torch.empty((f, h), dtype=dt, device=dev)
+    db1 = torch.empty((f,), dtype=dt, device=dev)
+    flags = TPMLP_WS_RECOMPUTE | (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
+    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
+    tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events)
+    return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
 
 
 def tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, *, stream=None,

@@ -395,6 +395,44 @@ BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
   return w;
 }
 
+// Workspace front of the recomputing backward: [Z_i [T][f]] then, when the
+// first GEMM stages, [A_i^T [f][h + pad]]; the backward's own workspace
+// follows at `bytes`.
+struct RcWs {
+  size_t at_off, bytes;
+  bool at;
+};
+
+RcWs rc_ws(const tpmlp_shape& s) {
+  RcWs r{};
+  const size_t e = elt_size(s.dtype);
+  r.at = stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
+  r.at_off = align256((size_t)(s.tokens * s.ffn_shard) * e);
+  r.bytes = r.at_off + (r.at ? align256((size_t)(s.ffn_shard * staged_ld(s.hidden)) * e) : 0);
+  return r;
+}
+
+// Z = X A_i + b1 into `Z` (H not kept), the forward's first step; events 0-2
+// bracket TA and F1.
+template <class S>
+int recompute_z(const tpmlp_shape& s, const void* X, const void* A, const void* b1, void* Z, const RcWs& r,
+                char* wsb, hipStream_t st, void* const* ev) {
+  using T = typename S::T;
+  const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
+  TPMLP_TRY(record(ev, 0, st));
+  if (r.at) {
+    TPMLP_HIP((run_transpose<S, false>(A, wsb + r.at_off, h, f, st)));
+    TPMLP_TRY(record(ev, 1, st));
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, X, h, wsb + r.at_off, staged_ld(h),
+                                              EpiBiasGelu<S>{(const T*)b1, (T*)Z, nullptr, f}, st)));
+  } else {
+    TPMLP_TRY(record(ev, 1, st));
+    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, f, h, X, h, A, f,
+                                               EpiBiasGelu<S>{(const T*)b1, (T*)Z, nullptr, f}, st)));
+  }
+  return TPMLP_OK;
+}
+
 template <class S>
 int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1, const void* B, void* Z, void* H,
              void* Yp, void* ws, size_t ws_bytes, hipStream_t st, void* const* ev) {
@@ -554,7 +592,8 @@ size_t tp_mlp_fwd_workspace_bytes(const tpmlp_shape* shape) {
 size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags) {
   if (check_shape(shape) != TPMLP_OK) return 0;
   const BwdWs w = bwd_ws(*shape, (flags & TPMLP_WS_DZ) != 0);
-  return (flags & TPMLP_WS_MINIMAL) ? w.minimal : w.total;
+  const size_t rc = (flags & TPMLP_WS_RECOMPUTE) ? rc_ws(*shape).bytes : 0;
+  return rc + ((flags & TPMLP_WS_MINIMAL) ? w.minimal : w.total);
 }
 
 int tp_mlp_fwd(const tpmlp_shape* shape, const void* X, const void* A, const void* b1, const void* B, void* Z,
@@ -632,6 +671,44 @@ int tp_mlp_bwd_main_grad(const tpmlp_shape* shape, const void* dY, const void* X
     default:
       return bwd_impl<StoreBF16, true>(s, dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, w, ws, ws_bytes,
                                        st, events);
+  }
+}
+
+int tp_mlp_bwd_recompute(const tpmlp_shape* shape, const void* dY, const void* X, const void* A, const void* b1,
+                         const void* B, void* dZ, void* dXp, void* dA, void* dB, void* db1, void* ws,
+                         size_t ws_bytes, void* stream, void* const* events) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  const size_t e = elt_size(s.dtype);
+  const size_t Th = (size_t)(s.tokens * s.hidden) * e, hf = (size_t)(s.hidden * s.ffn_shard) * e,
+               Tf = (size_t)(s.tokens * s.ffn_shard) * e, fb = (size_t)s.ffn_shard * e;
+  const RcWs r = rc_ws(s);
+  const BwdWs w = bwd_ws(s, dZ == nullptr);
+  const size_t rest = ws_bytes > r.bytes ? ws_bytes - r.bytes : 0;
+  const size_t ws_used = r.bytes + (rest >= w.total ? w.total : w.minimal);
+  const Span in[5] = {{dY, Th}, {X, Th}, {A, hf}, {b1, fb}, {B, hf}};
+  const bool in_req[5] = {true, true, true, true, true};
+  const Span out[6] = {{dZ, Tf}, {dXp, Th}, {dA, hf}, {dB, hf}, {db1, fb}, {ws, ws_used}};
+  const bool out_req[6] = {false, true, true, true, true, true};
+  TPMLP_TRY(check_buffers(in, 5, in_req, out, 6, out_req));
+  if (ws_bytes < r.bytes + w.minimal) return TPMLP_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(ws);
+  void* Z = wsb;  // Z_i recomputed at the front of the workspace
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* const* ev_b = events ? events + 2 : nullptr;
+  switch (s.dtype) {
+    case TPMLP_F32:
+      TPMLP_TRY(recompute_z<StoreF32>(s, X, A, b1, Z, r, wsb, st, events));
+      return bwd_impl<StoreF32, false>(s, dY, X, A, B, Z, nullptr, dZ, dXp, dA, dB, db1, w, wsb + r.bytes, rest, st,
+                                       ev_b);
+    case TPMLP_F16:
+      TPMLP_TRY(recompute_z<StoreF16>(s, X, A, b1, Z, r, wsb, st, events));
+      return bwd_impl<StoreF16, false>(s, dY, X, A, B, Z, nullptr, dZ, dXp, dA, dB, db1, w, wsb + r.bytes, rest, st,
+                                       ev_b);
+    default:
+      TPMLP_TRY(recompute_z<StoreBF16>(s, X, A, b1, Z, r, wsb, st, events));
+      return bwd_impl<StoreBF16, false>(s, dY, X, A, B, Z, nullptr, dZ, dXp, dA, dB, db1, w, wsb + r.bytes, rest,
+                                        st, ev_b);
   }
 }
 

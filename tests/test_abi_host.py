@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
     declared = _declared_functions()
     assert set(declared) == {"tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes",
                              "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad",
-                             "tp_mlp_reduce_partials"}
+                             "tp_mlp_bwd_recompute", "tp_mlp_reduce_partials"}
     raw = ctypes.CDLL(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "libtpmlp.so"))
     for name in declared:
         assert hasattr(raw, name), name
@@ -57,7 +57,8 @@ def test_abi_version_and_status_codes_match_header(lib):
     for name, code in (("TPMLP_F32", tpmlp.TPMLP_F32), ("TPMLP_F16", tpmlp.TPMLP_F16),
                        ("TPMLP_BF16", tpmlp.TPMLP_BF16)):
         assert _header_enum(name) == code
-    for name, code in (("TPMLP_WS_DZ", tpmlp.TPMLP_WS_DZ), ("TPMLP_WS_MINIMAL", tpmlp.TPMLP_WS_MINIMAL)):
+    for name, code in (("TPMLP_WS_DZ", tpmlp.TPMLP_WS_DZ), ("TPMLP_WS_MINIMAL", tpmlp.TPMLP_WS_MINIMAL),
+                       ("TPMLP_WS_RECOMPUTE", tpmlp.TPMLP_WS_RECOMPUTE)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)u", open(HEADER).read()).group(1)) == code
     assert _header_define("TPMLP_MAX_PARTS") == tpmlp.TPMLP_MAX_PARTS
 
@@ -227,6 +228,40 @@ def test_bwd_main_grad_validation_errors(lib):
     assert _bwd_main(lib, ok, dB=BASE + (8 << 32) + (64 << 10)) == 7
     assert _bwd_main(lib, ok, db1=BASE + 16) == 7                # db1_main inside dY
     assert _bwd_main(lib, _shape(64, 128, 256, 7)) == 4
+
+
+def test_recompute_workspace_bytes(lib):
+    """The recomputing backward's workspace: Z_i [T][f], then (when the first
+    GEMM stages) A_i^T [f][h + 256], in front of the plain backward's."""
+    ws = lambda T, h, f, flags=0: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)), flags)
+    RC = 4
+    z = 16384 * 10240 * 2
+    at = 10240 * (10240 + 256) * 2
+    assert ws(16384, 10240, 10240, RC) == z + at + ws(16384, 10240, 10240)
+    assert ws(16384, 10240, 10240, RC | MINIMAL) == z + at + ws(16384, 10240, 10240, MINIMAL)
+    assert ws(16384, 10240, 10240, RC | MINIMAL | DZ) == z + at + ws(16384, 10240, 10240, MINIMAL | DZ)
+    # small shapes stage nothing: just Z, rounded up to 256 bytes
+    assert ws(200, 136, 264, RC | MINIMAL) == (200 * 264 * 2 + 255) // 256 * 256 + ws(200, 136, 264, MINIMAL)
+
+
+def _bwd_rc(lib, shape, ws_bytes=1 << 30, **kw):
+    p = dict(dY=BASE, X=BASE + (1 << 32), A=BASE + (2 << 32), b1=BASE + (3 << 32), B=BASE + (4 << 32),
+             dZ=BASE + (6 << 32), dXp=BASE + (7 << 32), dA=BASE + (8 << 32), dB=BASE + (9 << 32),
+             db1=BASE + (10 << 32), ws=BASE + (11 << 32))
+    p.update(kw)
+    return lib.tp_mlp_bwd_recompute(ctypes.byref(shape), p["dY"], p["X"], p["A"], p["b1"], p["B"], p["dZ"],
+                                    p["dXp"], p["dA"], p["dB"], p["db1"], p["ws"], ws_bytes, None, None)
+
+
+def test_bwd_recompute_validation_errors(lib):
+    ok = _shape(64, 128, 256, 2)
+    need = lib.tp_mlp_workspace_bytes(ctypes.byref(ok), 4 | MINIMAL)
+    assert _bwd_rc(lib, ok, ws_bytes=need - 1) == 5
+    assert _bwd_rc(lib, ok, ws=None) == 1
+    assert _bwd_rc(lib, ok, b1=None) == 1
+    assert _bwd_rc(lib, ok, b1=BASE + (3 << 32) + 2) == 3
+    assert _bwd_rc(lib, ok, dA=BASE + (3 << 32)) == 7            # dA over b1
+    assert _bwd_rc(lib, _shape(64, 128, 256, 5)) == 4
 
 
 def _reduce(lib, shape, parts, bias=None, rb=0, re_=None, out=BASE + (20 << 32)):
