@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--recompute", action="store_true",
                     help="selective recomputation: the backward is tp_mlp_bwd_recompute (Z recomputed from X, the "
                          "forward's Z and H only scratch); value still counts the 12 T h f model flops")
+    ap.add_argument("--b-transposed", action="store_true",
+                    help="pass the second weight as B_i^T [hidden, ffn_shard] (TPMLP_LAYOUT_B_T); dB comes back "
+                         "in that order")
     ap.add_argument("--no-reduce", action="store_true",
                     help="skip timing tp_mlp_reduce_partials (the TP group's sum of partials, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -182,35 +185,40 @@ def main():
     td = torch_dtype(cfg.dtype)
     e = lambda *s: torch.empty(s, dtype=td, device=dev)
     Z, H, Yp = e(T, f), e(T, f), e(T, h)
-    dZ, dXp, dA, dB, db1 = e(T, f), e(T, h), e(h, f), e(f, h), e(f)
+    bt = args.b_transposed
+    layout = tpmlp.TPMLP_LAYOUT_B_T if bt else 0
+    if bt:
+        B = B.t().contiguous()
+    dZ, dXp, dA, dB, db1 = e(T, f), e(T, h), e(h, f), e(h, f) if bt else e(f, h), e(f)
     code = {"f32": tpmlp.TPMLP_F32, "f16": tpmlp.TPMLP_F16, "bf16": tpmlp.TPMLP_BF16}[cfg.dtype]
-    nws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code)
+    nws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code, 0, layout)
     ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
-    nfws = tpmlp.tp_mlp_fwd_workspace_bytes(T, h, f, code)
+    nfws = tpmlp.tp_mlp_fwd_workspace_bytes(T, h, f, code, layout)
     fws = torch.empty((nfws,), dtype=torch.uint8, device=dev) if nfws else None
     log(f"workspace: forward {nfws / 2**20:.0f} MiB, backward {nws / 2**20:.0f} MiB")
 
     if args.main_grad:
         f32 = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)
-        dA_main, dB_main, db1_main = f32(h, f), f32(f, h), f32(f)
+        dA_main, dB_main, db1_main = f32(h, f), f32(h, f) if bt else f32(f, h), f32(f)
 
     if args.recompute:
         if args.main_grad:
             sys.exit("--recompute and --main-grad are separate entry points; pick one")
-        nrws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code, tpmlp.TPMLP_WS_RECOMPUTE)
+        nrws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code, tpmlp.TPMLP_WS_RECOMPUTE, layout)
         rws = torch.empty((max(nrws, 1),), dtype=torch.uint8, device=dev)
 
     def step(fe=None, be=None):
         if args.recompute:
             # Z and H are scratch here (not kept for the backward, which recomputes them)
-            tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe)
-            tpmlp.tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, rws, events=be)
+            tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe, b_transposed=bt)
+            tpmlp.tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, rws, events=be, b_transposed=bt)
             return
-        tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe)
+        tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws, events=fe, b_transposed=bt)
         if args.main_grad:
-            tpmlp.tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, events=be)
+            tpmlp.tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, events=be,
+                                       b_transposed=bt)
         else:
-            tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be)
+            tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, events=be, b_transposed=bt)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -273,7 +281,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(cfg) + ("; fp32 main-gradient accumulation" if args.main_grad else "")
                    + ("; Z recomputed in the backward (value counts the 12 T h f model flops)" if args.recompute
-                      else ""),
+                      else "")
+                   + ("; second weight passed as B_i^T [hidden, ffn_shard]" if bt else ""),
                    "tokens": T, "hidden": h, "ffn_shard": f, "tp": cfg.tp},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "peak_tflops": peak,
@@ -286,7 +295,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": profiled_traffic(cfg.name, dom),
+            # counters were taken in the default mode only
+            "traffic": None if (args.main_grad or args.recompute or bt) else profiled_traffic(cfg.name, dom),
         },
         "cpu_baseline": None,
         "reduce_partials": reduce_line,

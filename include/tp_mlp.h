@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 5
+#define TPMLP_ABI_VERSION 6
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -82,12 +82,25 @@ typedef enum {
   TPMLP_ERR_ALIAS = 7      /* an output overlaps an input or another output */
 } tpmlp_status;
 
-/* Shape of one rank's share: X [tokens, hidden], A_i [hidden, ffn_shard]. */
+/*
+ * Shape of one rank's share: X [tokens, hidden], A_i [hidden, ffn_shard].
+ *
+ * layout: 0, or TPMLP_LAYOUT_B_T. With TPMLP_LAYOUT_B_T the second weight is
+ * passed as B_i^T [hidden, ffn_shard] (row-major), i.e. in the [out, in]
+ * order of a linear layer's weight, and its gradient dB (or dB_main) is
+ * written in that same [hidden, ffn_shard] order; every other tensor is as
+ * described above. The pages fix only which dimension of the second weight
+ * is split (its input rows), not the order in which a rank stores its block.
+ * Any other bit set is TPMLP_ERR_SHAPE. A zero-initialised struct (e.g.
+ * {tokens, hidden, ffn_shard, dtype}) is the default layout.
+ */
+#define TPMLP_LAYOUT_B_T 1
 typedef struct {
   int64_t tokens;
   int64_t hidden;
   int64_t ffn_shard;
-  int32_t dtype; /* tpmlp_dtype */
+  int32_t dtype;  /* tpmlp_dtype */
+  int32_t layout; /* 0 or TPMLP_LAYOUT_B_T */
 } tpmlp_shape;
 
 /* TPMLP_ABI_VERSION of the built library. */
@@ -123,7 +136,8 @@ const char* tp_mlp_status_string(int status);
  *                     recomputed Z_i (and a staged A_i^T) in front of
  *                     what the other flags ask for.
  * Without TPMLP_WS_MINIMAL the size also holds k-contiguous copies of H_i,
- * dY, X and dZ_i (each [rows][tokens]) for the weight-gradient GEMMs and
+ * dY, X and dZ_i (each [rows][tokens]) for the weight-gradient GEMMs (and,
+ * with TPMLP_LAYOUT_B_T, of B_i [ffn_shard][hidden] for the dZ GEMM) and
  * the k-split partial sums; tp_mlp_bwd uses them when ws_bytes reaches that
  * size, and otherwise reads the operands in place and splits nothing
  * (slower). A workspace below the minimal size is TPMLP_ERR_WORKSPACE.
@@ -141,7 +155,8 @@ size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags);
  *   X  [tokens, hidden]    in
  *   A  [hidden, ffn_shard] in   (A_i)
  *   b1 [ffn_shard]         in   (b1_i)
- *   B  [ffn_shard, hidden] in   (B_i)
+ *   B  [ffn_shard, hidden] in   (B_i; [hidden, ffn_shard] = B_i^T with
+ *                               TPMLP_LAYOUT_B_T)
  *   Z  [tokens, ffn_shard] out  pre-activation X A_i + b1_i (bias included)
  *   H  [tokens, ffn_shard] out, may be NULL: gelu(Z_i). When NULL, the second
  *                          GEMM applies the GeLU to Z_i while loading it.
@@ -151,7 +166,8 @@ size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags);
  *   events: NULL, or 5 hipEvent_t recorded on `stream`: before the first
  *           kernel and after each of: A_i transpose (TA), first GEMM (F1),
  *           B_i transpose (TB), second GEMM (F2). A transpose that does not
- *           run leaves its two events back to back.
+ *           run leaves its two events back to back (TB never runs with
+ *           TPMLP_LAYOUT_B_T: B_i^T is already k-contiguous for F2).
  */
 int tp_mlp_fwd(const tpmlp_shape* shape,
                const void* X, const void* A, const void* b1, const void* B,
@@ -170,7 +186,8 @@ int tp_mlp_fwd(const tpmlp_shape* shape,
  *                           the workspace (size it with TPMLP_WS_DZ).
  *   dXp [tokens, hidden]    out  dZ_i A_i^T (partial over ranks)
  *   dA  [hidden, ffn_shard] out  X^T dZ_i
- *   dB  [ffn_shard, hidden] out  H_i^T dY
+ *   dB  [ffn_shard, hidden] out  H_i^T dY ([hidden, ffn_shard] = dY^T H_i
+ *                                with TPMLP_LAYOUT_B_T)
  *   db1 [ffn_shard]         out  column sums of dZ_i
  *   ws, ws_bytes            workspace of at least
  *                           tp_mlp_workspace_bytes(shape, TPMLP_WS_MINIMAL |
@@ -181,7 +198,9 @@ int tp_mlp_fwd(const tpmlp_shape* shape,
  *           (B1), db1 finish (B5), H_i transpose (TH), dY transpose (TdY),
  *           dB GEMM (B2), X transpose (TX), dZ_i transpose (TdZ), dA GEMM
  *           (B3), dXp GEMM (B4). A transpose that does not run leaves its
- *           two events back to back.
+ *           two events back to back. With TPMLP_LAYOUT_B_T and the staged
+ *           workspace, B1's interval also holds a transpose of B_i^T into
+ *           the workspace, from which the dZ GEMM reads B_i k-contiguous.
  */
 int tp_mlp_bwd(const tpmlp_shape* shape,
                const void* dY, const void* X, const void* A, const void* B,
@@ -218,7 +237,8 @@ int tp_mlp_bwd_recompute(const tpmlp_shape* shape,
  * ADDED (beta = 1) to fp32 buffers the caller keeps across micro-batches,
  * without a rounding to the storage dtype on the way:
  *   dA_main  [hidden, ffn_shard] fp32   += X^T dZ_i
- *   dB_main  [ffn_shard, hidden] fp32   += H_i^T dY
+ *   dB_main  [ffn_shard, hidden] fp32   += H_i^T dY   ([hidden, ffn_shard]
+ *                                              with TPMLP_LAYOUT_B_T)
  *   db1_main [ffn_shard]         fp32   += sum over tokens of dZ_i
  * (the pages train with fp16 products and fp32 master weights, "Megatron-LM
  * overview", section 3.1, and accumulate gradients over micro-batches,

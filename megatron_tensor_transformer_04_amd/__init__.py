@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     TPMLP_BF16,
     TPMLP_F16,
     TPMLP_F32,
+    TPMLP_LAYOUT_B_T,
     TPMLP_MAX_PARTS,
     TPMLP_WS_DZ,
     TPMLP_WS_MINIMAL,

@@ -38,9 +38,12 @@ class TpMlpError(RuntimeError):
         self.status = status
 
 
+TPMLP_LAYOUT_B_T = 1   # B passed as B_i^T [hidden, ffn_shard] (dB returned in that order)
+
+
 class tpmlp_shape(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
-                ("ffn_shard", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+                ("ffn_shard", ctypes.c_int64), ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,8 +123,12 @@ def _check(status: int):
         raise TpMlpError(status, load().tp_mlp_status_string(status).decode())
 
 
-def shape_of(tokens: int, hidden: int, ffn_shard: int, dtype: int) -> tpmlp_shape:
-    return tpmlp_shape(tokens, hidden, ffn_shard, dtype)
+def shape_of(tokens: int, hidden: int, ffn_shard: int, dtype: int, layout: int = 0) -> tpmlp_shape:
+    return tpmlp_shape(tokens, hidden, ffn_shard, dtype, layout)
+
+
+def _layout(b_transposed: bool) -> int:
+    return TPMLP_LAYOUT_B_T if b_transposed else 0
 
 
 def tp_mlp_abi_version() -> int:
@@ -132,13 +139,14 @@ def tp_mlp_status_string(status: int) -> str:
     return load().tp_mlp_status_string(status).decode()
 
 
-def tp_mlp_fwd_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int) -> int:
-    s = shape_of(tokens, hidden, ffn_shard, dtype)
+def tp_mlp_fwd_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int, layout: int = 0) -> int:
+    s = shape_of(tokens, hidden, ffn_shard, dtype, layout)
     return load().tp_mlp_fwd_workspace_bytes(ctypes.byref(s))
 
 
-def tp_mlp_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int, flags: int = 0) -> int:
-    s = shape_of(tokens, hidden, ffn_shard, dtype)
+def tp_mlp_workspace_bytes(tokens: int, hidden: int, ffn_shard: int, dtype: int, flags: int = 0,
+                           layout: int = 0) -> int:
+    s = shape_of(tokens, hidden, ffn_shard, dtype, layout)
     return load().tp_mlp_workspace_bytes(ctypes.byref(s), int(flags))
 
 
@@ -146,33 +154,34 @@ def _nbytes(ws):
     return 0 if ws is None else ws.numel() * ws.element_size()
 
 
-def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None) -> None:
+def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_transposed=False) -> None:
     """Forward of one TP rank into caller-allocated Z, H (or None) and Yp."""
-    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed))
     ev = _events(events)
     _check(load().tp_mlp_fwd(ctypes.byref(s), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),
                              _ptr(ws), _nbytes(ws), _stream(stream), ev))
 
 
-def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None) -> None:
+def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None, b_transposed=False) -> None:
     """Backward of one TP rank into caller-allocated gradients and workspace."""
-    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed))
     nbytes = _nbytes(ws)
     ev = _events(events)
     _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
                              _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
 
 
-def tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None) -> None:
+def tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None, b_transposed=False) -> None:
     """Backward of one TP rank that recomputes Z (and gelu(Z)) from X first."""
-    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed))
     ev = _events(events)
     _check(load().tp_mlp_bwd_recompute(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(dZ),
                                        _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), _nbytes(ws),
                                        _stream(stream), ev))
 
 
-def bwd_recompute(dY, X, A, b1, B, keep_dz: bool = True, staged: bool = True, stream=None, events=None):
+def bwd_recompute(dY, X, A, b1, B, keep_dz: bool = True, staged: bool = True, stream=None, events=None,
+                  b_transposed: bool = False):
     """Allocate the gradients and the workspace with torch and run
     tp_mlp_bwd_recompute."""
     import torch
@@ -181,24 +190,25 @@ def bwd_recompute(dY, X, A, b1, B, keep_dz: bool = True, staged: bool = True, st
     dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
     dXp = torch.empty((T, h), dtype=dt, device=dev)
     dA = torch.empty((h, f), dtype=dt, device=dev)
-    dB = torch.empty((f, h), dtype=dt, device=dev)
+    dB = torch.empty((h, f) if b_transposed else (f, h), dtype=dt, device=dev)
     db1 = torch.empty((f,), dtype=dt, device=dev)
     flags = TPMLP_WS_RECOMPUTE | (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
-    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags)
+    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags, _layout(b_transposed))
     ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
-    tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events)
+    tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events,
+                         b_transposed=b_transposed)
     return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
 
 
 def tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, *, stream=None,
-                         events=None) -> None:
+                         events=None, b_transposed=False) -> None:
     """Backward of one TP rank that adds the weight gradients to fp32 main
     gradients (dA_main [h, f], dB_main [f, h], db1_main [f], float32)."""
     import torch
     for t in (dA_main, dB_main, db1_main):
         if t is not None and t.dtype != torch.float32:
             raise TypeError("main gradients are float32")
-    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X))
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed))
     ev = _events(events)
     _check(load().tp_mlp_bwd_main_grad(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H),
                                        _ptr(dZ), _ptr(dXp), _ptr(dA_main), _ptr(dB_main), _ptr(db1_main), _ptr(ws),
@@ -219,20 +229,21 @@ def tp_mlp_reduce_partials(parts, bias, out, row_begin: int = 0, row_end=None, *
 
 # ---- convenience wrappers that allocate the outputs with torch ----
 
-def fwd(X, A, b1, B, keep_h: bool = True, staged: bool = True, stream=None, events=None):
+def fwd(X, A, b1, B, keep_h: bool = True, staged: bool = True, stream=None, events=None, b_transposed: bool = False):
     """Allocate the outputs (and, if `staged`, the workspace) with torch and run tp_mlp_fwd."""
     import torch
     T, f, h = X.shape[0], A.shape[1], X.shape[1]
     Z = torch.empty((T, f), dtype=X.dtype, device=X.device)
     H = torch.empty((T, f), dtype=X.dtype, device=X.device) if keep_h else None
     Yp = torch.empty((T, h), dtype=X.dtype, device=X.device)
-    nws = tp_mlp_fwd_workspace_bytes(T, h, f, _dtype_code(X)) if staged else 0
+    nws = tp_mlp_fwd_workspace_bytes(T, h, f, _dtype_code(X), _layout(b_transposed)) if staged else 0
     ws = torch.empty((nws,), dtype=torch.uint8, device=X.device) if nws else None
-    tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws, stream=stream, events=events)
+    tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws, stream=stream, events=events, b_transposed=b_transposed)
     return Z, H, Yp
 
 
-def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, stream=None, events=None):
+def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, stream=None, events=None,
+        b_transposed: bool = False):
     """Allocate the gradients and the workspace (the staged size, or the
     minimal one when `staged` is False) with torch and run tp_mlp_bwd."""
     import torch
@@ -241,10 +252,10 @@ def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, strea
     dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
     dXp = torch.empty((T, h), dtype=dt, device=dev)
     dA = torch.empty((h, f), dtype=dt, device=dev)
-    dB = torch.empty((f, h), dtype=dt, device=dev)
+    dB = torch.empty((h, f) if b_transposed else (f, h), dtype=dt, device=dev)
     db1 = torch.empty((f,), dtype=dt, device=dev)
     flags = (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
-    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags)
+    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags, _layout(b_transposed))
     ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
-    tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events)
+    tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events, b_transposed=b_transposed)
     return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}

@@ -149,4 +149,21 @@ struct EpiAccumF32 {
   __device__ __forceinline__ void colsum(int, int64_t, float) const {}
 };
 
+// Any per-element epilogue, with C stored transposed: C[m][n] goes where the
+// inner epilogue puts element (n, m). For the register-staged and fp32
+// engines (per-element apply); used where an operand needs the GeLU on load
+// but sits on the Q side of the GEMM that produces the wanted orientation.
+template <class Inner>
+struct EpiTransposed {
+  Inner inner;
+  static_assert(!Inner::kColSum, "column sums of a transposed store are row sums");
+  static constexpr bool kColSum = false;
+  static constexpr int kOuts = 1;
+  static constexpr bool kInput = false;
+  static constexpr bool kTailSplit = false;
+  static constexpr bool kDirectF32 = false;
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const { return inner.apply(n, m, acc); }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
 }  // namespace tpmlp

@@ -258,8 +258,12 @@ int check_shape(const tpmlp_shape* s) {
   for (int64_t v : d) {
     if (v % mult) return TPMLP_ERR_ALIGN;
   }
+  if (s->layout & ~TPMLP_LAYOUT_B_T) return TPMLP_ERR_SHAPE;
   return TPMLP_OK;
 }
+
+// The second weight arrives as B_i^T [h][f] (and dB leaves as [h][f]).
+bool b_t(const tpmlp_shape& s) { return (s.layout & TPMLP_LAYOUT_B_T) != 0; }
 
 struct Span {
   const void* p;
@@ -341,24 +345,26 @@ FwdWs fwd_ws(const tpmlp_shape& s) {
   const size_t e = elt_size(s.dtype);
   const size_t at_b = (size_t)(s.ffn_shard * staged_ld(s.hidden)) * e, bt_b = (size_t)(s.hidden * staged_ld(s.ffn_shard)) * e;
   w.at = stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
-  w.bt = stages(s.dtype, s.tokens, s.hidden, s.ffn_shard);
+  // B_i^T given (b_t): already the k-contiguous operand of F2, nothing to stage
+  w.bt = !b_t(s) && stages(s.dtype, s.tokens, s.hidden, s.ffn_shard);
   w.at_off = 0;
   w.bt_off = w.at ? align256(at_b) : 0;
   w.tail_off = w.bt_off + (w.bt ? align256(bt_b) : 0);
-  w.tail_bytes = gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard, w.bt);
+  w.tail_bytes = gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard, w.bt || b_t(s));
   w.total = w.tail_off + align256(w.tail_bytes);
   return w;
 }
 
 // Backward workspace: [dZ (if kept here)] [db1 partials fp32 [tiles][f]]
 // then, when the weight-gradient GEMMs stage: [H^T][dY^T] for dB and
-// [X^T][dZ^T] for dA (each [rows][T + pad]); then the tail partials of the
+// [X^T][dZ^T] for dA (each [rows][T + pad]); with B_i^T given, B_i
+// [f][h + pad] for the dZ GEMM when it stages; then the tail partials of the
 // plain-store GEMMs (dB, dA, dXp run one after another and share them).
 struct BwdWs {
   size_t dz_off, dz_bytes, part_off, part_bytes, minimal;
-  size_t ht_off, dyt_off, xt_off, dzt_off, tail_off, tail_bytes, total;
+  size_t ht_off, dyt_off, xt_off, dzt_off, bs_off, tail_off, tail_bytes, total;
   int part_tiles;
-  bool stage_b2, stage_b3;
+  bool stage_b2, stage_b3, stage_b1;
 };
 
 BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
@@ -386,12 +392,19 @@ BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
     w.dzt_off = at + th;
     at += th + tf;
   }
+  w.stage_b1 = b_t(s) && stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
+  if (w.stage_b1) {
+    w.bs_off = at;
+    at += align256((size_t)(s.ffn_shard * staged_ld(s.hidden)) * e);
+  }
+  // dB is the same GEMM with its operands swapped when B_i^T is given
   const size_t tail = std::max({gemm_tail_bytes(s.dtype, s.ffn_shard, s.hidden, s.tokens, w.stage_b2),
+                                 gemm_tail_bytes(s.dtype, s.hidden, s.ffn_shard, s.tokens, w.stage_b2),
                                  gemm_tail_bytes(s.dtype, s.hidden, s.ffn_shard, s.tokens, w.stage_b3),
                                  gemm_tail_bytes(s.dtype, s.tokens, s.hidden, s.ffn_shard, true)});
   w.tail_off = at;
   w.tail_bytes = tail;
-  w.total = (w.stage_b2 || w.stage_b3 || tail) ? at + align256(tail) : w.minimal;
+  w.total = (w.stage_b2 || w.stage_b3 || w.stage_b1 || tail) ? at + align256(tail) : w.minimal;
   return w;
 }
 
@@ -457,7 +470,16 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
   TPMLP_TRY(record(ev, 2, st));
   // TB + F2: Yp = H B_i (gelu(Z) on load when H is not kept); P [T,f]
   // k-contiguous, Q = B_i [f,h] (n-contiguous) or B_i^T [h,f] (k-contiguous)
-  if (!H) {
+  if (b_t(s)) {
+    // B given as B_i^T [h,f]: Q[k][n] = B_i^T[n][k] is k-contiguous as it stands
+    TPMLP_TRY(record(ev, 3, st));
+    if (!H)
+      TPMLP_HIP((run_gemm<S, true, true, true>(s.dtype, Tn, h, f, Z, f, B, f, EpiStore<S>{(T*)Yp, h}, st)));
+    else
+      TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, H, f, B, f, EpiStore<S>{(T*)Yp, h}, st,
+                                                room ? reinterpret_cast<float*>(wsb + w.tail_off) : nullptr,
+                                                room ? w.tail_bytes : 0)));
+  } else if (!H) {
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_HIP((run_gemm<S, true, false, true>(s.dtype, Tn, h, f, Z, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
   } else if (room && w.bt) {
@@ -484,9 +506,11 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
              size_t ws_bytes, hipStream_t st, void* const* ev) {
   using T = typename S::T;
   const int64_t Tn = s.tokens, h = s.hidden, f = s.ffn_shard;
+  const bool bt = b_t(s);
+  // dB [f][h], or [h][f] when B_i^T is given
   auto epi_dB = [&]() {
-    if constexpr (ACC) return EpiAccumF32<S>{static_cast<float*>(dB), h};
-    else return EpiStore<S>{static_cast<T*>(dB), h};
+    if constexpr (ACC) return EpiAccumF32<S>{static_cast<float*>(dB), bt ? f : h};
+    else return EpiStore<S>{static_cast<T*>(dB), bt ? f : h};
   };
   auto epi_dA = [&]() {
     if constexpr (ACC) return EpiAccumF32<S>{static_cast<float*>(dA), f};
@@ -500,9 +524,20 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
   const size_t tcap = room ? w.tail_bytes : 0;
 
   TPMLP_TRY(record(ev, 0, st));
-  // B1: dZ = (dY B_i^T) * gelu'(Z), plus per-tile column sums; Q[k][n] = B_i[n][k] is k-contiguous
-  TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, dY, h, B, h,
-                                            EpiGeluGrad<S>{(const T*)Z, (T*)dZ, part, f}, st)));
+  // B1: dZ = (dY B_i^T) * gelu'(Z), plus per-tile column sums; Q[k][n] = B_i[n][k] is k-contiguous.
+  // With B_i^T [h,f] given, Q[k][n] = B_i^T[k][n] is n-contiguous: it is read
+  // in place, or from a k-contiguous copy B_i [f][h + pad] staged first.
+  if (!bt) {
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, dY, h, B, h,
+                                              EpiGeluGrad<S>{(const T*)Z, (T*)dZ, part, f}, st)));
+  } else if (room && w.stage_b1) {
+    TPMLP_HIP((run_transpose<S, false>(B, wsb + w.bs_off, h, f, st)));
+    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, f, h, dY, h, wsb + w.bs_off, staged_ld(h),
+                                              EpiGeluGrad<S>{(const T*)Z, (T*)dZ, part, f}, st)));
+  } else {
+    TPMLP_HIP((run_gemm<S, true, false, false>(s.dtype, Tn, f, h, dY, h, B, f,
+                                               EpiGeluGrad<S>{(const T*)Z, (T*)dZ, part, f}, st)));
+  }
   TPMLP_TRY(record(ev, 1, st));
   // B5: db1 = sum of the column partials
   if (f > 0) {
@@ -526,13 +561,21 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_HIP((run_transpose<S, false>(dY, wsb + w.dyt_off, Tn, h, st)));
     TPMLP_TRY(record(ev, 4, st));
-    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, staged_ld(Tn), wsb + w.dyt_off,
-                                              staged_ld(Tn),
-                                              epi_dB(), st, tail, tcap)));
+    if (bt)  // dB^T = dY^T H: the same staged operands, swapped
+      TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.dyt_off, staged_ld(Tn), wsb + w.ht_off,
+                                                staged_ld(Tn), epi_dB(), st, tail, tcap)));
+    else
+      TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, staged_ld(Tn), wsb + w.dyt_off,
+                                                staged_ld(Tn), epi_dB(), st, tail, tcap)));
   } else {
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_TRY(record(ev, 4, st));
-    if (H)
+    if (bt && H)  // dB^T [h,f] = dY^T H: P[m][k] = dY[k][m], Q[k][n] = H[k][n]
+      TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, dY, h, H, f, epi_dB(), st, tail, tcap)));
+    else if (bt)  // gelu applies to P only: compute H^T dY with gelu(Z) on load, store it transposed
+      TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h,
+                                                 EpiTransposed<decltype(epi_dB())>{epi_dB()}, st)));
+    else if (H)
       TPMLP_HIP(
           (run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, epi_dB(), st, tail, tcap)));
     else

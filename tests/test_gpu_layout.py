@@ -1,0 +1,147 @@
+"""Parity of the transposed-B layout (TPMLP_LAYOUT_B_T: the second weight
+passed as B_i^T [hidden, ffn_shard], its gradient returned in that order)
+against the float64 oracle, through the C ABI, on every tile engine, with
+and without H kept, staged and minimal workspaces, the fp32 main-gradient
+and the recomputing backward. Z and H do not depend on B and must equal the
+default layout's bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import TOL, compare, device_inputs, to_host
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dZ", "dXp", "dA", "dB", "db1")
+
+
+@pytest.fixture
+def tile(request, monkeypatch):
+    value = getattr(request, "param", None)
+    if value is None:
+        monkeypatch.delenv("TPMLP_TILE", raising=False)
+    else:
+        monkeypatch.setenv("TPMLP_TILE", str(value))
+    return value
+
+
+CASES = ([(None, "f32")] + [(t, d) for t in (None, 128, 256, "dma256", "dma320") for d in ("f16", "bf16")])
+
+
+def _ref(inp):
+    ref = {**oracle.shard_forward(inp.X, inp.A, inp.b1, inp.B),
+           **oracle.shard_backward(inp.X, inp.A, inp.b1, inp.B, inp.dY)}
+    ref["dB"] = ref["dB"].T.copy()   # returned as [h, f] in this layout
+    return ref
+
+
+@pytest.mark.parametrize("tile,dtype", CASES, indirect=["tile"])
+@pytest.mark.parametrize("T,h,f", [(200, 136, 264), (520, 264, 392)])
+@pytest.mark.parametrize("keep_h,staged", [(True, True), (False, True), (True, False), (False, False)])
+def test_b_transposed_matches_oracle(gpu_lib, tile, dtype, T, h, f, keep_h, staged):
+    import torch
+    print(f"case layout_b_t tile={tile} dtype={dtype} T={T} h={h} f={f} keep_h={keep_h} staged={staged}", flush=True)
+    inp = synth.draw_inputs(T, h, f, dtype, seed=3 * T + f, sigma_dy=1.0)
+    X, A, b1, B, dY = device_inputs(inp)
+    Bt = B.t().contiguous()
+    Z, H, Yp = gpu_lib.fwd(X, A, b1, Bt, keep_h=keep_h, staged=staged, b_transposed=True)
+    g = gpu_lib.bwd(dY, X, A, Bt, Z, H, staged=staged, b_transposed=True)
+    torch.cuda.synchronize()
+    assert tuple(g["dB"].shape) == (h, f)
+    got = {"Z": Z, "Yp": Yp, **g}
+    if H is not None:
+        got["H"] = H
+    compare(got, _ref(inp), TOL[dtype])
+    Z0, H0, _ = gpu_lib.fwd(X, A, b1, B, keep_h=keep_h, staged=staged)
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z0)
+    if keep_h:
+        assert torch.equal(H, H0)
+
+
+@pytest.mark.parametrize("tile", [None, 128, "dma256", "dma320"], indirect=True)
+@pytest.mark.parametrize("staged", [True, False])
+def test_b_transposed_main_grad_accumulates(gpu_lib, tile, staged):
+    """Two micro-batches add twice into the fp32 main gradients, dB_main in
+    [h, f] order; each addition matches the oracle's weight gradients."""
+    import torch
+    T, h, f, dtype = 520, 264, 392, "bf16"
+    inp = synth.draw_inputs(T, h, f, dtype, seed=77, sigma_dy=1.0)
+    X, A, b1, B, dY = device_inputs(inp)
+    Bt = B.t().contiguous()
+    rng = np.random.default_rng(5)
+    start = {"dA": rng.standard_normal((h, f)) * 1e-2, "dB": rng.standard_normal((h, f)) * 1e-2,
+             "db1": rng.standard_normal((f,)) * 1e-2}
+    mains = {k: torch.as_tensor(v, dtype=torch.float32, device="cuda") for k, v in start.items()}
+    ref = _ref(inp)
+    code = gpu_lib.TPMLP_BF16
+    flags = 0 if staged else gpu_lib.TPMLP_WS_MINIMAL
+    nws = gpu_lib.tp_mlp_workspace_bytes(T, h, f, code, flags, gpu_lib.TPMLP_LAYOUT_B_T)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device="cuda")
+    old = {k: v.copy() for k, v in start.items()}
+    for step in range(2):
+        Z, H, _ = gpu_lib.fwd(X, A, b1, Bt, staged=staged, b_transposed=True)
+        dZ = torch.empty((T, f), dtype=X.dtype, device="cuda")
+        dXp = torch.empty((T, h), dtype=X.dtype, device="cuda")
+        gpu_lib.tp_mlp_bwd_main_grad(dY, X, A, Bt, Z, H, dZ, dXp, mains["dA"], mains["dB"], mains["db1"], ws,
+                                     b_transposed=True)
+        torch.cuda.synchronize()
+        new = {k: to_host(v) for k, v in mains.items()}
+        for k in ("dA", "dB", "db1"):
+            err = float(np.max(np.abs(new[k] - old[k] - ref[k])) / np.max(np.abs(ref[k])))
+            assert err <= TOL[dtype], (step, k, err)
+        old = new
+
+
+@pytest.mark.parametrize("tile,dtype", [(None, "f32"), (None, "bf16"), (128, "f16"), ("dma256", "bf16"),
+                                        ("dma320", "f16")], indirect=["tile"])
+@pytest.mark.parametrize("staged", [True, False])
+def test_b_transposed_recompute(gpu_lib, tile, dtype, staged):
+    """The recomputing backward in this layout equals the plain backward
+    (H = NULL) in this layout bit for bit, and the oracle to tolerance."""
+    import torch
+    T, h, f = 520, 264, 392
+    inp = synth.draw_inputs(T, h, f, dtype, seed=91, sigma_dy=1.0)
+    X, A, b1, B, dY = device_inputs(inp)
+    Bt = B.t().contiguous()
+    got = gpu_lib.bwd_recompute(dY, X, A, b1, Bt, staged=staged, b_transposed=True)
+    torch.cuda.synchronize()
+    compare(got, _ref(inp), TOL[dtype], keys=GRADS)
+    Z, _, _ = gpu_lib.fwd(X, A, b1, Bt, keep_h=False, staged=staged, b_transposed=True)
+    plain = gpu_lib.bwd(dY, X, A, Bt, Z, None, staged=staged, b_transposed=True)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(got[k], plain[k]), k
+
+
+@pytest.mark.slow
+def test_b_transposed_full_size_h10240_sampled(gpu_lib):
+    """The h=10240 TP=4 shard (bf16) in this layout, in bench.py's launch
+    configuration (staged workspaces, H and dZ kept), on sampled rows and
+    columns against the oracle's restricted definitions."""
+    import torch
+    from tests.test_gpu_fullsize import _check, _samples
+    cfg = synth.get_config("gpt_h10240")
+    print(f"case full-size layout_b_t {cfg.name}", flush=True)
+    inp = synth.draw_config(cfg)
+    X, A, b1, B, dY = device_inputs(inp)
+    Bt = B.t().contiguous()
+    del B
+    Z, H, Yp = gpu_lib.fwd(X, A, b1, Bt, b_transposed=True)
+    g = gpu_lib.bwd(dY, X, A, Bt, Z, H, b_transposed=True)
+    torch.cuda.synchronize()
+    out = {"Z": Z, "H": H, "Yp": Yp, **g}
+    T, f = cfg.tokens, cfg.ffn_shard
+    rows, cols = _samples(T, 40, 0), _samples(f, 16, 1)
+    rr = oracle.sampled_rows(inp.X, inp.A, inp.b1, inp.B, inp.dY, rows)
+    rc = oracle.sampled_cols(inp.X, inp.A, inp.b1, inp.B, inp.dY, cols)
+    ri, ci = torch.as_tensor(rows, device="cuda"), torch.as_tensor(cols, device="cuda")
+    tol, errs = TOL[cfg.dtype], {}
+    for k in ("Z", "H", "Yp", "dZ", "dXp"):
+        _check(f"{k}[rows]", to_host(out[k].index_select(0, ri)), rr[k], tol, errs)
+    for k in ("Z", "H", "dZ", "dA"):
+        _check(f"{k}[:,cols]", to_host(out[k].index_select(1, ci)), rc[k], tol, errs)
+    _check("db1[cols]", to_host(out["db1"].index_select(0, ci)), rc["db1"], tol, errs)
+    _check("dB^T[:,cols]", to_host(out["dB"].index_select(1, ci)).T, rc["dB"], tol, errs)
+    print("errors", errs, flush=True)
