@@ -16,8 +16,10 @@ Values are i.i.d. Gaussians (no structure), drawn in float64 with NumPy's
 PCG64 and rounded to nearest-even into the storage dtype, so that the oracle
 and the GPU consume bit-identical operands.
 """
-from .configs import CONFIGS, Config, get_config, shard_width
+from .configs import ATTN_CONFIGS, CONFIGS, AttnConfig, Config, get_attn_config, get_config, shard_width
 from .draw import (
+    AttnInputs,
+    draw_attn_inputs,
     draw_config,
     Inputs,
     draw_inputs,
@@ -27,6 +29,11 @@ from .draw import (
 )
 
 __all__ = [
+    "ATTN_CONFIGS",
+    "AttnConfig",
+    "AttnInputs",
+    "draw_attn_inputs",
+    "get_attn_config",
     "CONFIGS",
     "Config",
     "get_config",

@@ -68,3 +68,53 @@ CONFIGS = {
 
 def get_config(name: str) -> Config:
     return CONFIGS[name]
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """Self-attention workload: n heads of width d = hidden / n over
+    micro-batch x seq tokens; one TP rank owns n / P heads."""
+    name: str
+    dtype: str
+    micro_batch: int
+    seq_len: int
+    hidden: int
+    heads: int          # all heads (all TP ranks together)
+    tp: int
+    causal: bool = True
+    sigma_x: float = 1.0
+    sigma_w: float = 0.02
+    sigma_b: float = 0.01
+    sigma_dy: float = 0.01
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.micro_batch * self.seq_len
+
+    @property
+    def head_dim(self) -> int:
+        return self.hidden // self.heads
+
+    @property
+    def heads_shard(self) -> int:
+        if self.heads % self.tp:
+            raise ValueError(f"{self.heads} heads are not divisible by TP degree {self.tp}")
+        return self.heads // self.tp
+
+
+# The 2.4B run prints hidden 2560, 32 attention heads, seq 2048 and
+# micro-batch 4 ("Training GPT-2 with Megatron-LM", section 4.1); one rank
+# of TP 4 (as for its MLP) owns 8 heads of width 80. The small case keeps the
+# same structure at sizes the oracle finishes in milliseconds.
+ATTN_CONFIGS = {
+    c.name: c
+    for c in [
+        AttnConfig("attn_small", "f16", 2, 64, 128, 4, 2, sigma_dy=1.0),
+        AttnConfig("attn_2p4b", "bf16", 4, 2048, 2560, 32, 4),
+    ]
+}
+
+
+def get_attn_config(name: str) -> AttnConfig:
+    return ATTN_CONFIGS[name]

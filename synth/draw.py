@@ -107,7 +107,7 @@ class Inputs:
 # (seed, t, c), so chunks can be drawn in parallel and the values do not
 # depend on the number of threads.
 DRAW_CHUNK = 1 << 22
-TENSOR_IDS = {"X": 0, "A": 1, "b1": 2, "B": 3, "dY": 4}
+TENSOR_IDS = {"X": 0, "A": 1, "b1": 2, "B": 3, "dY": 4, "Wqkv": 5, "bqkv": 6, "Wo": 7}
 
 
 def _threads() -> int:
@@ -164,3 +164,42 @@ def draw_config(cfg: Config) -> Inputs:
     return draw_inputs(cfg.tokens, cfg.hidden, width, cfg.dtype, seed=cfg.seed,
                        sigma_x=cfg.sigma_x, sigma_w=cfg.sigma_w, sigma_b=cfg.sigma_b,
                        sigma_dy=cfg.sigma_dy, tp=cfg.tp, full=cfg.all_shards)
+
+
+@dataclass
+class AttnInputs:
+    """One draw of the attention shard's operands (float64 values exact in
+    `dtype`): X [T, h], Wqkv [h, 3q], bqkv [3q], Wo [q, h], dY [T, h], with
+    q = heads * head_dim the width of the heads drawn (one rank's, or all of
+    them when full=True)."""
+    dtype: str
+    batch: int
+    heads: int
+    X: np.ndarray
+    Wqkv: np.ndarray
+    bqkv: np.ndarray
+    Wo: np.ndarray
+    dY: np.ndarray
+    full: bool = False
+
+    @property
+    def seq(self) -> int:
+        return self.X.shape[0] // self.batch
+
+    @property
+    def head_dim(self) -> int:
+        return self.Wo.shape[0] // self.heads
+
+
+def draw_attn_inputs(batch: int, seq: int, hidden: int, heads: int, head_dim: int, dtype: str, *, seed: int = 0,
+                     sigma_x: float = 1.0, sigma_w: float = 0.02, sigma_b: float = 0.01, sigma_dy: float = 0.01,
+                     full: bool = False) -> AttnInputs:
+    """Draw X, Wqkv, bqkv, Wo and dY for `heads` heads of width `head_dim`
+    (i.i.d. N(0, sigma^2) like draw_inputs, from their own PCG64 streams)."""
+    T, q = batch * seq, heads * head_dim
+    X = _normal(seed, "X", (T, hidden), sigma_x, dtype)
+    Wqkv = _normal(seed, "Wqkv", (hidden, 3 * q), sigma_w, dtype)
+    bqkv = _normal(seed, "bqkv", (3 * q,), sigma_b, dtype)
+    Wo = _normal(seed, "Wo", (q, hidden), sigma_w, dtype)
+    dY = _normal(seed, "dY", (T, hidden), sigma_dy, dtype)
+    return AttnInputs(dtype, batch, heads, X, Wqkv, bqkv, Wo, dY, full=full)
