@@ -138,6 +138,63 @@ def reduce_partials_rate(tpmlp, Yp, cfg, dev, reps=10):
             "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / 8000.0, 4)}
 
 
+def attention_rate(tpmlp, dev, reps=10):
+    """Forward + backward of one TP rank's attention share of the 2.4B model
+    (8 of 32 heads of width 80, 4 sequences of 2048 tokens, bf16, causal)
+    through tp_attn_fwd / tp_attn_bwd, timed with HIP events on the launch
+    stream. Not part of a step (the MLP block is); reported beside it. Flops
+    count every product as dense (the causal scores and P V are computed in
+    full, masked entries included): per pass 2 T h 3q + 2 T q h for the
+    projections and 2 x 2 Z s^2 d for the scores and P V, backward twice the
+    forward."""
+    import torch
+    import synth
+    from tests.gpu_util import to_device
+    cfg = synth.get_attn_config("attn_2p4b")
+    b, s, h, n, d = cfg.micro_batch, cfg.seq_len, cfg.hidden, cfg.heads_shard, cfg.head_dim
+    inp = synth.draw_attn_inputs(b, s, h, n, d, cfg.dtype, seed=cfg.seed, sigma_dy=cfg.sigma_dy)
+    X, Wqkv, bqkv, Wo, dY = (to_device(getattr(inp, k), cfg.dtype) for k in ("X", "Wqkv", "bqkv", "Wo", "dY"))
+    code = tpmlp.TPMLP_BF16
+    fws = torch.empty((tpmlp.tp_attn_fwd_workspace_bytes(b, s, h, n, d, code, cfg.causal),), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty((tpmlp.tp_attn_bwd_workspace_bytes(b, s, h, n, d, code, cfg.causal),), dtype=torch.uint8,
+                      device=dev)
+    T, q = b * s, n * d
+    e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=dev)
+    QKV, P, O, Yp = e(T, 3 * q), e(b * n, s, s), e(T, q), e(T, h)
+    dQKV, dXp, dWqkv, dbqkv, dWo = e(T, 3 * q), e(T, h), e(h, 3 * q), e(3 * q), e(q, h)
+
+    def fwd():
+        tpmlp.tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, fws, batch=b, heads=n, causal=cfg.causal)
+
+    def bwd():
+        tpmlp.tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, bws, batch=b, heads=n,
+                          causal=cfg.causal)
+
+    for _ in range(2):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        ev[r][0].record()
+        fwd()
+        ev[r][1].record()
+        bwd()
+        ev[r][2].record()
+    torch.cuda.synchronize()
+    f_ms = sum(x[0].elapsed_time(x[1]) for x in ev) / reps
+    b_ms = sum(x[1].elapsed_time(x[2]) for x in ev) / reps
+    Z = b * n
+    flops_f = 2.0 * T * h * 3 * q + 2.0 * T * q * h + 2 * 2.0 * Z * s * s * d
+    tflops = 3 * flops_f / ((f_ms + b_ms) * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    return {"workload": f"{cfg.name}: one TP={cfg.tp} rank's attention of hidden {h}, {cfg.heads} heads of width {d} "
+                        f"({n} on this rank), micro-batch {b} x seq {s}, causal, {cfg.dtype}",
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tflops, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +213,8 @@ def main():
                          "in that order")
     ap.add_argument("--no-reduce", action="store_true",
                     help="skip timing tp_mlp_reduce_partials (the TP group's sum of partials, not part of a step)")
+    ap.add_argument("--no-attn", action="store_true",
+                    help="skip timing the attention shard (tp_attn_fwd + tp_attn_bwd, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run one plain device copy of this many MiB (a known-size kernel that "
                          "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
@@ -265,6 +324,7 @@ def main():
     achieved = gemm_flops / (per[dom] * 1e-3) / 1e12
 
     reduce_line = None if args.no_reduce else reduce_partials_rate(tpmlp, Yp, cfg, dev)
+    attn_line = None if args.no_attn else attention_rate(tpmlp, dev)
 
     result = {
         "metric": METRIC,
@@ -300,6 +360,7 @@ def main():
         },
         "cpu_baseline": None,
         "reduce_partials": reduce_line,
+        "attention": attn_line,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)

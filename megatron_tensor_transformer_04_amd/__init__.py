@@ -1,9 +1,17 @@
 """MI355X (gfx950) tensor-parallel MLP shard: forward and backward of one
 rank's share of a Transformer FFN block, as hand-written HIP kernels behind
-the C ABI in include/tp_mlp.h. This package is the ctypes binding to that
+the C ABI in include/tp_mlp.h, and of the attention block's share
+(include/tp_attn.h). This package is the ctypes binding to that
 library (libtpmlp.so, built in-tree by _build.build()).
 """
 from ._binding import (  # noqa: F401
+    attn_bwd,
+    attn_fwd,
+    attn_shape,
+    tp_attn_bwd,
+    tp_attn_bwd_workspace_bytes,
+    tp_attn_fwd,
+    tp_attn_fwd_workspace_bytes,
     BWD_EVENTS,
     EXPORTS,
     FWD_EVENTS,

@@ -24,7 +24,8 @@ STATUS = {
     7: "TPMLP_ERR_ALIAS",
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
-           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials")
+           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
+           "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd")
 TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL, TPMLP_WS_RECOMPUTE = 1, 2, 4
 FWD_EVENTS = ("TA", "F1", "TB", "F2")                                     # steps bracketed by the 5 events
@@ -44,6 +45,12 @@ TPMLP_LAYOUT_B_T = 1   # B passed as B_i^T [hidden, ffn_shard] (dB returned in t
 class tpmlp_shape(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("ffn_shard", ctypes.c_int64), ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class tpattn_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32)]
 
 
 _lib = None
@@ -77,6 +84,15 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_reduce_partials.restype = ctypes.c_int
     lib.tp_mlp_reduce_partials.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int, ctypes.POINTER(vp), vp,
                                            ctypes.c_int64, ctypes.c_int64, vp, vp]
+    ap = ctypes.POINTER(tpattn_shape)
+    lib.tp_attn_fwd_workspace_bytes.restype = sz
+    lib.tp_attn_fwd_workspace_bytes.argtypes = [ap]
+    lib.tp_attn_bwd_workspace_bytes.restype = sz
+    lib.tp_attn_bwd_workspace_bytes.argtypes = [ap]
+    lib.tp_attn_fwd.restype = ctypes.c_int
+    lib.tp_attn_fwd.argtypes = [ap] + [vp] * 8 + [vp, sz, vp]
+    lib.tp_attn_bwd.restype = ctypes.c_int
+    lib.tp_attn_bwd.argtypes = [ap] + [vp] * 12 + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -259,3 +275,74 @@ def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, strea
     ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
     tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events, b_transposed=b_transposed)
     return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
+
+
+# ---- attention shard (include/tp_attn.h) ----
+
+def attn_shape(batch: int, seq: int, hidden: int, heads: int, head_dim: int, dtype: int,
+               causal: bool = True) -> tpattn_shape:
+    return tpattn_shape(batch, seq, hidden, heads, head_dim, dtype, 1 if causal else 0)
+
+
+def tp_attn_fwd_workspace_bytes(batch, seq, hidden, heads, head_dim, dtype, causal=True) -> int:
+    s = attn_shape(batch, seq, hidden, heads, head_dim, dtype, causal)
+    return load().tp_attn_fwd_workspace_bytes(ctypes.byref(s))
+
+
+def tp_attn_bwd_workspace_bytes(batch, seq, hidden, heads, head_dim, dtype, causal=True) -> int:
+    s = attn_shape(batch, seq, hidden, heads, head_dim, dtype, causal)
+    return load().tp_attn_bwd_workspace_bytes(ctypes.byref(s))
+
+
+def _attn_shape_of(X, Wo, batch, heads, causal):
+    T, h = X.shape
+    q = Wo.shape[0]
+    if T % batch or q % heads:
+        raise ValueError("tokens must split into `batch` sequences and Wo rows into `heads` heads")
+    return attn_shape(batch, T // batch, h, heads, q // heads, _dtype_code(X), causal)
+
+
+def tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, *, batch, heads, causal=True, stream=None) -> None:
+    """Forward of one rank's heads into caller-allocated QKV, P, O, Yp."""
+    s = _attn_shape_of(X, Wo, batch, heads, causal)
+    _check(load().tp_attn_fwd(ctypes.byref(s), _ptr(X), _ptr(Wqkv), _ptr(bqkv), _ptr(Wo), _ptr(QKV), _ptr(P),
+                              _ptr(O), _ptr(Yp), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, *, batch, heads, causal=True,
+                stream=None) -> None:
+    """Backward of one rank's heads into caller-allocated gradients."""
+    s = _attn_shape_of(X, Wo, batch, heads, causal)
+    _check(load().tp_attn_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(QKV), _ptr(P),
+                              _ptr(O), _ptr(dQKV), _ptr(dXp), _ptr(dWqkv), _ptr(dbqkv), _ptr(dWo), _ptr(ws),
+                              _nbytes(ws), _stream(stream)))
+
+
+def attn_fwd(X, Wqkv, bqkv, Wo, batch, heads, causal=True, ws=None, stream=None):
+    """Allocate the outputs (and the workspace unless given) with torch and run tp_attn_fwd."""
+    import torch
+    T, h = X.shape
+    q = Wo.shape[0]
+    s = T // batch
+    e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
+    QKV, P, O, Yp = e(T, 3 * q), e(batch * heads, s, s), e(T, q), e(T, h)
+    if ws is None:
+        n = tp_attn_fwd_workspace_bytes(batch, s, h, heads, q // heads, _dtype_code(X), causal)
+        ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
+    tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, batch=batch, heads=heads, causal=causal, stream=stream)
+    return {"QKV": QKV, "P": P, "O": O, "Yp": Yp}
+
+
+def attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, batch, heads, causal=True, ws=None, stream=None):
+    """Allocate the gradients (and the workspace unless given) with torch and run tp_attn_bwd."""
+    import torch
+    T, h = X.shape
+    q = Wo.shape[0]
+    e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
+    dQKV, dXp, dWqkv, dbqkv, dWo = e(T, 3 * q), e(T, h), e(h, 3 * q), e(3 * q), e(q, h)
+    if ws is None:
+        n = tp_attn_bwd_workspace_bytes(batch, T // batch, h, heads, q // heads, _dtype_code(X), causal)
+        ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
+    tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, batch=batch, heads=heads,
+                causal=causal, stream=stream)
+    return {"dQKV": dQKV, "dXp": dXp, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo}

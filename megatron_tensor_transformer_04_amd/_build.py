@@ -1,21 +1,26 @@
-"""Compile the HIP library libtpmlp.so for gfx950, in-tree, with hipcc."""
+"""Compile the HIP library libtpmlp.so for gfx950, in-tree, with hipcc.
+
+Each source is compiled to an object in parallel, then the objects are
+linked into one shared library (MLP shard and attention shard entry points).
+"""
 import os
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtpmlp.so")
-SOURCES = [os.path.join(CSRC, "tp_mlp.hip")]
+SOURCES = [os.path.join(CSRC, "tp_mlp.hip"), os.path.join(CSRC, "tp_attn.hip")]
+OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed-fp32 VALU forms stay off: scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -29,15 +34,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
-    """Compile SOURCES into `out` (atomically replaced) and return its path."""
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
+
+
+def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
+    """Compile SOURCES into `out` (atomically replaced) and return its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = hipcc()
+    objs = [os.path.join(OBJDIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in SOURCES]
+    cmds = [[cc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+            for src, obj in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = out + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

@@ -26,9 +26,20 @@
 // tiles that run together on one XCD share A row panels and B column panels.
 #pragma once
 
+#include <type_traits>
+
 #include "numerics.hpp"
 
 namespace tpmlp {
+
+// A batched epilogue (static constexpr bool kBatched = true) serves a grid
+// whose y index z selects one of several independent GEMMs of the same
+// shape: its select(z, P, Q) moves the two operands and its own outputs to
+// batch z's matrices before the tile is computed.
+template <class E, class = void>
+struct EpiBatched : std::false_type {};
+template <class E>
+struct EpiBatched<E, std::void_t<decltype(E::kBatched)>> : std::integral_constant<bool, E::kBatched> {};
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct MfmaTile {
@@ -145,6 +156,7 @@ template <class Cfg, class S, bool P_KC, bool Q_KC, bool GELU_P, class Epi>
 __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, Operand P, Operand Q, Epi epi) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, THREADS = Cfg::THREADS;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  if constexpr (EpiBatched<Epi>::value) epi.select((int)blockIdx.y, P, Q);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;

@@ -1,0 +1,463 @@
+// C ABI of the tensor-parallel self-attention shard (declared in
+// include/tp_attn.h): one rank's heads, forward and backward.
+//
+// Every product runs on the register-staged MFMA engine (gemm_mfma.hpp,
+// 128 x 128 tiles). The per-head products (scores, P V and the four
+// backward products) are one batched launch each: grid y runs over the
+// batch * heads (sequence, head) pairs, and a batched epilogue moves the
+// operands and its output to that pair's blocks before the tile is computed.
+// Operands are read where they lie (Q, K, V as column blocks of QKV with row
+// pitch 3q; O, dO with pitch q): a head's block is k-contiguous or
+// mn-contiguous for each product and the engine reads either layout.
+//
+// Between the products, two row kernels: the fused scale + causal mask +
+// softmax over fp32 scores (one wave per row), and its backward
+// dS = P * (dP - rowsum(P * dP)) / sqrt(d). dbqkv is a two-pass fixed-order
+// column sum.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "tp_attn.h"
+#include "epilogues.hpp"
+#include "gemm_mfma.hpp"
+
+namespace tpmlp {
+namespace {
+
+using CfgA = MfmaTile<128, 128, 2, 2>;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Offsets (in elements) of batch z = b * inner + j: operand P, operand Q and
+// the output each move by b * (stride per sequence) + j * (stride per head).
+struct BatchMap {
+  int inner;
+  int64_t p_b, p_j, q_b, q_j, o_b, o_j;
+};
+
+// Plain store of one (sequence, head) product into its block of a larger
+// matrix (row pitch ld), rounded once to the storage dtype.
+template <class S>
+struct EpiStoreBatched {
+  typename S::T* out;
+  int64_t ld;
+  BatchMap bm;
+  static constexpr bool kBatched = true;
+  static constexpr bool kColSum = false;
+  __device__ __forceinline__ void select(int z, Operand& P, Operand& Q) {
+    const int64_t b = z / bm.inner, j = z % bm.inner;
+    P.ptr += b * bm.p_b + j * bm.p_j;
+    Q.ptr += b * bm.q_b + j * bm.q_j;
+    out += b * bm.o_b + j * bm.o_j;
+  }
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    out[m * ld + n] = S::from_f(acc);
+    return 0.0f;
+  }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
+// fp32 store of a batched product (the scores, and dP in the backward).
+struct EpiStoreF32Batched {
+  float* out;
+  int64_t ld;
+  BatchMap bm;
+  static constexpr bool kBatched = true;
+  static constexpr bool kColSum = false;
+  __device__ __forceinline__ void select(int z, Operand& P, Operand& Q) {
+    const int64_t b = z / bm.inner, j = z % bm.inner;
+    P.ptr += b * bm.p_b + j * bm.p_j;
+    Q.ptr += b * bm.q_b + j * bm.q_j;
+    out += b * bm.o_b + j * bm.o_j;
+  }
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    out[m * ld + n] = acc;
+    return 0.0f;
+  }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
+// C[M][N] = sum_k P[m][k] Q[k][n] for `batches` independent products (grid y).
+template <class S, bool PK, bool QK, class Epi>
+hipError_t gemm(int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q, int64_t ldq,
+                const Epi& epi, int batches, hipStream_t st) {
+  if (M == 0 || N == 0 || batches == 0) return hipSuccess;
+  GemmShape sh{M, N, K, (int)cdiv(M, CfgA::BM), (int)cdiv(N, CfgA::BN), 1, std::max<int64_t>(K, 1)};
+  hipLaunchKernelGGL((gemm_mfma_kernel<CfgA, S, PK, QK, false, Epi>), dim3(sh.tiles_m * sh.tiles_n, batches),
+                     dim3(CfgA::THREADS), 0, st, sh, Operand{static_cast<const uint16_t*>(p), ldp},
+                     Operand{static_cast<const uint16_t*>(q), ldq}, epi);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Fused scale + causal mask + softmax, one wave per row of the fp32 scores
+// [rows][s] (row r is query r % s of its (sequence, head) pair):
+//   x_k = S[k] * scale for the visible keys k (k <= query when causal),
+//   P[k] = exp(x_k - max) / sum_k' exp(x_k' - max), 0 for masked keys,
+// rounded once to the storage dtype. Each lane takes four consecutive keys
+// per step; the max and the sum are reduced lane-strided then across the
+// wave in a fixed order.
+template <class S>
+__global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restrict__ sc, typename S::T* __restrict__ P,
+                                                          int64_t rows, int64_t s, float scale, int causal) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t qi = row % s;
+  const int64_t nv = causal ? qi + 1 : s;
+  const float* x = sc + row * s;
+  typename S::T* p = P + row * s;
+  float m = -INFINITY;
+  for (int64_t k = (int64_t)lane * 4; k < nv; k += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(x + k);
+    m = fmaxf(m, v.x * scale);
+    if (k + 1 < nv) m = fmaxf(m, v.y * scale);
+    if (k + 2 < nv) m = fmaxf(m, v.z * scale);
+    if (k + 3 < nv) m = fmaxf(m, v.w * scale);
+  }
+  m = wave_max(m);
+  float z = 0.0f;
+  for (int64_t k = (int64_t)lane * 4; k < nv; k += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(x + k);
+    z += expf(v.x * scale - m);
+    if (k + 1 < nv) z += expf(v.y * scale - m);
+    if (k + 2 < nv) z += expf(v.z * scale - m);
+    if (k + 3 < nv) z += expf(v.w * scale - m);
+  }
+  z = wave_sum(z);
+  const float rz = 1.0f / z;
+  for (int64_t k = (int64_t)lane * 4; k < s; k += 256) {
+    float e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (k < nv) {
+      const float4 v = *reinterpret_cast<const float4*>(x + k);
+      const float xv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = (k + i < nv) ? expf(xv[i] * scale - m) * rz : 0.0f;
+    }
+    uint2 w;
+    w.x = (uint32_t)S::from_f(e[0]) | ((uint32_t)S::from_f(e[1]) << 16);
+    w.y = (uint32_t)S::from_f(e[2]) | ((uint32_t)S::from_f(e[3]) << 16);
+    *reinterpret_cast<uint2*>(p + k) = w;
+  }
+}
+
+// Backward of the softmax, one wave per row: with the stored (rounded)
+// probabilities P and the fp32 dP = dO V^T,
+//   D = sum over visible keys of P[k] dP[k],  dS[k] = P[k] (dP[k] - D) * scale,
+// 0 for masked keys, rounded once to the storage dtype.
+template <class S>
+__global__ __launch_bounds__(256) void softmax_bwd_kernel(const float* __restrict__ dp,
+                                                          const typename S::T* __restrict__ P,
+                                                          typename S::T* __restrict__ dS, int64_t rows, int64_t s,
+                                                          float scale, int causal) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t qi = row % s;
+  const int64_t nv = causal ? qi + 1 : s;
+  const float* g = dp + row * s;
+  const typename S::T* p = P + row * s;
+  typename S::T* o = dS + row * s;
+  auto probs = [&](int64_t k, float (&pv)[4]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + k);
+    pv[0] = S::to_f((typename S::T)(w.x & 0xffffu));
+    pv[1] = S::to_f((typename S::T)(w.x >> 16));
+    pv[2] = S::to_f((typename S::T)(w.y & 0xffffu));
+    pv[3] = S::to_f((typename S::T)(w.y >> 16));
+  };
+  float d = 0.0f;
+  for (int64_t k = (int64_t)lane * 4; k < nv; k += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(g + k);
+    float pv[4];
+    probs(k, pv);
+    const float gv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (k + i < nv) d += pv[i] * gv[i];
+  }
+  d = wave_sum(d);
+  for (int64_t k = (int64_t)lane * 4; k < s; k += 256) {
+    float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (k < nv) {
+      const float4 v = *reinterpret_cast<const float4*>(g + k);
+      float pv[4];
+      probs(k, pv);
+      const float gv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (k + i < nv) ? pv[i] * (gv[i] - d) * scale : 0.0f;
+    }
+    uint2 w;
+    w.x = (uint32_t)S::from_f(r[0]) | ((uint32_t)S::from_f(r[1]) << 16);
+    w.y = (uint32_t)S::from_f(r[2]) | ((uint32_t)S::from_f(r[3]) << 16);
+    *reinterpret_cast<uint2*>(o + k) = w;
+  }
+}
+
+// Column sums of a [rows][cols] 16-bit matrix, first pass: block (x, y) sums
+// rows [256 y, 256 y + 256) of columns [256 x, 256 x + 256) in row order
+// into part[y][col] (fp32).
+template <class S>
+__global__ __launch_bounds__(256) void colsum_part_kernel(const typename S::T* __restrict__ m, int64_t rows,
+                                                          int64_t cols, float* __restrict__ part) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * 256, r1 = std::min<int64_t>(rows, r0 + 256);
+  float s = 0.0f;
+  for (int64_t r = r0; r < r1; ++r) s += S::to_f(m[r * cols + c]);
+  part[(int64_t)blockIdx.y * cols + c] = s;
+}
+
+// Second pass: out[c] = round(sum over blocks of part[b][c]) in block order.
+template <class S>
+__global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restrict__ part, int nblk, int64_t cols,
+                                                            typename S::T* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.0f;
+  for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * cols + c];
+  out[c] = S::from_f(s);
+}
+
+size_t a256(size_t b) { return (b + 255) / 256 * 256; }
+
+int check_attn_shape(const tpattn_shape* s) {
+  if (!s) return TPMLP_ERR_NULL;
+  if (s->dtype != TPMLP_F16 && s->dtype != TPMLP_BF16) return TPMLP_ERR_DTYPE;
+  const int64_t lim = int64_t(1) << 30;
+  const int64_t d[5] = {s->batch, s->seq, s->hidden, s->heads, s->head_dim};
+  for (int64_t v : d)
+    if (v <= 0 || v > lim) return TPMLP_ERR_SHAPE;
+  const int64_t T = s->batch * s->seq, q = s->heads * s->head_dim;
+  if (T > lim || q > lim / 3) return TPMLP_ERR_SHAPE;
+  const int64_t pairs = s->batch * s->heads;
+  if (pairs > 65535 || (double)pairs * (double)s->seq * (double)s->seq >= 1099511627776.0) return TPMLP_ERR_SHAPE;
+  if (cdiv(T, 256) > 65535) return TPMLP_ERR_SHAPE;  // grid y of the column-sum pass
+  // tile counts of the largest launches fit the 31-bit grid
+  if (cdiv(T, 128) * cdiv(std::max<int64_t>(3 * q, s->hidden), 128) > INT32_MAX / 2 ||
+      cdiv(s->seq, 128) * cdiv(s->seq, 128) > INT32_MAX / 2 || cdiv(s->hidden, 128) * cdiv(3 * q, 128) > INT32_MAX / 2)
+    return TPMLP_ERR_SHAPE;
+  if (s->seq % 8 || s->hidden % 8 || s->head_dim % 8) return TPMLP_ERR_ALIGN;
+  return TPMLP_OK;
+}
+
+struct AttnDims {
+  int64_t T, h, n, d, q, s, Z;
+  float scale;
+};
+
+AttnDims dims(const tpattn_shape& sh) {
+  AttnDims a;
+  a.T = sh.batch * sh.seq;
+  a.h = sh.hidden;
+  a.n = sh.heads;
+  a.d = sh.head_dim;
+  a.q = sh.heads * sh.head_dim;
+  a.s = sh.seq;
+  a.Z = sh.batch * sh.heads;
+  a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
+  return a;
+}
+
+// Backward workspace: [dP fp32 Z s s][dS 16-bit Z s s][dO 16-bit T q][colsum partials fp32]
+struct AttnBwdWs {
+  size_t dp_off, ds_off, do_off, part_off, total;
+  int part_blk;
+};
+
+AttnBwdWs bwd_layout(const AttnDims& a) {
+  AttnBwdWs w{};
+  const size_t zss = (size_t)(a.Z * a.s * a.s);
+  w.dp_off = 0;
+  w.ds_off = a256(zss * 4);
+  w.do_off = w.ds_off + a256(zss * 2);
+  w.part_off = w.do_off + a256((size_t)(a.T * a.q) * 2);
+  w.part_blk = (int)cdiv(a.T, 256);
+  w.total = w.part_off + a256((size_t)w.part_blk * (size_t)(3 * a.q) * 4);
+  return w;
+}
+
+struct Span2 {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Span2& a, const Span2& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int check_spans(const Span2* in, int n_in, const Span2* out, int n_out) {
+  for (int i = 0; i < n_in; ++i)
+    if (!in[i].p) return TPMLP_ERR_NULL;
+  for (int i = 0; i < n_out; ++i)
+    if (!out[i].p) return TPMLP_ERR_NULL;
+  for (int i = 0; i < n_in; ++i)
+    if ((uintptr_t)in[i].p & 15u) return TPMLP_ERR_ALIGN;
+  for (int i = 0; i < n_out; ++i)
+    if ((uintptr_t)out[i].p & 15u) return TPMLP_ERR_ALIGN;
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(out[i], in[j])) return TPMLP_ERR_ALIAS;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(out[i], out[j])) return TPMLP_ERR_ALIAS;
+  }
+  return TPMLP_OK;
+}
+
+#define ATTN_HIP(expr)                              \
+  do {                                              \
+    if ((expr) != hipSuccess) return TPMLP_ERR_HIP; \
+  } while (0)
+
+template <class S>
+int attn_fwd_impl(const AttnDims& a, int causal, const void* X, const void* Wqkv, const void* bqkv, const void* Wo,
+                  void* QKV, void* P, void* O, void* Yp, void* ws, hipStream_t st) {
+  using T = typename S::T;
+  const int64_t T3 = 3 * a.q;
+  const T* qkv = static_cast<const T*>(QKV);
+  // QKV = X Wqkv + bqkv: P = X [T,h] k-contiguous, Q = Wqkv [h,3q] n-contiguous
+  ATTN_HIP((gemm<S, true, false>(a.T, T3, a.h, X, a.h, Wqkv, T3,
+                                 EpiBiasGelu<S>{(const T*)bqkv, (T*)QKV, nullptr, T3}, 1, st)));
+  // S_bj = Q_bj K_bj^T in fp32: P = Q block [s,d] k-contiguous, Q[k][n] = K[n][k] k-contiguous
+  const BatchMap sc{(int)a.n, a.s * T3, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s};
+  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv, T3, qkv + a.q, T3,
+                                EpiStoreF32Batched{static_cast<float*>(ws), a.s, sc}, (int)a.Z, st)));
+  const int64_t rows = a.Z * a.s;
+  hipLaunchKernelGGL(softmax_fwd_kernel<S>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
+                     static_cast<const float*>(ws), static_cast<T*>(P), rows, a.s, a.scale, causal);
+  ATTN_HIP(hipGetLastError());
+  // O_bj = P_bj V_bj: P_bj [s,s] k-contiguous, Q[k][n] = V[k][n] n-contiguous (pitch 3q)
+  const BatchMap pv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * a.q, a.d};
+  ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, P, a.s, qkv + 2 * a.q, T3, EpiStoreBatched<S>{(T*)O, a.q, pv},
+                                 (int)a.Z, st)));
+  // Yp = O Wo: P = O [T,q] k-contiguous, Q = Wo [q,h] n-contiguous
+  ATTN_HIP((gemm<S, true, false>(a.T, a.h, a.q, O, a.q, Wo, a.h, EpiStore<S>{(T*)Yp, a.h}, 1, st)));
+  return TPMLP_OK;
+}
+
+template <class S>
+int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, const void* Wqkv, const void* Wo,
+                  const void* QKV, const void* P, const void* O, void* dQKV, void* dXp, void* dWqkv, void* dbqkv,
+                  void* dWo, void* ws, hipStream_t st) {
+  using T = typename S::T;
+  const int64_t T3 = 3 * a.q;
+  const AttnBwdWs w = bwd_layout(a);
+  char* wsb = static_cast<char*>(ws);
+  float* dp = reinterpret_cast<float*>(wsb + w.dp_off);
+  T* ds = reinterpret_cast<T*>(wsb + w.ds_off);
+  T* dO = reinterpret_cast<T*>(wsb + w.do_off);
+  float* part = reinterpret_cast<float*>(wsb + w.part_off);
+  const T* qkv = static_cast<const T*>(QKV);
+  T* dqkv = static_cast<T*>(dQKV);
+  // dO = dY Wo^T: Q[k=h][n=q] = Wo[n][k] k-contiguous
+  ATTN_HIP((gemm<S, true, true>(a.T, a.q, a.h, dY, a.h, Wo, a.h, EpiStore<S>{dO, a.q}, 1, st)));
+  // dWo = O^T dY: P[m=q][k=T] = O[k][m], Q = dY [T,h]: both mn-contiguous
+  ATTN_HIP((gemm<S, false, false>(a.q, a.h, a.T, O, a.q, dY, a.h, EpiStore<S>{(T*)dWo, a.h}, 1, st)));
+  // dV_bj = P_bj^T dO_bj: P[m=key][k=query] = P_bj[k][m], Q = dO block: both mn-contiguous
+  const BatchMap dv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * a.q, a.d, a.s * T3, a.d};
+  ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, P, a.s, dO, a.q, EpiStoreBatched<S>{dqkv + 2 * a.q, T3, dv},
+                                  (int)a.Z, st)));
+  // dP_bj = dO_bj V_bj^T (fp32): P = dO block k-contiguous, Q[k=d][n=key] = V[n][k] k-contiguous
+  const BatchMap dpm{(int)a.n, a.s * a.q, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s};
+  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, dO, a.q, qkv + 2 * a.q, T3, EpiStoreF32Batched{dp, a.s, dpm},
+                                (int)a.Z, st)));
+  const int64_t rows = a.Z * a.s;
+  hipLaunchKernelGGL(softmax_bwd_kernel<S>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st, dp,
+                     static_cast<const T*>(P), ds, rows, a.s, a.scale, causal);
+  ATTN_HIP(hipGetLastError());
+  // dQ_bj = dS_bj K_bj: P = dS [s,s] k-contiguous, Q[k=key][n=d] = K[k][n] n-contiguous
+  const BatchMap dq{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * T3, a.d};
+  ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, ds, a.s, qkv + a.q, T3, EpiStoreBatched<S>{dqkv, T3, dq},
+                                 (int)a.Z, st)));
+  // dK_bj = dS_bj^T Q_bj: P[m=key][k=query] = dS[k][m], Q[k=query][n=d] = Q[k][n]: both mn-contiguous
+  ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, ds, a.s, qkv, T3, EpiStoreBatched<S>{dqkv + a.q, T3, dq},
+                                  (int)a.Z, st)));
+  // dbqkv = column sums of dQKV
+  hipLaunchKernelGGL(colsum_part_kernel<S>, dim3((unsigned)cdiv(T3, 256), (unsigned)w.part_blk), dim3(256), 0, st,
+                     static_cast<const T*>(dQKV), a.T, T3, part);
+  ATTN_HIP(hipGetLastError());
+  hipLaunchKernelGGL(colsum_finish_kernel<S>, dim3((unsigned)cdiv(T3, 256)), dim3(256), 0, st, part, w.part_blk, T3,
+                     static_cast<T*>(dbqkv));
+  ATTN_HIP(hipGetLastError());
+  // dWqkv = X^T dQKV: P[m=h][k=T] = X[k][m], Q = dQKV [T,3q]: both mn-contiguous
+  ATTN_HIP((gemm<S, false, false>(a.h, T3, a.T, X, a.h, dQKV, T3, EpiStore<S>{(T*)dWqkv, T3}, 1, st)));
+  // dXp = dQKV Wqkv^T: P = dQKV k-contiguous, Q[k=3q][n=h] = Wqkv[n][k] k-contiguous
+  ATTN_HIP((gemm<S, true, true>(a.T, a.h, T3, dQKV, T3, Wqkv, T3, EpiStore<S>{(T*)dXp, a.h}, 1, st)));
+  return TPMLP_OK;
+}
+
+}  // namespace
+}  // namespace tpmlp
+
+using namespace tpmlp;
+
+extern "C" {
+
+size_t tp_attn_fwd_workspace_bytes(const tpattn_shape* shape) {
+  if (check_attn_shape(shape) != TPMLP_OK) return 0;
+  const AttnDims a = dims(*shape);
+  return a256((size_t)(a.Z * a.s * a.s) * 4);
+}
+
+size_t tp_attn_bwd_workspace_bytes(const tpattn_shape* shape) {
+  if (check_attn_shape(shape) != TPMLP_OK) return 0;
+  return bwd_layout(dims(*shape)).total;
+}
+
+int tp_attn_fwd(const tpattn_shape* shape, const void* X, const void* Wqkv, const void* bqkv, const void* Wo,
+                void* QKV, void* P, void* O, void* Yp, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = check_attn_shape(shape);
+  if (rc != TPMLP_OK) return rc;
+  const AttnDims a = dims(*shape);
+  const size_t e = 2, need = tp_attn_fwd_workspace_bytes(shape);
+  const Span2 in[4] = {{X, (size_t)(a.T * a.h) * e}, {Wqkv, (size_t)(a.h * 3 * a.q) * e},
+                       {bqkv, (size_t)(3 * a.q) * e}, {Wo, (size_t)(a.q * a.h) * e}};
+  const Span2 out[5] = {{QKV, (size_t)(a.T * 3 * a.q) * e}, {P, (size_t)(a.Z * a.s * a.s) * e},
+                        {O, (size_t)(a.T * a.q) * e}, {Yp, (size_t)(a.T * a.h) * e}, {ws, need}};
+  const int bc = check_spans(in, 4, out, 5);
+  if (bc != TPMLP_OK) return bc;
+  if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (shape->dtype == TPMLP_F16)
+    return attn_fwd_impl<StoreF16>(a, shape->causal, X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, st);
+  return attn_fwd_impl<StoreBF16>(a, shape->causal, X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, st);
+}
+
+int tp_attn_bwd(const tpattn_shape* shape, const void* dY, const void* X, const void* Wqkv, const void* Wo,
+                const void* QKV, const void* P, const void* O, void* dQKV, void* dXp, void* dWqkv, void* dbqkv,
+                void* dWo, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = check_attn_shape(shape);
+  if (rc != TPMLP_OK) return rc;
+  const AttnDims a = dims(*shape);
+  const size_t e = 2, need = tp_attn_bwd_workspace_bytes(shape);
+  const size_t Th = (size_t)(a.T * a.h) * e, T3 = (size_t)(a.T * 3 * a.q) * e, h3 = (size_t)(a.h * 3 * a.q) * e,
+               qh = (size_t)(a.q * a.h) * e;
+  const Span2 in[7] = {{dY, Th}, {X, Th}, {Wqkv, h3}, {Wo, qh}, {QKV, T3}, {P, (size_t)(a.Z * a.s * a.s) * e},
+                       {O, (size_t)(a.T * a.q) * e}};
+  const Span2 out[6] = {{dQKV, T3}, {dXp, Th}, {dWqkv, h3}, {dbqkv, (size_t)(3 * a.q) * e}, {dWo, qh}, {ws, need}};
+  const int bc = check_spans(in, 7, out, 6);
+  if (bc != TPMLP_OK) return bc;
+  if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (shape->dtype == TPMLP_F16)
+    return attn_bwd_impl<StoreF16>(a, shape->causal, dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws,
+                                   st);
+  return attn_bwd_impl<StoreBF16>(a, shape->causal, dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws,
+                                  st);
+}
+
+}  // extern "C"
