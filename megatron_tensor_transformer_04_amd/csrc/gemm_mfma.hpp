@@ -35,7 +35,11 @@ namespace tpmlp {
 // A batched epilogue (static constexpr bool kBatched = true) serves a grid
 // whose y index z selects one of several independent GEMMs of the same
 // shape: its select(z, P, Q) moves the two operands and its own outputs to
-// batch z's matrices before the tile is computed.
+// batch z's matrices before the tile is computed. It also bounds the work of
+// a tile: skip(m0, n0) drops a tile whose outputs are never read, and
+// k_window(m0, kbeg, kend) narrows its k-range to where the operands can be
+// nonzero (both for the triangular structure of causal attention; the
+// narrowed range must start on a multiple of 64).
 template <class E, class = void>
 struct EpiBatched : std::false_type {};
 template <class E>
@@ -156,15 +160,19 @@ template <class Cfg, class S, bool P_KC, bool Q_KC, bool GELU_P, class Epi>
 __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, Operand P, Operand Q, Epi epi) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, THREADS = Cfg::THREADS;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
-  if constexpr (EpiBatched<Epi>::value) epi.select((int)blockIdx.y, P, Q);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   int split, tm, tn;
   map_tile<Cfg::GROUP>(blockIdx.x, gridDim.x, sh.tiles_m, sh.tiles_n, split, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kbeg = (int64_t)split * sh.k_per;
-  const int64_t kend = min(sh.K, kbeg + sh.k_per);
+  int64_t kbeg = (int64_t)split * sh.k_per;
+  int64_t kend = min(sh.K, kbeg + sh.k_per);
+  if constexpr (EpiBatched<Epi>::value) {
+    epi.select((int)blockIdx.y, P, Q);
+    if (epi.skip(m0, n0)) return;
+    epi.k_window(m0, kbeg, kend);
+  }
   const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
 
   f32x4 acc[Cfg::FM][Cfg::FN];

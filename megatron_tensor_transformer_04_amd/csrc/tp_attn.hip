@@ -32,10 +32,34 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Offsets (in elements) of batch z = b * inner + j: operand P, operand Q and
 // the output each move by b * (stride per sequence) + j * (stride per head).
+// `tri` is the causal structure the product can exploit (all of it zero
+// when the mask is off):
+//   kSkipUpper  outputs [query][key]: tiles whose keys all follow their
+//               queries are never read (the softmax and its backward read
+//               only keys <= query), so they are not computed;
+//   kKeysUpTo   k runs over keys and P[query][key] = 0 for key > query:
+//               a tile of queries [m0, m0 + BM) needs keys < m0 + BM only;
+//   kQueriesFrom  rows are keys and k runs over queries: P[query][key] = 0
+//               for query < key, so a tile of keys [m0, ...) needs queries
+//               >= m0 only.
+enum Tri : int { kNone = 0, kSkipUpper = 1, kKeysUpTo = 2, kQueriesFrom = 3 };
+
 struct BatchMap {
   int inner;
   int64_t p_b, p_j, q_b, q_j, o_b, o_j;
+  int tri;
 };
+
+template <int BM, int BN>
+__device__ __forceinline__ bool tri_skip(int tri, int64_t m0, int64_t n0) {
+  return tri == kSkipUpper && n0 > m0 + BM - 1;
+}
+
+template <int BM>
+__device__ __forceinline__ void tri_window(int tri, int64_t m0, int64_t& kbeg, int64_t& kend) {
+  if (tri == kKeysUpTo) kend = min(kend, m0 + BM);
+  if (tri == kQueriesFrom) kbeg = max(kbeg, m0);
+}
 
 // Plain store of one (sequence, head) product into its block of a larger
 // matrix (row pitch ld), rounded once to the storage dtype.
@@ -51,6 +75,12 @@ struct EpiStoreBatched {
     P.ptr += b * bm.p_b + j * bm.p_j;
     Q.ptr += b * bm.q_b + j * bm.q_j;
     out += b * bm.o_b + j * bm.o_j;
+  }
+  __device__ __forceinline__ bool skip(int64_t m0, int64_t n0) const {
+    return tri_skip<CfgA::BM, CfgA::BN>(bm.tri, m0, n0);
+  }
+  __device__ __forceinline__ void k_window(int64_t m0, int64_t& kbeg, int64_t& kend) const {
+    tri_window<CfgA::BM>(bm.tri, m0, kbeg, kend);
   }
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
     out[m * ld + n] = S::from_f(acc);
@@ -71,6 +101,12 @@ struct EpiStoreF32Batched {
     P.ptr += b * bm.p_b + j * bm.p_j;
     Q.ptr += b * bm.q_b + j * bm.q_j;
     out += b * bm.o_b + j * bm.o_j;
+  }
+  __device__ __forceinline__ bool skip(int64_t m0, int64_t n0) const {
+    return tri_skip<CfgA::BM, CfgA::BN>(bm.tri, m0, n0);
+  }
+  __device__ __forceinline__ void k_window(int64_t m0, int64_t& kbeg, int64_t& kend) const {
+    tri_window<CfgA::BM>(bm.tri, m0, kbeg, kend);
   }
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
     out[m * ld + n] = acc;
@@ -333,7 +369,7 @@ int attn_fwd_impl(const AttnDims& a, int causal, const void* X, const void* Wqkv
   ATTN_HIP((gemm<S, true, false>(a.T, T3, a.h, X, a.h, Wqkv, T3,
                                  EpiBiasGelu<S>{(const T*)bqkv, (T*)QKV, nullptr, T3}, 1, st)));
   // S_bj = Q_bj K_bj^T in fp32: P = Q block [s,d] k-contiguous, Q[k][n] = K[n][k] k-contiguous
-  const BatchMap sc{(int)a.n, a.s * T3, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s};
+  const BatchMap sc{(int)a.n, a.s * T3, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipUpper : kNone};
   ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv, T3, qkv + a.q, T3,
                                 EpiStoreF32Batched{static_cast<float*>(ws), a.s, sc}, (int)a.Z, st)));
   const int64_t rows = a.Z * a.s;
@@ -341,7 +377,7 @@ int attn_fwd_impl(const AttnDims& a, int causal, const void* X, const void* Wqkv
                      static_cast<const float*>(ws), static_cast<T*>(P), rows, a.s, a.scale, causal);
   ATTN_HIP(hipGetLastError());
   // O_bj = P_bj V_bj: P_bj [s,s] k-contiguous, Q[k][n] = V[k][n] n-contiguous (pitch 3q)
-  const BatchMap pv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * a.q, a.d};
+  const BatchMap pv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * a.q, a.d, causal ? kKeysUpTo : kNone};
   ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, P, a.s, qkv + 2 * a.q, T3, EpiStoreBatched<S>{(T*)O, a.q, pv},
                                  (int)a.Z, st)));
   // Yp = O Wo: P = O [T,q] k-contiguous, Q = Wo [q,h] n-contiguous
@@ -368,11 +404,12 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
   // dWo = O^T dY: P[m=q][k=T] = O[k][m], Q = dY [T,h]: both mn-contiguous
   ATTN_HIP((gemm<S, false, false>(a.q, a.h, a.T, O, a.q, dY, a.h, EpiStore<S>{(T*)dWo, a.h}, 1, st)));
   // dV_bj = P_bj^T dO_bj: P[m=key][k=query] = P_bj[k][m], Q = dO block: both mn-contiguous
-  const BatchMap dv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * a.q, a.d, a.s * T3, a.d};
+  const BatchMap dv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * a.q, a.d, a.s * T3, a.d,
+                    causal ? kQueriesFrom : kNone};
   ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, P, a.s, dO, a.q, EpiStoreBatched<S>{dqkv + 2 * a.q, T3, dv},
                                   (int)a.Z, st)));
   // dP_bj = dO_bj V_bj^T (fp32): P = dO block k-contiguous, Q[k=d][n=key] = V[n][k] k-contiguous
-  const BatchMap dpm{(int)a.n, a.s * a.q, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s};
+  const BatchMap dpm{(int)a.n, a.s * a.q, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipUpper : kNone};
   ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, dO, a.q, qkv + 2 * a.q, T3, EpiStoreF32Batched{dp, a.s, dpm},
                                 (int)a.Z, st)));
   const int64_t rows = a.Z * a.s;
@@ -380,11 +417,13 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
                      static_cast<const T*>(P), ds, rows, a.s, a.scale, causal);
   ATTN_HIP(hipGetLastError());
   // dQ_bj = dS_bj K_bj: P = dS [s,s] k-contiguous, Q[k=key][n=d] = K[k][n] n-contiguous
-  const BatchMap dq{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * T3, a.d};
+  const BatchMap dq{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * T3, a.d, causal ? kKeysUpTo : kNone};
   ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, ds, a.s, qkv + a.q, T3, EpiStoreBatched<S>{dqkv, T3, dq},
                                  (int)a.Z, st)));
   // dK_bj = dS_bj^T Q_bj: P[m=key][k=query] = dS[k][m], Q[k=query][n=d] = Q[k][n]: both mn-contiguous
-  ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, ds, a.s, qkv, T3, EpiStoreBatched<S>{dqkv + a.q, T3, dq},
+  BatchMap dk = dq;
+  dk.tri = causal ? kQueriesFrom : kNone;
+  ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, ds, a.s, qkv, T3, EpiStoreBatched<S>{dqkv + a.q, T3, dk},
                                   (int)a.Z, st)));
   // dbqkv = column sums of dQKV
   hipLaunchKernelGGL(colsum_part_kernel<S>, dim3((unsigned)cdiv(T3, 256), (unsigned)w.part_blk), dim3(256), 0, st,
