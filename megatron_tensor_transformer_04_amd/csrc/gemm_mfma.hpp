@@ -45,6 +45,14 @@ struct EpiBatched : std::false_type {};
 template <class E>
 struct EpiBatched<E, std::void_t<decltype(E::kBatched)>> : std::integral_constant<bool, E::kBatched> {};
 
+// An epilogue with kApply4 = true takes each lane's four accumulators of a
+// 16x16 fragment at once: apply4(m, n, v) with v[r] = C[m + r][n], m a
+// multiple of 4 (M must then be a multiple of 4).
+template <class E, class = void>
+struct EpiApply4 : std::false_type {};
+template <class E>
+struct EpiApply4<E, std::void_t<decltype(E::kApply4)>> : std::integral_constant<bool, E::kApply4> {};
+
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
@@ -239,10 +247,15 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, O
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int64_t n = n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
+      if constexpr (EpiApply4<Epi>::value) {
+        const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
+        if (m < sh.M && n < sh.N) epi.apply4(m, n, acc[i][j]);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4 + r;
-        if (m < sh.M && n < sh.N) cs[j] += epi.apply(m, n, acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4 + r;
+          if (m < sh.M && n < sh.N) cs[j] += epi.apply(m, n, acc[i][j][r]);
+        }
       }
     }
   }

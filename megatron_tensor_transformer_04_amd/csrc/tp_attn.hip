@@ -42,17 +42,21 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   kQueriesFrom  rows are keys and k runs over queries: P[query][key] = 0
 //               for query < key, so a tile of keys [m0, ...) needs queries
 //               >= m0 only.
-enum Tri : int { kNone = 0, kSkipUpper = 1, kKeysUpTo = 2, kQueriesFrom = 3 };
+//   kSkipLower  outputs [key][query] (the transposed scores): tiles whose
+//               keys all follow their queries are not computed.
+enum Tri : int { kNone = 0, kSkipUpper = 1, kKeysUpTo = 2, kQueriesFrom = 3, kSkipLower = 4 };
 
 struct BatchMap {
   int inner;
   int64_t p_b, p_j, q_b, q_j, o_b, o_j;
   int tri;
+  int64_t k_total, k_chunk;  // k-split use (inner = 1): batch z covers k in [z k_chunk, (z + 1) k_chunk) of
+                             // k_total (the operand offsets p_b, q_b step by k_chunk rows); 0 otherwise
 };
 
 template <int BM, int BN>
 __device__ __forceinline__ bool tri_skip(int tri, int64_t m0, int64_t n0) {
-  return tri == kSkipUpper && n0 > m0 + BM - 1;
+  return (tri == kSkipUpper && n0 > m0 + BM - 1) || (tri == kSkipLower && m0 > n0 + BN - 1);
 }
 
 template <int BM>
@@ -89,12 +93,49 @@ struct EpiStoreBatched {
   __device__ __forceinline__ void colsum(int, int64_t, float) const {}
 };
 
-// fp32 store of a batched product (the scores, and dP in the backward).
+// fp32 store of a batched product (the scores, and dP in the backward; and
+// the per-range partial sums of a k-split product, whose batch z covers
+// k in [z K, z K + K) of bm.k_total).
 struct EpiStoreF32Batched {
   float* out;
   int64_t ld;
   BatchMap bm;
+  int64_t klim;
   static constexpr bool kBatched = true;
+  static constexpr bool kColSum = false;
+  __device__ __forceinline__ void select(int z, Operand& P, Operand& Q) {
+    const int64_t b = z / bm.inner, j = z % bm.inner;
+    P.ptr += b * bm.p_b + j * bm.p_j;
+    Q.ptr += b * bm.q_b + j * bm.q_j;
+    out += b * bm.o_b + j * bm.o_j;
+    klim = bm.k_total;
+    if (bm.k_total) klim -= (int64_t)z * bm.k_chunk;
+  }
+  __device__ __forceinline__ bool skip(int64_t m0, int64_t n0) const {
+    return tri_skip<CfgA::BM, CfgA::BN>(bm.tri, m0, n0);
+  }
+  __device__ __forceinline__ void k_window(int64_t m0, int64_t& kbeg, int64_t& kend) const {
+    tri_window<CfgA::BM>(bm.tri, m0, kbeg, kend);
+    if (bm.k_total) kend = min(kend, klim);
+  }
+  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
+    out[m * ld + n] = acc;
+    return 0.0f;
+  }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
+// Transposed fp32 store of a batched product C [M = keys][N = queries]:
+// out[n][m .. m + 3] = C[m .. m + 3][n] as one 16-byte store per lane and
+// fragment (the MFMA result gives each lane four consecutive rows of one
+// column). Computing the scores (and dP) as K Q^T (V dO^T) with this store
+// writes each query's row of keys in 16-byte pieces.
+struct EpiStoreF32TBatched {
+  float* out;
+  int64_t ld;
+  BatchMap bm;
+  static constexpr bool kBatched = true;
+  static constexpr bool kApply4 = true;
   static constexpr bool kColSum = false;
   __device__ __forceinline__ void select(int z, Operand& P, Operand& Q) {
     const int64_t b = z / bm.inner, j = z % bm.inner;
@@ -108,10 +149,10 @@ struct EpiStoreF32Batched {
   __device__ __forceinline__ void k_window(int64_t m0, int64_t& kbeg, int64_t& kend) const {
     tri_window<CfgA::BM>(bm.tri, m0, kbeg, kend);
   }
-  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
-    out[m * ld + n] = acc;
-    return 0.0f;
+  __device__ __forceinline__ void apply4(int64_t m, int64_t n, f32x4 v) const {
+    *reinterpret_cast<f32x4*>(out + n * ld + m) = v;
   }
+  __device__ __forceinline__ float apply(int64_t, int64_t, float) const { return 0.0f; }
   __device__ __forceinline__ void colsum(int, int64_t, float) const {}
 };
 
@@ -143,10 +184,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // [rows][s] (row r is query r % s of its (sequence, head) pair):
 //   x_k = S[k] * scale for the visible keys k (k <= query when causal),
 //   P[k] = exp(x_k - max) / sum_k' exp(x_k' - max), 0 for masked keys,
-// rounded once to the storage dtype. Each lane takes four consecutive keys
-// per step; the max and the sum are reduced lane-strided then across the
-// wave in a fixed order.
-template <class S>
+// rounded once to the storage dtype. Lane l holds keys 4 l + 256 c, c < CH,
+// in registers (s <= 256 CH): the row is read from HBM once. The max and
+// the sum are reduced per lane in key order, then across the wave in a
+// fixed butterfly order.
+template <class S, int CH>
 __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restrict__ sc, typename S::T* __restrict__ P,
                                                           int64_t rows, int64_t s, float scale, int causal) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -156,45 +198,54 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restric
   const int64_t nv = causal ? qi + 1 : s;
   const float* x = sc + row * s;
   typename S::T* p = P + row * s;
+  float v[CH][4];
   float m = -INFINITY;
-  for (int64_t k = (int64_t)lane * 4; k < nv; k += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + k);
-    m = fmaxf(m, v.x * scale);
-    if (k + 1 < nv) m = fmaxf(m, v.y * scale);
-    if (k + 2 < nv) m = fmaxf(m, v.z * scale);
-    if (k + 3 < nv) m = fmaxf(m, v.w * scale);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k = (int64_t)lane * 4 + 256 * c;
+    float4 t = {0.f, 0.f, 0.f, 0.f};
+    if (k < nv) t = *reinterpret_cast<const float4*>(x + k);
+    v[c][0] = t.x * scale;
+    v[c][1] = t.y * scale;
+    v[c][2] = t.z * scale;
+    v[c][3] = t.w * scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (k + i < nv) m = fmaxf(m, v[c][i]);
   }
   m = wave_max(m);
   float z = 0.0f;
-  for (int64_t k = (int64_t)lane * 4; k < nv; k += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + k);
-    z += expf(v.x * scale - m);
-    if (k + 1 < nv) z += expf(v.y * scale - m);
-    if (k + 2 < nv) z += expf(v.z * scale - m);
-    if (k + 3 < nv) z += expf(v.w * scale - m);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k = (int64_t)lane * 4 + 256 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[c][i] = (k + i < nv) ? expf(v[c][i] - m) : 0.0f;
+      z += v[c][i];
+    }
   }
   z = wave_sum(z);
   const float rz = 1.0f / z;
-  for (int64_t k = (int64_t)lane * 4; k < s; k += 256) {
-    float e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (k < nv) {
-      const float4 v = *reinterpret_cast<const float4*>(x + k);
-      const float xv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = (k + i < nv) ? expf(xv[i] * scale - m) * rz : 0.0f;
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k = (int64_t)lane * 4 + 256 * c;
+    if (k < s) {
+      uint2 w;
+      w.x = (uint32_t)S::from_f(v[c][0] * rz) | ((uint32_t)S::from_f(v[c][1] * rz) << 16);
+      w.y = (uint32_t)S::from_f(v[c][2] * rz) | ((uint32_t)S::from_f(v[c][3] * rz) << 16);
+      *reinterpret_cast<uint2*>(p + k) = w;
     }
-    uint2 w;
-    w.x = (uint32_t)S::from_f(e[0]) | ((uint32_t)S::from_f(e[1]) << 16);
-    w.y = (uint32_t)S::from_f(e[2]) | ((uint32_t)S::from_f(e[3]) << 16);
-    *reinterpret_cast<uint2*>(p + k) = w;
   }
 }
 
-// Backward of the softmax, one wave per row: with the stored (rounded)
-// probabilities P and the fp32 dP = dO V^T,
+// Backward of the softmax, one wave per row, row in registers as above: with
+// the stored (rounded) probabilities P and the fp32 dP = dO V^T,
 //   D = sum over visible keys of P[k] dP[k],  dS[k] = P[k] (dP[k] - D) * scale,
-// 0 for masked keys, rounded once to the storage dtype.
-template <class S>
+// 0 for masked keys, rounded once to the storage dtype. With the causal mask
+// only keys below the end of the query's 128-wide block are written: the
+// products that read dS (k-windowed on the same 128-row tiles) read no
+// further.
+template <class S, int CH>
 __global__ __launch_bounds__(256) void softmax_bwd_kernel(const float* __restrict__ dp,
                                                           const typename S::T* __restrict__ P,
                                                           typename S::T* __restrict__ dS, int64_t rows, int64_t s,
@@ -204,56 +255,83 @@ __global__ __launch_bounds__(256) void softmax_bwd_kernel(const float* __restric
   if (row >= rows) return;
   const int64_t qi = row % s;
   const int64_t nv = causal ? qi + 1 : s;
+  const int64_t nw = causal ? min(s, (qi / CfgA::BM + 1) * CfgA::BM) : s;
   const float* g = dp + row * s;
   const typename S::T* p = P + row * s;
   typename S::T* o = dS + row * s;
-  auto probs = [&](int64_t k, float (&pv)[4]) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p + k);
-    pv[0] = S::to_f((typename S::T)(w.x & 0xffffu));
-    pv[1] = S::to_f((typename S::T)(w.x >> 16));
-    pv[2] = S::to_f((typename S::T)(w.y & 0xffffu));
-    pv[3] = S::to_f((typename S::T)(w.y >> 16));
-  };
+  float pv[CH][4], gv[CH][4];
   float d = 0.0f;
-  for (int64_t k = (int64_t)lane * 4; k < nv; k += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(g + k);
-    float pv[4];
-    probs(k, pv);
-    const float gv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k = (int64_t)lane * 4 + 256 * c;
+    float4 t = {0.f, 0.f, 0.f, 0.f};
+    uint2 w = {0u, 0u};
+    if (k < nv) {
+      t = *reinterpret_cast<const float4*>(g + k);
+      w = *reinterpret_cast<const uint2*>(p + k);
+    }
+    gv[c][0] = t.x;
+    gv[c][1] = t.y;
+    gv[c][2] = t.z;
+    gv[c][3] = t.w;
+    pv[c][0] = S::to_f((typename S::T)(w.x & 0xffffu));
+    pv[c][1] = S::to_f((typename S::T)(w.x >> 16));
+    pv[c][2] = S::to_f((typename S::T)(w.y & 0xffffu));
+    pv[c][3] = S::to_f((typename S::T)(w.y >> 16));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (k + i < nv) d += pv[i] * gv[i];
+      if (k + i < nv) d += pv[c][i] * gv[c][i];
   }
   d = wave_sum(d);
-  for (int64_t k = (int64_t)lane * 4; k < s; k += 256) {
-    float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (k < nv) {
-      const float4 v = *reinterpret_cast<const float4*>(g + k);
-      float pv[4];
-      probs(k, pv);
-      const float gv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (k + i < nv) ? pv[i] * (gv[i] - d) * scale : 0.0f;
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k = (int64_t)lane * 4 + 256 * c;
+    if (k < nw) {
+      float r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (k + i < nv) ? pv[c][i] * (gv[c][i] - d) * scale : 0.0f;
+      uint2 w;
+      w.x = (uint32_t)S::from_f(r[0]) | ((uint32_t)S::from_f(r[1]) << 16);
+      w.y = (uint32_t)S::from_f(r[2]) | ((uint32_t)S::from_f(r[3]) << 16);
+      *reinterpret_cast<uint2*>(o + k) = w;
     }
-    uint2 w;
-    w.x = (uint32_t)S::from_f(r[0]) | ((uint32_t)S::from_f(r[1]) << 16);
-    w.y = (uint32_t)S::from_f(r[2]) | ((uint32_t)S::from_f(r[3]) << 16);
-    *reinterpret_cast<uint2*>(o + k) = w;
   }
 }
 
-// Column sums of a [rows][cols] 16-bit matrix, first pass: block (x, y) sums
-// rows [256 y, 256 y + 256) of columns [256 x, 256 x + 256) in row order
-// into part[y][col] (fp32).
+// Column sums of a [rows][cols] 16-bit matrix (cols a multiple of 8), first
+// pass: block (x, y) covers columns [256 x, 256 x + 256) and rows
+// [256 y, 256 y + 256). Thread t reads 16-byte chunks (8 columns) of the rows
+// r = 256 y + t / 32 + 8 i in order; the 8 row groups are then added in
+// group order through LDS into part[y][col] (fp32).
 template <class S>
 __global__ __launch_bounds__(256) void colsum_part_kernel(const typename S::T* __restrict__ m, int64_t rows,
                                                           int64_t cols, float* __restrict__ part) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  const int64_t r0 = (int64_t)blockIdx.y * 256, r1 = std::min<int64_t>(rows, r0 + 256);
-  float s = 0.0f;
-  for (int64_t r = r0; r < r1; ++r) s += S::to_f(m[r * cols + c]);
-  part[(int64_t)blockIdx.y * cols + c] = s;
+  __shared__ float red[8][256];
+  const int t = threadIdx.x, cc = t & 31, rg = t >> 5;
+  const int64_t c0 = (int64_t)blockIdx.x * 256 + cc * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * 256, r1 = min(rows, r0 + 256);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < cols) {
+    for (int64_t r = r0 + rg; r < r1; r += 8) {
+      const uint4 w = *reinterpret_cast<const uint4*>(m + r * cols + c0);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += S::to_f((typename S::T)(u[i] & 0xffffu));
+        acc[2 * i + 1] += S::to_f((typename S::T)(u[i] >> 16));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rg][cc * 8 + i] = acc[i];
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * 256 + t;
+  if (c < cols) {
+    float v = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) v += red[g][t];
+    part[(int64_t)blockIdx.y * cols + c] = v;
+  }
 }
 
 // Second pass: out[c] = round(sum over blocks of part[b][c]) in block order.
@@ -267,7 +345,71 @@ __global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restr
   out[c] = S::from_f(s);
 }
 
+// Sum of the k-range partials of a k-split product, in range order, rounded
+// once: out[i] = round(sum_z part[z][i]) over n = M N elements (n % 4 == 0).
+template <class S>
+__global__ __launch_bounds__(256) void ksum_kernel(const float* __restrict__ part, int splits, int64_t n,
+                                                   typename S::T* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 a = *reinterpret_cast<const float4*>(part + i);
+  for (int z = 1; z < splits; ++z) {
+    const float4 b = *reinterpret_cast<const float4*>(part + (int64_t)z * n + i);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  uint2 w;
+  w.x = (uint32_t)S::from_f(a.x) | ((uint32_t)S::from_f(a.y) << 16);
+  w.y = (uint32_t)S::from_f(a.z) | ((uint32_t)S::from_f(a.w) << 16);
+  *reinterpret_cast<uint2*>(out + i) = w;
+}
+
 size_t a256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Longest sequence: a softmax row of 4096 keys is 64 fp32 values per lane.
+constexpr int64_t kMaxSeq = 4096;
+
+template <class S>
+hipError_t softmax_fwd(const float* sc, typename S::T* P, int64_t rows, int64_t s, float scale, int causal,
+                       hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  if (s <= 256) hipLaunchKernelGGL((softmax_fwd_kernel<S, 1>), grid, block, 0, st, sc, P, rows, s, scale, causal);
+  else if (s <= 512) hipLaunchKernelGGL((softmax_fwd_kernel<S, 2>), grid, block, 0, st, sc, P, rows, s, scale, causal);
+  else if (s <= 1024) hipLaunchKernelGGL((softmax_fwd_kernel<S, 4>), grid, block, 0, st, sc, P, rows, s, scale, causal);
+  else if (s <= 2048) hipLaunchKernelGGL((softmax_fwd_kernel<S, 8>), grid, block, 0, st, sc, P, rows, s, scale, causal);
+  else hipLaunchKernelGGL((softmax_fwd_kernel<S, 16>), grid, block, 0, st, sc, P, rows, s, scale, causal);
+  return hipGetLastError();
+}
+
+template <class S>
+hipError_t softmax_bwd(const float* dp, const typename S::T* P, typename S::T* dS, int64_t rows, int64_t s,
+                       float scale, int causal, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  if (s <= 256) hipLaunchKernelGGL((softmax_bwd_kernel<S, 1>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
+  else if (s <= 512) hipLaunchKernelGGL((softmax_bwd_kernel<S, 2>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
+  else if (s <= 1024) hipLaunchKernelGGL((softmax_bwd_kernel<S, 4>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
+  else if (s <= 2048) hipLaunchKernelGGL((softmax_bwd_kernel<S, 8>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
+  else hipLaunchKernelGGL((softmax_bwd_kernel<S, 16>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
+  return hipGetLastError();
+}
+
+// k-split of a product whose output tiles do not fill the chip: ranges of
+// whole 64-wide k-steps, enough of them for about two tiles per CU, at
+// most 8 and each at least 512 long.
+struct KSplit {
+  int splits;
+  int64_t chunk;
+};
+
+KSplit plan_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(M, CfgA::BM) * cdiv(N, CfgA::BN);
+  int sp = tiles >= 512 ? 1 : (int)std::min<int64_t>(8, cdiv(512, std::max<int64_t>(tiles, 1)));
+  while (sp > 1 && K < (int64_t)sp * 512) --sp;
+  const int64_t chunk = cdiv(cdiv(K, sp), 64) * 64;
+  return KSplit{(int)cdiv(K, chunk), chunk};
+}
 
 int check_attn_shape(const tpattn_shape* s) {
   if (!s) return TPMLP_ERR_NULL;
@@ -281,6 +423,7 @@ int check_attn_shape(const tpattn_shape* s) {
   const int64_t pairs = s->batch * s->heads;
   if (pairs > 65535 || (double)pairs * (double)s->seq * (double)s->seq >= 1099511627776.0) return TPMLP_ERR_SHAPE;
   if (cdiv(T, 256) > 65535) return TPMLP_ERR_SHAPE;  // grid y of the column-sum pass
+  if (s->seq > kMaxSeq) return TPMLP_ERR_SHAPE;      // softmax rows are held in registers
   // tile counts of the largest launches fit the 31-bit grid
   if (cdiv(T, 128) * cdiv(std::max<int64_t>(3 * q, s->hidden), 128) > INT32_MAX / 2 ||
       cdiv(s->seq, 128) * cdiv(s->seq, 128) > INT32_MAX / 2 || cdiv(s->hidden, 128) * cdiv(3 * q, 128) > INT32_MAX / 2)
@@ -307,10 +450,13 @@ AttnDims dims(const tpattn_shape& sh) {
   return a;
 }
 
-// Backward workspace: [dP fp32 Z s s][dS 16-bit Z s s][dO 16-bit T q][colsum partials fp32]
+// Backward workspace: [dP fp32 Z s s][dS 16-bit Z s s][dO 16-bit T q]
+// [column partials of dQKV fp32 [T/256][3q]][k-split partials of dWo and
+// dWqkv fp32 (they run one after the other and share the room)].
 struct AttnBwdWs {
-  size_t dp_off, ds_off, do_off, part_off, total;
+  size_t dp_off, ds_off, do_off, part_off, ks_off, total;
   int part_blk;
+  KSplit ks_wo, ks_wqkv;
 };
 
 AttnBwdWs bwd_layout(const AttnDims& a) {
@@ -321,8 +467,33 @@ AttnBwdWs bwd_layout(const AttnDims& a) {
   w.do_off = w.ds_off + a256(zss * 2);
   w.part_off = w.do_off + a256((size_t)(a.T * a.q) * 2);
   w.part_blk = (int)cdiv(a.T, 256);
-  w.total = w.part_off + a256((size_t)w.part_blk * (size_t)(3 * a.q) * 4);
+  w.ks_off = w.part_off + a256((size_t)w.part_blk * (size_t)(3 * a.q) * 4);
+  w.ks_wo = plan_ksplit(a.q, a.h, a.T);
+  w.ks_wqkv = plan_ksplit(a.h, 3 * a.q, a.T);
+  const size_t ks = std::max(w.ks_wo.splits > 1 ? (size_t)w.ks_wo.splits * (size_t)(a.q * a.h) * 4 : 0,
+                             w.ks_wqkv.splits > 1 ? (size_t)w.ks_wqkv.splits * (size_t)(a.h * 3 * a.q) * 4 : 0);
+  w.total = w.ks_off + a256(ks);
   return w;
+}
+
+// C [M][N] (16-bit, row pitch N) = P^T Q with both operands mn-contiguous
+// (P[m][k] = p[k ldp + m], Q[k][n] = q[k ldq + n]), k-split by `ks` into
+// fp32 partials at `part` and summed in range order.
+template <class S>
+int gemm_mc_ksplit(int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q, int64_t ldq,
+                   typename S::T* out, const KSplit& ks, float* part, hipStream_t st) {
+  if (ks.splits <= 1) {
+    if (gemm<S, false, false>(M, N, K, p, ldp, q, ldq, EpiStore<S>{out, N}, 1, st) != hipSuccess)
+      return TPMLP_ERR_HIP;
+    return TPMLP_OK;
+  }
+  BatchMap bm{1, ks.chunk * ldp, 0, ks.chunk * ldq, 0, M * N, 0, kNone, K, ks.chunk};
+  if (gemm<S, false, false>(M, N, ks.chunk, p, ldp, q, ldq, EpiStoreF32Batched{part, N, bm}, ks.splits, st) !=
+      hipSuccess)
+    return TPMLP_ERR_HIP;
+  const int64_t n = M * N;
+  hipLaunchKernelGGL(ksum_kernel<S>, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, part, ks.splits, n, out);
+  return hipGetLastError() == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
 }
 
 struct Span2 {
@@ -368,14 +539,12 @@ int attn_fwd_impl(const AttnDims& a, int causal, const void* X, const void* Wqkv
   // QKV = X Wqkv + bqkv: P = X [T,h] k-contiguous, Q = Wqkv [h,3q] n-contiguous
   ATTN_HIP((gemm<S, true, false>(a.T, T3, a.h, X, a.h, Wqkv, T3,
                                  EpiBiasGelu<S>{(const T*)bqkv, (T*)QKV, nullptr, T3}, 1, st)));
-  // S_bj = Q_bj K_bj^T in fp32: P = Q block [s,d] k-contiguous, Q[k][n] = K[n][k] k-contiguous
-  const BatchMap sc{(int)a.n, a.s * T3, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipUpper : kNone};
-  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv, T3, qkv + a.q, T3,
-                                EpiStoreF32Batched{static_cast<float*>(ws), a.s, sc}, (int)a.Z, st)));
-  const int64_t rows = a.Z * a.s;
-  hipLaunchKernelGGL(softmax_fwd_kernel<S>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
-                     static_cast<const float*>(ws), static_cast<T*>(P), rows, a.s, a.scale, causal);
-  ATTN_HIP(hipGetLastError());
+  // S_bj [query][key] in fp32, computed as S^T = K_bj Q_bj^T [key][query] and stored transposed:
+  // P = K block [s,d] k-contiguous, Q[k=d][n=query] = Q_bj[n][k] k-contiguous
+  const BatchMap sc{(int)a.n, a.s * T3, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipLower : kNone};
+  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv + a.q, T3, qkv, T3,
+                                EpiStoreF32TBatched{static_cast<float*>(ws), a.s, sc}, (int)a.Z, st)));
+  ATTN_HIP(softmax_fwd<S>(static_cast<const float*>(ws), static_cast<T*>(P), a.Z * a.s, a.s, a.scale, causal, st));
   // O_bj = P_bj V_bj: P_bj [s,s] k-contiguous, Q[k][n] = V[k][n] n-contiguous (pitch 3q)
   const BatchMap pv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * a.q, a.d, causal ? kKeysUpTo : kNone};
   ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, P, a.s, qkv + 2 * a.q, T3, EpiStoreBatched<S>{(T*)O, a.q, pv},
@@ -401,21 +570,23 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
   T* dqkv = static_cast<T*>(dQKV);
   // dO = dY Wo^T: Q[k=h][n=q] = Wo[n][k] k-contiguous
   ATTN_HIP((gemm<S, true, true>(a.T, a.q, a.h, dY, a.h, Wo, a.h, EpiStore<S>{dO, a.q}, 1, st)));
-  // dWo = O^T dY: P[m=q][k=T] = O[k][m], Q = dY [T,h]: both mn-contiguous
-  ATTN_HIP((gemm<S, false, false>(a.q, a.h, a.T, O, a.q, dY, a.h, EpiStore<S>{(T*)dWo, a.h}, 1, st)));
+  // dWo = O^T dY: P[m=q][k=T] = O[k][m], Q = dY [T,h]: both mn-contiguous (k-split over tokens)
+  float* ksp = reinterpret_cast<float*>(wsb + w.ks_off);
+  {
+    const int rc = gemm_mc_ksplit<S>(a.q, a.h, a.T, O, a.q, dY, a.h, static_cast<T*>(dWo), w.ks_wo, ksp, st);
+    if (rc != TPMLP_OK) return rc;
+  }
   // dV_bj = P_bj^T dO_bj: P[m=key][k=query] = P_bj[k][m], Q = dO block: both mn-contiguous
   const BatchMap dv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * a.q, a.d, a.s * T3, a.d,
                     causal ? kQueriesFrom : kNone};
   ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, P, a.s, dO, a.q, EpiStoreBatched<S>{dqkv + 2 * a.q, T3, dv},
                                   (int)a.Z, st)));
-  // dP_bj = dO_bj V_bj^T (fp32): P = dO block k-contiguous, Q[k=d][n=key] = V[n][k] k-contiguous
-  const BatchMap dpm{(int)a.n, a.s * a.q, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipUpper : kNone};
-  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, dO, a.q, qkv + 2 * a.q, T3, EpiStoreF32Batched{dp, a.s, dpm},
+  // dP_bj = dO_bj V_bj^T [query][key] (fp32), computed as dP^T = V_bj dO_bj^T and stored transposed:
+  // P = V block k-contiguous, Q[k=d][n=query] = dO[n][k] k-contiguous
+  const BatchMap dpm{(int)a.n, a.s * T3, a.d, a.s * a.q, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipLower : kNone};
+  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv + 2 * a.q, T3, dO, a.q, EpiStoreF32TBatched{dp, a.s, dpm},
                                 (int)a.Z, st)));
-  const int64_t rows = a.Z * a.s;
-  hipLaunchKernelGGL(softmax_bwd_kernel<S>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st, dp,
-                     static_cast<const T*>(P), ds, rows, a.s, a.scale, causal);
-  ATTN_HIP(hipGetLastError());
+  ATTN_HIP(softmax_bwd<S>(dp, static_cast<const T*>(P), ds, a.Z * a.s, a.s, a.scale, causal, st));
   // dQ_bj = dS_bj K_bj: P = dS [s,s] k-contiguous, Q[k=key][n=d] = K[k][n] n-contiguous
   const BatchMap dq{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * T3, a.d, causal ? kKeysUpTo : kNone};
   ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, ds, a.s, qkv + a.q, T3, EpiStoreBatched<S>{dqkv, T3, dq},
@@ -432,8 +603,11 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
   hipLaunchKernelGGL(colsum_finish_kernel<S>, dim3((unsigned)cdiv(T3, 256)), dim3(256), 0, st, part, w.part_blk, T3,
                      static_cast<T*>(dbqkv));
   ATTN_HIP(hipGetLastError());
-  // dWqkv = X^T dQKV: P[m=h][k=T] = X[k][m], Q = dQKV [T,3q]: both mn-contiguous
-  ATTN_HIP((gemm<S, false, false>(a.h, T3, a.T, X, a.h, dQKV, T3, EpiStore<S>{(T*)dWqkv, T3}, 1, st)));
+  // dWqkv = X^T dQKV: P[m=h][k=T] = X[k][m], Q = dQKV [T,3q]: both mn-contiguous (k-split over tokens)
+  {
+    const int rc = gemm_mc_ksplit<S>(a.h, T3, a.T, X, a.h, dQKV, T3, static_cast<T*>(dWqkv), w.ks_wqkv, ksp, st);
+    if (rc != TPMLP_OK) return rc;
+  }
   // dXp = dQKV Wqkv^T: P = dQKV k-contiguous, Q[k=3q][n=h] = Wqkv[n][k] k-contiguous
   ATTN_HIP((gemm<S, true, true>(a.T, a.h, T3, dQKV, T3, Wqkv, T3, EpiStore<S>{(T*)dXp, a.h}, 1, st)));
   return TPMLP_OK;

@@ -336,12 +336,15 @@ def test_attention_workspace_sizes_and_validation(lib):
     big = sh(4, 2048, 2560, 8, 80, 2)
     Z = 32 * 2048 * 2048
     assert fws(big) == Z * 4
-    # dP fp32, dS bf16, dO [8192, 640], column partials [32][1920] fp32
-    assert bws(big) == Z * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4
+    # dP fp32, dS bf16, dO [8192, 640], column partials [8192 / 256][1920] fp32, then the k-split partials:
+    # dWo (5 x 20 tiles of 128 x 128) in 6 token ranges of 1408, dWqkv (20 x 15 tiles) in 2 of 4096
+    ks = max(6 * 640 * 2560 * 4, 2 * 2560 * 1920 * 4)
+    assert bws(big) == Z * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
     assert fws(sh(4, 2048, 2560, 8, 80, 0)) == 0          # fp32 storage is not supported
     assert fws(sh(4, 2044, 2560, 8, 80, 2)) == 0          # seq not a multiple of 8
     assert fws(sh(4, 2048, 2560, 8, 0, 2)) == 0           # empty heads
     assert bws(sh(70000, 8, 16, 1, 8, 2)) == 0            # more pairs than the grid's y range
+    assert fws(sh(1, 4104, 16, 1, 8, 2)) == 0             # softmax rows of at most 4096 keys
     bad = sh(1, 12, 16, 1, 8, 1)
     args = [None] * 8
     assert lib.tp_attn_fwd(ctypes.byref(bad), *args, None, 0, None) == 3          # TPMLP_ERR_ALIGN
