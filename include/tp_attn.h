@@ -73,9 +73,10 @@ typedef struct {
  * Workspace bytes (16-byte aligned device memory the caller owns; contents
  * on entry ignored; must not overlap any tensor argument):
  *   forward:  fp32 scores [batch*heads][seq][seq];
- *   backward: fp32 dP [batch*heads][seq][seq], dS [batch*heads][seq][seq]
- *             in the storage dtype, dO [T, q], and fp32 per-256-row column
- *             partials of dQKV for dbqkv.
+ *   backward: fp32 row terms rowsum(dO * O) [batch*heads][seq], dS
+ *             [batch*heads][seq][seq] in the storage dtype, dO [T, q], fp32
+ *             per-256-row column partials of dQKV for dbqkv, and fp32
+ *             partial sums of the two weight gradients (split over tokens).
  * 0 on an invalid shape.
  */
 size_t tp_attn_fwd_workspace_bytes(const tpattn_shape* shape);

@@ -53,6 +53,16 @@ struct EpiApply4 : std::false_type {};
 template <class E>
 struct EpiApply4<E, std::void_t<decltype(E::kApply4)>> : std::integral_constant<bool, E::kApply4> {};
 
+// An apply4 epilogue that also reads an input at the output positions
+// (kFetch4 = true) splits the read off: fetch4(m, n) returns what
+// apply4(m, n, v, fetched) needs. The kernel issues every fetch of the tile
+// before the first store, since the compiler cannot move a load above a store
+// to memory it cannot prove distinct.
+template <class E, class = void>
+struct EpiFetch4 : std::false_type {};
+template <class E>
+struct EpiFetch4<E, std::void_t<decltype(E::kFetch4)>> : std::integral_constant<bool, E::kFetch4> {};
+
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
@@ -242,12 +252,32 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, O
   float cs[Cfg::FN];
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) cs[j] = 0.0f;
+  if constexpr (EpiFetch4<Epi>::value) {
+    typename Epi::Fetched fe[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int64_t n = n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
+        const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
+        if (m < sh.M && n < sh.N) fe[i][j] = epi.fetch4(m, n);
+      }
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int64_t n = n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
+        const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
+        if (m < sh.M && n < sh.N) epi.apply4(m, n, acc[i][j], fe[i][j]);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int64_t n = n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
-      if constexpr (EpiApply4<Epi>::value) {
+      if constexpr (EpiApply4<Epi>::value && !EpiFetch4<Epi>::value) {
         const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
         if (m < sh.M && n < sh.N) epi.apply4(m, n, acc[i][j]);
       } else {

@@ -156,6 +156,62 @@ struct EpiStoreF32TBatched {
   __device__ __forceinline__ void colsum(int, int64_t, float) const {}
 };
 
+// The softmax's backward fused into the dP product: the product is computed
+// transposed, dP^T = V dO^T [key][query], and each lane's four consecutive
+// keys of one query become
+//   dS[query][key] = P[query][key] (dP[query][key] - D[query]) * scale,
+// rounded once to the storage dtype (8-byte loads of P, all issued before
+// the tile's first store; 8-byte stores of dS). P is exactly 0 at masked keys, so dS is too; tiles wholly above the
+// diagonal are skipped (kSkipLower) and never read by dQ or dK.
+template <class S>
+struct EpiSoftmaxGradTBatched {
+  typename S::T* ds;
+  const typename S::T* p;
+  const float* drow;  // D [pairs][s]
+  int64_t ld;         // s
+  float scale;
+  BatchMap bm;
+  static constexpr bool kBatched = true;
+  static constexpr bool kApply4 = true;
+  static constexpr bool kFetch4 = true;
+  static constexpr bool kColSum = false;
+  struct Fetched {
+    uint2 p;
+    float d;
+  };
+  __device__ __forceinline__ void select(int z, Operand& P, Operand& Q) {
+    const int64_t b = z / bm.inner, j = z % bm.inner;
+    P.ptr += b * bm.p_b + j * bm.p_j;
+    Q.ptr += b * bm.q_b + j * bm.q_j;
+    const int64_t off = b * bm.o_b + j * bm.o_j;
+    ds += off;
+    p += off;
+    drow += (int64_t)z * ld;
+  }
+  __device__ __forceinline__ bool skip(int64_t m0, int64_t n0) const {
+    return tri_skip<CfgA::BM, CfgA::BN>(bm.tri, m0, n0);
+  }
+  __device__ __forceinline__ void k_window(int64_t m0, int64_t& kbeg, int64_t& kend) const {
+    tri_window<CfgA::BM>(bm.tri, m0, kbeg, kend);
+  }
+  __device__ __forceinline__ Fetched fetch4(int64_t m, int64_t n) const {
+    return Fetched{*reinterpret_cast<const uint2*>(p + n * ld + m), drow[n]};
+  }
+  __device__ __forceinline__ void apply4(int64_t m, int64_t n, f32x4 v, const Fetched& f) const {
+    const uint2 w = f.p;
+    const float dn = f.d;
+    const float pv[4] = {S::to_f((typename S::T)(w.x & 0xffffu)), S::to_f((typename S::T)(w.x >> 16)),
+                         S::to_f((typename S::T)(w.y & 0xffffu)), S::to_f((typename S::T)(w.y >> 16))};
+    uint16_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = S::from_f(pv[i] * (v[i] - dn) * scale);
+    *reinterpret_cast<uint2*>(ds + n * ld + m) =
+        uint2{(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+  }
+  __device__ __forceinline__ float apply(int64_t, int64_t, float) const { return 0.0f; }
+  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
+};
+
 // C[M][N] = sum_k P[m][k] Q[k][n] for `batches` independent products (grid y).
 template <class S, bool PK, bool QK, class Epi>
 hipError_t gemm(int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q, int64_t ldq,
@@ -238,64 +294,32 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restric
   }
 }
 
-// Backward of the softmax, one wave per row, row in registers as above: with
-// the stored (rounded) probabilities P and the fp32 dP = dO V^T,
-//   D = sum over visible keys of P[k] dP[k],  dS[k] = P[k] (dP[k] - D) * scale,
-// 0 for masked keys, rounded once to the storage dtype. With the causal mask
-// only keys below the end of the query's 128-wide block are written: the
-// products that read dS (k-windowed on the same 128-row tiles) read no
-// further.
-template <class S, int CH>
-__global__ __launch_bounds__(256) void softmax_bwd_kernel(const float* __restrict__ dp,
-                                                          const typename S::T* __restrict__ P,
-                                                          typename S::T* __restrict__ dS, int64_t rows, int64_t s,
-                                                          float scale, int causal) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const int64_t qi = row % s;
-  const int64_t nv = causal ? qi + 1 : s;
-  const int64_t nw = causal ? min(s, (qi / CfgA::BM + 1) * CfgA::BM) : s;
-  const float* g = dp + row * s;
-  const typename S::T* p = P + row * s;
-  typename S::T* o = dS + row * s;
-  float pv[CH][4], gv[CH][4];
-  float d = 0.0f;
+// Row terms of the softmax backward: for each (sequence, head) pair z and
+// query t, D[z][t] = sum_e dO[t][e] O[t][e] over the head's d columns (fp32,
+// in e order). In exact arithmetic D = sum_k P[t][k] dP[t][k], since
+// dP = dO V^T and O = P V; it is the term the softmax's backward subtracts.
+template <class S>
+__global__ __launch_bounds__(256) void softmax_rowdot_kernel(const typename S::T* __restrict__ dO,
+                                                             const typename S::T* __restrict__ O, float* __restrict__ D,
+                                                             int64_t T, int64_t s, int heads, int d, int64_t q) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // token * heads + head
+  if (i >= T * heads) return;
+  const int64_t t = i / heads;
+  const int j = (int)(i % heads);
+  const typename S::T* a = dO + t * q + (int64_t)j * d;
+  const typename S::T* o = O + t * q + (int64_t)j * d;
+  float acc = 0.0f;
+  for (int e = 0; e < d; e += 8) {
+    const uint4 wa = *reinterpret_cast<const uint4*>(a + e), wo = *reinterpret_cast<const uint4*>(o + e);
+    const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w}, uo[4] = {wo.x, wo.y, wo.z, wo.w};
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int64_t k = (int64_t)lane * 4 + 256 * c;
-    float4 t = {0.f, 0.f, 0.f, 0.f};
-    uint2 w = {0u, 0u};
-    if (k < nv) {
-      t = *reinterpret_cast<const float4*>(g + k);
-      w = *reinterpret_cast<const uint2*>(p + k);
-    }
-    gv[c][0] = t.x;
-    gv[c][1] = t.y;
-    gv[c][2] = t.z;
-    gv[c][3] = t.w;
-    pv[c][0] = S::to_f((typename S::T)(w.x & 0xffffu));
-    pv[c][1] = S::to_f((typename S::T)(w.x >> 16));
-    pv[c][2] = S::to_f((typename S::T)(w.y & 0xffffu));
-    pv[c][3] = S::to_f((typename S::T)(w.y >> 16));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (k + i < nv) d += pv[c][i] * gv[c][i];
-  }
-  d = wave_sum(d);
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int64_t k = (int64_t)lane * 4 + 256 * c;
-    if (k < nw) {
-      float r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (k + i < nv) ? pv[c][i] * (gv[c][i] - d) * scale : 0.0f;
-      uint2 w;
-      w.x = (uint32_t)S::from_f(r[0]) | ((uint32_t)S::from_f(r[1]) << 16);
-      w.y = (uint32_t)S::from_f(r[2]) | ((uint32_t)S::from_f(r[3]) << 16);
-      *reinterpret_cast<uint2*>(o + k) = w;
+    for (int k = 0; k < 4; ++k) {
+      acc += S::to_f((typename S::T)(ua[k] & 0xffffu)) * S::to_f((typename S::T)(uo[k] & 0xffffu));
+      acc += S::to_f((typename S::T)(ua[k] >> 16)) * S::to_f((typename S::T)(uo[k] >> 16));
     }
   }
+  const int64_t b = t / s, pos = t % s;
+  D[((b * heads) + j) * s + pos] = acc;
 }
 
 // Column sums of a [rows][cols] 16-bit matrix (cols a multiple of 8), first
@@ -383,18 +407,6 @@ hipError_t softmax_fwd(const float* sc, typename S::T* P, int64_t rows, int64_t 
   return hipGetLastError();
 }
 
-template <class S>
-hipError_t softmax_bwd(const float* dp, const typename S::T* P, typename S::T* dS, int64_t rows, int64_t s,
-                       float scale, int causal, hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(rows, 4)), block(256);
-  if (s <= 256) hipLaunchKernelGGL((softmax_bwd_kernel<S, 1>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
-  else if (s <= 512) hipLaunchKernelGGL((softmax_bwd_kernel<S, 2>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
-  else if (s <= 1024) hipLaunchKernelGGL((softmax_bwd_kernel<S, 4>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
-  else if (s <= 2048) hipLaunchKernelGGL((softmax_bwd_kernel<S, 8>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
-  else hipLaunchKernelGGL((softmax_bwd_kernel<S, 16>), grid, block, 0, st, dp, P, dS, rows, s, scale, causal);
-  return hipGetLastError();
-}
-
 // k-split of a product whose output tiles do not fill the chip: ranges of
 // whole 64-wide k-steps, enough of them for about two tiles per CU, at
 // most 8 and each at least 512 long.
@@ -450,11 +462,11 @@ AttnDims dims(const tpattn_shape& sh) {
   return a;
 }
 
-// Backward workspace: [dP fp32 Z s s][dS 16-bit Z s s][dO 16-bit T q]
+// Backward workspace: [D fp32 Z s][dS 16-bit Z s s][dO 16-bit T q]
 // [column partials of dQKV fp32 [T/256][3q]][k-split partials of dWo and
 // dWqkv fp32 (they run one after the other and share the room)].
 struct AttnBwdWs {
-  size_t dp_off, ds_off, do_off, part_off, ks_off, total;
+  size_t drow_off, ds_off, do_off, part_off, ks_off, total;
   int part_blk;
   KSplit ks_wo, ks_wqkv;
 };
@@ -462,8 +474,8 @@ struct AttnBwdWs {
 AttnBwdWs bwd_layout(const AttnDims& a) {
   AttnBwdWs w{};
   const size_t zss = (size_t)(a.Z * a.s * a.s);
-  w.dp_off = 0;
-  w.ds_off = a256(zss * 4);
+  w.drow_off = 0;
+  w.ds_off = a256((size_t)(a.Z * a.s) * 4);
   w.do_off = w.ds_off + a256(zss * 2);
   w.part_off = w.do_off + a256((size_t)(a.T * a.q) * 2);
   w.part_blk = (int)cdiv(a.T, 256);
@@ -562,7 +574,7 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
   const int64_t T3 = 3 * a.q;
   const AttnBwdWs w = bwd_layout(a);
   char* wsb = static_cast<char*>(ws);
-  float* dp = reinterpret_cast<float*>(wsb + w.dp_off);
+  float* drow = reinterpret_cast<float*>(wsb + w.drow_off);
   T* ds = reinterpret_cast<T*>(wsb + w.ds_off);
   T* dO = reinterpret_cast<T*>(wsb + w.do_off);
   float* part = reinterpret_cast<float*>(wsb + w.part_off);
@@ -581,12 +593,15 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
                     causal ? kQueriesFrom : kNone};
   ATTN_HIP((gemm<S, false, false>(a.s, a.d, a.s, P, a.s, dO, a.q, EpiStoreBatched<S>{dqkv + 2 * a.q, T3, dv},
                                   (int)a.Z, st)));
-  // dP_bj = dO_bj V_bj^T [query][key] (fp32), computed as dP^T = V_bj dO_bj^T and stored transposed:
-  // P = V block k-contiguous, Q[k=d][n=query] = dO[n][k] k-contiguous
+  // D = rowsum(dO * O) per (pair, query); then dP_bj = dO_bj V_bj^T, computed as dP^T = V_bj dO_bj^T
+  // (P = V block k-contiguous, Q[k=d][n=query] = dO[n][k] k-contiguous), becomes dS in its epilogue
+  hipLaunchKernelGGL(softmax_rowdot_kernel<S>, dim3((unsigned)cdiv(a.T * a.n, 256)), dim3(256), 0, st, dO,
+                     static_cast<const T*>(O), drow, a.T, a.s, (int)a.n, (int)a.d, a.q);
+  ATTN_HIP(hipGetLastError());
   const BatchMap dpm{(int)a.n, a.s * T3, a.d, a.s * a.q, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipLower : kNone};
-  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv + 2 * a.q, T3, dO, a.q, EpiStoreF32TBatched{dp, a.s, dpm},
+  ATTN_HIP((gemm<S, true, true>(a.s, a.s, a.d, qkv + 2 * a.q, T3, dO, a.q,
+                                EpiSoftmaxGradTBatched<S>{ds, static_cast<const T*>(P), drow, a.s, a.scale, dpm},
                                 (int)a.Z, st)));
-  ATTN_HIP(softmax_bwd<S>(dp, static_cast<const T*>(P), ds, a.Z * a.s, a.s, a.scale, causal, st));
   // dQ_bj = dS_bj K_bj: P = dS [s,s] k-contiguous, Q[k=key][n=d] = K[k][n] n-contiguous
   const BatchMap dq{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * T3, a.d, causal ? kKeysUpTo : kNone};
   ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, ds, a.s, qkv + a.q, T3, EpiStoreBatched<S>{dqkv, T3, dq},
@@ -640,7 +655,7 @@ int tp_attn_fwd(const tpattn_shape* shape, const void* X, const void* Wqkv, cons
   const Span2 in[4] = {{X, (size_t)(a.T * a.h) * e}, {Wqkv, (size_t)(a.h * 3 * a.q) * e},
                        {bqkv, (size_t)(3 * a.q) * e}, {Wo, (size_t)(a.q * a.h) * e}};
   const Span2 out[5] = {{QKV, (size_t)(a.T * 3 * a.q) * e}, {P, (size_t)(a.Z * a.s * a.s) * e},
-                        {O, (size_t)(a.T * a.q) * e}, {Yp, (size_t)(a.T * a.h) * e}, {ws, need}};
+                        {O, (size_t)(a.T * a.q) * e}, {Yp, (size_t)(a.T * a.h) * e}, {ws, std::min(need, ws_bytes)}};
   const int bc = check_spans(in, 4, out, 5);
   if (bc != TPMLP_OK) return bc;
   if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;
@@ -661,7 +676,8 @@ int tp_attn_bwd(const tpattn_shape* shape, const void* dY, const void* X, const 
                qh = (size_t)(a.q * a.h) * e;
   const Span2 in[7] = {{dY, Th}, {X, Th}, {Wqkv, h3}, {Wo, qh}, {QKV, T3}, {P, (size_t)(a.Z * a.s * a.s) * e},
                        {O, (size_t)(a.T * a.q) * e}};
-  const Span2 out[6] = {{dQKV, T3}, {dXp, Th}, {dWqkv, h3}, {dbqkv, (size_t)(3 * a.q) * e}, {dWo, qh}, {ws, need}};
+  const Span2 out[6] = {{dQKV, T3}, {dXp, Th}, {dWqkv, h3}, {dbqkv, (size_t)(3 * a.q) * e}, {dWo, qh},
+                        {ws, std::min(need, ws_bytes)}};
   const int bc = check_spans(in, 7, out, 6);
   if (bc != TPMLP_OK) return bc;
   if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;

@@ -336,10 +336,10 @@ def test_attention_workspace_sizes_and_validation(lib):
     big = sh(4, 2048, 2560, 8, 80, 2)
     Z = 32 * 2048 * 2048
     assert fws(big) == Z * 4
-    # dP fp32, dS bf16, dO [8192, 640], column partials [8192 / 256][1920] fp32, then the k-split partials:
-    # dWo (5 x 20 tiles of 128 x 128) in 6 token ranges of 1408, dWqkv (20 x 15 tiles) in 2 of 4096
+    # D fp32 [32][2048], dS bf16, dO [8192, 640], column partials [8192 / 256][1920] fp32, then the k-split
+    # partials: dWo (5 x 20 tiles of 128 x 128) in 6 token ranges of 1408, dWqkv (20 x 15 tiles) in 2 of 4096
     ks = max(6 * 640 * 2560 * 4, 2 * 2560 * 1920 * 4)
-    assert bws(big) == Z * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
+    assert bws(big) == 32 * 2048 * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
     assert fws(sh(4, 2048, 2560, 8, 80, 0)) == 0          # fp32 storage is not supported
     assert fws(sh(4, 2044, 2560, 8, 80, 2)) == 0          # seq not a multiple of 8
     assert fws(sh(4, 2048, 2560, 8, 0, 2)) == 0           # empty heads
@@ -353,6 +353,12 @@ def test_attention_workspace_sizes_and_validation(lib):
     fake = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
     ws = ctypes.c_void_p(0x100000)
     assert lib.tp_attn_fwd(ctypes.byref(ok), *fake, ws, 0, None) == 5             # workspace too small
+    fake12 = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(12)]
+    ws2 = ctypes.c_void_p(0x200000)
+    assert lib.tp_attn_bwd(ctypes.byref(ok), *fake12, ws2, 0, None) == 5
+    # a workspace that is too small is reported as such even where the full
+    # size would run into another buffer
+    assert lib.tp_attn_bwd(ctypes.byref(ok), *fake12, ctypes.c_void_p(0xC0000 - 256), 16, None) == 5
     unaligned = list(fake)
     unaligned[0] = ctypes.c_void_p(0x10008)
     assert lib.tp_attn_fwd(ctypes.byref(ok), *unaligned, ws, 1 << 20, None) == 3  # X not 16-byte aligned

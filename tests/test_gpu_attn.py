@@ -41,7 +41,8 @@ def _ref(inp, causal):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("batch,seq,hidden,heads,d", [(2, 64, 128, 2, 32), (2, 136, 72, 3, 24), (1, 200, 96, 2, 80),
-                                                      (3, 8, 16, 1, 8), (1, 264, 136, 4, 40)])
+                                                      (3, 8, 16, 1, 8), (1, 264, 136, 4, 40), (2, 72, 64, 1, 128),
+                                                      (1, 136, 48, 2, 136)])
 def test_attention_shard_matches_oracle(gpu_lib, dtype, causal, batch, seq, hidden, heads, d):
     print(f"case attn dtype={dtype} causal={causal} b={batch} s={seq} h={hidden} n={heads} d={d}", flush=True)
     inp = synth.draw_attn_inputs(batch, seq, hidden, heads, d, dtype, seed=seq + 7 * d, sigma_w=0.1,
@@ -102,8 +103,9 @@ def test_attention_rejects_bad_arguments(gpu_lib):
         gpu_lib.attn_fwd(X.float(), Wqkv.float(), bqkv.float(), Wo.float(), 1, 1)
     assert e.value.status == 4  # fp32 is not an attention storage dtype
     small = torch.empty((16,), dtype=torch.uint8, device="cuda")
+    fw = gpu_lib.attn_fwd(X, Wqkv, bqkv, Wo, 1, 1)
     with pytest.raises(gpu_lib.TpMlpError) as e:
-        gpu_lib.attn_fwd(X, Wqkv, bqkv, Wo, 1, 1, ws=small)
+        gpu_lib.attn_bwd(dY, X, Wqkv, Wo, fw["QKV"], fw["P"], fw["O"], 1, 1, ws=small)
     assert e.value.status == 5
 
 
@@ -119,3 +121,4 @@ def test_attention_2p4b_shard_full(gpu_lib):
     got = _run(gpu_lib, *_dev(inp), cfg.micro_batch, cfg.heads_shard, cfg.causal)
     errs = compare(got, _ref(inp, cfg.causal), TOL[cfg.dtype], keys=FWD + BWD)
     print("errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+
