@@ -146,7 +146,21 @@ def reduce_partials_rate(tpmlp, Yp, cfg, dev, reps=10):
             "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / 8000.0, 4)}
 
 
-def attention_rate(tpmlp, dev, reps=10):
+def attention_cpu_baseline(inp, cfg, flops_per_seq):
+    """The float64 attention oracle (as it stands) on the first sequence of
+    the same shard (all of its heads), forward + backward."""
+    import oracle
+    s = cfg.seq_len
+    t0 = time.perf_counter()
+    oracle.attn_shard_forward(inp.X[:s], inp.Wqkv, inp.bqkv, inp.Wo, 1, cfg.heads_shard, cfg.causal)
+    oracle.attn_shard_backward(inp.X[:s], inp.Wqkv, inp.bqkv, inp.Wo, inp.dY[:s], 1, cfg.heads_shard, cfg.causal)
+    dt = time.perf_counter() - t0
+    return {"value": flops_per_seq / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, forward+backward of the same shard on 1 of {cfg.micro_batch} sequences "
+                      f"({s} tokens, {cfg.heads_shard} heads), {dt:.1f} s"}
+
+
+def attention_rate(tpmlp, dev, reps=10, cpu=True):
     """Forward + backward of one TP rank's attention share of the 2.4B model
     (8 of 32 heads of width 80, 4 sequences of 2048 tokens, bf16, causal)
     through tp_attn_fwd / tp_attn_bwd, timed with HIP events on the launch
@@ -197,10 +211,13 @@ def attention_rate(tpmlp, dev, reps=10):
     flops_f = 2.0 * T * h * 3 * q + 2.0 * T * q * h + 2 * 2.0 * Z * s * s * d * (0.5 if cfg.causal else 1.0)
     tflops = 3 * flops_f / ((f_ms + b_ms) * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
-    return {"workload": f"{cfg.name}: one TP={cfg.tp} rank's attention of hidden {h}, {cfg.heads} heads of width {d} "
-                        f"({n} on this rank), micro-batch {b} x seq {s}, causal, {cfg.dtype}",
-            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tflops, 2), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}
+    out = {"workload": f"{cfg.name}: one TP={cfg.tp} rank's attention of hidden {h}, {cfg.heads} heads of width {d} "
+                       f"({n} on this rank), micro-batch {b} x seq {s}, causal, {cfg.dtype}",
+           "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tflops, 2), "peak": peak,
+           "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "bound": "mfma", "cpu_baseline": None}
+    if cpu:
+        out["cpu_baseline"] = attention_cpu_baseline(inp, cfg, 3 * flops_f / b)
+    return out
 
 
 def main():
@@ -332,7 +349,7 @@ def main():
     achieved = gemm_flops / (per[dom] * 1e-3) / 1e12
 
     reduce_line = None if args.no_reduce else reduce_partials_rate(tpmlp, Yp, cfg, dev)
-    attn_line = None if args.no_attn else attention_rate(tpmlp, dev)
+    attn_line = None if args.no_attn else attention_rate(tpmlp, dev, cpu=not args.no_cpu_baseline)
 
     result = {
         "metric": METRIC,
