@@ -91,14 +91,25 @@ int64_t wave_cost(int64_t M, int64_t N, int bm, int bn) {
   return ceil_div(ceil_div(M, bm) * ceil_div(N, bn), kCUs) * bm * bn;
 }
 
+// A launch of fewer 256 x 256 tiles than this runs on 128 x 128 tiles
+// (measured on MI355X: from about three quarters of a wave the direct-load
+// engine's 256-wide tiles win, e.g. 1.3-1.6x on the 2560- and 4096-wide
+// shards' GEMMs), unless it is a long reduction that the k-split below
+// spreads over the chip.
+constexpr int64_t kDmaMinTiles = 192;
+// Reductions at least this long may split a sub-wave launch into k-ranges.
+constexpr int64_t kSubWaveSplitK = 2048;
+
 // Tile choice for the 16-bit engines. Large tiles (256x256) once they give
-// at least two full waves over the 256 CUs, else 128x128. Large tiles use the
-// direct-to-LDS engine unless P needs the GeLU applied on load (that engine
-// has no register stage to apply it in) or an operand is too large for its
-// 32-bit offsets; with both operands k-contiguous (kc) it takes 256x320
-// tiles unless they cost more whole waves. TPMLP_TILE=128, 256
-// (register-staged), dma256 or dma320 (kc only) in the environment forces
-// one engine where it applies (read on every call; for tuning and tests).
+// at least kDmaMinTiles of them (or at least 16 with a reduction of
+// kSubWaveSplitK or more, which plan_tail splits into k-ranges), else
+// 128x128. Large tiles use the direct-to-LDS engine unless P needs the GeLU
+// applied on load (that engine has no register stage to apply it in) or an
+// operand is too large for its 32-bit offsets; with both operands
+// k-contiguous (kc) it takes 256x320 tiles unless they cost more whole
+// waves. TPMLP_TILE=128, 256 (register-staged), dma256 or dma320 (kc only)
+// in the environment forces one engine where it applies (read on every
+// call; for tuning and tests).
 Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
   const bool dma_fits = !gelu_p && M * (K + kStagePad) <= kDmaMaxElems && N * (K + kStagePad) <= kDmaMaxElems;
   if (const char* e = std::getenv("TPMLP_TILE")) {
@@ -107,7 +118,9 @@ Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
     if (!std::strcmp(e, "dma256")) return dma_fits ? Engine::Dma256 : Engine::Mfma256;
     if (!std::strcmp(e, "dma320")) return !dma_fits ? Engine::Mfma256 : kc ? Engine::Dma320 : Engine::Dma256;
   }
-  if (ceil_div(M, 256) * ceil_div(N, 256) < 512) return Engine::Mfma128;
+  const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+  const bool split_candidate = t256 >= 16 && t256 <= kCUs / 2 && K >= kSubWaveSplitK;
+  if (t256 < kDmaMinTiles && !split_candidate) return Engine::Mfma128;
   if (!dma_fits) return Engine::Mfma256;
   if (kc && wave_cost(M, N, CfgD320::BM, CfgD320::BN) <= wave_cost(M, N, CfgD256::BM, CfgD256::BN))
     return Engine::Dma320;
@@ -141,7 +154,9 @@ void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q,
 
 // Split of the last partial wave of a direct-load GEMM (see TailSplit): when
 // fewer than half the CUs would get a tile in the last wave, those tiles are
-// split into up to four k-ranges of at least 512. Only plain-store epilogues.
+// split into up to four k-ranges of at least 128. A launch of less than half
+// a wave is split the same way (every tile) if its reduction is at least
+// kSubWaveSplitK long. Only plain-store epilogues.
 // TPMLP_TAIL_CUS in the environment replaces the CU count of this plan (read
 // on every call; lets tests exercise tail splits at small sizes).
 TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
@@ -151,7 +166,8 @@ TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
   if (const char* e = std::getenv("TPMLP_TAIL_CUS")) cus = std::max(1, std::atoi(e));
   const int r = ntile % cus;
   const bool dma = pl.eng == Engine::Dma256 || pl.eng == Engine::Dma320;
-  if (!allowed || !dma || ntile < cus || r == 0 || r > cus / 2) return t;
+  if (!allowed || !dma || r == 0 || r > cus / 2) return t;
+  if (ntile < cus && K < kSubWaveSplitK) return t;
   int parts = std::min(4, cus / r);
   while (parts > 1 && K < (int64_t)parts * 128) --parts;
   if (parts < 2) return t;

@@ -88,7 +88,10 @@ def test_workspace_bytes(lib):
     # 16-bit: the dZ GEMM uses 128- or 256-row tiles
     part = (16384 // 256) * 10240 * 4
     assert ws(16384, 10240, 10240, 2, MINIMAL) == part
-    assert ws(4096, 768, 3072, 1, MINIMAL) == (4096 // 128) * 3072 * 4
+    # GPT-2-small shard (T=4096, h=768, f=3072): the dZ GEMM has 16 x 12 = 192 tiles of 256 x 256, enough for
+    # the direct-load engine and its 256-row partials
+    part2 = (4096 // 256) * 3072 * 4
+    assert ws(4096, 768, 3072, 1, MINIMAL) == part2
     # large shards stage k-contiguous copies of H, dY, X and dZ for the
     # weight-gradient GEMMs (each [rows][T] in 16 bits), after the minimal
     # part, each row padded by 256 elements. Their GEMMs then run on 256 x 320
@@ -105,9 +108,17 @@ def test_workspace_bytes(lib):
     t8 = 8192 * (16384 + 256) * 2
     assert fws(16384, 8192, 8192, 2) == 2 * 8192 * (8192 + 256) * 2
     assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240 + 4 * t8
+    # ... its weight gradients (12 x 3 = 36 tiles, K = 4096) and dXp (16 x 3 = 48 tiles, K = 3072) are
+    # launches of less than half a wave with long reductions: direct-load engine on staged copies of H, dY,
+    # X and dZ, every tile split into 4 k-ranges (the largest, dXp's, sizes the shared partials)
+    t2 = lambda rows: rows * (4096 + 256) * 2
+    assert ws(4096, 768, 3072, 1) == part2 + 2 * t2(3072) + 2 * t2(768) + 48 * 4 * 256 * 256 * 4
+    # ... and its forward stages A_i^T (first GEMM: 192 tiles) and B_i^T (second GEMM: 48 tiles, K = 3072,
+    # split into 4 k-ranges)
+    assert fws(4096, 768, 3072, 1) == 3072 * (768 + 256) * 2 + 768 * (3072 + 256) * 2 + 48 * 4 * 256 * 256 * 4
     # small shapes and fp32 stage nothing
-    assert ws(4096, 768, 3072, 1) == ws(4096, 768, 3072, 1, MINIMAL)
-    assert fws(4096, 768, 3072, 1) == 0 and fws(64, 128, 256, 0) == 0
+    assert ws(520, 264, 392, 1) == ws(520, 264, 392, 1, MINIMAL)
+    assert fws(520, 264, 392, 1) == 0 and fws(64, 128, 256, 0) == 0
     # nothing to reduce for empty token or FFN dimensions
     assert ws(0, 128, 256, 2) == 0
     assert ws(64, 128, 0, 2) == 0
@@ -318,7 +329,7 @@ def test_b_transposed_layout_workspace_and_validation(lib):
     assert ws(1, MINIMAL) == ws(0, MINIMAL)
     assert ws(2) == 0 and fws(4) == 0 and ws(-1) == 0
     # small shapes stage nothing in either layout
-    small = lambda layout: tpmlp_shape(4096, 768, 3072, 1, layout)
+    small = lambda layout: tpmlp_shape(520, 264, 392, 1, layout)
     assert lib.tp_mlp_workspace_bytes(ctypes.byref(small(1)), 0) == lib.tp_mlp_workspace_bytes(
         ctypes.byref(small(0)), 0)
     bad = tpmlp_shape(64, 128, 256, 2, 2)
