@@ -146,6 +146,47 @@ def reduce_partials_rate(tpmlp, Yp, cfg, dev, reps=10):
             "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / 8000.0, 4)}
 
 
+OTHER_CONFIGS = ("gpt2_small", "gpt_2p4b", "gpt_7b")
+
+
+def config_rate(tpmlp, name, dev, steps=10, warmup=3):
+    """Whole-step rate of another MLP workload (default launch configuration:
+    staged workspaces, H and dZ kept), timed with HIP events on the launch
+    stream; reported beside the main workload, whose line this is."""
+    import torch
+    import synth
+    from tests.gpu_util import device_inputs
+    cfg = synth.get_config(name)
+    T, h, f = cfg.tokens, cfg.hidden, cfg.ffn_shard
+    inp = synth.draw_config(cfg)
+    X, A, b1, B, dY = device_inputs(inp)
+    td = X.dtype
+    e = lambda *s: torch.empty(s, dtype=td, device=dev)
+    Z, H, Yp, dZ, dXp, dA, dB, db1 = e(T, f), e(T, f), e(T, h), e(T, f), e(T, h), e(h, f), e(f, h), e(f)
+    code = {"f32": tpmlp.TPMLP_F32, "f16": tpmlp.TPMLP_F16, "bf16": tpmlp.TPMLP_BF16}[cfg.dtype]
+    nws, nfws = tpmlp.tp_mlp_workspace_bytes(T, h, f, code), tpmlp.tp_mlp_fwd_workspace_bytes(T, h, f, code)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
+    fws = torch.empty((nfws,), dtype=torch.uint8, device=dev) if nfws else None
+
+    def step():
+        tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws)
+        tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 12.0 * T * h * f / (ms * 1e-3) / 1e12
+    return {"workload": workload_name(cfg), "dtype": cfg.dtype, "ms_per_step": round(ms, 4),
+            "tflops": round(tflops, 2), "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[cfg.dtype], 2)}
+
+
 def attention_cpu_baseline(inp, cfg, flops_per_seq):
     """The float64 attention oracle (as it stands) on the first sequence of
     the same shard (all of its heads), forward + backward."""
@@ -238,6 +279,8 @@ def main():
                          "in that order")
     ap.add_argument("--no-reduce", action="store_true",
                     help="skip timing tp_mlp_reduce_partials (the TP group's sum of partials, not part of a step)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other MLP workloads (GPT-2-small, the 2.4B and 7B shards)")
     ap.add_argument("--no-attn", action="store_true",
                     help="skip timing the attention shard (tp_attn_fwd + tp_attn_bwd, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -350,6 +393,9 @@ def main():
 
     reduce_line = None if args.no_reduce else reduce_partials_rate(tpmlp, Yp, cfg, dev)
     attn_line = None if args.no_attn else attention_rate(tpmlp, dev, cpu=not args.no_cpu_baseline)
+    other = None
+    if not args.no_configs and not (args.main_grad or args.recompute or bt):
+        other = {n: config_rate(tpmlp, n, dev) for n in OTHER_CONFIGS if n != cfg.name}
 
     result = {
         "metric": METRIC,
@@ -386,6 +432,7 @@ def main():
         "cpu_baseline": None,
         "reduce_partials": reduce_line,
         "attention": attn_line,
+        "configs": other,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
