@@ -100,6 +100,23 @@ constexpr int64_t kDmaMinTiles = 192;
 // Reductions at least this long may split a sub-wave launch into k-ranges.
 constexpr int64_t kSubWaveSplitK = 2048;
 
+// k-ranges per tile of a launch of `ntile` tiles that plan_tail splits as a
+// sub-wave launch (1 if it does not).
+int subwave_parts(int64_t ntile, int64_t K) {
+  if (ntile > kCUs / 2 || K < kSubWaveSplitK) return 1;
+  int parts = (int)std::min<int64_t>(4, kCUs / ntile);
+  while (parts > 1 && K < (int64_t)parts * 128) --parts;
+  return parts;
+}
+
+// Cost of a k-split sub-wave launch in whole waves of its work items times
+// the work of one item.
+int64_t subwave_cost(int64_t M, int64_t N, int64_t K, int bm, int bn) {
+  const int64_t ntile = ceil_div(M, bm) * ceil_div(N, bn);
+  const int parts = subwave_parts(ntile, K);
+  return ceil_div(ntile * parts, kCUs) * bm * bn * ceil_div(K, parts);
+}
+
 // Tile choice for the 16-bit engines. Large tiles (256x256) once they give
 // at least kDmaMinTiles of them (or at least 16 with a reduction of
 // kSubWaveSplitK or more, which plan_tail splits into k-ranges), else
@@ -122,6 +139,10 @@ Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
   const bool split_candidate = t256 >= 16 && t256 <= kCUs / 2 && K >= kSubWaveSplitK;
   if (t256 < kDmaMinTiles && !split_candidate) return Engine::Mfma128;
   if (!dma_fits) return Engine::Mfma256;
+  if (kc && split_candidate)  // the k-split's work items decide which tile fills the chip better
+    return subwave_cost(M, N, K, CfgD320::BM, CfgD320::BN) < subwave_cost(M, N, K, CfgD256::BM, CfgD256::BN)
+               ? Engine::Dma320
+               : Engine::Dma256;
   if (kc && wave_cost(M, N, CfgD320::BM, CfgD320::BN) <= wave_cost(M, N, CfgD256::BM, CfgD256::BN))
     return Engine::Dma320;
   return Engine::Dma256;

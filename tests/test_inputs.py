@@ -134,3 +134,18 @@ def test_chunked_draws_do_not_depend_on_threads(monkeypatch):
     # chunk 1 of X is the second stream of the X tensor
     x1 = np.random.Generator(np.random.PCG64([3, 0, 1])).standard_normal(64)
     assert np.array_equal(a.X.reshape(-1)[64:128], round_to_storage(x1, "f16"))
+
+
+def test_attention_workload_matches_the_pages():
+    """The attention shard's workload is the 2.4B run's printed attention
+    shape (hidden, heads, seq, micro-batch), one rank of TP 4 like its MLP."""
+    g = _golden()
+    a = synth.get_attn_config("attn_2p4b")
+    c3 = synth.get_config("gpt_2p4b")
+    assert (a.hidden, a.heads, a.seq_len, a.micro_batch) == (g["p2_2p4b_hidden"], g["p2_2p4b_heads"],
+                                                             g["p2_2p4b_seq"], g["p2_2p4b_micro_batch"])
+    assert a.tp == c3.tp and a.head_dim * a.heads == a.hidden and a.heads_shard * a.tp == a.heads
+    x = synth.draw_attn_inputs(1, 8, 16, 2, 8, "bf16", seed=3)
+    y = synth.draw_attn_inputs(1, 8, 16, 2, 8, "bf16", seed=3)
+    assert all(np.array_equal(getattr(x, k), getattr(y, k)) for k in ("X", "Wqkv", "bqkv", "Wo", "dY"))
+    assert x.Wqkv.shape == (16, 48) and x.Wo.shape == (16, 16) and x.seq == 8 and x.head_dim == 8
