@@ -76,7 +76,9 @@ typedef struct {
  *   backward: fp32 row terms rowsum(dO * O) [batch*heads][seq], dS
  *             [batch*heads][seq][seq] in the storage dtype, dO [T, q], fp32
  *             per-256-row column partials of dQKV for dbqkv, and fp32
- *             partial sums of the two weight gradients (split over tokens).
+ *             k-split partial sums of the projections' GEMMs.
+ *   The forward's score buffer also holds the output projection's k-split
+ *   partials, once the scores are consumed.
  * 0 on an invalid shape.
  */
 size_t tp_attn_fwd_workspace_bytes(const tpattn_shape* shape);

@@ -1,9 +1,12 @@
 // C ABI of the tensor-parallel self-attention shard (declared in
 // include/tp_attn.h): one rank's heads, forward and backward.
 //
-// Every product runs on the register-staged MFMA engine (gemm_mfma.hpp,
-// 128 x 128 tiles). The per-head products (scores, P V and the four
-// backward products) are one batched launch each: grid y runs over the
+// The projections (QKV, the output projection and their gradients) go
+// through the MLP shard's GEMM planner (shard_gemm.hpp): direct-load engine
+// with k-split partials where the shapes fill the chip that way. The
+// per-head products run on the register-staged MFMA engine (gemm_mfma.hpp,
+// 128 x 128 tiles), one batched launch each (scores, P V and the four
+// backward products): grid y runs over the
 // batch * heads (sequence, head) pairs, and a batched epilogue moves the
 // operands and its output to that pair's blocks before the tile is computed.
 // Operands are read where they lie (Q, K, V as column blocks of QKV with row
@@ -22,6 +25,7 @@
 #include "tp_attn.h"
 #include "epilogues.hpp"
 #include "gemm_mfma.hpp"
+#include "shard_gemm.hpp"
 
 namespace tpmlp {
 namespace {
@@ -50,8 +54,6 @@ struct BatchMap {
   int inner;
   int64_t p_b, p_j, q_b, q_j, o_b, o_j;
   int tri;
-  int64_t k_total, k_chunk;  // k-split use (inner = 1): batch z covers k in [z k_chunk, (z + 1) k_chunk) of
-                             // k_total (the operand offsets p_b, q_b step by k_chunk rows); 0 otherwise
 };
 
 template <int BM, int BN>
@@ -88,38 +90,6 @@ struct EpiStoreBatched {
   }
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
     out[m * ld + n] = S::from_f(acc);
-    return 0.0f;
-  }
-  __device__ __forceinline__ void colsum(int, int64_t, float) const {}
-};
-
-// fp32 store of a batched product (the scores, and dP in the backward; and
-// the per-range partial sums of a k-split product, whose batch z covers
-// k in [z K, z K + K) of bm.k_total).
-struct EpiStoreF32Batched {
-  float* out;
-  int64_t ld;
-  BatchMap bm;
-  int64_t klim;
-  static constexpr bool kBatched = true;
-  static constexpr bool kColSum = false;
-  __device__ __forceinline__ void select(int z, Operand& P, Operand& Q) {
-    const int64_t b = z / bm.inner, j = z % bm.inner;
-    P.ptr += b * bm.p_b + j * bm.p_j;
-    Q.ptr += b * bm.q_b + j * bm.q_j;
-    out += b * bm.o_b + j * bm.o_j;
-    klim = bm.k_total;
-    if (bm.k_total) klim -= (int64_t)z * bm.k_chunk;
-  }
-  __device__ __forceinline__ bool skip(int64_t m0, int64_t n0) const {
-    return tri_skip<CfgA::BM, CfgA::BN>(bm.tri, m0, n0);
-  }
-  __device__ __forceinline__ void k_window(int64_t m0, int64_t& kbeg, int64_t& kend) const {
-    tri_window<CfgA::BM>(bm.tri, m0, kbeg, kend);
-    if (bm.k_total) kend = min(kend, klim);
-  }
-  __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const {
-    out[m * ld + n] = acc;
     return 0.0f;
   }
   __device__ __forceinline__ void colsum(int, int64_t, float) const {}
@@ -369,27 +339,6 @@ __global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restr
   out[c] = S::from_f(s);
 }
 
-// Sum of the k-range partials of a k-split product, in range order, rounded
-// once: out[i] = round(sum_z part[z][i]) over n = M N elements (n % 4 == 0).
-template <class S>
-__global__ __launch_bounds__(256) void ksum_kernel(const float* __restrict__ part, int splits, int64_t n,
-                                                   typename S::T* __restrict__ out) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  float4 a = *reinterpret_cast<const float4*>(part + i);
-  for (int z = 1; z < splits; ++z) {
-    const float4 b = *reinterpret_cast<const float4*>(part + (int64_t)z * n + i);
-    a.x += b.x;
-    a.y += b.y;
-    a.z += b.z;
-    a.w += b.w;
-  }
-  uint2 w;
-  w.x = (uint32_t)S::from_f(a.x) | ((uint32_t)S::from_f(a.y) << 16);
-  w.y = (uint32_t)S::from_f(a.z) | ((uint32_t)S::from_f(a.w) << 16);
-  *reinterpret_cast<uint2*>(out + i) = w;
-}
-
 size_t a256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Longest sequence: a softmax row of 4096 keys is 64 fp32 values per lane.
@@ -405,22 +354,6 @@ hipError_t softmax_fwd(const float* sc, typename S::T* P, int64_t rows, int64_t 
   else if (s <= 2048) hipLaunchKernelGGL((softmax_fwd_kernel<S, 8>), grid, block, 0, st, sc, P, rows, s, scale, causal);
   else hipLaunchKernelGGL((softmax_fwd_kernel<S, 16>), grid, block, 0, st, sc, P, rows, s, scale, causal);
   return hipGetLastError();
-}
-
-// k-split of a product whose output tiles do not fill the chip: ranges of
-// whole 64-wide k-steps, enough of them for about two tiles per CU, at
-// most 8 and each at least 512 long.
-struct KSplit {
-  int splits;
-  int64_t chunk;
-};
-
-KSplit plan_ksplit(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = cdiv(M, CfgA::BM) * cdiv(N, CfgA::BN);
-  int sp = tiles >= 512 ? 1 : (int)std::min<int64_t>(8, cdiv(512, std::max<int64_t>(tiles, 1)));
-  while (sp > 1 && K < (int64_t)sp * 512) --sp;
-  const int64_t chunk = cdiv(cdiv(K, sp), 64) * 64;
-  return KSplit{(int)cdiv(K, chunk), chunk};
 }
 
 int check_attn_shape(const tpattn_shape* s) {
@@ -463,49 +396,30 @@ AttnDims dims(const tpattn_shape& sh) {
 }
 
 // Backward workspace: [D fp32 Z s][dS 16-bit Z s s][dO 16-bit T q]
-// [column partials of dQKV fp32 [T/256][3q]][k-split partials of dWo and
-// dWqkv fp32 (they run one after the other and share the room)].
+// [column partials of dQKV fp32 [T/256][3q]][k-split partials of the
+// projections' plain-store GEMMs (dO, dWo, dWqkv, dXp run one after the
+// other and share the room)].
 struct AttnBwdWs {
-  size_t drow_off, ds_off, do_off, part_off, ks_off, total;
+  size_t drow_off, ds_off, do_off, part_off, tail_off, tail_bytes, total;
   int part_blk;
-  KSplit ks_wo, ks_wqkv;
 };
 
-AttnBwdWs bwd_layout(const AttnDims& a) {
+AttnBwdWs bwd_layout(const AttnDims& a, int dtype) {
   AttnBwdWs w{};
   const size_t zss = (size_t)(a.Z * a.s * a.s);
+  const int64_t T3 = 3 * a.q;
   w.drow_off = 0;
   w.ds_off = a256((size_t)(a.Z * a.s) * 4);
   w.do_off = w.ds_off + a256(zss * 2);
   w.part_off = w.do_off + a256((size_t)(a.T * a.q) * 2);
   w.part_blk = (int)cdiv(a.T, 256);
-  w.ks_off = w.part_off + a256((size_t)w.part_blk * (size_t)(3 * a.q) * 4);
-  w.ks_wo = plan_ksplit(a.q, a.h, a.T);
-  w.ks_wqkv = plan_ksplit(a.h, 3 * a.q, a.T);
-  const size_t ks = std::max(w.ks_wo.splits > 1 ? (size_t)w.ks_wo.splits * (size_t)(a.q * a.h) * 4 : 0,
-                             w.ks_wqkv.splits > 1 ? (size_t)w.ks_wqkv.splits * (size_t)(a.h * 3 * a.q) * 4 : 0);
-  w.total = w.ks_off + a256(ks);
+  w.tail_off = w.part_off + a256((size_t)w.part_blk * (size_t)T3 * 4);
+  w.tail_bytes = std::max({planned_gemm_tail_bytes(dtype, a.T, a.q, a.h, true),
+                           planned_gemm_tail_bytes(dtype, a.q, a.h, a.T, false),
+                           planned_gemm_tail_bytes(dtype, a.h, T3, a.T, false),
+                           planned_gemm_tail_bytes(dtype, a.T, a.h, T3, true)});
+  w.total = w.tail_off + a256(w.tail_bytes);
   return w;
-}
-
-// C [M][N] (16-bit, row pitch N) = P^T Q with both operands mn-contiguous
-// (P[m][k] = p[k ldp + m], Q[k][n] = q[k ldq + n]), k-split by `ks` into
-// fp32 partials at `part` and summed in range order.
-template <class S>
-int gemm_mc_ksplit(int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, const void* q, int64_t ldq,
-                   typename S::T* out, const KSplit& ks, float* part, hipStream_t st) {
-  if (ks.splits <= 1) {
-    if (gemm<S, false, false>(M, N, K, p, ldp, q, ldq, EpiStore<S>{out, N}, 1, st) != hipSuccess)
-      return TPMLP_ERR_HIP;
-    return TPMLP_OK;
-  }
-  BatchMap bm{1, ks.chunk * ldp, 0, ks.chunk * ldq, 0, M * N, 0, kNone, K, ks.chunk};
-  if (gemm<S, false, false>(M, N, ks.chunk, p, ldp, q, ldq, EpiStoreF32Batched{part, N, bm}, ks.splits, st) !=
-      hipSuccess)
-    return TPMLP_ERR_HIP;
-  const int64_t n = M * N;
-  hipLaunchKernelGGL(ksum_kernel<S>, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, part, ks.splits, n, out);
-  return hipGetLastError() == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
 }
 
 struct Span2 {
@@ -543,14 +457,13 @@ int check_spans(const Span2* in, int n_in, const Span2* out, int n_out) {
   } while (0)
 
 template <class S>
-int attn_fwd_impl(const AttnDims& a, int causal, const void* X, const void* Wqkv, const void* bqkv, const void* Wo,
-                  void* QKV, void* P, void* O, void* Yp, void* ws, hipStream_t st) {
+int attn_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, const void* Wqkv, const void* bqkv,
+                  const void* Wo, void* QKV, void* P, void* O, void* Yp, void* ws, size_t ws_bytes, hipStream_t st) {
   using T = typename S::T;
   const int64_t T3 = 3 * a.q;
   const T* qkv = static_cast<const T*>(QKV);
   // QKV = X Wqkv + bqkv: P = X [T,h] k-contiguous, Q = Wqkv [h,3q] n-contiguous
-  ATTN_HIP((gemm<S, true, false>(a.T, T3, a.h, X, a.h, Wqkv, T3,
-                                 EpiBiasGelu<S>{(const T*)bqkv, (T*)QKV, nullptr, T3}, 1, st)));
+  ATTN_HIP(planned_gemm(dtype, true, false, a.T, T3, a.h, X, a.h, Wqkv, T3, QKV, T3, bqkv, nullptr, 0, st));
   // S_bj [query][key] in fp32, computed as S^T = K_bj Q_bj^T [key][query] and stored transposed:
   // P = K block [s,d] k-contiguous, Q[k=d][n=query] = Q_bj[n][k] k-contiguous
   const BatchMap sc{(int)a.n, a.s * T3, a.d, a.s * T3, a.d, a.n * a.s * a.s, a.s * a.s, causal ? kSkipLower : kNone};
@@ -561,18 +474,20 @@ int attn_fwd_impl(const AttnDims& a, int causal, const void* X, const void* Wqkv
   const BatchMap pv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * T3, a.d, a.s * a.q, a.d, causal ? kKeysUpTo : kNone};
   ATTN_HIP((gemm<S, true, false>(a.s, a.d, a.s, P, a.s, qkv + 2 * a.q, T3, EpiStoreBatched<S>{(T*)O, a.q, pv},
                                  (int)a.Z, st)));
-  // Yp = O Wo: P = O [T,q] k-contiguous, Q = Wo [q,h] n-contiguous
-  ATTN_HIP((gemm<S, true, false>(a.T, a.h, a.q, O, a.q, Wo, a.h, EpiStore<S>{(T*)Yp, a.h}, 1, st)));
+  // Yp = O Wo: P = O [T,q] k-contiguous, Q = Wo [q,h] n-contiguous; the scores' room (free now)
+  // takes the k-split partials if the plan has any and they fit
+  ATTN_HIP(planned_gemm(dtype, true, false, a.T, a.h, a.q, O, a.q, Wo, a.h, Yp, a.h, nullptr,
+                        static_cast<float*>(ws), ws_bytes, st));
   return TPMLP_OK;
 }
 
 template <class S>
-int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, const void* Wqkv, const void* Wo,
-                  const void* QKV, const void* P, const void* O, void* dQKV, void* dXp, void* dWqkv, void* dbqkv,
-                  void* dWo, void* ws, hipStream_t st) {
+int attn_bwd_impl(const AttnDims& a, int dtype, int causal, const void* dY, const void* X, const void* Wqkv,
+                  const void* Wo, const void* QKV, const void* P, const void* O, void* dQKV, void* dXp, void* dWqkv,
+                  void* dbqkv, void* dWo, void* ws, hipStream_t st) {
   using T = typename S::T;
   const int64_t T3 = 3 * a.q;
-  const AttnBwdWs w = bwd_layout(a);
+  const AttnBwdWs w = bwd_layout(a, dtype);
   char* wsb = static_cast<char*>(ws);
   float* drow = reinterpret_cast<float*>(wsb + w.drow_off);
   T* ds = reinterpret_cast<T*>(wsb + w.ds_off);
@@ -580,14 +495,12 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
   float* part = reinterpret_cast<float*>(wsb + w.part_off);
   const T* qkv = static_cast<const T*>(QKV);
   T* dqkv = static_cast<T*>(dQKV);
+  float* tail = reinterpret_cast<float*>(wsb + w.tail_off);
   // dO = dY Wo^T: Q[k=h][n=q] = Wo[n][k] k-contiguous
-  ATTN_HIP((gemm<S, true, true>(a.T, a.q, a.h, dY, a.h, Wo, a.h, EpiStore<S>{dO, a.q}, 1, st)));
-  // dWo = O^T dY: P[m=q][k=T] = O[k][m], Q = dY [T,h]: both mn-contiguous (k-split over tokens)
-  float* ksp = reinterpret_cast<float*>(wsb + w.ks_off);
-  {
-    const int rc = gemm_mc_ksplit<S>(a.q, a.h, a.T, O, a.q, dY, a.h, static_cast<T*>(dWo), w.ks_wo, ksp, st);
-    if (rc != TPMLP_OK) return rc;
-  }
+  ATTN_HIP(planned_gemm(dtype, true, true, a.T, a.q, a.h, dY, a.h, Wo, a.h, dO, a.q, nullptr, tail, w.tail_bytes, st));
+  // dWo = O^T dY: P[m=q][k=T] = O[k][m], Q = dY [T,h]: both mn-contiguous
+  ATTN_HIP(planned_gemm(dtype, false, false, a.q, a.h, a.T, O, a.q, dY, a.h, dWo, a.h, nullptr, tail, w.tail_bytes,
+                        st));
   // dV_bj = P_bj^T dO_bj: P[m=key][k=query] = P_bj[k][m], Q = dO block: both mn-contiguous
   const BatchMap dv{(int)a.n, a.n * a.s * a.s, a.s * a.s, a.s * a.q, a.d, a.s * T3, a.d,
                     causal ? kQueriesFrom : kNone};
@@ -618,13 +531,12 @@ int attn_bwd_impl(const AttnDims& a, int causal, const void* dY, const void* X, 
   hipLaunchKernelGGL(colsum_finish_kernel<S>, dim3((unsigned)cdiv(T3, 256)), dim3(256), 0, st, part, w.part_blk, T3,
                      static_cast<T*>(dbqkv));
   ATTN_HIP(hipGetLastError());
-  // dWqkv = X^T dQKV: P[m=h][k=T] = X[k][m], Q = dQKV [T,3q]: both mn-contiguous (k-split over tokens)
-  {
-    const int rc = gemm_mc_ksplit<S>(a.h, T3, a.T, X, a.h, dQKV, T3, static_cast<T*>(dWqkv), w.ks_wqkv, ksp, st);
-    if (rc != TPMLP_OK) return rc;
-  }
+  // dWqkv = X^T dQKV: P[m=h][k=T] = X[k][m], Q = dQKV [T,3q]: both mn-contiguous
+  ATTN_HIP(planned_gemm(dtype, false, false, a.h, T3, a.T, X, a.h, dQKV, T3, dWqkv, T3, nullptr, tail, w.tail_bytes,
+                        st));
   // dXp = dQKV Wqkv^T: P = dQKV k-contiguous, Q[k=3q][n=h] = Wqkv[n][k] k-contiguous
-  ATTN_HIP((gemm<S, true, true>(a.T, a.h, T3, dQKV, T3, Wqkv, T3, EpiStore<S>{(T*)dXp, a.h}, 1, st)));
+  ATTN_HIP(planned_gemm(dtype, true, true, a.T, a.h, T3, dQKV, T3, Wqkv, T3, dXp, a.h, nullptr, tail, w.tail_bytes,
+                        st));
   return TPMLP_OK;
 }
 
@@ -643,7 +555,7 @@ size_t tp_attn_fwd_workspace_bytes(const tpattn_shape* shape) {
 
 size_t tp_attn_bwd_workspace_bytes(const tpattn_shape* shape) {
   if (check_attn_shape(shape) != TPMLP_OK) return 0;
-  return bwd_layout(dims(*shape)).total;
+  return bwd_layout(dims(*shape), shape->dtype).total;
 }
 
 int tp_attn_fwd(const tpattn_shape* shape, const void* X, const void* Wqkv, const void* bqkv, const void* Wo,
@@ -661,8 +573,8 @@ int tp_attn_fwd(const tpattn_shape* shape, const void* X, const void* Wqkv, cons
   if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (shape->dtype == TPMLP_F16)
-    return attn_fwd_impl<StoreF16>(a, shape->causal, X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, st);
-  return attn_fwd_impl<StoreBF16>(a, shape->causal, X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, st);
+    return attn_fwd_impl<StoreF16>(a, shape->dtype, shape->causal, X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, need, st);
+  return attn_fwd_impl<StoreBF16>(a, shape->dtype, shape->causal, X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, need, st);
 }
 
 int tp_attn_bwd(const tpattn_shape* shape, const void* dY, const void* X, const void* Wqkv, const void* Wo,
@@ -683,10 +595,10 @@ int tp_attn_bwd(const tpattn_shape* shape, const void* dY, const void* X, const 
   if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (shape->dtype == TPMLP_F16)
-    return attn_bwd_impl<StoreF16>(a, shape->causal, dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws,
-                                   st);
-  return attn_bwd_impl<StoreBF16>(a, shape->causal, dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws,
-                                  st);
+    return attn_bwd_impl<StoreF16>(a, shape->dtype, shape->causal, dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv,
+                                   dbqkv, dWo, ws, st);
+  return attn_bwd_impl<StoreBF16>(a, shape->dtype, shape->causal, dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv,
+                                  dbqkv, dWo, ws, st);
 }
 
 }  // extern "C"

@@ -25,6 +25,7 @@
 #include "gemm_mfma.hpp"
 #include "gemm_simt.hpp"
 #include "reduce.hpp"
+#include "shard_gemm.hpp"
 #include "transpose.hpp"
 
 namespace tpmlp {
@@ -642,6 +643,44 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
 }
 
 }  // namespace
+
+template <class S, bool PK, bool QK>
+static hipError_t planned_gemm_t(int dtype, int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp,
+                                 const void* q, int64_t ldq, void* out, int64_t ldo, const void* bias,
+                                 float* tail_ws, size_t tail_cap, hipStream_t st) {
+  using T = typename S::T;
+  if (bias)
+    return run_gemm<S, PK, QK, false>(dtype, M, N, K, p, ldp, q, ldq,
+                                      EpiBiasGelu<S>{static_cast<const T*>(bias), static_cast<T*>(out), nullptr, ldo},
+                                      st);
+  return run_gemm<S, PK, QK, false>(dtype, M, N, K, p, ldp, q, ldq, EpiStore<S>{static_cast<T*>(out), ldo}, st,
+                                    tail_ws, tail_cap);
+}
+
+template <class S>
+static hipError_t planned_gemm_s(int dtype, bool pk, bool qk, int64_t M, int64_t N, int64_t K, const void* p,
+                                 int64_t ldp, const void* q, int64_t ldq, void* out, int64_t ldo, const void* bias,
+                                 float* tail_ws, size_t tail_cap, hipStream_t st) {
+  if (pk && qk) return planned_gemm_t<S, true, true>(dtype, M, N, K, p, ldp, q, ldq, out, ldo, bias, tail_ws, tail_cap, st);
+  if (pk) return planned_gemm_t<S, true, false>(dtype, M, N, K, p, ldp, q, ldq, out, ldo, bias, tail_ws, tail_cap, st);
+  if (qk) return planned_gemm_t<S, false, true>(dtype, M, N, K, p, ldp, q, ldq, out, ldo, bias, tail_ws, tail_cap, st);
+  return planned_gemm_t<S, false, false>(dtype, M, N, K, p, ldp, q, ldq, out, ldo, bias, tail_ws, tail_cap, st);
+}
+
+hipError_t planned_gemm(int dtype, bool pk, bool qk, int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp,
+                        const void* q, int64_t ldq, void* out, int64_t ldo, const void* bias, float* tail_ws,
+                        size_t tail_cap, hipStream_t st) {
+  if (dtype == TPMLP_F16)
+    return planned_gemm_s<StoreF16>(dtype, pk, qk, M, N, K, p, ldp, q, ldq, out, ldo, bias, tail_ws, tail_cap, st);
+  if (dtype == TPMLP_BF16)
+    return planned_gemm_s<StoreBF16>(dtype, pk, qk, M, N, K, p, ldp, q, ldq, out, ldo, bias, tail_ws, tail_cap, st);
+  return hipErrorInvalidValue;
+}
+
+size_t planned_gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K, bool kc) {
+  return gemm_tail_bytes(dtype, M, N, K, kc);
+}
+
 }  // namespace tpmlp
 
 using namespace tpmlp;

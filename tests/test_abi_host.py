@@ -348,8 +348,10 @@ def test_attention_workspace_sizes_and_validation(lib):
     Z = 32 * 2048 * 2048
     assert fws(big) == Z * 4
     # D fp32 [32][2048], dS bf16, dO [8192, 640], column partials [8192 / 256][1920] fp32, then the k-split
-    # partials: dWo (5 x 20 tiles of 128 x 128) in 6 token ranges of 1408, dWqkv (20 x 15 tiles) in 2 of 4096
-    ks = max(6 * 640 * 2560 * 4, 2 * 2560 * 1920 * 4)
+    # partials of the projections, sized by the largest: dO = dY Wo^T is 32 x 2 tiles of 256 x 320 (less than
+    # half a wave, K = 2560), each split into 4 k-ranges (dWo: 3 x 10 tiles of 256 x 256 in 4 ranges;
+    # dWqkv: 10 x 8 in 3; dXp: one full wave of 256 x 320, no split)
+    ks = max(64 * 4 * 256 * 320 * 4, 30 * 4 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
     assert bws(big) == 32 * 2048 * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
     assert fws(sh(4, 2048, 2560, 8, 80, 0)) == 0          # fp32 storage is not supported
     assert fws(sh(4, 2044, 2560, 8, 80, 2)) == 0          # seq not a multiple of 8
