@@ -314,3 +314,21 @@ def test_epilogue_rounding_is_nearest_even(gpu_lib, dtype):
         assert not bad.any(), (name, list(zip(z[bad][:5], g[bad][:5], exact[bad][:5])))
         well = z >= -3.0
         assert np.mean(g[well] == r[well]) > 0.99, name
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,h,f,keep_dz", [(2048, 1024, 1024, True), (2056, 1032, 1048, False)])
+def test_sub_wave_k_split(gpu_lib, dtype, T, h, f, keep_dz):
+    """Weight gradients with few output tiles and a long reduction (T >= 2048
+    tokens): 16-25 tiles of 256 x 256, every tile split into 4 k-ranges
+    whose fp32 partials are summed in a fixed order (the ragged case ends in
+    a short last range). Against the oracle, and bitwise run to run."""
+    import torch
+    print(f"case sub-wave k-split dtype={dtype} T={T} h={h} f={f}", flush=True)
+    inp = synth.draw_inputs(T, h, f, dtype, seed=T + f, sigma_dy=1.0)
+    dev = device_inputs(inp)
+    out = run_shard(gpu_lib, *dev, keep_dz=keep_dz)
+    compare(out, _oracle_shard(inp), TOL[dtype])
+    again = run_shard(gpu_lib, *dev, keep_dz=keep_dz)
+    for k in ("dA", "dB", "dXp", "db1"):
+        assert torch.equal(out[k], again[k]), k
