@@ -368,6 +368,7 @@ int check_attn_shape(const tpattn_shape* s) {
   const int64_t pairs = s->batch * s->heads;
   if (pairs > 65535 || (double)pairs * (double)s->seq * (double)s->seq >= 1099511627776.0) return TPMLP_ERR_SHAPE;
   if (cdiv(T, 256) > 65535) return TPMLP_ERR_SHAPE;  // grid y of the column-sum pass
+  if (cdiv(T * s->heads, 256) > INT32_MAX) return TPMLP_ERR_SHAPE;  // grid of the row terms (one thread per token, head)
   if (s->seq > kMaxSeq) return TPMLP_ERR_SHAPE;      // softmax rows are held in registers
   // tile counts of the largest launches fit the 31-bit grid
   if (cdiv(T, 128) * cdiv(std::max<int64_t>(3 * q, s->hidden), 128) > INT32_MAX / 2 ||
