@@ -56,12 +56,17 @@ struct EpiApply4<E, std::void_t<decltype(E::kApply4)>> : std::integral_constant<
 // An apply4 epilogue that also reads an input at the output positions
 // (kFetch4 = true) splits the read off: fetch4(m, n) returns what
 // apply4(m, n, v, fetched) needs. The kernel issues every fetch of the tile
-// before the first store, since the compiler cannot move a load above a store
-// to memory it cannot prove distinct.
+// before its k-loop (the reads do not depend on the product), and so before
+// the first store, which the compiler could not move them above.
 template <class E, class = void>
 struct EpiFetch4 : std::false_type {};
 template <class E>
 struct EpiFetch4<E, std::void_t<decltype(E::kFetch4)>> : std::integral_constant<bool, E::kFetch4> {};
+struct NoFetchEpi {
+  struct Fetched {};
+};
+template <class E>
+using FetchedOf = typename std::conditional_t<EpiFetch4<E>::value, E, NoFetchEpi>::Fetched;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct MfmaTile {
@@ -192,6 +197,19 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, O
     epi.k_window(m0, kbeg, kend);
   }
   const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
+  // An epilogue's reads of its own input do not depend on the product: they
+  // are issued here, ahead of the k-loop, and land while it runs.
+  FetchedOf<Epi> fe[Cfg::FM][Cfg::FN];
+  if constexpr (EpiFetch4<Epi>::value) {
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int64_t n = n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
+        const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
+        if (m < sh.M && n < sh.N) fe[i][j] = epi.fetch4(m, n);
+      }
+  }
 
   f32x4 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -253,15 +271,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, O
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) cs[j] = 0.0f;
   if constexpr (EpiFetch4<Epi>::value) {
-    typename Epi::Fetched fe[Cfg::FM][Cfg::FN];
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) {
-        const int64_t n = n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
-        const int64_t m = m0 + wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
-        if (m < sh.M && n < sh.N) fe[i][j] = epi.fetch4(m, n);
-      }
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
