@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 6
+#define TPMLP_ABI_VERSION 7
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -254,6 +254,29 @@ int tp_mlp_bwd_main_grad(const tpmlp_shape* shape,
                          void* dZ, void* dXp, float* dA_main, float* dB_main, float* db1_main,
                          void* ws, size_t ws_bytes,
                          void* stream, void* const* events);
+
+/*
+ * Gradient of the second bias b2, which the caller adds once after the sum
+ * over ranks (so its gradient is the same on every rank, from the replicated
+ * dY): db2[c] = sum over tokens t of dY[t][c]. The pages accumulate weight
+ * gradients over micro-batches in fp32 master copies ("Training GPT-2 with
+ * Megatron-LM", section 4.3; "Megatron-LM overview", section 3.1), hence
+ * the accumulate form.
+ *   dY   [tokens, hidden]   in
+ *   db2  [hidden]           out: with accumulate == 0, in the storage dtype,
+ *                           rounded once from the fp32 sum; with accumulate
+ *                           != 0, an fp32 main gradient, db2 += the fp32 sum
+ *   ws, ws_bytes            at least tp_mlp_db2_workspace_bytes (fp32
+ *                           partial sums per 256 tokens; 0 for fp32 storage);
+ *                           may be NULL when that is 0
+ * The sum runs in a fixed order (256-token blocks, then blocks in order):
+ * bitwise deterministic. tokens may be 0 (db2 = 0, or unchanged when
+ * accumulating); more than 65535 x 256 tokens is TPMLP_ERR_SHAPE.
+ * ffn_shard is not used but must be valid.
+ */
+size_t tp_mlp_db2_workspace_bytes(const tpmlp_shape* shape);
+int tp_mlp_db2(const tpmlp_shape* shape, const void* dY, void* db2, int accumulate, void* ws, size_t ws_bytes,
+               void* stream);
 
 /*
  * Sum over ranks of the row-parallel partials, for P ranks whose partials

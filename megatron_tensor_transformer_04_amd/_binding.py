@@ -25,6 +25,7 @@ STATUS = {
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
            "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
+           "tp_mlp_db2_workspace_bytes", "tp_mlp_db2",
            "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd")
 TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL, TPMLP_WS_RECOMPUTE = 1, 2, 4
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_reduce_partials.restype = ctypes.c_int
     lib.tp_mlp_reduce_partials.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int, ctypes.POINTER(vp), vp,
                                            ctypes.c_int64, ctypes.c_int64, vp, vp]
+    lib.tp_mlp_db2_workspace_bytes.restype = sz
+    lib.tp_mlp_db2_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape)]
+    lib.tp_mlp_db2.restype = ctypes.c_int
+    lib.tp_mlp_db2.argtypes = [ctypes.POINTER(tpmlp_shape), vp, vp, ctypes.c_int, vp, sz, vp]
     ap = ctypes.POINTER(tpattn_shape)
     lib.tp_attn_fwd_workspace_bytes.restype = sz
     lib.tp_attn_fwd_workspace_bytes.argtypes = [ap]
@@ -241,6 +246,35 @@ def tp_mlp_reduce_partials(parts, bias, out, row_begin: int = 0, row_end=None, *
     arr = (ctypes.c_void_p * max(len(parts), 1))(*[_ptr(p) for p in parts])
     _check(load().tp_mlp_reduce_partials(ctypes.byref(s), len(parts), arr, _ptr(bias), int(row_begin), int(row_end),
                                          _ptr(out), _stream(stream)))
+
+
+def tp_mlp_db2_workspace_bytes(tokens: int, hidden: int, dtype: int) -> int:
+    s = shape_of(tokens, hidden, 8 if dtype != TPMLP_F32 else 4, dtype)
+    return load().tp_mlp_db2_workspace_bytes(ctypes.byref(s))
+
+
+def tp_mlp_db2(dY, db2, ws=None, *, accumulate: bool = False, stream=None) -> None:
+    """db2 = column sums of dY [T, h] (storage dtype), or db2 += them when
+    `accumulate` (db2 an fp32 main gradient)."""
+    import torch
+    if accumulate and db2.dtype != torch.float32:
+        raise TypeError("an accumulated db2 is a float32 main gradient")
+    T, h = dY.shape
+    code = _dtype_code(dY)
+    s = shape_of(T, h, 8 if code != TPMLP_F32 else 4, code)
+    _check(load().tp_mlp_db2(ctypes.byref(s), _ptr(dY), _ptr(db2), 1 if accumulate else 0, _ptr(ws), _nbytes(ws),
+                             _stream(stream)))
+
+
+def db2(dY, stream=None):
+    """Allocate db2 (and the workspace) with torch and run tp_mlp_db2."""
+    import torch
+    T, h = dY.shape
+    out = torch.empty((h,), dtype=dY.dtype, device=dY.device)
+    n = tp_mlp_db2_workspace_bytes(T, h, _dtype_code(dY))
+    ws = torch.empty((n,), dtype=torch.uint8, device=dY.device) if n else None
+    tp_mlp_db2(dY, out, ws, stream=stream)
+    return out
 
 
 # ---- convenience wrappers that allocate the outputs with torch ----

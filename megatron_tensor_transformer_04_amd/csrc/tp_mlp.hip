@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "tp_mlp.h"
+#include "colsum.hpp"
 #include "epilogues.hpp"
 #include "gemm_dma.hpp"
 #include "gemm_mfma.hpp"
@@ -50,6 +51,18 @@ __global__ __launch_bounds__(256) void db1_accum_kernel(const float* partial, in
   float s = 0.0f;
   for (int t = 0; t < tiles_m; ++t) s += partial[(int64_t)t * f + n];
   db1_main[n] += s;
+}
+
+// Column sums of an fp32 [rows][cols] matrix, one thread per column, rows in
+// order (the fp32 storage type's db2; its workloads are small).
+template <bool ACC>
+__global__ __launch_bounds__(256) void colsum_f32_kernel(const float* m, int64_t rows, int64_t cols, float* out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.0f;
+  for (int64_t r = 0; r < rows; ++r) s += m[r * cols + c];
+  if constexpr (ACC) out[c] += s;
+  else out[c] = s;
 }
 
 enum class Engine { Simt, Mfma128, Mfma256, Dma256, Dma320 };
@@ -829,6 +842,59 @@ int tp_mlp_bwd_recompute(const tpmlp_shape* shape, const void* dY, const void* X
       return bwd_impl<StoreBF16, false>(s, dY, X, A, B, Z, nullptr, dZ, dXp, dA, dB, db1, w, wsb + r.bytes, rest,
                                         st, ev_b);
   }
+}
+
+size_t tp_mlp_db2_workspace_bytes(const tpmlp_shape* shape) {
+  if (check_shape(shape) != TPMLP_OK || shape->dtype == TPMLP_F32) return 0;
+  return (size_t)ceil_div(shape->tokens, 256) * (size_t)shape->hidden * sizeof(float);
+}
+
+int tp_mlp_db2(const tpmlp_shape* shape, const void* dY, void* db2, int accumulate, void* ws, size_t ws_bytes,
+               void* stream) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  if (ceil_div(s.tokens, 256) > 65535) return TPMLP_ERR_SHAPE;  // grid y of the first pass
+  const size_t e = elt_size(s.dtype);
+  const size_t need = tp_mlp_db2_workspace_bytes(shape);
+  const size_t ob = (size_t)s.hidden * (accumulate ? sizeof(float) : e);
+  const Span in[1] = {{dY, (size_t)(s.tokens * s.hidden) * e}};
+  const bool in_req[1] = {true};
+  const Span out[2] = {{db2, ob}, {ws, std::min(need, ws_bytes)}};
+  const bool out_req[2] = {true, need > 0};
+  TPMLP_TRY(check_buffers(in, 1, in_req, out, 2, out_req));
+  if (ws_bytes < need) return TPMLP_ERR_WORKSPACE;
+  if (s.hidden == 0) return TPMLP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned gx = (unsigned)ceil_div(s.hidden, 256);
+  if (s.dtype == TPMLP_F32) {
+    if (accumulate)
+      hipLaunchKernelGGL(colsum_f32_kernel<true>, dim3(gx), dim3(256), 0, st, static_cast<const float*>(dY), s.tokens,
+                         s.hidden, static_cast<float*>(db2));
+    else
+      hipLaunchKernelGGL(colsum_f32_kernel<false>, dim3(gx), dim3(256), 0, st, static_cast<const float*>(dY),
+                         s.tokens, s.hidden, static_cast<float*>(db2));
+    return hipGetLastError() == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
+  }
+  const int nblk = (int)ceil_div(s.tokens, 256);
+  float* part = static_cast<float*>(ws);
+  if (nblk > 0) {
+    if (s.dtype == TPMLP_F16)
+      hipLaunchKernelGGL(colsum_part_kernel<StoreF16>, dim3(gx, (unsigned)nblk), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(dY), s.tokens, s.hidden, part);
+    else
+      hipLaunchKernelGGL(colsum_part_kernel<StoreBF16>, dim3(gx, (unsigned)nblk), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(dY), s.tokens, s.hidden, part);
+    TPMLP_HIP(hipGetLastError());
+  }
+  if (accumulate)
+    hipLaunchKernelGGL(colsum_accum_kernel, dim3(gx), dim3(256), 0, st, part, nblk, s.hidden, static_cast<float*>(db2));
+  else if (s.dtype == TPMLP_F16)
+    hipLaunchKernelGGL(colsum_finish_kernel<StoreF16>, dim3(gx), dim3(256), 0, st, part, nblk, s.hidden,
+                       static_cast<uint16_t*>(db2));
+  else
+    hipLaunchKernelGGL(colsum_finish_kernel<StoreBF16>, dim3(gx), dim3(256), 0, st, part, nblk, s.hidden,
+                       static_cast<uint16_t*>(db2));
+  return hipGetLastError() == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
 }
 
 int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* const* parts, const void* bias,

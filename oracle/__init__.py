@@ -21,6 +21,7 @@ from .attn import (
 )
 from .mlp import (
     GELU_C,
+    bias2_grad,
     SQRT_2_OVER_PI,
     gelu,
     gelu_grad,
@@ -44,6 +45,7 @@ __all__ = [
     "attn_shard_backward",
     "softmax_rows",
     "GELU_C",
+    "bias2_grad",
     "SQRT_2_OVER_PI",
     "gelu",
     "gelu_grad",

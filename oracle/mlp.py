@@ -65,6 +65,13 @@ def mlp_forward(X, A, b1, B, b2=None):
     return {"Z": Z, "H": H, "Y": Y}
 
 
+def bias2_grad(dY):
+    """Gradient of the second bias: Y = H B + 1 b2^T, so dL/db2 = sum over
+    tokens of dY (the same on every rank, since b2 is added once after the
+    sum over ranks and dY is replicated)."""
+    return np.asarray(dY, dtype=np.float64).sum(axis=0)
+
+
 def mlp_backward(X, A, b1, B, dY, Z=None):
     """Backward of the MLP for a given output gradient dY [T,h].
 
@@ -82,7 +89,7 @@ def mlp_backward(X, A, b1, B, dY, Z=None):
     dA = X.T @ dZ
     db1 = dZ.sum(axis=0)
     dX = dZ @ A.T
-    db2 = dY.sum(axis=0)
+    db2 = bias2_grad(dY)
     return {"dZ": dZ, "dH": dH, "dA": dA, "db1": db1, "dB": dB, "dX": dX, "db2": db2}
 
 

@@ -44,7 +44,8 @@ def test_exports_every_declared_function(lib):
     declared = _declared_functions()
     assert set(declared) == {"tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes",
                              "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad",
-                             "tp_mlp_bwd_recompute", "tp_mlp_reduce_partials", "tp_attn_fwd_workspace_bytes",
+                             "tp_mlp_bwd_recompute", "tp_mlp_reduce_partials", "tp_mlp_db2_workspace_bytes",
+                             "tp_mlp_db2", "tp_attn_fwd_workspace_bytes",
                              "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd"}
     raw = ctypes.CDLL(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "libtpmlp.so"))
     for name in declared:
@@ -378,3 +379,24 @@ def test_attention_workspace_sizes_and_validation(lib):
     alias = list(fake)
     alias[4] = fake[0]                                                            # QKV on top of X
     assert lib.tp_attn_fwd(ctypes.byref(ok), *alias, ws, 1 << 20, None) == 7
+
+
+def test_db2_workspace_and_validation(lib):
+    """tp_mlp_db2: fp32 partial sums per 256 tokens for 16-bit storage, none
+    for fp32; checks that return before any launch."""
+    from megatron_tensor_transformer_04_amd._binding import tpmlp_shape
+    wsb = lambda T, h, dt: lib.tp_mlp_db2_workspace_bytes(ctypes.byref(tpmlp_shape(T, h, 8, dt)))
+    assert wsb(16384, 10240, 2) == 64 * 10240 * 4
+    assert wsb(200, 136, 1) == 1 * 136 * 4
+    assert wsb(0, 136, 1) == 0 and wsb(64, 128, 0) == 0
+    assert wsb(64, 12, 2) == 0  # hidden not a multiple of 8: invalid shape
+    ok = tpmlp_shape(64, 128, 8, 2)
+    dY, out, ws = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)
+    assert lib.tp_mlp_db2(ctypes.byref(ok), None, out, 0, ws, 1024, None) == 1       # dY NULL
+    assert lib.tp_mlp_db2(ctypes.byref(ok), dY, None, 0, ws, 1024, None) == 1        # db2 NULL
+    assert lib.tp_mlp_db2(ctypes.byref(ok), dY, out, 0, None, 0, None) == 5          # no workspace: too small
+    assert lib.tp_mlp_db2(ctypes.byref(ok), dY, out, 0, ws, 16, None) == 5           # workspace too small
+    assert lib.tp_mlp_db2(ctypes.byref(ok), dY, ctypes.c_void_p(0x10008), 0, ws, 1024, None) == 3  # unaligned
+    assert lib.tp_mlp_db2(ctypes.byref(ok), dY, ctypes.c_void_p(0x10000 + 4096), 0, ws, 1024, None) == 7  # in dY
+    big = tpmlp_shape(65536 * 256, 8, 8, 2)
+    assert lib.tp_mlp_db2(ctypes.byref(big), dY, out, 0, ws, 1 << 30, None) == 2

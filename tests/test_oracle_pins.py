@@ -260,3 +260,26 @@ def test_rel_err_definition():
     assert oracle.rel_err(np.array([1.0, 2.0]), np.array([1.0, 4.0])) == 0.5
     assert oracle.rel_err(np.zeros(0), np.zeros(0)) == 0.0
     assert oracle.rel_err(np.array([0.5]), np.array([0.0])) == 0.5
+
+
+def test_second_bias_gradient():
+    """db2 of the full MLP (with b2): against torch float64 autograd, a
+    directional finite difference of <dY, Y> along b2, and a scalar loop."""
+    import torch
+    rng = np.random.default_rng(17)
+    T, h, F = 6, 5, 7
+    X, A, b1, B, dY = (rng.standard_normal(s) for s in ((T, h), (h, F), (F,), (F, h), (T, h)))
+    b2 = rng.standard_normal(h)
+    g = oracle.mlp_backward(X, A, b1, B, dY)["db2"]
+    assert np.array_equal(g, oracle.bias2_grad(dY))
+    tb2 = torch.tensor(b2, requires_grad=True)
+    Y = torch.nn.functional.gelu(torch.tensor(X) @ torch.tensor(A) + torch.tensor(b1), approximate="tanh") \
+        @ torch.tensor(B) + tb2
+    (Y * torch.tensor(dY)).sum().backward()
+    assert np.max(np.abs(tb2.grad.numpy() - g)) <= 1e-12
+    D, eps = rng.standard_normal(h), 1e-6
+    L = lambda bb: float(np.sum(dY * oracle.mlp_forward(X, A, b1, B, b2=bb)["Y"]))
+    fd = (L(b2 + eps * D) - L(b2 - eps * D)) / (2 * eps)
+    assert abs(fd - float(g @ D)) <= 1e-7 * max(1.0, abs(fd))
+    loop = [sum(dY[t][c] for t in range(T)) for c in range(h)]
+    assert np.max(np.abs(np.array(loop) - g)) <= 1e-12
