@@ -182,9 +182,24 @@ def config_rate(tpmlp, name, dev, steps=10, warmup=3):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    tflops = 12.0 * T * h * f / (ms * 1e-3) / 1e12
+    # cold caches: a 512 MiB buffer (twice the MALL) is written between steps, each step timed alone
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(5):
+        flush.fill_(1)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        z.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(z))
+    del flush
+    cold_ms = sorted(cold)[len(cold) // 2]
+    flops = 12.0 * T * h * f
+    tflops = flops / (ms * 1e-3) / 1e12
     return {"workload": workload_name(cfg), "dtype": cfg.dtype, "ms_per_step": round(ms, 4),
-            "tflops": round(tflops, 2), "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[cfg.dtype], 2)}
+            "tflops": round(tflops, 2), "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
+            "cold_ms_per_step": round(cold_ms, 4), "cold_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2)}
 
 
 def attention_cpu_baseline(inp, cfg, flops_per_call, target_s=8.0, max_calls=4):
@@ -386,6 +401,10 @@ def main():
             per[n] += bev[k][i].elapsed_time(bev[k][i + 1])
     per = {n: v / K for n, v in per.items()}
     gpu_ms = fev[0][0].elapsed_time(bev[K - 1][len(bwd_steps)]) / K
+    fwd_each = [fev[k][0].elapsed_time(fev[k][len(FWD_STEPS)]) for k in range(K)]
+    bwd_each = [bev[k][0].elapsed_time(bev[k][len(bwd_steps)]) for k in range(K)]
+    step_each = sorted(a + b for a, b in zip(fwd_each, bwd_each))
+    med = lambda v: sorted(v)[len(v) // 2]
     ms = wall / K * 1e3
     flops = 12.0 * T * h * f
     value = flops / (ms * 1e-3) / 1e12
@@ -421,6 +440,10 @@ def main():
         "pct_of_peak": round(100.0 * value / peak, 2),
         "peak_tflops": peak,
         "gpu_ms_per_step": round(gpu_ms, 4),
+        "step_ms_median": round(med(step_each), 4),
+        "step_ms_min": round(step_each[0], 4),
+        "fwd_ms_median": round(med(fwd_each), 4),
+        "bwd_ms_median": round(med(bwd_each), 4),
         "kernel_ms": {n: round(v, 4) for n, v in per.items()},
         "roofline": {
             "kernel": dom,
