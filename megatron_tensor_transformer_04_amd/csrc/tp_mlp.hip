@@ -32,25 +32,29 @@
 namespace tpmlp {
 namespace {
 
-// Sum of the per-tile fp32 column partials in tile order, rounded once.
-template <class S>
-__global__ __launch_bounds__(256) void db1_finish_kernel(const float* partial, int tiles_m, int64_t f,
-                                                         typename S::T* db1) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= f) return;
+// Sum of the per-tile fp32 column partials [tiles_m][f], in a fixed order:
+// a block of 256 threads covers 32 columns; thread (g, c) adds the tiles
+// t = g, g + 8, g + 16, ... of column c in increasing t, then the 8 groups
+// are added in group order. With ACC the sum is added to an fp32 main
+// gradient (beta = 1); otherwise it is rounded once. Both forms add in the
+// same order, so rounding the accumulated form (from zero) gives the other.
+template <class S, bool ACC>
+__global__ __launch_bounds__(256) void db1_finish_kernel(const float* partial, int tiles_m, int64_t f, void* db1) {
+  __shared__ float red[8][32];
+  const int c = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int64_t n = (int64_t)blockIdx.x * 32 + c;
   float s = 0.0f;
-  for (int t = 0; t < tiles_m; ++t) s += partial[(int64_t)t * f + n];
-  db1[n] = S::from_f(s);
-}
-
-// The same sum, added to an fp32 main gradient (beta = 1).
-__global__ __launch_bounds__(256) void db1_accum_kernel(const float* partial, int tiles_m, int64_t f,
-                                                        float* db1_main) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= f) return;
-  float s = 0.0f;
-  for (int t = 0; t < tiles_m; ++t) s += partial[(int64_t)t * f + n];
-  db1_main[n] += s;
+  if (n < f)
+    for (int t = g; t < tiles_m; t += 8) s += partial[(int64_t)t * f + n];
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && n < f) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v += red[k][c];
+    if constexpr (ACC) static_cast<float*>(db1)[n] += v;
+    else static_cast<typename S::T*>(db1)[n] = S::from_f(v);
+  }
 }
 
 // Column sums of an fp32 [rows][cols] matrix, one thread per column, rows in
@@ -592,12 +596,8 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
   TPMLP_TRY(record(ev, 1, st));
   // B5: db1 = sum of the column partials
   if (f > 0) {
-    if constexpr (ACC)
-      hipLaunchKernelGGL(db1_accum_kernel, dim3((unsigned)ceil_div(f, 256)), dim3(256), 0, st, part, w.part_tiles,
-                         f, static_cast<float*>(db1));
-    else
-      hipLaunchKernelGGL((db1_finish_kernel<S>), dim3((unsigned)ceil_div(f, 256)), dim3(256), 0, st, part,
-                         w.part_tiles, f, (T*)db1);
+    hipLaunchKernelGGL((db1_finish_kernel<S, ACC>), dim3((unsigned)ceil_div(f, 32)), dim3(256), 0, st, part,
+                       w.part_tiles, f, db1);
     TPMLP_HIP(hipGetLastError());
   }
   TPMLP_TRY(record(ev, 2, st));
