@@ -115,14 +115,20 @@ int64_t wave_cost(int64_t M, int64_t N, int bm, int bn) {
 // shards' GEMMs), unless it is a long reduction that the k-split below
 // spreads over the chip.
 constexpr int64_t kDmaMinTiles = 192;
-// Reductions at least this long may split a sub-wave launch into k-ranges.
+// Reductions at least this long may split a sub-wave launch into k-ranges:
+// up to four, or up to eight for reductions of kSubWaveLongK or more (the
+// fp32 partials cost parts x tile bytes each way, which a long reduction's
+// ranges amortise; measured on MI355X: eight ranges of K = 4096 GEMMs were
+// slower than four, of K = 8192 ones faster).
 constexpr int64_t kSubWaveSplitK = 2048;
+constexpr int64_t kSubWaveLongK = 8192;
+int subwave_max_parts(int64_t K) { return K >= kSubWaveLongK ? 8 : 4; }
 
 // k-ranges per tile of a launch of `ntile` tiles that plan_tail splits as a
 // sub-wave launch (1 if it does not).
 int subwave_parts(int64_t ntile, int64_t K) {
   if (ntile > kCUs / 2 || K < kSubWaveSplitK) return 1;
-  int parts = (int)std::min<int64_t>(4, kCUs / ntile);
+  int parts = (int)std::min<int64_t>(subwave_max_parts(K), kCUs / ntile);
   while (parts > 1 && K < (int64_t)parts * 128) --parts;
   return parts;
 }
@@ -194,8 +200,9 @@ void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q,
 // Split of the last partial wave of a direct-load GEMM (see TailSplit): when
 // fewer than half the CUs would get a tile in the last wave, those tiles are
 // split into up to four k-ranges of at least 128. A launch of less than half
-// a wave is split the same way (every tile) if its reduction is at least
-// kSubWaveSplitK long. Only plain-store epilogues.
+// a wave is split the same way (every tile, into up to subwave_max_parts
+// ranges) if its reduction is at least kSubWaveSplitK long. Only plain-store
+// epilogues.
 // TPMLP_TAIL_CUS in the environment replaces the CU count of this plan (read
 // on every call; lets tests exercise tail splits at small sizes).
 TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
@@ -207,7 +214,7 @@ TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
   const bool dma = pl.eng == Engine::Dma256 || pl.eng == Engine::Dma320;
   if (!allowed || !dma || r == 0 || r > cus / 2) return t;
   if (ntile < cus && K < kSubWaveSplitK) return t;
-  int parts = std::min(4, cus / r);
+  int parts = std::min(ntile < cus ? subwave_max_parts(K) : 4, cus / r);
   while (parts > 1 && K < (int64_t)parts * 128) --parts;
   if (parts < 2) return t;
   t.full = ntile - r;

@@ -111,7 +111,8 @@ def test_workspace_bytes(lib):
     assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240 + 4 * t8
     # ... its weight gradients (12 x 3 = 36 tiles, K = 4096) and dXp (16 x 3 = 48 tiles, K = 3072) are
     # launches of less than half a wave with long reductions: direct-load engine on staged copies of H, dY,
-    # X and dZ, every tile split into 4 k-ranges (the largest, dXp's, sizes the shared partials)
+    # X and dZ, every tile split into 4 k-ranges (at most 4 below K = 8192; the largest partials, dXp's,
+    # size the shared room)
     t2 = lambda rows: rows * (4096 + 256) * 2
     assert ws(4096, 768, 3072, 1) == part2 + 2 * t2(3072) + 2 * t2(768) + 48 * 4 * 256 * 256 * 4
     # ... and its forward stages A_i^T (first GEMM: 192 tiles) and B_i^T (second GEMM: 48 tiles, K = 3072,
@@ -350,9 +351,9 @@ def test_attention_workspace_sizes_and_validation(lib):
     assert fws(big) == Z * 4
     # D fp32 [32][2048], dS bf16, dO [8192, 640], column partials [8192 / 256][1920] fp32, then the k-split
     # partials of the projections, sized by the largest: dO = dY Wo^T is 32 x 2 tiles of 256 x 320 (less than
-    # half a wave, K = 2560), each split into 4 k-ranges (dWo: 3 x 10 tiles of 256 x 256 in 4 ranges;
+    # half a wave, K = 2560), each split into 4 k-ranges (dWo: 3 x 10 tiles of 256 x 256, K = 8192, in 8 ranges;
     # dWqkv: 10 x 8 in 3; dXp: one full wave of 256 x 320, no split)
-    ks = max(64 * 4 * 256 * 320 * 4, 30 * 4 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
+    ks = max(64 * 4 * 256 * 320 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
     assert bws(big) == 32 * 2048 * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
     assert fws(sh(4, 2048, 2560, 8, 80, 0)) == 0          # fp32 storage is not supported
     assert fws(sh(4, 2044, 2560, 8, 80, 2)) == 0          # seq not a multiple of 8
