@@ -122,3 +122,17 @@ def test_attention_2p4b_shard_full(gpu_lib):
     errs = compare(got, _ref(inp, cfg.causal), TOL[cfg.dtype], keys=FWD + BWD)
     print("errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
 
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype,causal,batch", [("f16", True, 4), ("bf16", False, 2)])
+def test_attention_2p4b_shape_other_dtype_and_mask(gpu_lib, dtype, causal, batch):
+    """The 2.4B shard's heads (8 of width 80, seq 2048) in fp16 with the
+    causal mask, and unmasked in bf16, every output against the oracle."""
+    cfg = synth.get_attn_config("attn_2p4b")
+    print(f"case attn 2p4b-shaped dtype={dtype} causal={causal} batch={batch}", flush=True)
+    inp = synth.draw_attn_inputs(batch, cfg.seq_len, cfg.hidden, cfg.heads_shard, cfg.head_dim, dtype,
+                                 seed=7, sigma_dy=cfg.sigma_dy)
+    got = _run(gpu_lib, *_dev(inp), batch, cfg.heads_shard, causal)
+    errs = compare(got, _ref(inp, causal), TOL[dtype], keys=FWD + BWD)
+    print("errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
