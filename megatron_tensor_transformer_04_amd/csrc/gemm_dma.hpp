@@ -37,20 +37,26 @@
 //
 // Pipeline. Within one output tile, k-tile t lives in stage (t + s0) % S
 // and is consumed in BK/16 substeps (fragments double-buffered in
-// registers). Tiles 0..S-1 are issued first; iteration t then does
+// registers). Tiles 0..S-1 are issued first; iteration t (BK = 64, four
+// substeps) then does
 //   read frags (t, 1)        | MFMAs (t, 0)
-//   ...
-//   read frags (t, last)     | MFMAs (t, last-1)
+//   read frags (t, 2)        | MFMAs (t, 1)
+//   read frags (t, 3)
 //   -- wait until tile t+1 has landed (later tiles may still be in flight),
 //      barrier: every wave is done with stage t % S --
-//   load tile t+S into stage t % S
-//   read frags (t+1, 0)      | MFMAs (t, last)
-// so LDS reads overlap MFMAs and a tile's global loads have S-1 iterations
-// of MFMA work to land. Scheduling constraints hold this order (the
-// compiler's own schedule serialises each read with its first use), and
-// after the barrier the loads and reads are interleaved with the MFMAs.
-// Workgroups are persistent (see gemm_dma_kernel): the next output tile's
-// k-tile 0 is issued before the current tile's epilogue.
+//   first half of the loads of tile t+S into stage t % S | MFMAs (t, 2)
+//   rest of those loads, read frags (t+1, 0)              | MFMAs (t, 3)
+// so LDS reads overlap MFMAs and a tile's global loads have about S-1
+// iterations of MFMA work to land. Placing the barrier one substep before
+// the end of the tile spreads each wave's loads over 20 MFMAs instead of
+// 10: issued in one burst after the barrier, the loads of all eight waves
+// filled the texture unit's queues and stalled the MFMAs interleaved with
+// them (measured on MI355X with the SQ_VMEM_TA_*_FIFO_FULL counters).
+// Scheduling constraints hold this order (the compiler's own schedule
+// serialises each read with its first use), and after the barrier the
+// loads and reads are interleaved with the MFMAs. Workgroups are
+// persistent (see gemm_dma_kernel): the next output tile's k-tile 0 is
+// issued before the current tile's epilogue.
 //
 // Workgroup -> tile order: see map_work and tile_coords.
 #pragma once
@@ -388,31 +394,39 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   };
 
   typedef __attribute__((address_space(3))) void lds_void;
-  // Direct loads of k-tile t of item `it` into stage `stage`. On a K-tail
-  // tile, chunks at or beyond the item's k-range take kOobOffset (one 32-bit
-  // compare per load); a tile past the end (t >= nk) is all kOobOffset and
-  // fills its stage with zeros that nothing reads, which keeps the loop body
-  // free of branches.
+  constexpr int LOADS = LP + LQ;      // direct loads per wave per tile
+  constexpr int FIRST = (LOADS + 1) / 2;  // loads in the first half (see the k-loop)
+  // Direct loads of k-tile t of item `it` into stage `stage`: all of them
+  // (PART 2), or the first FIRST (PART 0) or the rest (PART 1) in P-then-Q
+  // order. On a K-tail tile, chunks at or beyond the item's k-range take
+  // kOobOffset (one 32-bit compare per load); a tile past the end
+  // (t >= nk) is all kOobOffset and fills its stage with zeros that nothing
+  // reads, which keeps the loop body free of branches.
   auto issue_tile = [&](const Item& it, __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs,
-                        const uint32_t(&pv)[LP], const uint32_t(&qv)[LQ], int t, int stage)
+                        const uint32_t(&pv)[LP], const uint32_t(&qv)[LQ], int t, int stage, auto part_c)
       __attribute__((always_inline)) {
+    constexpr int PART = decltype(part_c)::value;
     const int krem = it.kspan - t * BK;  // k extent left from this tile on
     const int64_t k0 = krem > 0 ? it.kbeg + (int64_t)t * BK : 0;
     const int psoff = __builtin_amdgcn_readfirstlane((int)((P_KC ? k0 : k0 * P.ld) * 2));
     const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
     char* const sp = smem + stage * STG;
     static_for<0, LP>([&](auto c) {
-      const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + (c * Cfg::WAVES + wave) * 1024), 16, off,
-                                               psoff, 0, 0);
+      if constexpr (PART == 2 || (PART == 0) == (c < FIRST)) {
+        const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + (c * Cfg::WAVES + wave) * 1024), 16, off,
+                                                 psoff, 0, 0);
+      }
     });
     static_for<0, LQ>([&](auto c) {
-      const uint32_t off = qk0 + dma_kstep<Q_KC, BN, Cfg::WAVES>(c) < krem ? qv[c] : kOobOffset;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qrs, (lds_void*)(sp + Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024), 16, off, qsoff, 0, 0);
+      if constexpr (PART == 2 || (PART == 0) == (LP + c < FIRST)) {
+        const uint32_t off = qk0 + dma_kstep<Q_KC, BN, Cfg::WAVES>(c) < krem ? qv[c] : kOobOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qrs, (lds_void*)(sp + Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024), 16, off, qsoff, 0, 0);
+      }
     });
   };
-  constexpr int LOADS = LP + LQ;  // direct loads per wave per tile
+  constexpr auto kAll = std::integral_constant<int, 2>{};
 
   FragAddr<P_KC, BM, BK, FM> pa;
   FragAddr<Q_KC, BN, BK, FN> qa;
@@ -442,7 +456,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const Item first = decode(v);
     uint32_t pv[LP], qv[LQ];
     offsets(first, pv, qv);
-    issue_tile(first, p_rsrc(first), q_rsrc(first), pv, qv, 0, 0);
+    issue_tile(first, p_rsrc(first), q_rsrc(first), pv, qv, 0, 0, kAll);
   }
   while (true) {
     // Everything derived from the lane index is recomputed per item: hoisted
@@ -453,7 +467,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const __amdgpu_buffer_rsrc_t prs = p_rsrc(cur), qrs = q_rsrc(cur);
     uint32_t pv[LP], qv[LQ];
     offsets(cur, pv, qv);
-    static_for<1, ST>([&](auto t) { issue_tile(cur, prs, qrs, pv, qv, t, (t + s0) % ST); });
+    static_for<1, ST>([&](auto t) { issue_tile(cur, prs, qrs, pv, qv, t, (t + s0) % ST, kAll); });
     static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
     pa.init(lane, s0 * STG, wm * Cfg::WTM);
     qa.init(lane, s0 * STG + Cfg::LDS_P, wn * Cfg::WTN);
@@ -474,32 +488,65 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       barrier_lds();
       read_frags(fa0, fb0, std::integral_constant<int, 0>{});
       for (int t = 0; t < cur.nk; ++t) {
-        static_for<0, NKS - 1>([&](auto ks) {
-          if constexpr (ks % 2 == 0) {
-            read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
-            sched_fence();
-            mfmas(fa0, fb0);
-          } else {
-            read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
-            sched_fence();
-            mfmas(fa1, fb1);
-          }
-          sched_fence();
-        });
-        // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight. The
-        // barrier also orders every wave's reads of tile t's stage before
-        // the loads that refill it.
-        wait_vmcnt<(ST - 2) * LOADS>();
-        barrier_lds();
-        sched_fence();
         const int st_t = (t + s0) % ST;
-        issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t);
         const bool wrap = st_t == ST - 1;  // tile t+1 sits in stage 0
-        pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-        qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-        read_frags(fa0, fb0, std::integral_constant<int, 0>{});
-        mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
-        sched_interleave<FM * FN, LOADS, DSR>();
+        if constexpr (NKS >= 4) {
+          // Substeps 0 .. NKS-3, then the reads of the last substep; with
+          // those, this wave is done with stage st_t and the barrier comes
+          // one substep before the end of the tile: the loads that refill
+          // the stage are spread over the last two substeps' MFMAs (half
+          // each) instead of all landing on the texture unit at once.
+          static_for<0, NKS - 2>([&](auto ks) {
+            if constexpr (ks % 2 == 0) {
+              read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+              sched_fence();
+              mfmas(fa0, fb0);
+            } else {
+              read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+              sched_fence();
+              mfmas(fa1, fb1);
+            }
+            sched_fence();
+          });
+          read_frags(fa1, fb1, std::integral_constant<int, NKS - 1>{});  // NKS even: substep NKS-1 in set 1
+          // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight.
+          // The barrier also orders every wave's reads of tile t's stage
+          // before the loads that refill it.
+          wait_vmcnt<(ST - 2) * LOADS>();
+          barrier_lds();
+          sched_fence();
+          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, std::integral_constant<int, 0>{});
+          mfmas(fa0, fb0);  // substep NKS-2
+          sched_interleave<FM * FN, FIRST, 0>();
+          pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, std::integral_constant<int, 1>{});
+          read_frags(fa0, fb0, std::integral_constant<int, 0>{});
+          mfmas(fa1, fb1);  // substep NKS-1
+          sched_interleave<FM * FN, LOADS - FIRST, DSR>();
+        } else {
+          static_for<0, NKS - 1>([&](auto ks) {
+            if constexpr (ks % 2 == 0) {
+              read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+              sched_fence();
+              mfmas(fa0, fb0);
+            } else {
+              read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+              sched_fence();
+              mfmas(fa1, fb1);
+            }
+            sched_fence();
+          });
+          wait_vmcnt<(ST - 2) * LOADS>();
+          barrier_lds();
+          sched_fence();
+          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, kAll);
+          pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          read_frags(fa0, fb0, std::integral_constant<int, 0>{});
+          mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
+          sched_interleave<FM * FN, LOADS, DSR>();
+        }
       }
     }
     // Drain this wave's loads of the tiles past the end (they write LDS).
@@ -518,7 +565,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       uint32_t pv2[LP], qv2[LQ];
       offsets(nxt, pv2, qv2);
       const __amdgpu_buffer_rsrc_t prs2 = p_rsrc(nxt), qrs2 = q_rsrc(nxt);
-      static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST); });
+      static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST, kAll); });
     }
 
     const Item done = decode(opaque_s(v));
