@@ -306,6 +306,29 @@ int tp_mlp_db2(const tpmlp_shape* shape, const void* dY, void* db2, int accumula
 int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* const* parts, const void* bias,
                            int64_t row_begin, int64_t row_end, void* out, void* stream);
 
+/*
+ * Tile-plan override, for tests and tuning only (production callers leave
+ * it alone). It forces the GEMM engine of every 16-bit product and the CU
+ * count the k-split planner assumes, so that small shapes exercise the
+ * large-tile engines and their k-split paths. Process-wide; applies to
+ * calls that start after it returns (workspace sizes included).
+ *   tile      TPMLP_PLAN_AUTO (the planner's choice), TPMLP_PLAN_REG128 /
+ *             TPMLP_PLAN_REG256 (register-staged 128x128 / 256x256 tiles),
+ *             TPMLP_PLAN_DMA256 (direct-load 256x256), TPMLP_PLAN_DMA320
+ *             (direct-load 256x320 where both operands are k-contiguous,
+ *             256x256 elsewhere). A forced direct-load engine still yields
+ *             to the register-staged 256x256 one where an operand exceeds
+ *             its 32-bit offsets or GeLU is applied on load.
+ *   tail_cus  CU count of the k-split plan, 1 .. 4096; 0 = the chip's 256.
+ * Returns TPMLP_ERR_SHAPE for values out of range (nothing changes then).
+ */
+#define TPMLP_PLAN_AUTO 0
+#define TPMLP_PLAN_REG128 1
+#define TPMLP_PLAN_REG256 2
+#define TPMLP_PLAN_DMA256 3
+#define TPMLP_PLAN_DMA320 4
+int tp_mlp_debug_plan(int tile, int tail_cus);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ STATUS = {
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
            "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
-           "tp_mlp_db2_workspace_bytes", "tp_mlp_db2",
+           "tp_mlp_db2_workspace_bytes", "tp_mlp_db2", "tp_mlp_debug_plan",
            "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd")
 TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL, TPMLP_WS_RECOMPUTE = 1, 2, 4
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_db2_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape)]
     lib.tp_mlp_db2.restype = ctypes.c_int
     lib.tp_mlp_db2.argtypes = [ctypes.POINTER(tpmlp_shape), vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.tp_mlp_debug_plan.restype = ctypes.c_int
+    lib.tp_mlp_debug_plan.argtypes = [ctypes.c_int, ctypes.c_int]
     ap = ctypes.POINTER(tpattn_shape)
     lib.tp_attn_fwd_workspace_bytes.restype = sz
     lib.tp_attn_fwd_workspace_bytes.argtypes = [ap]
@@ -119,10 +121,29 @@ def _ptr(t):
 
 
 def _stream(stream):
+    """hipStream_t handle of `stream` (a torch stream or a raw handle), or of
+    torch's current stream when it is None."""
     if stream is not None:
-        return stream
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
     import torch
     return torch.cuda.current_stream().cuda_stream
+
+
+def _on_stream(stream):
+    """Context for the wrappers that allocate with torch: inside it, torch's
+    current stream is the launch stream `stream` (None: torch's current
+    stream, nothing changes). Outputs and workspaces allocated there belong
+    to the launch stream in torch's caching allocator, so a workspace freed
+    when the wrapper returns is reused only by work ordered after the
+    library's kernels on that stream, never by other streams' work that
+    could overlap them."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    import torch
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
 
 
 def _events(events):
@@ -150,6 +171,34 @@ def shape_of(tokens: int, hidden: int, ffn_shard: int, dtype: int, layout: int =
 
 def _layout(b_transposed: bool) -> int:
     return TPMLP_LAYOUT_B_T if b_transposed else 0
+
+
+# tile names of tp_mlp_debug_plan (TPMLP_PLAN_* in include/tp_mlp.h)
+PLAN_TILES = {None: 0, "auto": 0, 128: 1, "128": 1, 256: 2, "256": 2, "dma256": 3, "dma320": 4}
+
+
+def tp_mlp_debug_plan(tile=None, tail_cus: int = 0) -> None:
+    """Force a GEMM engine and the k-split planner's CU count for the calls
+    that follow (tests and tuning only; None / 0 restore the defaults)."""
+    if tile not in PLAN_TILES:
+        raise ValueError(f"unknown tile {tile!r}; one of {sorted(map(str, PLAN_TILES))}")
+    _check(load().tp_mlp_debug_plan(PLAN_TILES[tile], int(tail_cus)))
+
+
+class debug_plan:
+    """Context manager around tp_mlp_debug_plan that restores the default
+    plan on exit."""
+
+    def __init__(self, tile=None, tail_cus: int = 0):
+        self.tile, self.tail_cus = tile, tail_cus
+
+    def __enter__(self):
+        tp_mlp_debug_plan(self.tile, self.tail_cus)
+        return self
+
+    def __exit__(self, *exc):
+        tp_mlp_debug_plan(None, 0)
+        return False
 
 
 def tp_mlp_abi_version() -> int:
@@ -206,19 +255,20 @@ def bwd_recompute(dY, X, A, b1, B, keep_dz: bool = True, staged: bool = True, st
     """Allocate the gradients and the workspace with torch and run
     tp_mlp_bwd_recompute."""
     import torch
-    T, f, h = X.shape[0], A.shape[1], X.shape[1]
-    dev, dt = X.device, X.dtype
-    dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
-    dXp = torch.empty((T, h), dtype=dt, device=dev)
-    dA = torch.empty((h, f), dtype=dt, device=dev)
-    dB = torch.empty((h, f) if b_transposed else (f, h), dtype=dt, device=dev)
-    db1 = torch.empty((f,), dtype=dt, device=dev)
-    flags = TPMLP_WS_RECOMPUTE | (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
-    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags, _layout(b_transposed))
-    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
-    tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events,
-                         b_transposed=b_transposed)
-    return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
+    with _on_stream(stream):
+        T, f, h = X.shape[0], A.shape[1], X.shape[1]
+        dev, dt = X.device, X.dtype
+        dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
+        dXp = torch.empty((T, h), dtype=dt, device=dev)
+        dA = torch.empty((h, f), dtype=dt, device=dev)
+        dB = torch.empty((h, f) if b_transposed else (f, h), dtype=dt, device=dev)
+        db1 = torch.empty((f,), dtype=dt, device=dev)
+        flags = TPMLP_WS_RECOMPUTE | (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
+        nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags, _layout(b_transposed))
+        ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
+        tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events,
+                             b_transposed=b_transposed)
+        return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
 
 
 def tp_mlp_bwd_main_grad(dY, X, A, B, Z, H, dZ, dXp, dA_main, dB_main, db1_main, ws, *, stream=None,
@@ -269,12 +319,13 @@ def tp_mlp_db2(dY, db2, ws=None, *, accumulate: bool = False, stream=None) -> No
 def db2(dY, stream=None):
     """Allocate db2 (and the workspace) with torch and run tp_mlp_db2."""
     import torch
-    T, h = dY.shape
-    out = torch.empty((h,), dtype=dY.dtype, device=dY.device)
-    n = tp_mlp_db2_workspace_bytes(T, h, _dtype_code(dY))
-    ws = torch.empty((n,), dtype=torch.uint8, device=dY.device) if n else None
-    tp_mlp_db2(dY, out, ws, stream=stream)
-    return out
+    with _on_stream(stream):
+        T, h = dY.shape
+        out = torch.empty((h,), dtype=dY.dtype, device=dY.device)
+        n = tp_mlp_db2_workspace_bytes(T, h, _dtype_code(dY))
+        ws = torch.empty((n,), dtype=torch.uint8, device=dY.device) if n else None
+        tp_mlp_db2(dY, out, ws, stream=stream)
+        return out
 
 
 # ---- convenience wrappers that allocate the outputs with torch ----
@@ -282,14 +333,15 @@ def db2(dY, stream=None):
 def fwd(X, A, b1, B, keep_h: bool = True, staged: bool = True, stream=None, events=None, b_transposed: bool = False):
     """Allocate the outputs (and, if `staged`, the workspace) with torch and run tp_mlp_fwd."""
     import torch
-    T, f, h = X.shape[0], A.shape[1], X.shape[1]
-    Z = torch.empty((T, f), dtype=X.dtype, device=X.device)
-    H = torch.empty((T, f), dtype=X.dtype, device=X.device) if keep_h else None
-    Yp = torch.empty((T, h), dtype=X.dtype, device=X.device)
-    nws = tp_mlp_fwd_workspace_bytes(T, h, f, _dtype_code(X), _layout(b_transposed)) if staged else 0
-    ws = torch.empty((nws,), dtype=torch.uint8, device=X.device) if nws else None
-    tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws, stream=stream, events=events, b_transposed=b_transposed)
-    return Z, H, Yp
+    with _on_stream(stream):
+        T, f, h = X.shape[0], A.shape[1], X.shape[1]
+        Z = torch.empty((T, f), dtype=X.dtype, device=X.device)
+        H = torch.empty((T, f), dtype=X.dtype, device=X.device) if keep_h else None
+        Yp = torch.empty((T, h), dtype=X.dtype, device=X.device)
+        nws = tp_mlp_fwd_workspace_bytes(T, h, f, _dtype_code(X), _layout(b_transposed)) if staged else 0
+        ws = torch.empty((nws,), dtype=torch.uint8, device=X.device) if nws else None
+        tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws, stream=stream, events=events, b_transposed=b_transposed)
+        return Z, H, Yp
 
 
 def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, stream=None, events=None,
@@ -297,18 +349,19 @@ def bwd(dY, X, A, B, Z, H=None, keep_dz: bool = True, staged: bool = True, strea
     """Allocate the gradients and the workspace (the staged size, or the
     minimal one when `staged` is False) with torch and run tp_mlp_bwd."""
     import torch
-    T, f, h = X.shape[0], A.shape[1], X.shape[1]
-    dev, dt = X.device, X.dtype
-    dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
-    dXp = torch.empty((T, h), dtype=dt, device=dev)
-    dA = torch.empty((h, f), dtype=dt, device=dev)
-    dB = torch.empty((h, f) if b_transposed else (f, h), dtype=dt, device=dev)
-    db1 = torch.empty((f,), dtype=dt, device=dev)
-    flags = (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
-    nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags, _layout(b_transposed))
-    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
-    tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events, b_transposed=b_transposed)
-    return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
+    with _on_stream(stream):
+        T, f, h = X.shape[0], A.shape[1], X.shape[1]
+        dev, dt = X.device, X.dtype
+        dZ = torch.empty((T, f), dtype=dt, device=dev) if keep_dz else None
+        dXp = torch.empty((T, h), dtype=dt, device=dev)
+        dA = torch.empty((h, f), dtype=dt, device=dev)
+        dB = torch.empty((h, f) if b_transposed else (f, h), dtype=dt, device=dev)
+        db1 = torch.empty((f,), dtype=dt, device=dev)
+        flags = (0 if keep_dz else TPMLP_WS_DZ) | (0 if staged else TPMLP_WS_MINIMAL)
+        nws = tp_mlp_workspace_bytes(T, h, f, _dtype_code(X), flags, _layout(b_transposed))
+        ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev) if nws else None
+        tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, stream=stream, events=events, b_transposed=b_transposed)
+        return {"dZ": dZ, "dXp": dXp, "dA": dA, "dB": dB, "db1": db1}
 
 
 # ---- attention shard (include/tp_attn.h) ----
@@ -355,28 +408,30 @@ def tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, *,
 def attn_fwd(X, Wqkv, bqkv, Wo, batch, heads, causal=True, ws=None, stream=None):
     """Allocate the outputs (and the workspace unless given) with torch and run tp_attn_fwd."""
     import torch
-    T, h = X.shape
-    q = Wo.shape[0]
-    s = T // batch
-    e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
-    QKV, P, O, Yp = e(T, 3 * q), e(batch * heads, s, s), e(T, q), e(T, h)
-    if ws is None:
-        n = tp_attn_fwd_workspace_bytes(batch, s, h, heads, q // heads, _dtype_code(X), causal)
-        ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
-    tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, batch=batch, heads=heads, causal=causal, stream=stream)
-    return {"QKV": QKV, "P": P, "O": O, "Yp": Yp}
+    with _on_stream(stream):
+        T, h = X.shape
+        q = Wo.shape[0]
+        s = T // batch
+        e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
+        QKV, P, O, Yp = e(T, 3 * q), e(batch * heads, s, s), e(T, q), e(T, h)
+        if ws is None:
+            n = tp_attn_fwd_workspace_bytes(batch, s, h, heads, q // heads, _dtype_code(X), causal)
+            ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
+        tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, ws, batch=batch, heads=heads, causal=causal, stream=stream)
+        return {"QKV": QKV, "P": P, "O": O, "Yp": Yp}
 
 
 def attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, batch, heads, causal=True, ws=None, stream=None):
     """Allocate the gradients (and the workspace unless given) with torch and run tp_attn_bwd."""
     import torch
-    T, h = X.shape
-    q = Wo.shape[0]
-    e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
-    dQKV, dXp, dWqkv, dbqkv, dWo = e(T, 3 * q), e(T, h), e(h, 3 * q), e(3 * q), e(q, h)
-    if ws is None:
-        n = tp_attn_bwd_workspace_bytes(batch, T // batch, h, heads, q // heads, _dtype_code(X), causal)
-        ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
-    tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, batch=batch, heads=heads,
-                causal=causal, stream=stream)
-    return {"dQKV": dQKV, "dXp": dXp, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo}
+    with _on_stream(stream):
+        T, h = X.shape
+        q = Wo.shape[0]
+        e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
+        dQKV, dXp, dWqkv, dbqkv, dWo = e(T, 3 * q), e(T, h), e(h, 3 * q), e(3 * q), e(q, h)
+        if ws is None:
+            n = tp_attn_bwd_workspace_bytes(batch, T // batch, h, heads, q // heads, _dtype_code(X), causal)
+            ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
+        tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, batch=batch, heads=heads,
+                    causal=causal, stream=stream)
+        return {"dQKV": dQKV, "dXp": dXp, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo}

@@ -15,8 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
+#include <atomic>
 #include <type_traits>
 
 #include "tp_mlp.h"
@@ -148,16 +147,19 @@ int64_t subwave_cost(int64_t M, int64_t N, int64_t K, int bm, int bn) {
 // applied on load (that engine has no register stage to apply it in) or an
 // operand is too large for its 32-bit offsets; with both operands
 // k-contiguous (kc) it takes 256x320 tiles unless they cost more whole
-// waves. TPMLP_TILE=128, 256 (register-staged), dma256 or dma320 (kc only)
-// in the environment forces one engine where it applies (read on every
-// call; for tuning and tests).
+// waves. tp_mlp_debug_plan can force one engine where it applies (tests and
+// tuning only).
+std::atomic<int> g_plan_tile{TPMLP_PLAN_AUTO};
+std::atomic<int> g_plan_cus{0};
+
 Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc) {
   const bool dma_fits = !gelu_p && M * (K + kStagePad) <= kDmaMaxElems && N * (K + kStagePad) <= kDmaMaxElems;
-  if (const char* e = std::getenv("TPMLP_TILE")) {
-    if (!std::strcmp(e, "128")) return Engine::Mfma128;
-    if (!std::strcmp(e, "256")) return Engine::Mfma256;
-    if (!std::strcmp(e, "dma256")) return dma_fits ? Engine::Dma256 : Engine::Mfma256;
-    if (!std::strcmp(e, "dma320")) return !dma_fits ? Engine::Mfma256 : kc ? Engine::Dma320 : Engine::Dma256;
+  switch (g_plan_tile.load(std::memory_order_relaxed)) {
+    case TPMLP_PLAN_REG128: return Engine::Mfma128;
+    case TPMLP_PLAN_REG256: return Engine::Mfma256;
+    case TPMLP_PLAN_DMA256: return dma_fits ? Engine::Dma256 : Engine::Mfma256;
+    case TPMLP_PLAN_DMA320: return !dma_fits ? Engine::Mfma256 : kc ? Engine::Dma320 : Engine::Dma256;
+    default: break;
   }
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
   const bool split_candidate = t256 >= 16 && t256 <= kCUs / 2 && K >= kSubWaveSplitK;
@@ -203,13 +205,13 @@ void launch_mfma(const GemmShape& sh, const void* p, int64_t ldp, const void* q,
 // a wave is split the same way (every tile, into up to subwave_max_parts
 // ranges) if its reduction is at least kSubWaveSplitK long. Only plain-store
 // epilogues.
-// TPMLP_TAIL_CUS in the environment replaces the CU count of this plan (read
-// on every call; lets tests exercise tail splits at small sizes).
+// tp_mlp_debug_plan can replace the CU count of this plan (lets tests
+// exercise tail splits at small sizes).
 TailSplit plan_tail(const Plan& pl, int64_t K, bool allowed) {
   const int ntile = pl.tiles_m * pl.tiles_n;
   TailSplit t{ntile, 1, K, nullptr};
-  int cus = kCUs;
-  if (const char* e = std::getenv("TPMLP_TAIL_CUS")) cus = std::max(1, std::atoi(e));
+  const int forced = g_plan_cus.load(std::memory_order_relaxed);
+  const int cus = forced > 0 ? forced : kCUs;
   const int r = ntile % cus;
   const bool dma = pl.eng == Engine::Dma256 || pl.eng == Engine::Dma320;
   if (!allowed || !dma || r == 0 || r > cus / 2) return t;
@@ -946,6 +948,13 @@ int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* con
       break;
   }
   return hipGetLastError() == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
+}
+
+int tp_mlp_debug_plan(int tile, int tail_cus) {
+  if (tile < TPMLP_PLAN_AUTO || tile > TPMLP_PLAN_DMA320 || tail_cus < 0 || tail_cus > 4096) return TPMLP_ERR_SHAPE;
+  g_plan_tile.store(tile, std::memory_order_relaxed);
+  g_plan_cus.store(tail_cus, std::memory_order_relaxed);
+  return TPMLP_OK;
 }
 
 }  // extern "C"

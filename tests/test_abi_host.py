@@ -19,6 +19,16 @@ def lib():
     return tpmlp.load()
 
 
+@pytest.fixture
+def plan(lib):
+    """Setter of the tile-plan override (tp_mlp_debug_plan); the default plan
+    is restored when the test ends."""
+    def set_plan(tile, cus):
+        assert lib.tp_mlp_debug_plan(tile, cus) == 0
+    yield set_plan
+    assert lib.tp_mlp_debug_plan(0, 0) == 0
+
+
 ATTN_HEADER = os.path.join(ROOT, "include", "tp_attn.h")
 
 
@@ -45,7 +55,7 @@ def test_exports_every_declared_function(lib):
     assert set(declared) == {"tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes",
                              "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad",
                              "tp_mlp_bwd_recompute", "tp_mlp_reduce_partials", "tp_mlp_db2_workspace_bytes",
-                             "tp_mlp_db2", "tp_attn_fwd_workspace_bytes",
+                             "tp_mlp_db2", "tp_mlp_debug_plan", "tp_attn_fwd_workspace_bytes",
                              "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd"}
     raw = ctypes.CDLL(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "libtpmlp.so"))
     for name in declared:
@@ -130,40 +140,40 @@ def test_workspace_bytes(lib):
     assert ws(64, 128, 256, 7) == 0
 
 
-def test_k_split_tail_workspace_full_shard(lib, monkeypatch):
+def test_k_split_tail_workspace_full_shard(lib, plan):
     """With 256 x 256 tiles forced, dB and dA of the h = 10240 shard have
     40 x 40 = 1600 tiles: six full waves and 64 tiles left, each split into
     4 k-ranges of fp32 partials; dXp (2560 tiles) splits nothing."""
     ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
-    monkeypatch.setenv("TPMLP_TILE", "dma256")
+    plan(3, 0)
     part = (16384 // 256) * 10240 * 4
     t = 10240 * (16384 + 256) * 2
     assert ws() == part + 4 * t + 64 * 4 * 256 * 256 * 4
 
 
-def test_k_split_tail_workspace(lib, monkeypatch):
+def test_k_split_tail_workspace(lib, plan):
     """The k-split plan (as if the chip had `cus` CUs) sizes the partials:
     [tail tiles][parts][256][256] fp32, the largest over dB, dA and dXp."""
     ws = lambda T, h, f: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)), 0)
     fws = lambda T, h, f: lib.tp_mlp_fwd_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)))
-    monkeypatch.setenv("TPMLP_TILE", "dma256")
+    plan(3, 0)
     base, fbase = ws(520, 264, 392), fws(520, 264, 392)
     short = fws(520, 264, 200)
     tile = 256 * 256 * 4
     # 3 CUs: dB and dA have 2 x 2 tiles, one left over, split into
     # ceil(520 / round_up(ceil(520 / 3), 64)) = 3 ranges; Yp / dXp (3 x 2) none
-    monkeypatch.setenv("TPMLP_TAIL_CUS", "3")
+    plan(3, 3)
     assert ws(520, 264, 392) == base + 1 * 3 * tile
     assert fws(520, 264, 392) == fbase
     # 4 CUs: Yp / dXp keep 2 of 6 tiles for the last wave, 2 ranges of K = 392
-    monkeypatch.setenv("TPMLP_TAIL_CUS", "4")
+    plan(3, 4)
     assert ws(520, 264, 392) == base + 2 * 2 * tile
     assert fws(520, 264, 392) == fbase + 2 * 2 * tile
     # ... unless K is too short for two ranges of at least 128
     assert fws(520, 264, 200) == short
     # 5 CUs: Yp / dXp leave 1 of 6 tiles; 4 ranges would be shorter than 128,
     # 3 of round_up(ceil(392 / 3), 64) = 192; dB and dA (4 tiles) fill no wave
-    monkeypatch.setenv("TPMLP_TAIL_CUS", "5")
+    plan(3, 5)
     assert ws(520, 264, 392) == base + 1 * 3 * tile
     assert fws(520, 264, 392) == fbase + 1 * 3 * tile
 
@@ -401,3 +411,32 @@ def test_db2_workspace_and_validation(lib):
     assert lib.tp_mlp_db2(ctypes.byref(ok), dY, ctypes.c_void_p(0x10000 + 4096), 0, ws, 1024, None) == 7  # in dY
     big = tpmlp_shape(65536 * 256, 8, 8, 2)
     assert lib.tp_mlp_db2(ctypes.byref(big), dY, out, 0, ws, 1 << 30, None) == 2
+
+
+def test_debug_plan_rejects_out_of_range_values(lib):
+    """tp_mlp_debug_plan accepts the TPMLP_PLAN_* codes and CU counts
+    0 .. 4096 only, and a rejected call changes nothing."""
+    ok, shape_err = _header_enum("TPMLP_OK"), _header_enum("TPMLP_ERR_SHAPE")
+    ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
+    base = ws()
+    assert lib.tp_mlp_debug_plan(-1, 0) == shape_err
+    assert lib.tp_mlp_debug_plan(_header_define("TPMLP_PLAN_DMA320") + 1, 0) == shape_err
+    assert lib.tp_mlp_debug_plan(0, -1) == shape_err
+    assert lib.tp_mlp_debug_plan(0, 4097) == shape_err
+    assert ws() == base
+    try:
+        assert lib.tp_mlp_debug_plan(_header_define("TPMLP_PLAN_DMA256"), 0) == ok
+        assert ws() != base  # 256 x 256 tiles leave a k-split tail at this shape
+    finally:
+        assert lib.tp_mlp_debug_plan(_header_define("TPMLP_PLAN_AUTO"), 0) == ok
+    assert ws() == base
+
+
+def test_no_environment_variable_changes_the_plan(lib, monkeypatch):
+    """The planner reads no environment variable: the variables the tuning
+    hooks once used leave the workspace size (and so the plan) unchanged."""
+    ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
+    base = ws()
+    monkeypatch.setenv("TPMLP_TILE", "dma256")
+    monkeypatch.setenv("TPMLP_TAIL_CUS", "3")
+    assert ws() == base

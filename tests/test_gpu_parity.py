@@ -18,14 +18,13 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture
-def tile(request, monkeypatch):
-    """Force one 16-bit tile size through TPMLP_TILE (None = automatic choice)."""
+def tile(request, gpu_lib):
+    """Force one 16-bit tile engine through tp_mlp_debug_plan (None = the
+    planner's choice); the default plan is restored afterwards."""
     value = getattr(request, "param", None)
-    if value is None:
-        monkeypatch.delenv("TPMLP_TILE", raising=False)
-    else:
-        monkeypatch.setenv("TPMLP_TILE", str(value))
-    return value
+    gpu_lib.tp_mlp_debug_plan(value, 0)
+    yield value
+    gpu_lib.tp_mlp_debug_plan(None, 0)
 
 
 def _oracle_shard(inp):
@@ -73,12 +72,12 @@ def test_operands_read_in_place(gpu_lib, tile, dtype, T, h, f):
 @pytest.mark.parametrize("cus", [3, 4, 5])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,h,f", [(520, 264, 392), (1000, 264, 392)])
-def test_k_split_last_wave(gpu_lib, tile, monkeypatch, cus, dtype, T, h, f):
+def test_k_split_last_wave(gpu_lib, tile, cus, dtype, T, h, f):
     """Tail tiles computed as k-ranges plus an ordered fp32 sum, planned as
     if the chip had `cus` CUs so that small shapes split (3 CUs: dB and dA
     split their one leftover tile into 3 ranges; 4 and 5: Yp and dXp split
     ragged K = 392 into 2 or 3)."""
-    monkeypatch.setenv("TPMLP_TAIL_CUS", str(cus))
+    gpu_lib.tp_mlp_debug_plan(tile, cus)
     print(f"case k-split cus={cus} dtype={dtype} T={T} h={h} f={f}", flush=True)
     inp = synth.draw_inputs(T, h, f, dtype, seed=T + cus, sigma_dy=1.0)
     ref = _oracle_shard(inp)
@@ -207,17 +206,31 @@ def test_deterministic_bitwise(gpu_lib):
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
 
 
-@pytest.mark.parametrize("tile,cus", [(128, None), (256, None), ("dma256", None), ("dma256", 4),
-                                      ("dma320", None), ("dma320", 2)],
+# A shape whose every GEMM has more than one full wave of work items (256
+# CUs): 17 x 17 tiles of 256 x 320 (or 17 x 22 of 256 x 256) for the token
+# GEMMs, 22 x 17 for the weight gradients, with a partial last wave that
+# the planner splits into k-ranges. It runs the XCD renumbering of full
+# waves (map_work) as well as the plain order of the last wave.
+FULL_WAVE = (4352, 5440, 5440)
+
+
+@pytest.mark.parametrize("tile,cus,shape", [(128, None, None), (256, None, None), ("dma256", None, None),
+                                            ("dma256", 4, None), ("dma320", None, None), ("dma320", 2, None),
+                                            (None, None, FULL_WAVE), ("dma256", None, FULL_WAVE),
+                                            ("dma320", None, FULL_WAVE)],
                          indirect=["tile"])
-def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, monkeypatch):
+def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, shape):
     """Each output lives between two poisoned guard regions, which must
-    survive forward + backward unchanged (cus: k-split tails planned as if
-    the chip had that many CUs, so that the partials use the workspace)."""
+    survive forward + backward unchanged, and every element of every output
+    must be overwritten (the poison value may not remain) and match the
+    oracle (cus: k-split tails planned as if the chip had that many CUs, so
+    that the partials use the workspace; FULL_WAVE: launches of more than
+    one full wave of work items)."""
     import torch
     if cus is not None:
-        monkeypatch.setenv("TPMLP_TAIL_CUS", str(cus))
-    T, h, f = (520, 264, 392) if cus else (200, 136, 264)
+        gpu_lib.tp_mlp_debug_plan(tile, cus)
+    T, h, f = shape if shape else (520, 264, 392) if cus else (200, 136, 264)
+    print(f"case guard bands tile={tile} cus={cus} T={T} h={h} f={f}", flush=True)
     inp = synth.draw_inputs(T, h, f, "bf16", seed=4, sigma_dy=1.0)
     X, A, b1, B, dY = device_inputs(inp)
     G = 4096  # guard elements on each side (keeps 16-byte alignment)

@@ -15,13 +15,13 @@ GRADS = ("dZ", "dXp", "dA", "dB", "db1")
 
 
 @pytest.fixture
-def tile(request, monkeypatch):
+def tile(request, gpu_lib):
+    """Force one 16-bit tile engine through tp_mlp_debug_plan (None = the
+    planner's choice); the default plan is restored afterwards."""
     value = getattr(request, "param", None)
-    if value is None:
-        monkeypatch.delenv("TPMLP_TILE", raising=False)
-    else:
-        monkeypatch.setenv("TPMLP_TILE", str(value))
-    return value
+    gpu_lib.tp_mlp_debug_plan(value, 0)
+    yield value
+    gpu_lib.tp_mlp_debug_plan(None, 0)
 
 
 CASES = ([(None, "f32")] + [(t, d) for t in (None, 128, 256, "dma256", "dma320") for d in ("f16", "bf16")])
@@ -73,18 +73,19 @@ def test_recompute_events_bracket_each_step(gpu_lib):
 
 @pytest.mark.slow
 def test_recompute_full_size_sampled(gpu_lib):
-    """The h=10240 shard (staged operands, 256 x 320 tiles): sampled rows and
-    columns against the oracle."""
+    """The h=10240 shard (staged operands, 256 x 320 tiles): tile-complete
+    samples of rows and columns (one in every 64-wide band) against the
+    oracle."""
     import torch
-    from tests.test_gpu_fullsize import _samples
+    from tests.gpu_util import tile_complete_samples
     cfg = synth.get_config("gpt_h10240")
     print(f"case recompute full size T={cfg.tokens} h={cfg.hidden} f={cfg.ffn_shard}", flush=True)
     inp = synth.draw_config(cfg)
     X, A, b1, B, dY = device_inputs(inp)
     got = gpu_lib.bwd_recompute(dY, X, A, b1, B)
     torch.cuda.synchronize()
-    rows = _samples(cfg.tokens, 24, 1)
-    cols = _samples(cfg.ffn_shard, 12, 2)
+    rows = tile_complete_samples(cfg.tokens, 1)
+    cols = tile_complete_samples(cfg.ffn_shard, 2)
     rr = oracle.sampled_rows(inp.X, inp.A, inp.b1, inp.B, inp.dY, rows)
     rc = oracle.sampled_cols(inp.X, inp.A, inp.b1, inp.B, inp.dY, cols)
     ri, ci = torch.as_tensor(rows, device="cuda"), torch.as_tensor(cols, device="cuda")
