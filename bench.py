@@ -155,7 +155,7 @@ def config_rate(tpmlp, name, dev, steps=10, warmup=3):
     stream; reported beside the main workload, whose line this is."""
     import torch
     import synth
-    from tests.gpu_util import device_inputs
+    from synth.device import device_inputs
     cfg = synth.get_config(name)
     T, h, f = cfg.tokens, cfg.hidden, cfg.ffn_shard
     inp = synth.draw_config(cfg)
@@ -230,7 +230,7 @@ def attention_rate(tpmlp, dev, reps=10, cpu=True):
     twice the forward."""
     import torch
     import synth
-    from tests.gpu_util import to_device
+    from synth.device import to_device
     cfg = synth.get_attn_config("attn_2p4b")
     b, s, h, n, d = cfg.micro_batch, cfg.seq_len, cfg.hidden, cfg.heads_shard, cfg.head_dim
     inp = synth.draw_attn_inputs(b, s, h, n, d, cfg.dtype, seed=cfg.seed, sigma_dy=cfg.sigma_dy)
@@ -323,7 +323,7 @@ def main():
         import oracle
         inp.A, inp.b1, inp.B = (x.copy() for x in oracle.shard_weights(inp.A, inp.b1, inp.B, cfg.tp, 0))
         inp._bits.clear()
-    from tests.gpu_util import device_inputs, torch_dtype
+    from synth.device import device_inputs, torch_dtype
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     X, A, b1, B, dY = device_inputs(inp)

@@ -3,36 +3,14 @@ rank's forward + backward through the C ABI, bring results back as float64.
 Torch is plumbing here (device memory, copies, the stream)."""
 import numpy as np
 
+from synth.device import device_inputs, to_device, torch_dtype  # noqa: F401  (re-exported for the tests)
+
 TOL = {"f32": 1e-4, "f16": 5e-3, "bf16": 2e-2}
-
-
-def torch_dtype(dtype: str):
-    import torch
-    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
-
-
-def to_device(values64: np.ndarray, dtype: str):
-    """float64 values exact in `dtype` -> contiguous device tensor of that dtype."""
-    import torch
-    from synth import storage_bits
-    bits = storage_bits(np.ascontiguousarray(values64), dtype)
-    if dtype == "bf16":
-        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
-    else:
-        t = torch.from_numpy(bits)
-    return t.to("cuda").contiguous()
 
 
 def to_host(t) -> np.ndarray:
     import torch
     return t.detach().to(torch.float64).cpu().numpy()
-
-
-def device_inputs(inp, A=None, b1=None, B=None):
-    """X, A, b1, B, dY of `inp` on the device (weights may be overridden, e.g. by a shard slice)."""
-    d = inp.dtype
-    return (to_device(inp.X, d), to_device(inp.A if A is None else A, d), to_device(inp.b1 if b1 is None else b1, d),
-            to_device(inp.B if B is None else B, d), to_device(inp.dY, d))
 
 
 def run_shard(tpmlp, X, A, b1, B, dY, keep_h=True, keep_dz=True, staged=True):
@@ -61,3 +39,17 @@ def compare(got: dict, ref: dict, tol: float, keys=None):
     bad = {k: e for k, e in errs.items() if not e <= tol}
     assert not bad, f"parity failed (tol {tol}): {bad}; all: {errs}"
     return errs
+
+
+def tile_complete_samples(n, seed, band=64):
+    """One random index in every `band`-wide band of [0, n), plus 0, n-1 and
+    the two indices on each side of every multiple of 256 and 320 (tile
+    edges of the planner's largest tiles)."""
+    rng = np.random.default_rng(seed)
+    idx = {0, n - 1}
+    for b0 in range(0, n, band):
+        idx.add(int(rng.integers(b0, min(n, b0 + band))))
+    for t in (256, 320):
+        for e in range(t, n, t):
+            idx.update((e - 1, e))
+    return np.array(sorted(i for i in idx if 0 <= i < n))
