@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 7
+#define TPMLP_ABI_VERSION 8
 
 typedef enum {
   TPMLP_F32 = 0,
@@ -79,7 +79,9 @@ typedef enum {
   TPMLP_ERR_DTYPE = 4,     /* dtype not one of tpmlp_dtype */
   TPMLP_ERR_WORKSPACE = 5, /* workspace smaller than tp_mlp_workspace_bytes() */
   TPMLP_ERR_HIP = 6,       /* a HIP call or kernel launch failed */
-  TPMLP_ERR_ALIAS = 7      /* an output overlaps an input or another output */
+  TPMLP_ERR_ALIAS = 7,     /* an output overlaps an input or another output */
+  TPMLP_ERR_SCRATCH = 8    /* tp_mlp_bwd_static: the shape needs more scratch than
+                              TPMLP_STATIC_SCRATCH_BYTES */
 } tpmlp_status;
 
 /*
@@ -208,6 +210,34 @@ int tp_mlp_bwd(const tpmlp_shape* shape,
                void* dZ, void* dXp, void* dA, void* dB, void* db1,
                void* ws, size_t ws_bytes,
                void* stream, void* const* events);
+
+/*
+ * Backward that allocates nothing and takes no workspace: for callers that
+ * cannot call hipMalloc or hand the library memory of its own (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same operation, arguments, layout, events and error codes as
+ * tp_mlp_bwd with a minimal workspace (TPMLP_WS_MINIMAL), minus ws and
+ * ws_bytes; the results are bitwise those of that call.
+ *   dZ  [tokens, ffn_shard] out, REQUIRED here (TPMLP_ERR_NULL if NULL):
+ *                           there is no workspace to keep it in.
+ * Its only scratch, the fp32 per-tile column partials of dZ_i that the db1
+ * finish adds up, lives in a device array of TPMLP_STATIC_SCRATCH_BYTES
+ * that the library defines once per GPU it runs on (held until the process
+ * ends; its address is looked up once per device, on the first call made
+ * with that device current). A shape whose partials need more returns
+ * TPMLP_ERR_SCRATCH before anything is enqueued; the size they need is
+ * tp_mlp_workspace_bytes(shape, TPMLP_WS_MINIMAL). Every call on one GPU
+ * uses that GPU's one array: calls that overlap on the same GPU (several
+ * streams or threads at once) race and give wrong results; serialise them.
+ * Nothing in the array needs clearing: each call overwrites every partial
+ * it reads.
+ */
+#define TPMLP_STATIC_SCRATCH_BYTES (32u << 20)
+int tp_mlp_bwd_static(const tpmlp_shape* shape,
+                      const void* dY, const void* X, const void* A, const void* B,
+                      const void* Z, const void* H,
+                      void* dZ, void* dXp, void* dA, void* dB, void* db1,
+                      void* stream, void* const* events);
 
 /*
  * Backward with selective recomputation: the forward's Z_i and H_i are not

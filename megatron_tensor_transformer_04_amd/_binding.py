@@ -22,13 +22,15 @@ STATUS = {
     5: "TPMLP_ERR_WORKSPACE",
     6: "TPMLP_ERR_HIP",
     7: "TPMLP_ERR_ALIAS",
+    8: "TPMLP_ERR_SCRATCH",
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
-           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
+           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_static", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
            "tp_mlp_db2_workspace_bytes", "tp_mlp_db2", "tp_mlp_debug_plan",
            "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd")
 TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL, TPMLP_WS_RECOMPUTE = 1, 2, 4
+TPMLP_STATIC_SCRATCH_BYTES = 32 << 20   # device scratch of tp_mlp_bwd_static
 FWD_EVENTS = ("TA", "F1", "TB", "F2")                                     # steps bracketed by the 5 events
 BWD_EVENTS = ("B1", "B5", "TH", "TdY", "B2", "TX", "TdZ", "B3", "B4")    # ... by the 10 events
 RECOMPUTE_EVENTS = ("TA", "F1") + BWD_EVENTS                              # ... by the 12 events
@@ -78,6 +80,8 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd.restype = ctypes.c_int
     lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_bwd_static.restype = ctypes.c_int
+    lib.tp_mlp_bwd_static.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd_recompute.restype = ctypes.c_int
     lib.tp_mlp_bwd_recompute.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 10 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd_main_grad.restype = ctypes.c_int
@@ -239,6 +243,16 @@ def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, even
     ev = _events(events)
     _check(load().tp_mlp_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H), _ptr(dZ),
                              _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def tp_mlp_bwd_static(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, *, stream=None, events=None,
+                      b_transposed=False) -> None:
+    """Backward of one TP rank that allocates nothing and takes no workspace
+    (its scratch is the library's static device array); dZ is required."""
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed))
+    ev = _events(events)
+    _check(load().tp_mlp_bwd_static(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(A), _ptr(B), _ptr(Z), _ptr(H),
+                                    _ptr(dZ), _ptr(dXp), _ptr(dA), _ptr(dB), _ptr(db1), _stream(stream), ev))
 
 
 def tp_mlp_bwd_recompute(dY, X, A, b1, B, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None, b_transposed=False) -> None:

@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "tp_mlp.h"
@@ -30,6 +31,31 @@
 
 namespace tpmlp {
 namespace {
+
+// Device scratch of tp_mlp_bwd_static (the callers that cannot allocate):
+// the fp32 column partials of dZ for db1. One copy per GPU, at its own
+// address; host code uses the address hipGetSymbolAddress returns for the
+// current device, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[TPMLP_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and cached.
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TPMLP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TPMLP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TPMLP_OK;
+}
 
 // Sum of the per-tile fp32 column partials [tiles_m][f], in a fixed order:
 // a block of 256 threads covers 32 columns; thread (g, c) adds the tiles
@@ -721,6 +747,7 @@ const char* tp_mlp_status_string(int status) {
     case TPMLP_ERR_WORKSPACE: return "workspace too small";
     case TPMLP_ERR_HIP: return "HIP error";
     case TPMLP_ERR_ALIAS: return "an output overlaps an input or another output";
+    case TPMLP_ERR_SCRATCH: return "shape needs more than the static scratch (TPMLP_STATIC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }
@@ -781,6 +808,37 @@ int tp_mlp_bwd(const tpmlp_shape* shape, const void* dY, const void* X, const vo
       return bwd_impl<StoreF16, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
     default:
       return bwd_impl<StoreBF16, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, ws_bytes, st, events);
+  }
+}
+
+int tp_mlp_bwd_static(const tpmlp_shape* shape, const void* dY, const void* X, const void* A, const void* B,
+                      const void* Z, const void* H, void* dZ, void* dXp, void* dA, void* dB, void* db1, void* stream,
+                      void* const* events) {
+  TPMLP_TRY(check_shape(shape));
+  const tpmlp_shape& s = *shape;
+  const size_t e = elt_size(s.dtype);
+  const size_t Th = (size_t)(s.tokens * s.hidden) * e, hf = (size_t)(s.hidden * s.ffn_shard) * e,
+               Tf = (size_t)(s.tokens * s.ffn_shard) * e, fb = (size_t)s.ffn_shard * e;
+  const BwdWs w = bwd_ws(s, false);
+  const Span in[6] = {{dY, Th}, {X, Th}, {A, hf}, {B, hf}, {Z, Tf}, {H, Tf}};
+  const bool in_req[6] = {true, true, true, true, true, false};
+  const Span out[5] = {{dZ, Tf}, {dXp, Th}, {dA, hf}, {dB, hf}, {db1, fb}};
+  const bool out_req[5] = {true, true, true, true, true};
+  TPMLP_TRY(check_buffers(in, 6, in_req, out, 5, out_req));
+  if (Tf && !dZ) return TPMLP_ERR_NULL;
+  if (w.minimal > TPMLP_STATIC_SCRATCH_BYTES) return TPMLP_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (w.minimal) TPMLP_TRY(static_scratch(&ws));
+  // With exactly the minimal size the plan is tp_mlp_bwd's minimal one:
+  // operands read in place, no staged copies, no k-split partials.
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (s.dtype) {
+    case TPMLP_F32:
+      return bwd_impl<StoreF32, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, w.minimal, st, events);
+    case TPMLP_F16:
+      return bwd_impl<StoreF16, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, w.minimal, st, events);
+    default:
+      return bwd_impl<StoreBF16, false>(s, dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, w, ws, w.minimal, st, events);
   }
 }
 
