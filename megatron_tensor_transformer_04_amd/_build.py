@@ -1,7 +1,12 @@
 """Compile the HIP library libtpmlp.so for gfx950, in-tree, with hipcc.
 
-Each source is compiled to an object in parallel, then the objects are
-linked into one shared library (MLP shard and attention shard entry points).
+The sources (csrc/ and include/) are first copied to a snapshot directory
+under _build/, so that edits made while a build runs cannot reach a compiler
+half way through (hipcc reads the sources once for the device pass and again
+for the host pass). Each source is compiled to an object in parallel (the MLP
+shard's launch sequences are split by storage type for that), then the
+objects are linked into one shared library (MLP shard and attention shard
+entry points).
 """
 import os
 import shutil
@@ -13,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtpmlp.so")
-SOURCES = [os.path.join(CSRC, "tp_mlp.hip"), os.path.join(CSRC, "tp_attn.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("mlp_bf16.hip", "mlp_f16.hip", "tp_attn.hip", "mlp_f32.hip", "tp_mlp.hip")]
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
@@ -46,8 +51,14 @@ def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     """Compile SOURCES into `out` (atomically replaced) and return its path."""
     os.makedirs(OBJDIR, exist_ok=True)
     cc = hipcc()
+    snap = os.path.join(OBJDIR, "src")
+    shutil.rmtree(snap, ignore_errors=True)
+    shutil.copytree(CSRC, os.path.join(snap, "csrc"))
+    shutil.copytree(INCLUDE, os.path.join(snap, "include"))
+    s_csrc, s_inc = os.path.join(snap, "csrc"), os.path.join(snap, "include")
     objs = [os.path.join(OBJDIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in SOURCES]
-    cmds = [[cc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    cmds = [[cc, *HIPCC_FLAGS, *extra_flags, "-I", s_inc, "-I", s_csrc, "-c",
+             os.path.join(s_csrc, os.path.basename(src)), "-o", obj]
             for src, obj in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
