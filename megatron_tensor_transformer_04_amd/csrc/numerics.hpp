@@ -3,7 +3,8 @@
 // GeLU is the tanh approximation of Hendrycks & Gimpel, "Gaussian Error
 // Linear Units" (2016); the pages fuse it with the first linear's bias
 // ("Training GPT-2 with Megatron-LM", section 6.2, fused_bias_gelu) without
-// stating a formula. tanh(u) enters only through exp(2u), see tanh_parts.
+// stating a formula. tanh(u) enters only through (1 + tanh(u)) / 2, the
+// logistic function of 2u, see gelu_sigma.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,31 +69,38 @@ struct StoreBF16 {
 constexpr float kSqrt2OverPi = 0.7978845608028654f;
 constexpr float kGeluC = 0.044715f;
 
-// With t = tanh(u), e = exp(2u) and r = 1 / (e + 1):
-//   1 + t = 2 e r,   1 - t = 2 r,   1 - t^2 = 4 e r^2,
-// forms without the cancellation of 1 +- t near t = -+1. 2u is clamped to
-// [-80, 40]: there tanh is already +-1 to fp32 precision and exp stays finite.
-__device__ __forceinline__ void tanh_parts(float u, float& e, float& r) {
-  const float u2 = fminf(fmaxf(2.0f * u, -80.0f), 40.0f);
-  e = __expf(u2);
-  r = __builtin_amdgcn_rcpf(e + 1.0f);
+// With u = sqrt(2/pi) (x + c x^3) and t = tanh(u), (1 + t) / 2 is the
+// logistic function of 2u:
+//   s = (1 + t) / 2 = 1 / (1 + exp(-2u)) = 1 / (1 + 2^(-x (A + B x^2))),
+//   A = 2 sqrt(2/pi) log2(e),  B = A c,
+// so gelu(x) = x (1 + t) / 2 = x s, and, since ds/du = 2 s (1 - s),
+//   gelu'(x) = s + x s (1 - s) 2 sqrt(2/pi) (1 + 3 c x^2)
+//            = s (1 + (1 - s) x (K1 + K2 x^2)),  K1 = 2 sqrt(2/pi), K2 = 3 c K1.
+// One exp2 and one reciprocal per element and no clamp: for large -x the
+// power overflows to +inf and s = 1/inf = 0; for large +x it underflows to
+// 0 and s = 1.
+constexpr float kGeluA = 2.0f * kSqrt2OverPi * 1.4426950408889634f;
+constexpr float kGeluB = kGeluA * kGeluC;
+constexpr float kGeluK1 = 2.0f * kSqrt2OverPi;
+constexpr float kGeluK2 = 3.0f * kGeluC * kGeluK1;
+
+__device__ __forceinline__ float gelu_sigma(float x, float x2) {
+  const float p = -x * fmaf(kGeluB, x2, kGeluA);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p));
 }
 
-// gelu(x) = x/2 (1 + tanh(u)) = x e r,  u = sqrt(2/pi) (x + c x^3)
-__device__ __forceinline__ float gelu_tanh(float x) {
-  float e, r;
-  tanh_parts(kSqrt2OverPi * (x + kGeluC * x * x * x), e, r);
-  return x * e * r;
-}
+// gelu(x) = x s
+__device__ __forceinline__ float gelu_tanh(float x) { return x * gelu_sigma(x, x * x); }
 
-// d/dx gelu(x) = (1 + t)/2 + x/2 (1 - t^2) sqrt(2/pi) (1 + 3 c x^2)
-//              = e r + 2 sqrt(2/pi) x (1 + 3 c x^2) e r^2
+// gelu'(x) = s (1 + (1 - s) q), q = x (K1 + K2 x^2). x is clamped to
+// [-16, 16] inside q only: beyond it s is exactly 0 or 1 in fp32 (the power
+// is 2^(+-458) or further), so (1 - s) q or s (...) is exactly 0 there and
+// the clamp changes nothing but keeps q finite.
 __device__ __forceinline__ float gelu_tanh_grad(float x) {
-  const float x2 = x * x;
-  float e, r;
-  tanh_parts(kSqrt2OverPi * (x + kGeluC * x2 * x), e, r);
-  const float er = e * r;
-  return er + 2.0f * kSqrt2OverPi * x * (1.0f + 3.0f * kGeluC * x2) * er * r;
+  const float s = gelu_sigma(x, x * x);
+  const float xc = __builtin_amdgcn_fmed3f(x, -16.0f, 16.0f);
+  const float q = xc * fmaf(kGeluK2, xc * xc, kGeluK1);
+  return s * fmaf(1.0f - s, q, 1.0f);
 }
 
 // Apply gelu to the eight 16-bit values packed in one 16-byte chunk.
