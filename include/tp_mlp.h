@@ -178,6 +178,34 @@ int tp_mlp_fwd(const tpmlp_shape* shape,
                void* stream, void* const* events);
 
 /*
+ * Forward of one rank under sequence parallelism: the tokens of X are split
+ * over the ranks as well ("Training GPT-2 with Megatron-LM", section 5.1,
+ * the --sequence-parallel switch), so rank r holds only token rows
+ * [r T/n, (r+1) T/n) of X. The column-split first linear needs every token,
+ * which the pages obtain by all-gathering the input ("Understanding the
+ * Megatron-LM architecture: how 3D parallelism assigns roles", section 1,
+ * the row-split item: "All-Gather the input, or All-Reduce the result").
+ * Here the gather is folded into the first GEMM's operand loads: it reads
+ * each token row straight from the slice that holds it, and no gathered copy
+ * of X is made. Everything else is tp_mlp_fwd; the outputs Z, H and Yp cover
+ * all T tokens, and rank r's reduce-scatter of Yp over the ranks is
+ * tp_mlp_reduce_partials over rows [r T/n, (r+1) T/n).
+ *   nslices     1 .. 16 (TPMLP_ERR_SHAPE otherwise); tokens must be a
+ *               multiple of nslices (TPMLP_ERR_SHAPE)
+ *   X_slices    HOST array of nslices DEVICE pointers, slice i holding token
+ *               rows [i T/n, (i+1) T/n) of X, each [tokens / nslices, hidden],
+ *               16-byte aligned; outputs may not overlap any slice
+ *   others      as in tp_mlp_fwd (same workspace size, same 5 events)
+ * fp16 and bf16 only (TPMLP_ERR_DTYPE for fp32). The results are bitwise
+ * those of tp_mlp_fwd on the gathered X.
+ */
+int tp_mlp_fwd_sp(const tpmlp_shape* shape, int nslices, const void* const* X_slices,
+                  const void* A, const void* b1, const void* B,
+                  void* Z, void* H, void* Yp,
+                  void* ws, size_t ws_bytes,
+                  void* stream, void* const* events);
+
+/*
  * Backward of one rank; see the top of this file for the operation.
  *   dY  [tokens, hidden]    in   output gradient (same on every rank)
  *   X, A, B                 in   as in tp_mlp_fwd

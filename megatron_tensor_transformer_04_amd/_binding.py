@@ -25,7 +25,7 @@ STATUS = {
     8: "TPMLP_ERR_SCRATCH",
 }
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
-           "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_static", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
+           "tp_mlp_fwd", "tp_mlp_fwd_sp", "tp_mlp_bwd", "tp_mlp_bwd_static", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
            "tp_mlp_db2_workspace_bytes", "tp_mlp_db2", "tp_mlp_debug_plan",
            "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd")
 TPMLP_MAX_PARTS = 16
@@ -78,6 +78,9 @@ def load(path: str = LIB_PATH):
     lib.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_uint]
     lib.tp_mlp_fwd.restype = ctypes.c_int
     lib.tp_mlp_fwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 7 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_fwd_sp.restype = ctypes.c_int
+    lib.tp_mlp_fwd_sp.argtypes = [ctypes.POINTER(tpmlp_shape), ctypes.c_int, ctypes.POINTER(vp)] + [vp] * 6 + \
+        [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd.restype = ctypes.c_int
     lib.tp_mlp_bwd.argtypes = [ctypes.POINTER(tpmlp_shape)] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.tp_mlp_bwd_static.restype = ctypes.c_int
@@ -234,6 +237,19 @@ def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_tr
     ev = _events(events)
     _check(load().tp_mlp_fwd(ctypes.byref(s), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),
                              _ptr(ws), _nbytes(ws), _stream(stream), ev))
+
+
+def tp_mlp_fwd_sp(X_slices, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_transposed=False) -> None:
+    """Forward of one TP rank under sequence parallelism: X given as equal
+    token-row slices (a list of [T/n, hidden] device tensors, one per rank),
+    read in place by the first GEMM instead of an all-gathered copy."""
+    n = len(X_slices)
+    T = sum(x.shape[0] for x in X_slices)
+    s = shape_of(T, X_slices[0].shape[1], A.shape[1], _dtype_code(X_slices[0]), _layout(b_transposed))
+    arr = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in X_slices])
+    ev = _events(events)
+    _check(load().tp_mlp_fwd_sp(ctypes.byref(s), n, arr, _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),
+                                _ptr(ws), _nbytes(ws), _stream(stream), ev))
 
 
 def tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws, *, stream=None, events=None, b_transposed=False) -> None:

@@ -313,11 +313,16 @@ struct FragAddr {
 // of the next item is loaded into the free stage while the epilogue of the
 // current one runs out of the other stage, so that its load latency hides
 // behind the epilogue instead of stalling a freshly started workgroup.
-template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi>
+//
+// SLICED_P: P (k-contiguous) is read from the row slices xs; every slice
+// holds a whole number of BM-row tiles (the host checks), so each work
+// item's P tile lies in one slice and gets that slice's buffer resource.
+template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi, bool SLICED_P = false>
 __global__ __launch_bounds__(Cfg::THREADS)
 __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
 void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi,
-                     TailSplit tail, int nwork) {
+                     TailSplit tail, int nwork, RowSlices xs) {
+  static_assert(!SLICED_P || P_KC, "row slices of a k-contiguous P only");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES, STG = Cfg::STG;
   static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
@@ -358,8 +363,13 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // with num_records = the operand's extent from there, so any offset past
   // the tensor reads zeros.
   auto p_rsrc = [&](const Item& it) __attribute__((always_inline)) {
-    const int64_t base = P_KC ? it.m0 * P.ld : it.m0;
-    return uniform_rsrc(P.ptr + base, (p_extent - base) * 2);
+    if constexpr (SLICED_P) {
+      const int64_t sl = it.m0 / xs.rows, r0 = it.m0 - sl * xs.rows;
+      return uniform_rsrc(xs.p[sl] + r0 * P.ld, (xs.rows - r0) * P.ld * 2);
+    } else {
+      const int64_t base = P_KC ? it.m0 * P.ld : it.m0;
+      return uniform_rsrc(P.ptr + base, (p_extent - base) * 2);
+    }
   };
   auto q_rsrc = [&](const Item& it) __attribute__((always_inline)) {
     const int64_t base = Q_KC ? it.n0 * Q.ld : it.n0;

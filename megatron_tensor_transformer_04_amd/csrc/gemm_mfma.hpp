@@ -97,6 +97,16 @@ struct Operand {
   int64_t ld;  // elements between consecutive rows in memory
 };
 
+// A k-contiguous operand held as equal slices of rows in separate buffers
+// (the token rows of X under sequence parallelism, one slice per rank):
+// row r lives in slice r / rows, at row r % rows of it, every slice with the
+// operand's row pitch. Passed by value to the kernels that read it.
+constexpr int kMaxSlices = 16;
+struct RowSlices {
+  const uint16_t* p[kMaxSlices];
+  int64_t rows;  // rows per slice
+};
+
 __device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
 
 template <int R>
@@ -142,6 +152,19 @@ __device__ __forceinline__ u32x4 load_chunk(const Operand& op, int64_t mn0, int6
   return v;
 }
 
+// load_chunk of a k-contiguous operand held as row slices (see RowSlices).
+template <int R>
+__device__ __forceinline__ u32x4 load_chunk_sliced(const RowSlices& xs, int64_t ld, int64_t mn0, int64_t MN,
+                                                   int64_t k0, int64_t kend, int q) {
+  const int64_t mn = mn0 + (q >> 3), k = k0 + ((q & 7) << 3);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (mn < MN && k < kend) {
+    const int64_t s = mn / xs.rows;
+    v = *reinterpret_cast<const u32x4*>(xs.p[s] + (mn - s * xs.rows) * ld + k);
+  }
+  return v;
+}
+
 template <bool KC, int R>
 __device__ __forceinline__ int lds_chunk_offset(int q) {
   if constexpr (KC) {
@@ -179,8 +202,11 @@ __device__ __forceinline__ u32x4 read_frag(const char* tile, int row0, int ks, i
   }
 }
 
-template <class Cfg, class S, bool P_KC, bool Q_KC, bool GELU_P, class Epi>
-__global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, Operand P, Operand Q, Epi epi) {
+// SLICED_P: P (k-contiguous) is read from the row slices xs instead of P.ptr.
+template <class Cfg, class S, bool P_KC, bool Q_KC, bool GELU_P, class Epi, bool SLICED_P = false>
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, Operand P, Operand Q, Epi epi,
+                                                                 RowSlices xs) {
+  static_assert(!SLICED_P || P_KC, "row slices of a k-contiguous P only");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, THREADS = Cfg::THREADS;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
 
@@ -221,7 +247,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_mfma_kernel(GemmShape sh, O
   auto load_stage = [&](int64_t k0) {
 #pragma unroll
     for (int c = 0; c < Cfg::CH_P; ++c)
-      rp[c] = load_chunk<P_KC, BM, THREADS>(P, m0, sh.M, k0, kend, tid + c * THREADS);
+      if constexpr (SLICED_P)
+        rp[c] = load_chunk_sliced<BM>(xs, P.ld, m0, sh.M, k0, kend, tid + c * THREADS);
+      else
+        rp[c] = load_chunk<P_KC, BM, THREADS>(P, m0, sh.M, k0, kend, tid + c * THREADS);
 #pragma unroll
     for (int c = 0; c < Cfg::CH_Q; ++c)
       rq[c] = load_chunk<Q_KC, BN, THREADS>(Q, n0, sh.N, k0, kend, tid + c * THREADS);

@@ -191,7 +191,7 @@ hipError_t gemm(int64_t M, int64_t N, int64_t K, const void* p, int64_t ldp, con
   GemmShape sh{M, N, K, (int)cdiv(M, CfgA::BM), (int)cdiv(N, CfgA::BN), 1, std::max<int64_t>(K, 1)};
   hipLaunchKernelGGL((gemm_mfma_kernel<CfgA, S, PK, QK, false, Epi>), dim3(sh.tiles_m * sh.tiles_n, batches),
                      dim3(CfgA::THREADS), 0, st, sh, Operand{static_cast<const uint16_t*>(p), ldp},
-                     Operand{static_cast<const uint16_t*>(q), ldq}, epi);
+                     Operand{static_cast<const uint16_t*>(q), ldq}, epi, RowSlices{});
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ def test_exports_every_declared_function(lib):
     assert set(declared) == {"tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes",
                              "tp_mlp_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_main_grad",
                              "tp_mlp_bwd_recompute", "tp_mlp_reduce_partials", "tp_mlp_db2_workspace_bytes",
-                             "tp_mlp_db2", "tp_mlp_debug_plan", "tp_mlp_bwd_static", "tp_attn_fwd_workspace_bytes",
+                             "tp_mlp_db2", "tp_mlp_debug_plan", "tp_mlp_bwd_static", "tp_mlp_fwd_sp",
+                             "tp_attn_fwd_workspace_bytes",
                              "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd"}
     raw = ctypes.CDLL(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "libtpmlp.so"))
     for name in declared:
@@ -481,3 +482,31 @@ def test_bwd_static_validation_errors(lib):
 def _header_define_expr(name):
     m = re.search(rf"#define\s+{name}\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
     return int(m.group(1)) << int(m.group(2))
+
+
+def _fwd_sp(lib, shape, n, slices=None, **kw):
+    p = dict(A=BASE + (20 << 32), b1=BASE + (21 << 32), B=BASE + (22 << 32), Z=BASE + (23 << 32),
+             H=BASE + (24 << 32), Yp=BASE + (25 << 32), ws=None, ws_bytes=0)
+    p.update(kw)
+    if slices is None:
+        slices = [BASE + (i << 32) for i in range(n)]
+    arr = (ctypes.c_void_p * max(len(slices), 1))(*slices)
+    return lib.tp_mlp_fwd_sp(ctypes.byref(shape), n, arr, p["A"], p["b1"], p["B"], p["Z"], p["H"], p["Yp"],
+                             p["ws"], p["ws_bytes"], None, None)
+
+
+def test_fwd_sp_validation_errors(lib):
+    """The sequence-parallel forward checks the slice count, the token split,
+    each slice pointer and that no output overlaps a slice, before anything
+    is enqueued; fp32 is not offered."""
+    err = {n: _header_enum(n) for n in ("TPMLP_ERR_NULL", "TPMLP_ERR_SHAPE", "TPMLP_ERR_ALIGN", "TPMLP_ERR_DTYPE",
+                                        "TPMLP_ERR_ALIAS")}
+    ok = _shape(64, 128, 256, 2)
+    assert _fwd_sp(lib, ok, 0) == err["TPMLP_ERR_SHAPE"]
+    assert _fwd_sp(lib, ok, 17) == err["TPMLP_ERR_SHAPE"]
+    assert _fwd_sp(lib, ok, 3) == err["TPMLP_ERR_SHAPE"]          # 64 tokens do not split in 3
+    assert _fwd_sp(lib, _shape(64, 128, 256, 0), 2) == err["TPMLP_ERR_DTYPE"]
+    assert _fwd_sp(lib, ok, 2, slices=[BASE, None]) == err["TPMLP_ERR_NULL"]
+    assert _fwd_sp(lib, ok, 2, slices=[BASE, BASE + (1 << 32) + 8]) == err["TPMLP_ERR_ALIGN"]
+    assert _fwd_sp(lib, ok, 2, Yp=BASE + (1 << 32) + 64) == err["TPMLP_ERR_ALIAS"]   # Yp inside slice 1
+    assert _fwd_sp(lib, ok, 2, Z=None) == err["TPMLP_ERR_NULL"]
