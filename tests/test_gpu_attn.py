@@ -136,3 +136,24 @@ def test_attention_2p4b_shape_other_dtype_and_mask(gpu_lib, dtype, causal, batch
     got = _run(gpu_lib, *_dev(inp), batch, cfg.heads_shard, causal)
     errs = compare(got, _ref(inp, causal), TOL[dtype], keys=FWD + BWD)
     print("errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("seq", [1024, 4096, 3000])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_long_rows(gpu_lib, seq, causal):
+    """Sequences whose softmax rows take 4 (seq 1024) and 16 (seq 3000 and
+    4096, the longest the shape check admits) fp32 values per lane, one
+    sequence of two heads of width 40, fp16, causal and unmasked, every
+    output against the oracle."""
+    print(f"case attn long rows seq={seq} causal={causal}", flush=True)
+    inp = synth.draw_attn_inputs(1, seq, 64, 2, 40, "f16", seed=seq, sigma_w=0.1, sigma_dy=1.0)
+    got = _run(gpu_lib, *_dev(inp), 1, 2, causal)
+    errs = compare(got, _ref(inp, causal), TOL["f16"], keys=FWD + BWD)
+    print("errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    if causal:
+        import torch
+        P = got["P"].float().cpu()
+        upper = torch.triu(torch.ones(seq, seq, dtype=torch.bool), diagonal=1)
+        assert bool((P[:, upper] == 0).all())
+
