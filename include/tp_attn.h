@@ -119,6 +119,49 @@ int tp_attn_bwd(const tpattn_shape* shape,
                 void* dQKV, void* dXp, void* dWqkv, void* dbqkv, void* dWo,
                 void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Fused path: the same rank's share, with the attention core computed one
+ * block of keys at a time on chip so that nothing of size seq x seq is
+ * stored (the "flash" form of attention: an online softmax with a running
+ * maximum and sum per query row). The forward keeps, per (sequence, head)
+ * pair z = b * heads + j and query t, the log-sum-exp of the row's scaled,
+ * masked scores,
+ *   LSE[z][t] = log sum_{visible k} exp(S[t][k])   (fp32, natural log),
+ * instead of P; the backward recomputes P[t][k] = exp(S[t][k] - LSE[z][t])
+ * from it. Results equal those of tp_attn_fwd / tp_attn_bwd up to rounding
+ * (the probabilities enter P V unnormalized, scaled by the row sum at the
+ * end). Bitwise deterministic (no atomics).
+ * Shapes: as above, without the sequence cap and without the
+ * batch * heads * seq * seq bound; head_dim <= 128 (TPMLP_ERR_SHAPE).
+ *
+ * Workspace bytes (0 on an invalid shape):
+ *   forward:  the output projection's k-split partials, 256 at least;
+ *   backward: fp32 row terms rowsum(dO * O) [batch*heads][seq], dO [T, q],
+ *             fp32 per-256-row column partials of dQKV for dbqkv, and fp32
+ *             k-split partials of the projections' GEMMs.
+ */
+size_t tp_attn_flash_fwd_workspace_bytes(const tpattn_shape* shape);
+size_t tp_attn_flash_bwd_workspace_bytes(const tpattn_shape* shape);
+
+/*
+ * Fused forward of one rank: as tp_attn_fwd, with
+ *   LSE  [batch*heads, seq] fp32     out (kept for the backward) in place of P.
+ */
+int tp_attn_flash_fwd(const tpattn_shape* shape,
+                      const void* X, const void* Wqkv, const void* bqkv, const void* Wo,
+                      void* QKV, void* LSE, void* O, void* Yp,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fused backward of one rank: as tp_attn_bwd, reading the forward's LSE
+ * (fp32 [batch*heads, seq]) in place of P.
+ */
+int tp_attn_flash_bwd(const tpattn_shape* shape,
+                      const void* dY, const void* X, const void* Wqkv, const void* Wo,
+                      const void* QKV, const void* LSE, const void* O,
+                      void* dQKV, void* dXp, void* dWqkv, void* dbqkv, void* dWo,
+                      void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

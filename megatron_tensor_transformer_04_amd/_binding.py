@@ -27,7 +27,9 @@ STATUS = {
 EXPORTS = ("tp_mlp_abi_version", "tp_mlp_status_string", "tp_mlp_fwd_workspace_bytes", "tp_mlp_workspace_bytes",
            "tp_mlp_fwd", "tp_mlp_fwd_sp", "tp_mlp_bwd", "tp_mlp_bwd_static", "tp_mlp_bwd_recompute", "tp_mlp_bwd_main_grad", "tp_mlp_reduce_partials",
            "tp_mlp_db2_workspace_bytes", "tp_mlp_db2", "tp_mlp_debug_plan",
-           "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd")
+           "tp_attn_fwd_workspace_bytes", "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd",
+           "tp_attn_flash_fwd_workspace_bytes", "tp_attn_flash_bwd_workspace_bytes", "tp_attn_flash_fwd",
+           "tp_attn_flash_bwd")
 TPMLP_MAX_PARTS = 16
 TPMLP_WS_DZ, TPMLP_WS_MINIMAL, TPMLP_WS_RECOMPUTE = 1, 2, 4
 TPMLP_STATIC_SCRATCH_BYTES = 32 << 20   # device scratch of tp_mlp_bwd_static
@@ -107,6 +109,13 @@ def load(path: str = LIB_PATH):
     lib.tp_attn_fwd.argtypes = [ap] + [vp] * 8 + [vp, sz, vp]
     lib.tp_attn_bwd.restype = ctypes.c_int
     lib.tp_attn_bwd.argtypes = [ap] + [vp] * 12 + [vp, sz, vp]
+    for name in ("tp_attn_flash_fwd_workspace_bytes", "tp_attn_flash_bwd_workspace_bytes"):
+        getattr(lib, name).restype = sz
+        getattr(lib, name).argtypes = [ap]
+    lib.tp_attn_flash_fwd.restype = ctypes.c_int
+    lib.tp_attn_flash_fwd.argtypes = [ap] + [vp] * 8 + [vp, sz, vp]
+    lib.tp_attn_flash_bwd.restype = ctypes.c_int
+    lib.tp_attn_flash_bwd.argtypes = [ap] + [vp] * 12 + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -464,4 +473,66 @@ def attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, batch, heads, causal=True, ws=None, str
             ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
         tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, batch=batch, heads=heads,
                     causal=causal, stream=stream)
+        return {"dQKV": dQKV, "dXp": dXp, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo}
+
+
+# ---- fused attention path (include/tp_attn.h, tp_attn_flash_*) ----
+
+def tp_attn_flash_fwd_workspace_bytes(batch, seq, hidden, heads, head_dim, dtype, causal=True) -> int:
+    s = attn_shape(batch, seq, hidden, heads, head_dim, dtype, causal)
+    return load().tp_attn_flash_fwd_workspace_bytes(ctypes.byref(s))
+
+
+def tp_attn_flash_bwd_workspace_bytes(batch, seq, hidden, heads, head_dim, dtype, causal=True) -> int:
+    s = attn_shape(batch, seq, hidden, heads, head_dim, dtype, causal)
+    return load().tp_attn_flash_bwd_workspace_bytes(ctypes.byref(s))
+
+
+def tp_attn_flash_fwd(X, Wqkv, bqkv, Wo, QKV, LSE, O, Yp, ws, *, batch, heads, causal=True, stream=None) -> None:
+    """Fused forward of one rank's heads into caller-allocated QKV, LSE (fp32), O, Yp."""
+    s = _attn_shape_of(X, Wo, batch, heads, causal)
+    _check(load().tp_attn_flash_fwd(ctypes.byref(s), _ptr(X), _ptr(Wqkv), _ptr(bqkv), _ptr(Wo), _ptr(QKV),
+                                    _ptr(LSE), _ptr(O), _ptr(Yp), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def tp_attn_flash_bwd(dY, X, Wqkv, Wo, QKV, LSE, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, *, batch, heads, causal=True,
+                      stream=None) -> None:
+    """Fused backward of one rank's heads into caller-allocated gradients."""
+    s = _attn_shape_of(X, Wo, batch, heads, causal)
+    _check(load().tp_attn_flash_bwd(ctypes.byref(s), _ptr(dY), _ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(QKV),
+                                    _ptr(LSE), _ptr(O), _ptr(dQKV), _ptr(dXp), _ptr(dWqkv), _ptr(dbqkv), _ptr(dWo),
+                                    _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def attn_flash_fwd(X, Wqkv, bqkv, Wo, batch, heads, causal=True, ws=None, stream=None):
+    """Allocate the outputs (and the workspace unless given) with torch and run tp_attn_flash_fwd."""
+    import torch
+    with _on_stream(stream):
+        T, h = X.shape
+        q = Wo.shape[0]
+        s = T // batch
+        e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
+        QKV, O, Yp = e(T, 3 * q), e(T, q), e(T, h)
+        LSE = torch.empty((batch * heads, s), dtype=torch.float32, device=X.device)
+        if ws is None:
+            n = tp_attn_flash_fwd_workspace_bytes(batch, s, h, heads, q // heads, _dtype_code(X), causal)
+            ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
+        tp_attn_flash_fwd(X, Wqkv, bqkv, Wo, QKV, LSE, O, Yp, ws, batch=batch, heads=heads, causal=causal,
+                          stream=stream)
+        return {"QKV": QKV, "LSE": LSE, "O": O, "Yp": Yp}
+
+
+def attn_flash_bwd(dY, X, Wqkv, Wo, QKV, LSE, O, batch, heads, causal=True, ws=None, stream=None):
+    """Allocate the gradients (and the workspace unless given) with torch and run tp_attn_flash_bwd."""
+    import torch
+    with _on_stream(stream):
+        T, h = X.shape
+        q = Wo.shape[0]
+        e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=X.device)
+        dQKV, dXp, dWqkv, dbqkv, dWo = e(T, 3 * q), e(T, h), e(h, 3 * q), e(3 * q), e(q, h)
+        if ws is None:
+            n = tp_attn_flash_bwd_workspace_bytes(batch, T // batch, h, heads, q // heads, _dtype_code(X), causal)
+            ws = torch.empty((n,), dtype=torch.uint8, device=X.device)
+        tp_attn_flash_bwd(dY, X, Wqkv, Wo, QKV, LSE, O, dQKV, dXp, dWqkv, dbqkv, dWo, ws, batch=batch, heads=heads,
+                          causal=causal, stream=stream)
         return {"dQKV": dQKV, "dXp": dXp, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo}

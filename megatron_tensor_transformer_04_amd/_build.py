@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtpmlp.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("mlp_bf16.hip", "mlp_f16.hip", "tp_attn.hip", "mlp_f32.hip", "tp_mlp.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("mlp_bf16.hip", "mlp_f16.hip", "tp_attn.hip", "tp_attn_flash.hip", "mlp_f32.hip", "tp_mlp.hip")]
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [

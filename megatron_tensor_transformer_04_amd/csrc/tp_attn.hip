@@ -23,6 +23,7 @@
 #include <cmath>
 
 #include "tp_attn.h"
+#include "attn_common.hpp"
 #include "colsum.hpp"
 #include "epilogues.hpp"
 #include "gemm_mfma.hpp"
@@ -31,9 +32,8 @@
 namespace tpmlp {
 namespace {
 
+using namespace attn;
 using CfgA = MfmaTile<128, 128, 2, 2>;
-
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Offsets (in elements) of batch z = b * inner + j: operand P, operand Q and
 // the output each move by b * (stride per sequence) + j * (stride per head).
@@ -265,39 +265,6 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restric
   }
 }
 
-// Row terms of the softmax backward: for each (sequence, head) pair z and
-// query t, D[z][t] = sum_e dO[t][e] O[t][e] over the head's d columns (fp32,
-// in e order). In exact arithmetic D = sum_k P[t][k] dP[t][k], since
-// dP = dO V^T and O = P V; it is the term the softmax's backward subtracts.
-template <class S>
-__global__ __launch_bounds__(256) void softmax_rowdot_kernel(const typename S::T* __restrict__ dO,
-                                                             const typename S::T* __restrict__ O, float* __restrict__ D,
-                                                             int64_t T, int64_t s, int heads, int d, int64_t q) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // token * heads + head
-  if (i >= T * heads) return;
-  const int64_t t = i / heads;
-  const int j = (int)(i % heads);
-  const typename S::T* a = dO + t * q + (int64_t)j * d;
-  const typename S::T* o = O + t * q + (int64_t)j * d;
-  float acc = 0.0f;
-  for (int e = 0; e < d; e += 8) {
-    const uint4 wa = *reinterpret_cast<const uint4*>(a + e), wo = *reinterpret_cast<const uint4*>(o + e);
-    const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w}, uo[4] = {wo.x, wo.y, wo.z, wo.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc += S::to_f((typename S::T)(ua[k] & 0xffffu)) * S::to_f((typename S::T)(uo[k] & 0xffffu));
-      acc += S::to_f((typename S::T)(ua[k] >> 16)) * S::to_f((typename S::T)(uo[k] >> 16));
-    }
-  }
-  const int64_t b = t / s, pos = t % s;
-  D[((b * heads) + j) * s + pos] = acc;
-}
-
-size_t a256(size_t b) { return (b + 255) / 256 * 256; }
-
-// Longest sequence: a softmax row of 4096 keys is 64 fp32 values per lane.
-constexpr int64_t kMaxSeq = 4096;
-
 template <class S>
 hipError_t softmax_fwd(const float* sc, typename S::T* P, int64_t rows, int64_t s, float scale, int causal,
                        hipStream_t st) {
@@ -308,46 +275,6 @@ hipError_t softmax_fwd(const float* sc, typename S::T* P, int64_t rows, int64_t 
   else if (s <= 2048) hipLaunchKernelGGL((softmax_fwd_kernel<S, 8>), grid, block, 0, st, sc, P, rows, s, scale, causal);
   else hipLaunchKernelGGL((softmax_fwd_kernel<S, 16>), grid, block, 0, st, sc, P, rows, s, scale, causal);
   return hipGetLastError();
-}
-
-int check_attn_shape(const tpattn_shape* s) {
-  if (!s) return TPMLP_ERR_NULL;
-  if (s->dtype != TPMLP_F16 && s->dtype != TPMLP_BF16) return TPMLP_ERR_DTYPE;
-  const int64_t lim = int64_t(1) << 30;
-  const int64_t d[5] = {s->batch, s->seq, s->hidden, s->heads, s->head_dim};
-  for (int64_t v : d)
-    if (v <= 0 || v > lim) return TPMLP_ERR_SHAPE;
-  const int64_t T = s->batch * s->seq, q = s->heads * s->head_dim;
-  if (T > lim || q > lim / 3) return TPMLP_ERR_SHAPE;
-  const int64_t pairs = s->batch * s->heads;
-  if (pairs > 65535 || (double)pairs * (double)s->seq * (double)s->seq >= 1099511627776.0) return TPMLP_ERR_SHAPE;
-  if (cdiv(T, 256) > 65535) return TPMLP_ERR_SHAPE;  // grid y of the column-sum pass
-  if (cdiv(T * s->heads, 256) > INT32_MAX) return TPMLP_ERR_SHAPE;  // grid of the row terms (one thread per token, head)
-  if (s->seq > kMaxSeq) return TPMLP_ERR_SHAPE;      // softmax rows are held in registers
-  // tile counts of the largest launches fit the 31-bit grid
-  if (cdiv(T, 128) * cdiv(std::max<int64_t>(3 * q, s->hidden), 128) > INT32_MAX / 2 ||
-      cdiv(s->seq, 128) * cdiv(s->seq, 128) > INT32_MAX / 2 || cdiv(s->hidden, 128) * cdiv(3 * q, 128) > INT32_MAX / 2)
-    return TPMLP_ERR_SHAPE;
-  if (s->seq % 8 || s->hidden % 8 || s->head_dim % 8) return TPMLP_ERR_ALIGN;
-  return TPMLP_OK;
-}
-
-struct AttnDims {
-  int64_t T, h, n, d, q, s, Z;
-  float scale;
-};
-
-AttnDims dims(const tpattn_shape& sh) {
-  AttnDims a;
-  a.T = sh.batch * sh.seq;
-  a.h = sh.hidden;
-  a.n = sh.heads;
-  a.d = sh.head_dim;
-  a.q = sh.heads * sh.head_dim;
-  a.s = sh.seq;
-  a.Z = sh.batch * sh.heads;
-  a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
-  return a;
 }
 
 // Backward workspace: [D fp32 Z s][dS 16-bit Z s s][dO 16-bit T q]
@@ -376,40 +303,6 @@ AttnBwdWs bwd_layout(const AttnDims& a, int dtype) {
   w.total = w.tail_off + a256(w.tail_bytes);
   return w;
 }
-
-struct Span2 {
-  const void* p;
-  size_t bytes;
-};
-
-bool overlaps(const Span2& a, const Span2& b) {
-  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
-  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
-  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
-}
-
-int check_spans(const Span2* in, int n_in, const Span2* out, int n_out) {
-  for (int i = 0; i < n_in; ++i)
-    if (!in[i].p) return TPMLP_ERR_NULL;
-  for (int i = 0; i < n_out; ++i)
-    if (!out[i].p) return TPMLP_ERR_NULL;
-  for (int i = 0; i < n_in; ++i)
-    if ((uintptr_t)in[i].p & 15u) return TPMLP_ERR_ALIGN;
-  for (int i = 0; i < n_out; ++i)
-    if ((uintptr_t)out[i].p & 15u) return TPMLP_ERR_ALIGN;
-  for (int i = 0; i < n_out; ++i) {
-    for (int j = 0; j < n_in; ++j)
-      if (overlaps(out[i], in[j])) return TPMLP_ERR_ALIAS;
-    for (int j = i + 1; j < n_out; ++j)
-      if (overlaps(out[i], out[j])) return TPMLP_ERR_ALIAS;
-  }
-  return TPMLP_OK;
-}
-
-#define ATTN_HIP(expr)                              \
-  do {                                              \
-    if ((expr) != hipSuccess) return TPMLP_ERR_HIP; \
-  } while (0)
 
 template <class S>
 int attn_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, const void* Wqkv, const void* bqkv,
@@ -503,19 +396,19 @@ using namespace tpmlp;
 extern "C" {
 
 size_t tp_attn_fwd_workspace_bytes(const tpattn_shape* shape) {
-  if (check_attn_shape(shape) != TPMLP_OK) return 0;
+  if (check_attn_shape(shape, false) != TPMLP_OK) return 0;
   const AttnDims a = dims(*shape);
   return a256((size_t)(a.Z * a.s * a.s) * 4);
 }
 
 size_t tp_attn_bwd_workspace_bytes(const tpattn_shape* shape) {
-  if (check_attn_shape(shape) != TPMLP_OK) return 0;
+  if (check_attn_shape(shape, false) != TPMLP_OK) return 0;
   return bwd_layout(dims(*shape), shape->dtype).total;
 }
 
 int tp_attn_fwd(const tpattn_shape* shape, const void* X, const void* Wqkv, const void* bqkv, const void* Wo,
                 void* QKV, void* P, void* O, void* Yp, void* ws, size_t ws_bytes, void* stream) {
-  const int rc = check_attn_shape(shape);
+  const int rc = check_attn_shape(shape, false);
   if (rc != TPMLP_OK) return rc;
   const AttnDims a = dims(*shape);
   const size_t e = 2, need = tp_attn_fwd_workspace_bytes(shape);
@@ -535,7 +428,7 @@ int tp_attn_fwd(const tpattn_shape* shape, const void* X, const void* Wqkv, cons
 int tp_attn_bwd(const tpattn_shape* shape, const void* dY, const void* X, const void* Wqkv, const void* Wo,
                 const void* QKV, const void* P, const void* O, void* dQKV, void* dXp, void* dWqkv, void* dbqkv,
                 void* dWo, void* ws, size_t ws_bytes, void* stream) {
-  const int rc = check_attn_shape(shape);
+  const int rc = check_attn_shape(shape, false);
   if (rc != TPMLP_OK) return rc;
   const AttnDims a = dims(*shape);
   const size_t e = 2, need = tp_attn_bwd_workspace_bytes(shape);

@@ -17,7 +17,9 @@ from .attn import (
     attn_shard_weights,
     attn_shard_forward,
     attn_shard_backward,
+    row_logsumexp,
     softmax_rows,
+    split_heads,
 )
 from .mlp import (
     GELU_C,
@@ -43,7 +45,9 @@ __all__ = [
     "attn_shard_weights",
     "attn_shard_forward",
     "attn_shard_backward",
+    "row_logsumexp",
     "softmax_rows",
+    "split_heads",
     "GELU_C",
     "bias2_grad",
     "SQRT_2_OVER_PI",

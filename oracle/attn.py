@@ -21,6 +21,11 @@ What is computed, and where it comes from:
   the keys, O = P V. The pages enable a fused "scale + mask + softmax" step
   ("Training GPT-2 with Megatron-LM", section 6.2, the fused_softmax
   switch). Dropout is not applied (its random numbers are not on the pages).
+* The log-sum-exp of each row of scaled, masked scores,
+  L = log sum_{visible k} exp(S_k), is what the fused ("flash") form of
+  attention keeps from its forward in place of P: P_k = exp(S_k - L).
+  Written out as the definition, with the row maximum taken out first so
+  that the exponentials cannot overflow.
 * Backward by the chain rule (the pages give none): dO = dY Wo^T,
   dWo = O^T dY, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)),
   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dWqkv = X^T dQKV,
@@ -62,10 +67,23 @@ def softmax_rows(S, causal):
     return E / E.sum(axis=-1, keepdims=True)
 
 
+def row_logsumexp(S, causal):
+    """L = log(sum over the visible keys of exp(S)) along the last axis, in
+    natural log; with `causal`, keys after the query are not visible.
+    Computed as m + log(sum exp(S - m)), m the row's largest visible score."""
+    S = np.array(S, dtype=np.float64, copy=True)
+    s_q, s_k = S.shape[-2:]
+    if causal:
+        S[..., np.triu(np.ones((s_q, s_k), dtype=bool), k=1)] = -np.inf
+    m = S.max(axis=-1)
+    return m + np.log(np.exp(S - m[..., None]).sum(axis=-1))
+
+
 def attn_forward(X, Wqkv, bqkv, Wo, batch, heads, causal=True, bo=None):
     """Self-attention block (or one shard of it, with that shard's weights
     and its number of heads): returns QKV [T, 3q], P [batch, heads, s, s],
-    O [T, q] and Y [T, h] (= O Wo (+ bo))."""
+    L [batch, heads, s] (the rows' log-sum-exp), O [T, q] and
+    Y [T, h] (= O Wo (+ bo))."""
     X, Wqkv, bqkv, Wo = _f64(X, Wqkv, bqkv, Wo)
     q = Wqkv.shape[1] // 3
     d = q // heads
@@ -77,7 +95,7 @@ def attn_forward(X, Wqkv, bqkv, Wo, batch, heads, causal=True, bo=None):
     Y = O @ Wo
     if bo is not None:
         Y = Y + np.asarray(bo, dtype=np.float64)[None, :]
-    return {"QKV": QKV, "P": P, "O": O, "Y": Y}
+    return {"QKV": QKV, "P": P, "L": row_logsumexp(S, causal), "O": O, "Y": Y}
 
 
 def attn_backward(X, Wqkv, bqkv, Wo, dY, batch, heads, causal=True):
@@ -122,9 +140,9 @@ def attn_shard_weights(Wqkv, bqkv, Wo, heads, tp, rank):
 
 
 def attn_shard_forward(X, Wqkv_i, bqkv_i, Wo_i, batch, heads_i, causal=True):
-    """One rank's forward: QKV_i, P_i, O_i and the partial Y_p,i (no bo)."""
+    """One rank's forward: QKV_i, P_i, L_i, O_i and the partial Y_p,i (no bo)."""
     fw = attn_forward(X, Wqkv_i, bqkv_i, Wo_i, batch, heads_i, causal)
-    return {"QKV": fw["QKV"], "P": fw["P"], "O": fw["O"], "Yp": fw["Y"]}
+    return {"QKV": fw["QKV"], "P": fw["P"], "L": fw["L"], "O": fw["O"], "Yp": fw["Y"]}
 
 
 def attn_shard_backward(X, Wqkv_i, bqkv_i, Wo_i, dY, batch, heads_i, causal=True):

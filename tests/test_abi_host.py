@@ -57,7 +57,9 @@ def test_exports_every_declared_function(lib):
                              "tp_mlp_bwd_recompute", "tp_mlp_reduce_partials", "tp_mlp_db2_workspace_bytes",
                              "tp_mlp_db2", "tp_mlp_debug_plan", "tp_mlp_bwd_static", "tp_mlp_fwd_sp",
                              "tp_attn_fwd_workspace_bytes",
-                             "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd"}
+                             "tp_attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd",
+                             "tp_attn_flash_fwd_workspace_bytes", "tp_attn_flash_bwd_workspace_bytes",
+                             "tp_attn_flash_fwd", "tp_attn_flash_bwd"}
     raw = ctypes.CDLL(os.path.join(ROOT, "megatron_tensor_transformer_04_amd", "libtpmlp.so"))
     for name in declared:
         assert hasattr(raw, name), name
@@ -391,6 +393,44 @@ def test_attention_workspace_sizes_and_validation(lib):
     alias = list(fake)
     alias[4] = fake[0]                                                            # QKV on top of X
     assert lib.tp_attn_fwd(ctypes.byref(ok), *alias, ws, 1 << 20, None) == 7
+
+
+def test_flash_attention_workspace_sizes_and_validation(lib):
+    """Workspace sizes of the fused attention path (nothing of size
+    seq x seq) and the checks that return before any launch."""
+    import megatron_tensor_transformer_04_amd as tpmlp
+    sh = tpmlp.attn_shape
+    fws = lambda s: lib.tp_attn_flash_fwd_workspace_bytes(ctypes.byref(s))
+    bws = lambda s: lib.tp_attn_flash_bwd_workspace_bytes(ctypes.byref(s))
+    big = sh(4, 2048, 2560, 8, 80, 2)
+    # Yp = O Wo is 32 x 8 tiles of 256 x 320 in one wave (K = 640): no k-split, the 256-byte minimum
+    assert fws(big) == 256
+    # the materialized layout without dS: D, dO, column partials, then the same k-split room
+    ks = max(64 * 4 * 256 * 320 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
+    assert bws(big) == 32 * 2048 * 4 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
+    assert bws(big) == lib.tp_attn_bwd_workspace_bytes(ctypes.byref(big)) - 32 * 2048 * 2048 * 2
+    # no sequence cap: 65536 tokens of one sequence
+    assert fws(sh(1, 65536, 64, 1, 64, 2)) > 0 and bws(sh(1, 65536, 64, 1, 64, 2)) > 0
+    assert lib.tp_attn_fwd_workspace_bytes(ctypes.byref(sh(1, 65536, 64, 1, 64, 2))) == 0
+    assert fws(sh(1, 64, 64, 1, 136, 2)) == 0             # head_dim above 128
+    assert fws(sh(1, 64, 64, 1, 128, 2)) > 0
+    assert fws(sh(4, 2048, 2560, 8, 80, 0)) == 0          # fp32 storage is not supported
+    assert fws(sh(4, 2044, 2560, 8, 80, 2)) == 0          # seq not a multiple of 8
+    ok = sh(1, 16, 16, 1, 8, 1)
+    args = [None] * 8
+    assert lib.tp_attn_flash_fwd(ctypes.byref(ok), *args, None, 0, None) == 1     # TPMLP_ERR_NULL
+    assert lib.tp_attn_flash_fwd(ctypes.byref(sh(1, 16, 16, 1, 136, 1)), *args, None, 0, None) == 2  # SHAPE
+    fake = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
+    ws = ctypes.c_void_p(0x100000)
+    assert lib.tp_attn_flash_fwd(ctypes.byref(ok), *fake, ws, 0, None) == 5       # workspace too small
+    fake12 = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(12)]
+    assert lib.tp_attn_flash_bwd(ctypes.byref(ok), *fake12, ctypes.c_void_p(0x200000), 0, None) == 5
+    unaligned = list(fake)
+    unaligned[5] = ctypes.c_void_p(0x60004)                                        # LSE not 16-byte aligned
+    assert lib.tp_attn_flash_fwd(ctypes.byref(ok), *unaligned, ws, 1 << 20, None) == 3
+    alias = list(fake)
+    alias[5] = fake[6]                                                             # LSE on top of O
+    assert lib.tp_attn_flash_fwd(ctypes.byref(ok), *alias, ws, 1 << 20, None) == 7
 
 
 def test_db2_workspace_and_validation(lib):

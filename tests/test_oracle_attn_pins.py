@@ -171,3 +171,63 @@ def test_tensor_parallel_split_identities(tp):
         assert math.isclose(float(np.sum(sb["dWo"] * Woi)), float(np.sum(dY * sf["Yp"])), rel_tol=1e-12)
     assert np.allclose(Y, full_f["Y"], atol=1e-12)
     assert np.allclose(dX, full_b["dX"], atol=1e-12)
+
+
+def _loops_logsumexp(X, Wqkv, bqkv, batch, heads, causal):
+    """L[b][j][i] = log(sum over the visible keys k of exp(q_i . k_k / sqrt(d))),
+    written from the definition with scalar loops (no maximum taken out:
+    the tiny draws keep every exponential in range)."""
+    T, h = X.shape
+    q = Wqkv.shape[1] // 3
+    d, s = q // heads, T // batch
+    qkv = [[bqkv[c] + sum(X[t][k] * Wqkv[k][c] for k in range(h)) for c in range(3 * q)] for t in range(T)]
+    L = np.zeros((batch, heads, s))
+    for b in range(batch):
+        for j in range(heads):
+            for i in range(s):
+                keys = range(i + 1) if causal else range(s)
+                tot = math.fsum(math.exp(sum(qkv[b * s + i][j * d + e] * qkv[b * s + k][q + j * d + e]
+                                             for e in range(d)) / math.sqrt(d)) for k in keys)
+                L[b, j, i] = math.log(tot)
+    return L
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("batch,seq,hidden,heads,d", [(1, 3, 4, 1, 2), (2, 5, 4, 3, 2)])
+def test_logsumexp_matches_scalar_loops(causal, batch, seq, hidden, heads, d):
+    X, Wqkv, bqkv, Wo, _ = _draw(batch, seq, hidden, heads, d, seed=batch * 5 + seq)
+    L = oracle.attn_forward(X, Wqkv, bqkv, Wo, batch, heads, causal)["L"]
+    ref = _loops_logsumexp(X, Wqkv, bqkv, batch, heads, causal)
+    assert np.max(np.abs(L - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_logsumexp_closed_forms_and_invariants():
+    """Zero queries: every visible score is 0, so L[t] = log(t + 1) (causal)
+    or log(seq); exp(S - L) is the softmax P; a shift of every score by c
+    shifts L by c, also where exp(S) alone would overflow; the first causal
+    query's L is its own score."""
+    batch, seq, hidden, heads, d = 2, 6, 5, 2, 3
+    X, Wqkv, bqkv, Wo, _ = _draw(batch, seq, hidden, heads, d, seed=11)
+    q = heads * d
+    Z = Wqkv.copy()
+    Z[:, :q] = 0.0
+    bz = bqkv.copy()
+    bz[:q] = 0.0
+    for causal, ref in ((True, np.log(np.arange(1, seq + 1))), (False, np.full(seq, np.log(seq)))):
+        L = oracle.attn_forward(X, Z, bz, Wo, batch, heads, causal)["L"]
+        assert np.allclose(L, np.broadcast_to(ref, L.shape), rtol=0, atol=1e-14)
+    fw = oracle.attn_forward(X, Wqkv, bqkv, Wo, batch, heads, True)
+    QKV = fw["QKV"]
+    Q, K = (oracle.split_heads(QKV[:, i * q:(i + 1) * q], batch, heads) for i in range(2))
+    S = Q @ K.transpose(0, 1, 3, 2) / math.sqrt(d)
+    lower = np.tril(np.ones((seq, seq), dtype=bool))
+    P = np.where(lower, np.exp(S - fw["L"][..., None]), 0.0)
+    assert np.allclose(P, fw["P"], rtol=0, atol=1e-14)
+    assert np.allclose(fw["L"][..., 0], S[..., 0, 0], rtol=0, atol=1e-14)
+    rng = np.random.default_rng(12)
+    S2 = rng.standard_normal((3, 7, 7))
+    for causal in (True, False):
+        base = oracle.row_logsumexp(S2, causal)
+        shifted = oracle.row_logsumexp(S2 + 1000.0, causal)
+        assert np.all(np.isfinite(shifted))
+        assert np.allclose(shifted - 1000.0, base, rtol=0, atol=1e-11)
