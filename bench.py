@@ -41,9 +41,9 @@ def workload_name(cfg):
             f"tokens {cfg.tokens} (micro-batch {cfg.micro_batch} x seq {cfg.seq_len}), shard width {cfg.ffn_shard}")
 
 
-# The attention shard's own source: not part of the MLP kernels whose
+# The attention shard's own sources: not part of the MLP kernels whose
 # counters the profile summary holds.
-ATTN_ONLY_SOURCES = {"tp_attn.hip"}
+ATTN_ONLY_SOURCES = {"tp_attn.hip", "tp_attn_flash.hip", "flash_attn.hpp", "attn_common.hpp"}
 
 
 def source_hash():
@@ -225,13 +225,16 @@ def attention_cpu_baseline(inp, cfg, flops_per_call, target_s=8.0, max_calls=4):
 
 def attention_rate(tpmlp, dev, reps=10, cpu=True):
     """Forward + backward of one TP rank's attention share of the 2.4B model
-    (8 of 32 heads of width 80, 4 sequences of 2048 tokens, bf16, causal)
-    through tp_attn_fwd / tp_attn_bwd, timed with HIP events on the launch
-    stream. Not part of a step (the MLP block is); reported beside it.
+    (8 of 32 heads of width 80, 4 sequences of 2048 tokens, bf16, causal),
+    timed with HIP events on the launch stream, through the fused path
+    (tp_attn_flash_fwd / tp_attn_flash_bwd: the reported rate) and through
+    the materialized one (tp_attn_fwd / tp_attn_bwd, P stored: reported
+    beside it). Not part of a step (the MLP block is).
     Algorithmic flops: per pass 2 T h 3q + 2 T q h for the projections and
     2 x 2 Z s^2 d for the scores and P V, halved under the causal mask (the
     products that only meet masked entries are not work); the backward is
-    twice the forward."""
+    twice the forward (the fused backward's recomputation of the scores is
+    not counted)."""
     import torch
     import synth
     from synth.device import to_device
@@ -240,44 +243,54 @@ def attention_rate(tpmlp, dev, reps=10, cpu=True):
     inp = synth.draw_attn_inputs(b, s, h, n, d, cfg.dtype, seed=cfg.seed, sigma_dy=cfg.sigma_dy)
     X, Wqkv, bqkv, Wo, dY = (to_device(getattr(inp, k), cfg.dtype) for k in ("X", "Wqkv", "bqkv", "Wo", "dY"))
     code = tpmlp.TPMLP_BF16
-    fws = torch.empty((tpmlp.tp_attn_fwd_workspace_bytes(b, s, h, n, d, code, cfg.causal),), dtype=torch.uint8,
-                      device=dev)
-    bws = torch.empty((tpmlp.tp_attn_bwd_workspace_bytes(b, s, h, n, d, code, cfg.causal),), dtype=torch.uint8,
-                      device=dev)
-    T, q = b * s, n * d
+    u8 = lambda nbytes: torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    T, q, Z = b * s, n * d, b * n
     e = lambda *shape: torch.empty(shape, dtype=X.dtype, device=dev)
-    QKV, P, O, Yp = e(T, 3 * q), e(b * n, s, s), e(T, q), e(T, h)
+    QKV, O, Yp = e(T, 3 * q), e(T, q), e(T, h)
     dQKV, dXp, dWqkv, dbqkv, dWo = e(T, 3 * q), e(T, h), e(h, 3 * q), e(3 * q), e(q, h)
+    LSE = torch.empty((Z, s), dtype=torch.float32, device=dev)
+    kw = dict(batch=b, heads=n, causal=cfg.causal)
 
-    def fwd():
-        tpmlp.tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, fws, batch=b, heads=n, causal=cfg.causal)
+    def measure(fwd, bwd):
+        for _ in range(2):
+            fwd()
+            bwd()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for r in range(reps):
+            ev[r][0].record()
+            fwd()
+            ev[r][1].record()
+            bwd()
+            ev[r][2].record()
+        torch.cuda.synchronize()
+        return (sum(x[0].elapsed_time(x[1]) for x in ev) / reps, sum(x[1].elapsed_time(x[2]) for x in ev) / reps)
 
-    def bwd():
-        tpmlp.tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, bws, batch=b, heads=n,
-                          causal=cfg.causal)
-
-    for _ in range(2):
-        fwd()
-        bwd()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-    torch.cuda.synchronize()
-    for r in range(reps):
-        ev[r][0].record()
-        fwd()
-        ev[r][1].record()
-        bwd()
-        ev[r][2].record()
-    torch.cuda.synchronize()
-    f_ms = sum(x[0].elapsed_time(x[1]) for x in ev) / reps
-    b_ms = sum(x[1].elapsed_time(x[2]) for x in ev) / reps
-    Z = b * n
+    ffws = u8(tpmlp.tp_attn_flash_fwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
+    fbws = u8(tpmlp.tp_attn_flash_bwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
+    f_ms, b_ms = measure(lambda: tpmlp.tp_attn_flash_fwd(X, Wqkv, bqkv, Wo, QKV, LSE, O, Yp, ffws, **kw),
+                         lambda: tpmlp.tp_attn_flash_bwd(dY, X, Wqkv, Wo, QKV, LSE, O, dQKV, dXp, dWqkv, dbqkv, dWo,
+                                                         fbws, **kw))
+    del ffws, fbws
+    P = e(Z, s, s)
+    mfws = u8(tpmlp.tp_attn_fwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
+    mbws = u8(tpmlp.tp_attn_bwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
+    mf_ms, mb_ms = measure(lambda: tpmlp.tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, mfws, **kw),
+                           lambda: tpmlp.tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, mbws,
+                                                     **kw))
+    del P, mfws, mbws
     flops_f = 2.0 * T * h * 3 * q + 2.0 * T * q * h + 2 * 2.0 * Z * s * s * d * (0.5 if cfg.causal else 1.0)
-    tflops = 3 * flops_f / ((f_ms + b_ms) * 1e-3) / 1e12
+    rate = lambda fm, bm: 3 * flops_f / ((fm + bm) * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
+    tflops, m_tflops = rate(f_ms, b_ms), rate(mf_ms, mb_ms)
     out = {"workload": f"{cfg.name}: one TP={cfg.tp} rank's attention of hidden {h}, {cfg.heads} heads of width {d} "
                        f"({n} on this rank), micro-batch {b} x seq {s}, causal, {cfg.dtype}",
+           "path": "fused (tp_attn_flash_fwd + tp_attn_flash_bwd)",
            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tflops, 2), "peak": peak,
-           "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "bound": "mfma", "cpu_baseline": None}
+           "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "bound": "mfma",
+           "materialized": {"fwd_ms": round(mf_ms, 4), "bwd_ms": round(mb_ms, 4), "tflops": round(m_tflops, 2),
+                            "frac": round(m_tflops / peak, 4)},
+           "cpu_baseline": None}
     if cpu:  # forward, then a backward that recomputes the forward: 4 x the forward's work
         out["cpu_baseline"] = attention_cpu_baseline(inp, cfg, 4 * flops_f)
     return out
@@ -304,7 +317,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other MLP workloads (GPT-2-small, the 2.4B and 7B shards)")
     ap.add_argument("--no-attn", action="store_true",
-                    help="skip timing the attention shard (tp_attn_fwd + tp_attn_bwd, not part of a step)")
+                    help="skip timing the attention shard (fused and materialized paths, not part of a step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run one plain device copy of this many MiB (a known-size kernel that "
                          "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")

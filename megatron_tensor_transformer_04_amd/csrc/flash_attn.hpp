@@ -32,6 +32,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "numerics.hpp"
 
 namespace tpmlp {
@@ -51,28 +53,54 @@ constexpr int pitch() {
   return C * 2 + 16;
 }
 
-// Rows [r0, r0 + R) and columns [0, C) of a row-major 16-bit matrix with row
-// pitch ld, rows >= nrows and columns >= d read as 0, moved through
-// registers into an LDS tile (register-staged so that the loads of the next
-// block are in flight while the current one is computed).
+// Byte offset past the end of any buffer here: a buffer load from it
+// returns zeros.
+constexpr uint32_t kOob = 0x80000000u;
+
+// Raw buffer resource over `bytes` bytes at `p` (below 2^31), from
+// wave-uniform values so that it lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int64_t bytes) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+}
+
+// Rows [r0, r0 + R) and columns [0, C) of one head's block of a row-major
+// 16-bit matrix (row pitch ld), moved through registers into an LDS tile
+// (register-staged, so that the loads of the next block are in flight while
+// the current one is computed). The loads are buffer loads over the
+// sequence's rows of the head's block: rows past the sequence read as zeros
+// from the buffer's range check, columns >= d from an offset past the end.
+// Each thread's offsets are fixed (row r0 enters as the scalar offset).
+// `one_bits` != 0: column d of every row holds that 16-bit value (the
+// forward's column of ones, whose product with P^T is the row sum).
 template <int R, int C>
 struct TileCopy {
   static constexpr int CH = C / 8, NCH = R * CH, N = (NCH + kThreads - 1) / kThreads;
+  uint32_t off[N], one[N];
   u32x4 v[N];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int64_t r0, int64_t nrows, int d, int tid) {
+  __device__ __forceinline__ void init(int64_t ld, int d, int tid, uint32_t one_bits = 0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int c = tid + i * kThreads, r = c / CH, cc = c % CH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (c < NCH && r0 + r < nrows && cc * 8 < d) x = *reinterpret_cast<const u32x4*>(base + (r0 + r) * ld + cc * 8);
-      v[i] = x;
+      off[i] = c < NCH && cc * 8 < d ? (uint32_t)(r * ld * 2 + cc * 16) : kOob;
+      one[i] = c < NCH && cc * 8 == d ? one_bits : 0u;
     }
+  }
+  // the loaded registers are first touched by store(): no wait in between
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row_off) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], row_off, 0);
   }
   __device__ __forceinline__ void store(char* t, int tid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int c = tid + i * kThreads, r = c / CH, cc = c % CH;
-      if (c < NCH) *reinterpret_cast<u32x4*>(t + r * pitch<C>() + cc * 16) = v[i];
+      u32x4 x = v[i];
+      x[0] |= one[i];
+      if (c < NCH) *reinterpret_cast<u32x4*>(t + r * pitch<C>() + cc * 16) = x;
     }
   }
 };
@@ -139,6 +167,16 @@ __device__ __forceinline__ void store_t(uint16_t* orow, const f32x16& x, int d0,
   }
 }
 
+// Launch position pos (0 .. n-1, in units of Z workgroups) -> rank of the
+// row block by work, 0 the longest: the first half of the launch takes ranks
+// 0, 1, ..., the second half the shortest first. Where two workgroups share
+// a CU they are launch positions pos and pos + n/2, and their causal work
+// then adds up to about the same on every CU.
+__device__ __forceinline__ int balanced_rank(int pos, int n) {
+  const int half = (n + 1) / 2;
+  return pos < half ? pos : n - 1 - (pos - half);
+}
+
 struct Args {
   const uint16_t* qkv;  // [T][3q]: Q | K | V blocks, head j at columns j d .. j d + d - 1 of each
   const uint16_t* dO;   // [T][q] (backward)
@@ -150,17 +188,33 @@ struct Args {
   float scale_log2;          // log2(e) / sqrt(d)
   float scale;               // 1 / sqrt(d)
   int causal;
+  uint32_t one_bits;         // 1.0 in the storage format
 };
 
-// Forward: one workgroup per (pair z, 128 queries), longest (last) query
-// blocks first; wave w owns queries q0 + 32 w + c.
-template <class S, int KS, int FD>
-__global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
+// Largest of the 16 values of a fragment.
+__device__ __forceinline__ float frag_max(const f32x16& v) {
+  float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, v[15]));
+}
+
+// Forward: one workgroup per (pair z, 128 queries), balanced_rank order;
+// wave w owns queries q0 + 32 w + c. Scores stay in raw units (Q K^T) until
+// the exponent, exp2(x c - m c) with c = log2(e) / sqrt(d) in one FMA. The
+// running maximum m of a row only grows; O and the running sum are rescaled
+// by exp2((m_old - m_new) c) in the blocks where some lane's maximum grew.
+// ONES (d not a multiple of 32): V's zero padding gets a column of ones at
+// d, so that O^T's row d accumulates the row sum of the rounded
+// probabilities in the same products (rescaled with O); otherwise the lanes
+// add their probabilities.
+template <class S, int KS, int FD, bool ONES>
+__global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
   constexpr int DK = 16 * KS, DV = 32 * FD;
   constexpr int KB = kBlk * pitch<DK>(), STG = KB + kBlk * pitch<DV>();
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int qb = a.nblk - 1 - (int)(blockIdx.x / a.Z), z = (int)(blockIdx.x % a.Z);
+  const int qb = a.nblk - 1 - balanced_rank((int)(blockIdx.x / a.Z), a.nblk), z = (int)(blockIdx.x % a.Z);
   const int b = z / a.heads, j = z % a.heads;
   const int64_t q0 = (int64_t)qb * kRows, qw = q0 + 32 * wave, qi = qw + (lane & 31);
   const uint16_t* Qp = a.qkv + (int64_t)b * a.s * a.ld3 + (int64_t)j * a.d;
@@ -171,6 +225,8 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
   // keys this wave reads: none if all its queries are past the end, else up
   // to its last query when causal (wave-uniform)
   const int64_t wave_kend = qw >= a.s ? 0 : (a.causal ? min(kv_end, qw + 32) : kv_end);
+  const uint32_t ones = ONES ? a.one_bits : 0u;
+  const float c = a.scale_log2;
 
   u32x4 qf[KS];  // B operand of K Q^T: query qi, columns 16 ks + 8 h .. + 7
 #pragma unroll
@@ -180,67 +236,78 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
     if (qi < a.s && dd < a.d) v = *reinterpret_cast<const u32x4*>(Qp + qi * a.ld3 + dd);
     qf[ks] = v;
   }
+  const int rowb = (int)(a.ld3 * 2);
+  const auto krs = wave_rsrc(Kp, (a.s * a.ld3 - (int64_t)j * a.d - a.q) * 2);
+  const auto vrs = wave_rsrc(Vp, (a.s * a.ld3 - (int64_t)j * a.d - 2 * a.q) * 2);
   TileCopy<kBlk, DK> kt;
   TileCopy<kBlk, DV> vt;
+  kt.init(a.ld3, a.d, tid);
+  vt.init(a.ld3, a.d, tid, ones);
   f32x16 o[FD];
 #pragma unroll
   for (int f = 0; f < FD; ++f) o[f] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
   if (nkb > 0) {
-    kt.load(Kp, a.ld3, 0, a.s, a.d, tid);
-    vt.load(Vp, a.ld3, 0, a.s, a.d, tid);
+    kt.load(krs, 0);
+    vt.load(vrs, 0);
     kt.store(smem, tid);
     vt.store(smem + KB, tid);
   }
+  // every load issued so far (the Q fragments too) has landed: the loop's
+  // products then wait only for their own LDS reads, not for the next
+  // block's loads in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int64_t k0 = (int64_t)kb * kBlk;
     if (kb + 1 < nkb) {
-      kt.load(Kp, a.ld3, k0 + kBlk, a.s, a.d, tid);
-      vt.load(Vp, a.ld3, k0 + kBlk, a.s, a.d, tid);
+      kt.load(krs, (int)(k0 + kBlk) * rowb);
+      vt.load(vrs, (int)(k0 + kBlk) * rowb);
     }
     if (k0 < wave_kend) {
       const char* sk = smem + (kb & 1) * STG;
       const char* sv = sk + KB;
-      // x^T = K Q^T, scaled to log2 units: keys k0 + 32 mf + frag_row(r, h)
+      // x^T = K Q^T (raw): keys k0 + 32 mf + frag_row(r, h), query qi
       f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int mf = 0; mf < 2; ++mf)
           sc[mf] = S::mfma32x32x16(frag_rows<DK>(sk, 32 * mf, 16 * ks, lane), qf[ks], sc[mf]);
-      const bool diag = a.causal && k0 + kBlk - 1 > qw;
-      float mb = -INFINITY;
+      // keys past the end, or after the query: only in the last block and on
+      // the diagonal (wave-uniform)
+      if (k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw)) {
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
+        for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t ki = k0 + 32 * mf + frag_row(r, h);
-          float v = sc[mf][r] * a.scale_log2;
-          if (ki >= a.s || (diag && ki > qi)) v = -INFINITY;
-          sc[mf][r] = v;
-          mb = fmaxf(mb, v);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int64_t ki = k0 + 32 * mf + frag_row(r, h);
+            if (ki >= a.s || (a.causal && ki > qi)) sc[mf][r] = -INFINITY;
+          }
+      }
+      float mb = fmaxf(frag_max(sc[0]), frag_max(sc[1]));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
       const float m_new = fmaxf(m_run, mb);
-      // while no key of the row has been seen (m_new = -inf) every p is 0 and
-      // the state stays as it is
-      const float msub = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
+      if (__ballot(m_new != m_run)) {
+        // m_new stays -inf only while every key seen is masked: nothing to rescale then
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+        for (int f = 0; f < FD; ++f) o[f] *= alpha;
+        if (!ONES) l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
       float ls = 0.0f;
 #pragma unroll
       for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sc[mf][r] - msub);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[mf][r], c, -mc));
           sc[mf][r] = p;
-          ls += p;
+          if (!ONES) ls += p;
         }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int f = 0; f < FD; ++f) o[f] *= alpha;
+      if (!ONES) l_run += ls;
       // O^T += V^T P^T over four 16-key steps
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -259,27 +326,39 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
     __syncthreads();
   }
 
-  // O = O^T / l (rows d < a.d); L = (m + log2 l) ln 2
-  const float l_all = l_run + __shfl_xor(l_run, 32);
+  // the row sum: O^T's row d (in lanes h = 0, register 4 g1 of the last
+  // fragment), or the two halves' sums
+  float l_all;
+  if (ONES) {
+    const int g1 = (a.d - 32 * (FD - 1)) >> 3;
+    const f32x16& ol = o[FD - 1];
+    const float lv = g1 == 1 ? ol[4] : (g1 == 2 ? ol[8] : ol[12]);
+    l_all = __shfl(lv, lane & 31);
+  } else {
+    l_all = l_run + __shfl_xor(l_run, 32);
+  }
+  // O = O^T / l (rows d < a.d); L = (m c + log2 l) ln 2
   if (qi < a.s) {
     const float inv = 1.0f / l_all;
     uint16_t* orow = a.out + ((int64_t)b * a.s + qi) * a.ldo + (int64_t)j * a.d;
 #pragma unroll
     for (int f = 0; f < FD; ++f) store_t<S>(orow, o[f], 32 * f, a.d, h, inv);
-    if (h == 0) a.lse[(int64_t)z * a.s + qi] = (m_run + log2f(l_all)) * kLn2;
+    if (h == 0) a.lse[(int64_t)z * a.s + qi] = (m_run * c + log2f(l_all)) * kLn2;
   }
 }
 
-// dK and dV: one workgroup per (pair z, 128 keys), first (longest, when
-// causal) key blocks first; wave w owns keys k0 + 32 w + c and loops over
-// 64-query blocks (Q and dO tiles, L and D of those queries in LDS).
+// dK and dV: one workgroup per (pair z, 128 keys), balanced_rank order
+// (longest first: the first key blocks when causal); wave w owns keys
+// k0 + 32 w + c and loops over 64-query blocks (Q and dO tiles, and per
+// query L log2(e) and D / sqrt(d), in LDS):
+//   p = exp2(x c - L log2(e)),  dS = p (dP / sqrt(d) - D / sqrt(d)).
 template <class S, int KS, int FD>
 __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
   constexpr int DV = 32 * FD;
   constexpr int TB = kBlk * pitch<DV>(), STG = 2 * TB + 2 * kBlk * 4;
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int kblk = (int)(blockIdx.x / a.Z), z = (int)(blockIdx.x % a.Z);
+  const int kblk = balanced_rank((int)(blockIdx.x / a.Z), a.nblk), z = (int)(blockIdx.x % a.Z);
   const int b = z / a.heads, j = z % a.heads;
   const int64_t k0 = (int64_t)kblk * kRows, kw = k0 + 32 * wave, ki = kw + (lane & 31);
   const uint16_t* Qp = a.qkv + (int64_t)b * a.s * a.ld3 + (int64_t)j * a.d;
@@ -291,6 +370,7 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
   const int64_t qstart = a.causal ? k0 : 0;  // queries before the block's first key see none of its keys
   const int nqb = (int)((a.s - qstart + kBlk - 1) / kBlk);
   const bool live = kw < a.s;
+  const float c = a.scale_log2, sc_d = a.scale;
 
   u32x4 kf[KS], vf[KS];  // B operands of Q K^T and dO V^T: key ki, columns 16 ks + 8 h .. + 7
 #pragma unroll
@@ -304,37 +384,45 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
     kf[ks] = x;
     vf[ks] = y;
   }
+  const auto qrs = wave_rsrc(Qp, (a.s * a.ld3 - (int64_t)j * a.d) * 2);
+  const auto drs = wave_rsrc(dOp, (a.s * a.ldo - (int64_t)j * a.d) * 2);
+  const int rowq = (int)(a.ld3 * 2), rowd = (int)(a.ldo * 2);
   TileCopy<kBlk, DV> qt, dt;
-  float rowv = 0.0f;  // thread t < 64: L (log2 units) of query t of the block; 64 <= t < 128: D
+  qt.init(a.ld3, a.d, tid);
+  dt.init(a.ldo, a.d, tid);
+  // thread t < 64: L of query t of the block (+inf past the end: p = 0);
+  // 64 <= t < 128: its D; scaled to L log2(e) and D / sqrt(d) when stored
+  float rowv = 0.0f;
   auto load_rows = [&](int64_t r0) {
     const int t = tid & 63;
-    if (tid < 64) rowv = r0 + t < a.s ? Lz[r0 + t] * kLog2e : INFINITY;  // P = 0 past the end
+    if (tid < 64) rowv = r0 + t < a.s ? Lz[r0 + t] : INFINITY;
     else if (tid < 128) rowv = r0 + t < a.s ? Dz[r0 + t] : 0.0f;
   };
   auto store_stage = [&](char* t) {
     qt.store(t, tid);
     dt.store(t + TB, tid);
-    if (tid < 128) reinterpret_cast<float*>(t + 2 * TB)[tid] = rowv;
+    if (tid < 128) reinterpret_cast<float*>(t + 2 * TB)[tid] = rowv * (tid < 64 ? kLog2e : sc_d);
   };
   f32x16 dk[FD], dv[FD];
 #pragma unroll
   for (int f = 0; f < FD; ++f) dk[f] = dv[f] = f32x16{};
 
   if (nqb > 0) {
-    qt.load(Qp, a.ld3, qstart, a.s, a.d, tid);
-    dt.load(dOp, a.ldo, qstart, a.s, a.d, tid);
+    qt.load(qrs, (int)qstart * rowq);
+    dt.load(drs, (int)qstart * rowd);
     load_rows(qstart);
     store_stage(smem);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // as in the forward: nothing in flight before the loop
   __syncthreads();
   for (int ib = 0; ib < nqb; ++ib) {
     const int64_t q0 = qstart + (int64_t)ib * kBlk;
     if (ib + 1 < nqb) {
-      qt.load(Qp, a.ld3, q0 + kBlk, a.s, a.d, tid);
-      dt.load(dOp, a.ldo, q0 + kBlk, a.s, a.d, tid);
+      qt.load(qrs, (int)(q0 + kBlk) * rowq);
+      dt.load(drs, (int)(q0 + kBlk) * rowd);
       load_rows(q0 + kBlk);
     }
-    // causal: a block whose queries all precede the wave's keys has P = 0
+    // causal: a block whose queries all precede the wave's keys has p = 0
     if (live && !(a.causal && q0 + kBlk - 1 < kw)) {
       const char* sq = smem + (ib & 1) * STG;
       const char* sd = sq + TB;
@@ -348,23 +436,27 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
           p[mf] = S::mfma32x32x16(frag_rows<DV>(sq, 32 * mf, 16 * ks, lane), kf[ks], p[mf]);
           dp[mf] = S::mfma32x32x16(frag_rows<DV>(sd, 32 * mf, 16 * ks, lane), vf[ks], dp[mf]);
         }
-      const bool diag = a.causal && q0 < kw + 31;
+      auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
+        for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rr = 32 * mf + 8 * g + 4 * h;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + rr);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sl + kBlk + rr);
+          for (int g = 0; g < 4; ++g) {
+            const int rr = 32 * mf + 8 * g + 4 * h;
+            const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + rr);
+            const f32x4 D4 = *reinterpret_cast<const f32x4*>(sl + kBlk + rr);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float pv = __builtin_amdgcn_exp2f(p[mf][r] * a.scale_log2 - L4[e]);
-            if (diag && q0 + rr + e < ki) pv = 0.0f;
-            p[mf][r] = pv;
-            dp[mf][r] = pv * (dp[mf][r] - D4[e]) * a.scale;  // dS
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float pv = __builtin_amdgcn_exp2f(fmaf(p[mf][r], c, -L4[e]));
+              if (masked && q0 + rr + e < ki) pv = 0.0f;
+              p[mf][r] = pv;
+              dp[mf][r] = pv * fmaf(dp[mf][r], sc_d, -D4[e]);  // dS
+            }
           }
-        }
+      };
+      // queries before the wave's last key: only on the diagonal (wave-uniform)
+      if (a.causal && q0 < kw + 31) softmax_grad(std::true_type{});
+      else softmax_grad(std::false_type{});
       // dV^T += dO^T P and dK^T += Q^T dS over four 16-query steps
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -391,16 +483,16 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
   }
 }
 
-// dQ: one workgroup per (pair z, 128 queries), longest query blocks first;
-// wave w owns queries q0 + 32 w + c and loops over 64-key blocks (K and V
-// tiles in LDS), recomputing P^T and dS^T in the transposed layout.
+// dQ: one workgroup per (pair z, 128 queries), balanced_rank order; wave w
+// owns queries q0 + 32 w + c and loops over 64-key blocks (K and V tiles in
+// LDS), recomputing p and dS in the transposed layout.
 template <class S, int KS, int FD>
-__global__ __launch_bounds__(kThreads) void flash_bwd_q_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, KS <= 6 ? 2 : 1) void flash_bwd_q_kernel(Args a) {
   constexpr int DK = 16 * KS, DV = 32 * FD;
   constexpr int KB = kBlk * pitch<DV>(), STG = KB + kBlk * pitch<DK>();
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int qb = a.nblk - 1 - (int)(blockIdx.x / a.Z), z = (int)(blockIdx.x % a.Z);
+  const int qb = a.nblk - 1 - balanced_rank((int)(blockIdx.x / a.Z), a.nblk), z = (int)(blockIdx.x % a.Z);
   const int b = z / a.heads, j = z % a.heads;
   const int64_t q0 = (int64_t)qb * kRows, qw = q0 + 32 * wave, qi = qw + (lane & 31);
   const uint16_t* Qp = a.qkv + (int64_t)b * a.s * a.ld3 + (int64_t)j * a.d;
@@ -410,6 +502,7 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_q_kernel(Args a) {
   const int64_t kv_end = a.causal ? min(a.s, q0 + kRows) : a.s;
   const int nkb = (int)((kv_end + kBlk - 1) / kBlk);
   const int64_t wave_kend = qw >= a.s ? 0 : (a.causal ? min(kv_end, qw + 32) : kv_end);
+  const float c = a.scale_log2, sc_d = a.scale;
 
   u32x4 qf[KS], df[KS];  // B operands of K Q^T and V dO^T: query qi, columns 16 ks + 8 h .. + 7
 #pragma unroll
@@ -424,25 +517,31 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_q_kernel(Args a) {
     df[ks] = y;
   }
   const float Lq = qi < a.s ? a.lse[(int64_t)z * a.s + qi] * kLog2e : 0.0f;
-  const float Dq = qi < a.s ? a.D[(int64_t)z * a.s + qi] : 0.0f;
+  const float Dq = qi < a.s ? a.D[(int64_t)z * a.s + qi] * sc_d : 0.0f;
+  const int rowb = (int)(a.ld3 * 2);
+  const auto krs = wave_rsrc(Kp, (a.s * a.ld3 - (int64_t)j * a.d - a.q) * 2);
+  const auto vrs = wave_rsrc(Vp, (a.s * a.ld3 - (int64_t)j * a.d - 2 * a.q) * 2);
   TileCopy<kBlk, DV> kt;
   TileCopy<kBlk, DK> vt;
+  kt.init(a.ld3, a.d, tid);
+  vt.init(a.ld3, a.d, tid);
   f32x16 dq[FD];
 #pragma unroll
   for (int f = 0; f < FD; ++f) dq[f] = f32x16{};
 
   if (nkb > 0) {
-    kt.load(Kp, a.ld3, 0, a.s, a.d, tid);
-    vt.load(Vp, a.ld3, 0, a.s, a.d, tid);
+    kt.load(krs, 0);
+    vt.load(vrs, 0);
     kt.store(smem, tid);
     vt.store(smem + KB, tid);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // as in the forward: nothing in flight before the loop
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int64_t k0 = (int64_t)kb * kBlk;
     if (kb + 1 < nkb) {
-      kt.load(Kp, a.ld3, k0 + kBlk, a.s, a.d, tid);
-      vt.load(Vp, a.ld3, k0 + kBlk, a.s, a.d, tid);
+      kt.load(krs, (int)(k0 + kBlk) * rowb);
+      vt.load(vrs, (int)(k0 + kBlk) * rowb);
     }
     if (k0 < wave_kend) {
       const char* sk = smem + (kb & 1) * STG;
@@ -456,16 +555,22 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_q_kernel(Args a) {
           p[mf] = S::mfma32x32x16(frag_rows<DV>(sk, 32 * mf, 16 * ks, lane), qf[ks], p[mf]);
           dp[mf] = S::mfma32x32x16(frag_rows<DK>(sv, 32 * mf, 16 * ks, lane), df[ks], dp[mf]);
         }
-      const bool diag = a.causal && k0 + kBlk - 1 > qw;
+      auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
+        for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t kk = k0 + 32 * mf + frag_row(r, h);
-          float pv = __builtin_amdgcn_exp2f(p[mf][r] * a.scale_log2 - Lq);
-          if (kk >= a.s || (diag && kk > qi)) pv = 0.0f;
-          dp[mf][r] = pv * (dp[mf][r] - Dq) * a.scale;  // dS^T
-        }
+          for (int r = 0; r < 16; ++r) {
+            float pv = __builtin_amdgcn_exp2f(fmaf(p[mf][r], c, -Lq));
+            if (masked) {
+              const int64_t kk = k0 + 32 * mf + frag_row(r, h);
+              if (kk >= a.s || (a.causal && kk > qi)) pv = 0.0f;
+            }
+            dp[mf][r] = pv * fmaf(dp[mf][r], sc_d, -Dq);  // dS^T
+          }
+      };
+      // keys past the end or after the query: last block and diagonal only (wave-uniform)
+      if (k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw)) softmax_grad(std::true_type{});
+      else softmax_grad(std::false_type{});
       // dQ^T += K^T dS^T over four 16-key steps
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -489,31 +594,44 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_q_kernel(Args a) {
   }
 }
 
-// Launch one of the three kernels for head width d <= 128: KS = ceil(d / 16)
-// 16-wide steps of the d-sums, FD = ceil(d / 32) 32-row fragments of the
-// d-wide results. Grid: nblk * Z workgroups.
-#define TPMLP_FLASH_LAUNCH(KERNEL)                                                  \
-  template <class S>                                                               \
-  hipError_t launch_##KERNEL(const Args& a, hipStream_t st) {                      \
-    const dim3 grid((unsigned)((int64_t)a.nblk * a.Z)), block(kThreads);           \
-    switch ((a.d + 15) / 16) {                                                     \
-      case 1: hipLaunchKernelGGL((KERNEL<S, 1, 1>), grid, block, 0, st, a); break; \
-      case 2: hipLaunchKernelGGL((KERNEL<S, 2, 1>), grid, block, 0, st, a); break; \
-      case 3: hipLaunchKernelGGL((KERNEL<S, 3, 2>), grid, block, 0, st, a); break; \
-      case 4: hipLaunchKernelGGL((KERNEL<S, 4, 2>), grid, block, 0, st, a); break; \
-      case 5: hipLaunchKernelGGL((KERNEL<S, 5, 3>), grid, block, 0, st, a); break; \
-      case 6: hipLaunchKernelGGL((KERNEL<S, 6, 3>), grid, block, 0, st, a); break; \
-      case 7: hipLaunchKernelGGL((KERNEL<S, 7, 4>), grid, block, 0, st, a); break; \
-      case 8: hipLaunchKernelGGL((KERNEL<S, 8, 4>), grid, block, 0, st, a); break; \
-      default: return hipErrorInvalidValue;                                        \
-    }                                                                              \
-    return hipGetLastError();                                                      \
+// Launches for head width d <= 128: KS = ceil(d / 16) 16-wide steps of the
+// d-sums, FD = ceil(d / 32) 32-row fragments of the d-wide results; the
+// forward's column of ones where d is not a multiple of 32. Grid: nblk * Z
+// workgroups.
+#define TPMLP_FLASH_CASES(KERNEL, ...)                                                  \
+  switch ((a.d + 15) / 16) {                                                            \
+    case 1: hipLaunchKernelGGL((KERNEL<S, 1, 1 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 2: hipLaunchKernelGGL((KERNEL<S, 2, 1 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 3: hipLaunchKernelGGL((KERNEL<S, 3, 2 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 4: hipLaunchKernelGGL((KERNEL<S, 4, 2 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 5: hipLaunchKernelGGL((KERNEL<S, 5, 3 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 6: hipLaunchKernelGGL((KERNEL<S, 6, 3 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 7: hipLaunchKernelGGL((KERNEL<S, 7, 4 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    case 8: hipLaunchKernelGGL((KERNEL<S, 8, 4 __VA_ARGS__>), grid, block, 0, st, a); break; \
+    default: return hipErrorInvalidValue;                                               \
   }
 
-TPMLP_FLASH_LAUNCH(flash_fwd_kernel)
-TPMLP_FLASH_LAUNCH(flash_bwd_kv_kernel)
-TPMLP_FLASH_LAUNCH(flash_bwd_q_kernel)
-#undef TPMLP_FLASH_LAUNCH
+template <class S>
+hipError_t launch_fwd(const Args& a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.nblk * a.Z)), block(kThreads);
+  if (a.d % 32) {
+    TPMLP_FLASH_CASES(flash_fwd_kernel, , true)
+  } else {
+    TPMLP_FLASH_CASES(flash_fwd_kernel, , false)
+  }
+  return hipGetLastError();
+}
+
+template <class S>
+hipError_t launch_bwd(const Args& a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.nblk * a.Z)), block(kThreads);
+  TPMLP_FLASH_CASES(flash_bwd_kv_kernel)
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TPMLP_FLASH_CASES(flash_bwd_q_kernel)
+  return hipGetLastError();
+}
+#undef TPMLP_FLASH_CASES
 
 }  // namespace flash
 }  // namespace tpmlp

@@ -63,6 +63,7 @@ flash::Args core_args(const AttnDims& a, int causal, const void* QKV) {
   f.scale = a.scale;
   f.scale_log2 = flash::kLog2e * a.scale;
   f.causal = causal ? 1 : 0;
+  f.one_bits = 0;
   return f;
 }
 
@@ -76,7 +77,8 @@ int flash_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, cons
   flash::Args f = core_args(a, causal, QKV);
   f.lse = static_cast<float*>(LSE);
   f.out = static_cast<uint16_t*>(O);
-  ATTN_HIP(flash::launch_flash_fwd_kernel<S>(f, st));
+  f.one_bits = dtype == TPMLP_BF16 ? 0x3F80u : 0x3C00u;  // 1.0
+  ATTN_HIP(flash::launch_fwd<S>(f, st));
   // Yp = O Wo: P = O [T,q] k-contiguous, Q = Wo [q,h] n-contiguous
   ATTN_HIP(planned_gemm(dtype, true, false, a.T, a.h, a.q, O, a.q, Wo, a.h, Yp, a.h, nullptr,
                         static_cast<float*>(ws), ws_bytes, st));
@@ -110,8 +112,7 @@ int flash_bwd_impl(const AttnDims& a, int dtype, int causal, const void* dY, con
   f.D = drow;
   f.lse = const_cast<float*>(static_cast<const float*>(LSE));
   f.out = static_cast<uint16_t*>(dQKV);
-  ATTN_HIP(flash::launch_flash_bwd_kv_kernel<S>(f, st));
-  ATTN_HIP(flash::launch_flash_bwd_q_kernel<S>(f, st));
+  ATTN_HIP(flash::launch_bwd<S>(f, st));
   // dbqkv = column sums of dQKV
   hipLaunchKernelGGL(colsum_part_kernel<S>, dim3((unsigned)cdiv(T3, 256), (unsigned)w.part_blk), dim3(256), 0, st,
                      static_cast<const T*>(dQKV), a.T, T3, part);
