@@ -46,7 +46,8 @@ inline int check_attn_shape(const tpattn_shape* s, bool flash) {
   if (flash) {
     if (s->head_dim > kFlashMaxHeadDim) return TPMLP_ERR_SHAPE;
     if (cdiv(s->seq, 128) * pairs > INT32_MAX) return TPMLP_ERR_SHAPE;  // one workgroup per (pair, 128 rows)
-    if (s->seq * 3 * q * 2 >= (int64_t(1) << 31)) return TPMLP_ERR_SHAPE;  // a sequence's QKV rows: one buffer range
+    // a sequence's QKV rows (and one block of rows past them) as one buffer range
+    if ((s->seq + 128) * 3 * q * 2 >= (int64_t(1) << 31)) return TPMLP_ERR_SHAPE;
   } else {
     if ((double)pairs * (double)s->seq * (double)s->seq >= 1099511627776.0) return TPMLP_ERR_SHAPE;
     if (s->seq > kMaxSeq) return TPMLP_ERR_SHAPE;  // softmax rows are held in registers

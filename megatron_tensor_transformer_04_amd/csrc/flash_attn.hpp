@@ -7,7 +7,8 @@
 //             row (the online form of the softmax);
 //   backward: P = exp(x - L) recomputed from L, then
 //             dV = P^T dO, dS = P (dO V^T - D) / sqrt(d), D = rowsum(dO O),
-//             dK = dS^T Q (flash_bwd_kv_kernel, one workgroup per 128 keys)
+//             dK = dS^T Q (flash_bwd_kv_kernel, one workgroup per 128 keys,
+//             one launch for dV and one for dK)
 //             and dQ = dS K (flash_bwd_q_kernel, one workgroup per 128
 //             queries, recomputing P and dS): every output element is summed
 //             by one lane in a fixed order, no atomics.
@@ -44,6 +45,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kThreads = 256;  // four waves, 32 rows each
 constexpr int kRows = 128;     // rows (queries or keys) per workgroup
 constexpr int kBlk = 64;       // keys (queries) per block of the inner loop
+// The forward's reference maximum moves only when a row's scores exceed it
+// by more than this (log2 units): probabilities stay below 2^8.
+constexpr float kRescale = 8.0f;
 
 // Row pitch in bytes of a tile of C 16-bit columns in LDS: 16 bytes of
 // padding put the 32 rows of a 16-byte fragment read, and the 4 rows of a
@@ -141,7 +145,7 @@ __device__ __forceinline__ u32x4 pack_step(const f32x16& v, int st) {
   u32x4 w;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    w[e] = (uint32_t)S::from_f(v[8 * st + 2 * e]) | ((uint32_t)S::from_f(v[8 * st + 2 * e + 1]) << 16);
+    w[e] = S::pack2(v[8 * st + 2 * e], v[8 * st + 2 * e + 1]);
   return w;
 }
 
@@ -160,8 +164,8 @@ __device__ __forceinline__ void store_t(uint16_t* orow, const f32x16& x, int d0,
     const int dc = d0 + 8 * g + 4 * h;
     if (dc < d) {
       u32x2 w;
-      w[0] = (uint32_t)S::from_f(x[4 * g] * mul) | ((uint32_t)S::from_f(x[4 * g + 1] * mul) << 16);
-      w[1] = (uint32_t)S::from_f(x[4 * g + 2] * mul) | ((uint32_t)S::from_f(x[4 * g + 3] * mul) << 16);
+      w[0] = S::pack2(x[4 * g] * mul, x[4 * g + 1] * mul);
+      w[1] = S::pack2(x[4 * g + 2] * mul, x[4 * g + 3] * mul);
       *reinterpret_cast<u32x2*>(orow + dc) = w;
     }
   }
@@ -261,20 +265,36 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int64_t k0 = (int64_t)kb * kBlk;
-    if (kb + 1 < nkb) {
-      kt.load(krs, (int)(k0 + kBlk) * rowb);
-      vt.load(vrs, (int)(k0 + kBlk) * rowb);
-    }
+    // the next block's tiles (past the end in the last iteration: zeros,
+    // stored to the stage nothing reads any more)
+    kt.load(krs, (int)(k0 + kBlk) * rowb);
+    vt.load(vrs, (int)(k0 + kBlk) * rowb);
     if (k0 < wave_kend) {
       const char* sk = smem + (kb & 1) * STG;
       const char* sv = sk + KB;
-      // x^T = K Q^T (raw): keys k0 + 32 mf + frag_row(r, h), query qi
+      // x^T = K Q^T (raw): keys k0 + 32 mf + frag_row(r, h), query qi. All
+      // of the block's K fragments are read before the first product, and
+      // V's right after the last, so that the LDS latency is paid once per
+      // phase (the V reads land while the softmax runs).
+      u32x4 kfr[2][KS];
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kfr[mf][ks] = frag_rows<DK>(sk, 32 * mf, 16 * ks, lane);
       f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
-          sc[mf] = S::mfma32x32x16(frag_rows<DK>(sk, 32 * mf, 16 * ks, lane), qf[ks], sc[mf]);
+        for (int mf = 0; mf < 2; ++mf) sc[mf] = S::mfma32x32x16(kfr[mf][ks], qf[ks], sc[mf]);
+      // (V read ahead only while its 16 FD registers fit beside the rest)
+      constexpr bool kVAhead = FD <= 3;
+      u32x4 vfr[4][FD];
+      if constexpr (kVAhead) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int f = 0; f < FD; ++f) vfr[st][f] = frag_cols<DV>(sv, 16 * st, 32 * f, lane);
+      }
       // keys past the end, or after the query: only in the last block and on
       // the diagonal (wave-uniform)
       if (k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw)) {
@@ -288,8 +308,12 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
       }
       float mb = fmaxf(frag_max(sc[0]), frag_max(sc[1]));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float m_new = fmaxf(m_run, mb);
-      if (__ballot(m_new != m_run)) {
+      // m_run is the reference the exponents are taken against, not always
+      // the row's maximum: it moves (and O and the sum are rescaled) only
+      // where some row's maximum exceeds it by more than kRescale in log2
+      // units, so p <= 2^kRescale; the first block always sets it
+      if (__ballot((mb - m_run) * c > kRescale)) {
+        const float m_new = fmaxf(m_run, mb);
         // m_new stays -inf only while every key seen is masked: nothing to rescale then
         const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
 #pragma unroll
@@ -313,12 +337,13 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
       for (int st = 0; st < 4; ++st) {
         const u32x4 pf = pack_step<S>(sc[st >> 1], st & 1);
 #pragma unroll
-        for (int f = 0; f < FD; ++f) o[f] = S::mfma32x32x16(frag_cols<DV>(sv, 16 * st, 32 * f, lane), pf, o[f]);
+        for (int f = 0; f < FD; ++f)
+          o[f] = S::mfma32x32x16(kVAhead ? vfr[st][f] : frag_cols<DV>(sv, 16 * st, 32 * f, lane), pf, o[f]);
       }
     }
     // the other stage was last read in the previous iteration, before the
     // barrier that ended it
-    if (kb + 1 < nkb) {
+    {
       char* nx = smem + ((kb + 1) & 1) * STG;
       kt.store(nx, tid);
       vt.store(nx + KB, tid);
@@ -347,13 +372,16 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
   }
 }
 
-// dK and dV: one workgroup per (pair z, 128 keys), balanced_rank order
-// (longest first: the first key blocks when causal); wave w owns keys
-// k0 + 32 w + c and loops over 64-query blocks (Q and dO tiles, and per
-// query L log2(e) and D / sqrt(d), in LDS):
-//   p = exp2(x c - L log2(e)),  dS = p (dP / sqrt(d) - D / sqrt(d)).
-template <class S, int KS, int FD>
-__global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
+// dV (ROLE_DK false) or dK (ROLE_DK true): one workgroup per (pair z, 128
+// keys), balanced_rank order (longest first: the first key blocks when
+// causal); wave w owns keys k0 + 32 w + c and loops over 64-query blocks (Q
+// and dO tiles, and per query L log2(e) and D / sqrt(d), in LDS):
+//   p = exp2(x c - L log2(e));  dV^T += dO^T P;
+//   dS = p (dP / sqrt(d) - D / sqrt(d)), dP = dO V^T;  dK^T += Q^T dS.
+// The two gradients are separate launches that both recompute the scores:
+// each then holds one d-wide accumulator, and fits two waves per SIMD.
+template <class S, int KS, int FD, bool ROLE_DK>
+__global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bwd_kv_kernel(Args a) {
   constexpr int DV = 32 * FD;
   constexpr int TB = kBlk * pitch<DV>(), STG = 2 * TB + 2 * kBlk * 4;
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
@@ -379,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (ki < a.s && dd < a.d) {
       x = *reinterpret_cast<const u32x4*>(Kp + ki * a.ld3 + dd);
-      y = *reinterpret_cast<const u32x4*>(Vp + ki * a.ld3 + dd);
+      if (ROLE_DK) y = *reinterpret_cast<const u32x4*>(Vp + ki * a.ld3 + dd);
     }
     kf[ks] = x;
     vf[ks] = y;
@@ -396,16 +424,16 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
   auto load_rows = [&](int64_t r0) {
     const int t = tid & 63;
     if (tid < 64) rowv = r0 + t < a.s ? Lz[r0 + t] : INFINITY;
-    else if (tid < 128) rowv = r0 + t < a.s ? Dz[r0 + t] : 0.0f;
+    else if (ROLE_DK && tid < 128) rowv = r0 + t < a.s ? Dz[r0 + t] : 0.0f;
   };
   auto store_stage = [&](char* t) {
     qt.store(t, tid);
     dt.store(t + TB, tid);
-    if (tid < 128) reinterpret_cast<float*>(t + 2 * TB)[tid] = rowv * (tid < 64 ? kLog2e : sc_d);
+    if (tid < (ROLE_DK ? 128 : 64)) reinterpret_cast<float*>(t + 2 * TB)[tid] = rowv * (tid < 64 ? kLog2e : sc_d);
   };
-  f32x16 dk[FD], dv[FD];
+  f32x16 acc[FD];  // dV^T or dK^T: rows d, column key ki
 #pragma unroll
-  for (int f = 0; f < FD; ++f) dk[f] = dv[f] = f32x16{};
+  for (int f = 0; f < FD; ++f) acc[f] = f32x16{};
 
   if (nqb > 0) {
     qt.load(qrs, (int)qstart * rowq);
@@ -417,69 +445,75 @@ __global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
   __syncthreads();
   for (int ib = 0; ib < nqb; ++ib) {
     const int64_t q0 = qstart + (int64_t)ib * kBlk;
-    if (ib + 1 < nqb) {
-      qt.load(qrs, (int)(q0 + kBlk) * rowq);
-      dt.load(drs, (int)(q0 + kBlk) * rowd);
-      load_rows(q0 + kBlk);
-    }
+    // the next block (past the end in the last iteration, as in the forward)
+    qt.load(qrs, (int)(q0 + kBlk) * rowq);
+    dt.load(drs, (int)(q0 + kBlk) * rowd);
+    load_rows(q0 + kBlk);
     // causal: a block whose queries all precede the wave's keys has p = 0
     if (live && !(a.causal && q0 + kBlk - 1 < kw)) {
       const char* sq = smem + (ib & 1) * STG;
       const char* sd = sq + TB;
       const float* sl = reinterpret_cast<const float*>(sq + 2 * TB);
-      // x = Q K^T and dP = dO V^T: rows (queries) q0 + 32 mf + frag_row(r, h), column key ki
-      f32x16 p[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      // queries before the wave's last key: only on the diagonal (wave-uniform)
+      auto block = [&](auto masked) {
+        // one 32-query fragment at a time (mf): x = Q K^T (and dP = dO V^T),
+        // rows (queries) q0 + 32 mf + frag_row(r, h), column key ki
 #pragma unroll
         for (int mf = 0; mf < 2; ++mf) {
-          p[mf] = S::mfma32x32x16(frag_rows<DV>(sq, 32 * mf, 16 * ks, lane), kf[ks], p[mf]);
-          dp[mf] = S::mfma32x32x16(frag_rows<DV>(sd, 32 * mf, 16 * ks, lane), vf[ks], dp[mf]);
-        }
-      auto softmax_grad = [&](auto masked) {
+          // the fragment's LDS reads are all issued ahead of its products:
+          // Q (and dO) rows first, the transposed operand of the gradient
+          // product right after, landing while the softmax part runs
+          u32x4 qfr[KS], dfr[KS], tfr[2][FD];
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
+          for (int ks = 0; ks < KS; ++ks) {
+            qfr[ks] = frag_rows<DV>(sq, 32 * mf, 16 * ks, lane);
+            if (ROLE_DK) dfr[ks] = frag_rows<DV>(sd, 32 * mf, 16 * ks, lane);
+          }
+          f32x16 p = f32x16{}, dp = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            p = S::mfma32x32x16(qfr[ks], kf[ks], p);
+            if (ROLE_DK) dp = S::mfma32x32x16(dfr[ks], vf[ks], dp);
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int f = 0; f < FD; ++f) tfr[st][f] = frag_cols<DV>(ROLE_DK ? sq : sd, 32 * mf + 16 * st, 32 * f, lane);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int rr = 32 * mf + 8 * g + 4 * h;
             const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + rr);
-            const f32x4 D4 = *reinterpret_cast<const f32x4*>(sl + kBlk + rr);
+            f32x4 D4 = {};
+            if (ROLE_DK) D4 = *reinterpret_cast<const f32x4*>(sl + kBlk + rr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
-              float pv = __builtin_amdgcn_exp2f(fmaf(p[mf][r], c, -L4[e]));
+              float pv = __builtin_amdgcn_exp2f(fmaf(p[r], c, -L4[e]));
               if (masked && q0 + rr + e < ki) pv = 0.0f;
-              p[mf][r] = pv;
-              dp[mf][r] = pv * fmaf(dp[mf][r], sc_d, -D4[e]);  // dS
+              if (ROLE_DK) p[r] = pv * fmaf(dp[r], sc_d, -D4[e]);  // dS
+              else p[r] = pv;
             }
           }
-      };
-      // queries before the wave's last key: only on the diagonal (wave-uniform)
-      if (a.causal && q0 < kw + 31) softmax_grad(std::true_type{});
-      else softmax_grad(std::false_type{});
-      // dV^T += dO^T P and dK^T += Q^T dS over four 16-query steps
+          // dV^T += dO^T P, or dK^T += Q^T dS, over the fragment's two 16-query steps
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4 pf = pack_step<S>(p[st >> 1], st & 1);
-        const u32x4 sf = pack_step<S>(dp[st >> 1], st & 1);
+          for (int st = 0; st < 2; ++st) {
+            const u32x4 pf = pack_step<S>(p, st);
 #pragma unroll
-        for (int f = 0; f < FD; ++f) {
-          dv[f] = S::mfma32x32x16(frag_cols<DV>(sd, 16 * st, 32 * f, lane), pf, dv[f]);
-          dk[f] = S::mfma32x32x16(frag_cols<DV>(sq, 16 * st, 32 * f, lane), sf, dk[f]);
+            for (int f = 0; f < FD; ++f) acc[f] = S::mfma32x32x16(tfr[st][f], pf, acc[f]);
+          }
         }
-      }
+      };
+      if (a.causal && q0 < kw + 31) block(std::true_type{});
+      else block(std::false_type{});
     }
-    if (ib + 1 < nqb) store_stage(smem + ((ib + 1) & 1) * STG);
+    store_stage(smem + ((ib + 1) & 1) * STG);
     __syncthreads();
   }
 
   if (ki < a.s) {
-    uint16_t* row = a.out + ((int64_t)b * a.s + ki) * a.ld3 + (int64_t)j * a.d;
+    uint16_t* row = a.out + ((int64_t)b * a.s + ki) * a.ld3 + (int64_t)j * a.d + (ROLE_DK ? a.q : 2 * a.q);
 #pragma unroll
-    for (int f = 0; f < FD; ++f) {
-      store_t<S>(row + a.q, dk[f], 32 * f, a.d, h, 1.0f);
-      store_t<S>(row + 2 * a.q, dv[f], 32 * f, a.d, h, 1.0f);
-    }
+    for (int f = 0; f < FD; ++f) store_t<S>(row, acc[f], 32 * f, a.d, h, 1.0f);
   }
 }
 
@@ -539,47 +573,63 @@ __global__ __launch_bounds__(kThreads, KS <= 6 ? 2 : 1) void flash_bwd_q_kernel(
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int64_t k0 = (int64_t)kb * kBlk;
-    if (kb + 1 < nkb) {
-      kt.load(krs, (int)(k0 + kBlk) * rowb);
-      vt.load(vrs, (int)(k0 + kBlk) * rowb);
-    }
+    // the next block (past the end in the last iteration, as in the forward)
+    kt.load(krs, (int)(k0 + kBlk) * rowb);
+    vt.load(vrs, (int)(k0 + kBlk) * rowb);
     if (k0 < wave_kend) {
       const char* sk = smem + (kb & 1) * STG;
       const char* sv = sk + KB;
-      // x^T = K Q^T and dP^T = V dO^T: rows (keys) k0 + 32 mf + frag_row(r, h), column query qi
-      f32x16 p[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      // one 32-key fragment at a time (mf): x^T = K Q^T and dP^T = V dO^T,
+      // rows (keys) k0 + 32 mf + frag_row(r, h), column query qi; the
+      // fragment's LDS reads are all issued ahead of its products
+      auto block = [&](auto masked) {
 #pragma unroll
         for (int mf = 0; mf < 2; ++mf) {
-          p[mf] = S::mfma32x32x16(frag_rows<DV>(sk, 32 * mf, 16 * ks, lane), qf[ks], p[mf]);
-          dp[mf] = S::mfma32x32x16(frag_rows<DK>(sv, 32 * mf, 16 * ks, lane), df[ks], dp[mf]);
-        }
-      auto softmax_grad = [&](auto masked) {
+          u32x4 kfr[KS], vfr[KS], tfr[2][FD];
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
+          for (int ks = 0; ks < KS; ++ks) {
+            kfr[ks] = frag_rows<DV>(sk, 32 * mf, 16 * ks, lane);
+            vfr[ks] = frag_rows<DK>(sv, 32 * mf, 16 * ks, lane);
+          }
+          f32x16 p = f32x16{}, dp = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            p = S::mfma32x32x16(kfr[ks], qf[ks], p);
+            dp = S::mfma32x32x16(vfr[ks], df[ks], dp);
+          }
+          // (K^T read ahead only while its 8 FD registers fit beside the rest)
+          constexpr bool kTAhead = FD <= 2;
+          if constexpr (kTAhead) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int f = 0; f < FD; ++f) tfr[st][f] = frag_cols<DV>(sk, 32 * mf + 16 * st, 32 * f, lane);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(fmaf(p[mf][r], c, -Lq));
+            float pv = __builtin_amdgcn_exp2f(fmaf(p[r], c, -Lq));
             if (masked) {
               const int64_t kk = k0 + 32 * mf + frag_row(r, h);
               if (kk >= a.s || (a.causal && kk > qi)) pv = 0.0f;
             }
-            dp[mf][r] = pv * fmaf(dp[mf][r], sc_d, -Dq);  // dS^T
+            dp[r] = pv * fmaf(dp[r], sc_d, -Dq);  // dS^T
           }
+          // dQ^T += K^T dS^T over the fragment's two 16-key steps
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const u32x4 sf = pack_step<S>(dp, st);
+#pragma unroll
+            for (int f = 0; f < FD; ++f)
+              dq[f] = S::mfma32x32x16(kTAhead ? tfr[st][f] : frag_cols<DV>(sk, 32 * mf + 16 * st, 32 * f, lane), sf,
+                                      dq[f]);
+          }
+        }
       };
       // keys past the end or after the query: last block and diagonal only (wave-uniform)
-      if (k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw)) softmax_grad(std::true_type{});
-      else softmax_grad(std::false_type{});
-      // dQ^T += K^T dS^T over four 16-key steps
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4 sf = pack_step<S>(dp[st >> 1], st & 1);
-#pragma unroll
-        for (int f = 0; f < FD; ++f) dq[f] = S::mfma32x32x16(frag_cols<DV>(sk, 16 * st, 32 * f, lane), sf, dq[f]);
-      }
+      if (k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw)) block(std::true_type{});
+      else block(std::false_type{});
     }
-    if (kb + 1 < nkb) {
+    {
       char* nx = smem + ((kb + 1) & 1) * STG;
       kt.store(nx, tid);
       vt.store(nx + KB, tid);
@@ -625,8 +675,11 @@ hipError_t launch_fwd(const Args& a, hipStream_t st) {
 template <class S>
 hipError_t launch_bwd(const Args& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.nblk * a.Z)), block(kThreads);
-  TPMLP_FLASH_CASES(flash_bwd_kv_kernel)
+  TPMLP_FLASH_CASES(flash_bwd_kv_kernel, , false)
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TPMLP_FLASH_CASES(flash_bwd_kv_kernel, , true)
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   TPMLP_FLASH_CASES(flash_bwd_q_kernel)
   return hipGetLastError();

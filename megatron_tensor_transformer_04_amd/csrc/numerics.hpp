@@ -19,6 +19,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // fp32 storage (the plain-FMA path)
 struct StoreF32 {
@@ -35,6 +38,10 @@ struct StoreF16 {
   }
   static __device__ __forceinline__ uint16_t from_f(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+  // a and b rounded (as from_f) into the low and high halves: one v_cvt_pk_f16_f32
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
   }
   static __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -55,6 +62,10 @@ struct StoreBF16 {
   }
   static __device__ __forceinline__ uint16_t from_f(float v) {
     return __builtin_bit_cast(uint16_t, (__bf16)v);
+  }
+  // a and b rounded (as from_f) into the low and high halves: one v_cvt_pk_bf16_f32
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
   }
   static __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
