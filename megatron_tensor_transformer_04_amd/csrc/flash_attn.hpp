@@ -42,9 +42,10 @@ namespace flash {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kThreads = 256;  // four waves, 32 rows each
+constexpr int kThreads = 512;  // eight waves: four row groups of 32, each in two halves
 constexpr int kRows = 128;     // rows (queries or keys) per workgroup
 constexpr int kBlk = 64;       // keys (queries) per block of the inner loop
+constexpr int kStage = 128;    // rows per LDS stage: the blocks of both halves
 // The forward's reference maximum moves only when a row's scores exceed it
 // by more than this (log2 units): probabilities stay below 2^8.
 constexpr float kRescale = 8.0f;
@@ -171,16 +172,6 @@ __device__ __forceinline__ void store_t(uint16_t* orow, const f32x16& x, int d0,
   }
 }
 
-// Launch position pos (0 .. n-1, in units of Z workgroups) -> rank of the
-// row block by work, 0 the longest: the first half of the launch takes ranks
-// 0, 1, ..., the second half the shortest first. Where two workgroups share
-// a CU they are launch positions pos and pos + n/2, and their causal work
-// then adds up to about the same on every CU.
-__device__ __forceinline__ int balanced_rank(int pos, int n) {
-  const int half = (n + 1) / 2;
-  return pos < half ? pos : n - 1 - (pos - half);
-}
-
 struct Args {
   const uint16_t* qkv;  // [T][3q]: Q | K | V blocks, head j at columns j d .. j d + d - 1 of each
   const uint16_t* dO;   // [T][q] (backward)
@@ -203,29 +194,60 @@ __device__ __forceinline__ float frag_max(const f32x16& v) {
   return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, v[15]));
 }
 
-// Forward: one workgroup per (pair z, 128 queries), balanced_rank order;
-// wave w owns queries q0 + 32 w + c. Scores stay in raw units (Q K^T) until
-// the exponent, exp2(x c - m c) with c = log2(e) / sqrt(d) in one FMA. The
-// running maximum m of a row only grows; O and the running sum are rescaled
-// by exp2((m_old - m_new) c) in the blocks where some lane's maximum grew.
+// The two halves of a row group (waves g and g + 4) take alternate blocks
+// of the loop (even and odd), so that the longest row block's chain of
+// dependent blocks is half as long; at the end the second half hands its
+// accumulators (and two per-lane values) to the first through LDS, which
+// adds them in a fixed order. Buffer layout: group g's values at
+// buf[g][v][lane], v < FD * 16 + 2.
+template <int FD>
+__device__ __forceinline__ void half_put(float* buf, int g, int lane, const f32x16 (&x)[FD], float s0, float s1) {
+  float* p = buf + g * 64 * (FD * 16 + 2);
+#pragma unroll
+  for (int f = 0; f < FD; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[(f * 16 + r) * 64 + lane] = x[f][r];
+  p[FD * 16 * 64 + lane] = s0;
+  p[(FD * 16 + 1) * 64 + lane] = s1;
+}
+
+template <int FD>
+__device__ __forceinline__ void half_get(const float* buf, int g, int lane, f32x16 (&x)[FD], float& s0, float& s1) {
+  const float* p = buf + g * 64 * (FD * 16 + 2);
+#pragma unroll
+  for (int f = 0; f < FD; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[f][r] = p[(f * 16 + r) * 64 + lane];
+  s0 = p[FD * 16 * 64 + lane];
+  s1 = p[(FD * 16 + 1) * 64 + lane];
+}
+
+// Forward: one workgroup per (pair z, 128 queries), the last (longest, when
+// causal) query blocks first; wave w owns queries q0 + 32 (w % 4) + c and
+// the key blocks of parity w / 4. Scores stay in raw units (Q K^T) until
+// the exponent, exp2(x c - m c) with c = log2(e) / sqrt(d) in one FMA. m is
+// a reference maximum per row and half: it moves, and O and the running sum
+// are rescaled by exp2((m_old - m_new) c), only in the blocks where some
+// row's scores exceed it by more than kRescale (log2 units).
 // ONES (d not a multiple of 32): V's zero padding gets a column of ones at
 // d, so that O^T's row d accumulates the row sum of the rounded
 // probabilities in the same products (rescaled with O); otherwise the lanes
 // add their probabilities.
 template <class S, int KS, int FD, bool ONES>
-__global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
   constexpr int DK = 16 * KS, DV = 32 * FD;
-  constexpr int KB = kBlk * pitch<DK>(), STG = KB + kBlk * pitch<DV>();
+  constexpr int KB = kStage * pitch<DK>(), STG = KB + kStage * pitch<DV>();
+  static_assert(4 * 64 * (FD * 16 + 2) * 4 <= 2 * STG, "the halves' exchange fits in the stages");
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int qb = a.nblk - 1 - balanced_rank((int)(blockIdx.x / a.Z), a.nblk), z = (int)(blockIdx.x % a.Z);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, g = wave & 3, hk = wave >> 2;
+  const int qb = a.nblk - 1 - (int)(blockIdx.x / a.Z), z = (int)(blockIdx.x % a.Z);
   const int b = z / a.heads, j = z % a.heads;
-  const int64_t q0 = (int64_t)qb * kRows, qw = q0 + 32 * wave, qi = qw + (lane & 31);
+  const int64_t q0 = (int64_t)qb * kRows, qw = q0 + 32 * g, qi = qw + (lane & 31);
   const uint16_t* Qp = a.qkv + (int64_t)b * a.s * a.ld3 + (int64_t)j * a.d;
   const uint16_t* Kp = Qp + a.q;
   const uint16_t* Vp = Qp + 2 * a.q;
   const int64_t kv_end = a.causal ? min(a.s, q0 + kRows) : a.s;
-  const int nkb = (int)((kv_end + kBlk - 1) / kBlk);
+  const int nit = (int)((kv_end + kStage - 1) / kStage);
   // keys this wave reads: none if all its queries are past the end, else up
   // to its last query when causal (wave-uniform)
   const int64_t wave_kend = qw >= a.s ? 0 : (a.causal ? min(kv_end, qw + 32) : kv_end);
@@ -243,8 +265,8 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
   const int rowb = (int)(a.ld3 * 2);
   const auto krs = wave_rsrc(Kp, (a.s * a.ld3 - (int64_t)j * a.d - a.q) * 2);
   const auto vrs = wave_rsrc(Vp, (a.s * a.ld3 - (int64_t)j * a.d - 2 * a.q) * 2);
-  TileCopy<kBlk, DK> kt;
-  TileCopy<kBlk, DV> vt;
+  TileCopy<kStage, DK> kt;
+  TileCopy<kStage, DV> vt;
   kt.init(a.ld3, a.d, tid);
   vt.init(a.ld3, a.d, tid, ones);
   f32x16 o[FD];
@@ -252,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
   for (int f = 0; f < FD; ++f) o[f] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (nkb > 0) {
+  if (nit > 0) {
     kt.load(krs, 0);
     vt.load(vrs, 0);
     kt.store(smem, tid);
@@ -260,18 +282,18 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
   }
   // every load issued so far (the Q fragments too) has landed: the loop's
   // products then wait only for their own LDS reads, not for the next
-  // block's loads in flight
+  // stage's loads in flight
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int64_t k0 = (int64_t)kb * kBlk;
-    // the next block's tiles (past the end in the last iteration: zeros,
+  for (int it = 0; it < nit; ++it) {
+    // the next stage's tiles (past the end in the last iteration: zeros,
     // stored to the stage nothing reads any more)
-    kt.load(krs, (int)(k0 + kBlk) * rowb);
-    vt.load(vrs, (int)(k0 + kBlk) * rowb);
+    kt.load(krs, (it + 1) * kStage * rowb);
+    vt.load(vrs, (it + 1) * kStage * rowb);
+    const int64_t k0 = (int64_t)it * kStage + hk * kBlk;  // this half's block
     if (k0 < wave_kend) {
-      const char* sk = smem + (kb & 1) * STG;
-      const char* sv = sk + KB;
+      const char* sk = smem + (it & 1) * STG + hk * kBlk * pitch<DK>();
+      const char* sv = smem + (it & 1) * STG + KB + hk * kBlk * pitch<DV>();
       // x^T = K Q^T (raw): keys k0 + 32 mf + frag_row(r, h), query qi. All
       // of the block's K fragments are read before the first product, and
       // V's right after the last, so that the LDS latency is paid once per
@@ -308,10 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
       }
       float mb = fmaxf(frag_max(sc[0]), frag_max(sc[1]));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      // m_run is the reference the exponents are taken against, not always
-      // the row's maximum: it moves (and O and the sum are rescaled) only
-      // where some row's maximum exceeds it by more than kRescale in log2
-      // units, so p <= 2^kRescale; the first block always sets it
+      // the first block always sets the reference; p <= 2^kRescale after
       if (__ballot((mb - m_run) * c > kRescale)) {
         const float m_new = fmaxf(m_run, mb);
         // m_new stays -inf only while every key seen is masked: nothing to rescale then
@@ -344,15 +363,33 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
     // the other stage was last read in the previous iteration, before the
     // barrier that ended it
     {
-      char* nx = smem + ((kb + 1) & 1) * STG;
+      char* nx = smem + ((it + 1) & 1) * STG;
       kt.store(nx, tid);
       vt.store(nx + KB, tid);
     }
     __syncthreads();
   }
 
+  // the second half's O^T, reference maximum and sum to the first; every
+  // stage read is done (the loop's last barrier)
+  float* xbuf = reinterpret_cast<float*>(smem);
+  if (hk == 1) half_put<FD>(xbuf, g, lane, o, m_run, l_run);
+  __syncthreads();
+  if (hk == 1) return;
+  {
+    f32x16 o2[FD];
+    float m2, l2;
+    half_get<FD>(xbuf, g, lane, o2, m2, l2);
+    const float m = fmaxf(m_run, m2);
+    const float fa = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * c);
+    const float fb = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m2 - m) * c);
+#pragma unroll
+    for (int f = 0; f < FD; ++f) o[f] = o[f] * fa + o2[f] * fb;
+    l_run = l_run * fa + l2 * fb;
+    m_run = m;
+  }
   // the row sum: O^T's row d (in lanes h = 0, register 4 g1 of the last
-  // fragment), or the two halves' sums
+  // fragment), or the two lane halves' sums
   float l_all;
   if (ONES) {
     const int g1 = (a.d - 32 * (FD - 1)) >> 3;
@@ -373,22 +410,23 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Args a) {
 }
 
 // dV (ROLE_DK false) or dK (ROLE_DK true): one workgroup per (pair z, 128
-// keys), balanced_rank order (longest first: the first key blocks when
-// causal); wave w owns keys k0 + 32 w + c and loops over 64-query blocks (Q
-// and dO tiles, and per query L log2(e) and D / sqrt(d), in LDS):
+// keys), the first (longest, when causal) key blocks first; wave w owns keys
+// k0 + 32 (w % 4) + c and the query blocks of parity w / 4 (Q and dO tiles,
+// and per query L log2(e) and D / sqrt(d), in LDS):
 //   p = exp2(x c - L log2(e));  dV^T += dO^T P;
 //   dS = p (dP / sqrt(d) - D / sqrt(d)), dP = dO V^T;  dK^T += Q^T dS.
 // The two gradients are separate launches that both recompute the scores:
-// each then holds one d-wide accumulator, and fits two waves per SIMD.
+// each then holds one d-wide accumulator.
 template <class S, int KS, int FD, bool ROLE_DK>
-__global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bwd_kv_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) void flash_bwd_kv_kernel(Args a) {
   constexpr int DV = 32 * FD;
-  constexpr int TB = kBlk * pitch<DV>(), STG = 2 * TB + 2 * kBlk * 4;
+  constexpr int TB = kStage * pitch<DV>(), STG = 2 * TB + 2 * kStage * 4;
+  static_assert(4 * 64 * (FD * 16 + 2) * 4 <= 2 * STG, "the halves' exchange fits in the stages");
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int kblk = balanced_rank((int)(blockIdx.x / a.Z), a.nblk), z = (int)(blockIdx.x % a.Z);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, g = wave & 3, hq = wave >> 2;
+  const int kblk = (int)(blockIdx.x / a.Z), z = (int)(blockIdx.x % a.Z);
   const int b = z / a.heads, j = z % a.heads;
-  const int64_t k0 = (int64_t)kblk * kRows, kw = k0 + 32 * wave, ki = kw + (lane & 31);
+  const int64_t k0 = (int64_t)kblk * kRows, kw = k0 + 32 * g, ki = kw + (lane & 31);
   const uint16_t* Qp = a.qkv + (int64_t)b * a.s * a.ld3 + (int64_t)j * a.d;
   const uint16_t* Kp = Qp + a.q;
   const uint16_t* Vp = Qp + 2 * a.q;
@@ -396,7 +434,7 @@ __global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bw
   const float* Lz = a.lse + (int64_t)z * a.s;
   const float* Dz = a.D + (int64_t)z * a.s;
   const int64_t qstart = a.causal ? k0 : 0;  // queries before the block's first key see none of its keys
-  const int nqb = (int)((a.s - qstart + kBlk - 1) / kBlk);
+  const int nit = (int)((a.s - qstart + kStage - 1) / kStage);
   const bool live = kw < a.s;
   const float c = a.scale_log2, sc_d = a.scale;
 
@@ -415,27 +453,27 @@ __global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bw
   const auto qrs = wave_rsrc(Qp, (a.s * a.ld3 - (int64_t)j * a.d) * 2);
   const auto drs = wave_rsrc(dOp, (a.s * a.ldo - (int64_t)j * a.d) * 2);
   const int rowq = (int)(a.ld3 * 2), rowd = (int)(a.ldo * 2);
-  TileCopy<kBlk, DV> qt, dt;
+  TileCopy<kStage, DV> qt, dt;
   qt.init(a.ld3, a.d, tid);
   dt.init(a.ldo, a.d, tid);
-  // thread t < 64: L of query t of the block (+inf past the end: p = 0);
-  // 64 <= t < 128: its D; scaled to L log2(e) and D / sqrt(d) when stored
+  // thread t < 128: L of query t of the stage (+inf past the end: p = 0);
+  // 128 <= t < 256: its D; scaled to L log2(e) and D / sqrt(d) when stored
   float rowv = 0.0f;
   auto load_rows = [&](int64_t r0) {
-    const int t = tid & 63;
-    if (tid < 64) rowv = r0 + t < a.s ? Lz[r0 + t] : INFINITY;
-    else if (ROLE_DK && tid < 128) rowv = r0 + t < a.s ? Dz[r0 + t] : 0.0f;
+    const int t = tid & 127;
+    if (tid < 128) rowv = r0 + t < a.s ? Lz[r0 + t] : INFINITY;
+    else if (ROLE_DK && tid < 256) rowv = r0 + t < a.s ? Dz[r0 + t] : 0.0f;
   };
   auto store_stage = [&](char* t) {
     qt.store(t, tid);
     dt.store(t + TB, tid);
-    if (tid < (ROLE_DK ? 128 : 64)) reinterpret_cast<float*>(t + 2 * TB)[tid] = rowv * (tid < 64 ? kLog2e : sc_d);
+    if (tid < (ROLE_DK ? 256 : 128)) reinterpret_cast<float*>(t + 2 * TB)[tid] = rowv * (tid < 128 ? kLog2e : sc_d);
   };
   f32x16 acc[FD];  // dV^T or dK^T: rows d, column key ki
 #pragma unroll
   for (int f = 0; f < FD; ++f) acc[f] = f32x16{};
 
-  if (nqb > 0) {
+  if (nit > 0) {
     qt.load(qrs, (int)qstart * rowq);
     dt.load(drs, (int)qstart * rowd);
     load_rows(qstart);
@@ -443,17 +481,18 @@ __global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bw
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // as in the forward: nothing in flight before the loop
   __syncthreads();
-  for (int ib = 0; ib < nqb; ++ib) {
-    const int64_t q0 = qstart + (int64_t)ib * kBlk;
-    // the next block (past the end in the last iteration, as in the forward)
-    qt.load(qrs, (int)(q0 + kBlk) * rowq);
-    dt.load(drs, (int)(q0 + kBlk) * rowd);
-    load_rows(q0 + kBlk);
+  for (int it = 0; it < nit; ++it) {
+    const int64_t r0 = qstart + (int64_t)it * kStage;
+    // the next stage (past the end in the last iteration, as in the forward)
+    qt.load(qrs, (int)(r0 + kStage) * rowq);
+    dt.load(drs, (int)(r0 + kStage) * rowd);
+    load_rows(r0 + kStage);
+    const int64_t q0 = r0 + hq * kBlk;  // this half's block
     // causal: a block whose queries all precede the wave's keys has p = 0
-    if (live && !(a.causal && q0 + kBlk - 1 < kw)) {
-      const char* sq = smem + (ib & 1) * STG;
+    if (live && q0 < a.s && !(a.causal && q0 + kBlk - 1 < kw)) {
+      const char* sq = smem + (it & 1) * STG + hq * kBlk * pitch<DV>();
       const char* sd = sq + TB;
-      const float* sl = reinterpret_cast<const float*>(sq + 2 * TB);
+      const float* sl = reinterpret_cast<const float*>(smem + (it & 1) * STG + 2 * TB) + hq * kBlk;
       // queries before the wave's last key: only on the diagonal (wave-uniform)
       auto block = [&](auto masked) {
         // one 32-query fragment at a time (mf): x = Q K^T (and dP = dO V^T),
@@ -480,14 +519,14 @@ __global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bw
 #pragma unroll
             for (int f = 0; f < FD; ++f) tfr[st][f] = frag_cols<DV>(ROLE_DK ? sq : sd, 32 * mf + 16 * st, 32 * f, lane);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int rr = 32 * mf + 8 * g + 4 * h;
+          for (int gg = 0; gg < 4; ++gg) {
+            const int rr = 32 * mf + 8 * gg + 4 * h;
             const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + rr);
             f32x4 D4 = {};
-            if (ROLE_DK) D4 = *reinterpret_cast<const f32x4*>(sl + kBlk + rr);
+            if (ROLE_DK) D4 = *reinterpret_cast<const f32x4*>(sl + kStage + rr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
+              const int r = 4 * gg + e;
               float pv = __builtin_amdgcn_exp2f(fmaf(p[r], c, -L4[e]));
               if (masked && q0 + rr + e < ki) pv = 0.0f;
               if (ROLE_DK) p[r] = pv * fmaf(dp[r], sc_d, -D4[e]);  // dS
@@ -506,10 +545,22 @@ __global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bw
       if (a.causal && q0 < kw + 31) block(std::true_type{});
       else block(std::false_type{});
     }
-    store_stage(smem + ((ib + 1) & 1) * STG);
+    store_stage(smem + ((it + 1) & 1) * STG);
     __syncthreads();
   }
 
+  // the second half's partial sums to the first, added in that order
+  float* xbuf = reinterpret_cast<float*>(smem);
+  if (hq == 1) half_put<FD>(xbuf, g, lane, acc, 0.0f, 0.0f);
+  __syncthreads();
+  if (hq == 1) return;
+  {
+    f32x16 a2[FD];
+    float u0, u1;
+    half_get<FD>(xbuf, g, lane, a2, u0, u1);
+#pragma unroll
+    for (int f = 0; f < FD; ++f) acc[f] += a2[f];
+  }
   if (ki < a.s) {
     uint16_t* row = a.out + ((int64_t)b * a.s + ki) * a.ld3 + (int64_t)j * a.d + (ROLE_DK ? a.q : 2 * a.q);
 #pragma unroll
@@ -517,24 +568,26 @@ __global__ __launch_bounds__(kThreads, ROLE_DK && KS >= 7 ? 1 : 2) void flash_bw
   }
 }
 
-// dQ: one workgroup per (pair z, 128 queries), balanced_rank order; wave w
-// owns queries q0 + 32 w + c and loops over 64-key blocks (K and V tiles in
-// LDS), recomputing p and dS in the transposed layout.
+// dQ: one workgroup per (pair z, 128 queries), the last (longest, when
+// causal) query blocks first; wave w owns queries q0 + 32 (w % 4) + c and
+// the key blocks of parity w / 4 (K and V tiles in LDS), recomputing p and
+// dS in the transposed layout.
 template <class S, int KS, int FD>
-__global__ __launch_bounds__(kThreads, KS <= 6 ? 2 : 1) void flash_bwd_q_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) void flash_bwd_q_kernel(Args a) {
   constexpr int DK = 16 * KS, DV = 32 * FD;
-  constexpr int KB = kBlk * pitch<DV>(), STG = KB + kBlk * pitch<DK>();
+  constexpr int KB = kStage * pitch<DV>(), STG = KB + kStage * pitch<DK>();
+  static_assert(4 * 64 * (FD * 16 + 2) * 4 <= 2 * STG, "the halves' exchange fits in the stages");
   __shared__ __attribute__((aligned(16))) char smem[2 * STG];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int qb = a.nblk - 1 - balanced_rank((int)(blockIdx.x / a.Z), a.nblk), z = (int)(blockIdx.x % a.Z);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, g = wave & 3, hk = wave >> 2;
+  const int qb = a.nblk - 1 - (int)(blockIdx.x / a.Z), z = (int)(blockIdx.x % a.Z);
   const int b = z / a.heads, j = z % a.heads;
-  const int64_t q0 = (int64_t)qb * kRows, qw = q0 + 32 * wave, qi = qw + (lane & 31);
+  const int64_t q0 = (int64_t)qb * kRows, qw = q0 + 32 * g, qi = qw + (lane & 31);
   const uint16_t* Qp = a.qkv + (int64_t)b * a.s * a.ld3 + (int64_t)j * a.d;
   const uint16_t* Kp = Qp + a.q;
   const uint16_t* Vp = Qp + 2 * a.q;
   const uint16_t* dOp = a.dO + (int64_t)b * a.s * a.ldo + (int64_t)j * a.d;
   const int64_t kv_end = a.causal ? min(a.s, q0 + kRows) : a.s;
-  const int nkb = (int)((kv_end + kBlk - 1) / kBlk);
+  const int nit = (int)((kv_end + kStage - 1) / kStage);
   const int64_t wave_kend = qw >= a.s ? 0 : (a.causal ? min(kv_end, qw + 32) : kv_end);
   const float c = a.scale_log2, sc_d = a.scale;
 
@@ -555,15 +608,15 @@ __global__ __launch_bounds__(kThreads, KS <= 6 ? 2 : 1) void flash_bwd_q_kernel(
   const int rowb = (int)(a.ld3 * 2);
   const auto krs = wave_rsrc(Kp, (a.s * a.ld3 - (int64_t)j * a.d - a.q) * 2);
   const auto vrs = wave_rsrc(Vp, (a.s * a.ld3 - (int64_t)j * a.d - 2 * a.q) * 2);
-  TileCopy<kBlk, DV> kt;
-  TileCopy<kBlk, DK> vt;
+  TileCopy<kStage, DV> kt;
+  TileCopy<kStage, DK> vt;
   kt.init(a.ld3, a.d, tid);
   vt.init(a.ld3, a.d, tid);
   f32x16 dq[FD];
 #pragma unroll
   for (int f = 0; f < FD; ++f) dq[f] = f32x16{};
 
-  if (nkb > 0) {
+  if (nit > 0) {
     kt.load(krs, 0);
     vt.load(vrs, 0);
     kt.store(smem, tid);
@@ -571,14 +624,14 @@ __global__ __launch_bounds__(kThreads, KS <= 6 ? 2 : 1) void flash_bwd_q_kernel(
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // as in the forward: nothing in flight before the loop
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int64_t k0 = (int64_t)kb * kBlk;
-    // the next block (past the end in the last iteration, as in the forward)
-    kt.load(krs, (int)(k0 + kBlk) * rowb);
-    vt.load(vrs, (int)(k0 + kBlk) * rowb);
+  for (int it = 0; it < nit; ++it) {
+    // the next stage (past the end in the last iteration, as in the forward)
+    kt.load(krs, (it + 1) * kStage * rowb);
+    vt.load(vrs, (it + 1) * kStage * rowb);
+    const int64_t k0 = (int64_t)it * kStage + hk * kBlk;  // this half's block
     if (k0 < wave_kend) {
-      const char* sk = smem + (kb & 1) * STG;
-      const char* sv = sk + KB;
+      const char* sk = smem + (it & 1) * STG + hk * kBlk * pitch<DV>();
+      const char* sv = smem + (it & 1) * STG + KB + hk * kBlk * pitch<DK>();
       // one 32-key fragment at a time (mf): x^T = K Q^T and dP^T = V dO^T,
       // rows (keys) k0 + 32 mf + frag_row(r, h), column query qi; the
       // fragment's LDS reads are all issued ahead of its products
@@ -630,13 +683,25 @@ __global__ __launch_bounds__(kThreads, KS <= 6 ? 2 : 1) void flash_bwd_q_kernel(
       else block(std::false_type{});
     }
     {
-      char* nx = smem + ((kb + 1) & 1) * STG;
+      char* nx = smem + ((it + 1) & 1) * STG;
       kt.store(nx, tid);
       vt.store(nx + KB, tid);
     }
     __syncthreads();
   }
 
+  // the second half's partial sums to the first, added in that order
+  float* xbuf = reinterpret_cast<float*>(smem);
+  if (hk == 1) half_put<FD>(xbuf, g, lane, dq, 0.0f, 0.0f);
+  __syncthreads();
+  if (hk == 1) return;
+  {
+    f32x16 d2[FD];
+    float u0, u1;
+    half_get<FD>(xbuf, g, lane, d2, u0, u1);
+#pragma unroll
+    for (int f = 0; f < FD; ++f) dq[f] += d2[f];
+  }
   if (qi < a.s) {
     uint16_t* row = a.out + ((int64_t)b * a.s + qi) * a.ld3 + (int64_t)j * a.d;
 #pragma unroll
