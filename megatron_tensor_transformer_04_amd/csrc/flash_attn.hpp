@@ -303,11 +303,14 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
       for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kfr[mf][ks] = frag_rows<DK>(sk, 32 * mf, 16 * ks, lane);
+      // fragment 0's products first, then fragment 1's: the softmax of
+      // fragment 0 then runs while fragment 1's products execute, and that
+      // of fragment 1 while fragment 0's P V products do
       f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf) sc[mf] = S::mfma32x32x16(kfr[mf][ks], qf[ks], sc[mf]);
+        for (int ks = 0; ks < KS; ++ks) sc[mf] = S::mfma32x32x16(kfr[mf][ks], qf[ks], sc[mf]);
       // (V read ahead only while its 16 FD registers fit beside the rest)
       constexpr bool kVAhead = FD <= 3;
       u32x4 vfr[4][FD];
@@ -319,45 +322,46 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(Args a) {
       }
       // keys past the end, or after the query: only in the last block and on
       // the diagonal (wave-uniform)
-      if (k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw)) {
+      const bool masked = k0 + kBlk > a.s || (a.causal && k0 + kBlk - 1 > qw);
+      // one 32-key fragment at a time: its maximum and the reference update,
+      // its probabilities, then its two 16-key steps of O^T += V^T P^T
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
+      for (int mf = 0; mf < 2; ++mf) {
+        if (masked) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t ki = k0 + 32 * mf + frag_row(r, h);
             if (ki >= a.s || (a.causal && ki > qi)) sc[mf][r] = -INFINITY;
           }
-      }
-      float mb = fmaxf(frag_max(sc[0]), frag_max(sc[1]));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      // the first block always sets the reference; p <= 2^kRescale after
-      if (__ballot((mb - m_run) * c > kRescale)) {
-        const float m_new = fmaxf(m_run, mb);
-        // m_new stays -inf only while every key seen is masked: nothing to rescale then
-        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        }
+        float mb = frag_max(sc[mf]);
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        // the first fragment always sets the reference; p <= 2^kRescale after
+        if (__ballot((mb - m_run) * c > kRescale)) {
+          const float m_new = fmaxf(m_run, mb);
+          // m_new stays -inf only while every key seen is masked: nothing to rescale then
+          const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
 #pragma unroll
-        for (int f = 0; f < FD; ++f) o[f] *= alpha;
-        if (!ONES) l_run *= alpha;
-        m_run = m_new;
-      }
-      const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
-      float ls = 0.0f;
-#pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
+          for (int f = 0; f < FD; ++f) o[f] *= alpha;
+          if (!ONES) l_run *= alpha;
+          m_run = m_new;
+        }
+        const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
+        float ls = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[mf][r], c, -mc));
           sc[mf][r] = p;
           if (!ONES) ls += p;
         }
-      if (!ONES) l_run += ls;
-      // O^T += V^T P^T over four 16-key steps
+        if (!ONES) l_run += ls;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4 pf = pack_step<S>(sc[st >> 1], st & 1);
+        for (int st = 2 * mf; st < 2 * mf + 2; ++st) {
+          const u32x4 pf = pack_step<S>(sc[mf], st & 1);
 #pragma unroll
-        for (int f = 0; f < FD; ++f)
-          o[f] = S::mfma32x32x16(kVAhead ? vfr[st][f] : frag_cols<DV>(sv, 16 * st, 32 * f, lane), pf, o[f]);
+          for (int f = 0; f < FD; ++f)
+            o[f] = S::mfma32x32x16(kVAhead ? vfr[st][f] : frag_cols<DV>(sv, 16 * st, 32 * f, lane), pf, o[f]);
+        }
       }
     }
     // the other stage was last read in the previous iteration, before the
