@@ -23,4 +23,15 @@ hipError_t planned_gemm(int dtype, bool pk, bool qk, int64_t M, int64_t N, int64
 // uses (0 if it splits nothing); kc: both operands k-contiguous.
 size_t planned_gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K, bool kc);
 
+// Does a GEMM of this shape run on the large-tile direct-load engine once
+// both operands are k-contiguous (so that staging a transposed copy of an
+// mn-contiguous operand pays off)?
+bool planned_gemm_stages(int dtype, int64_t M, int64_t N, int64_t K);
+
+// out[c][r] = in[r][c] for a dense 16-bit [R][C] matrix; out has row pitch
+// staged_transpose_ld(R) (R plus padding that spreads its rows over the L2
+// channels).
+hipError_t staged_transpose(const void* in, void* out, int64_t R, int64_t C, hipStream_t st);
+int64_t staged_transpose_ld(int64_t R);
+
 }  // namespace tpmlp

@@ -20,11 +20,24 @@ namespace {
 
 using namespace attn;
 
-// Forward workspace: the output projection's k-split partials (256 bytes at
-// least, so that 0 keeps meaning an invalid shape).
-size_t flash_fwd_ws(const AttnDims& a, int dtype) {
-  return std::max<size_t>(256, a256(planned_gemm_tail_bytes(dtype, a.T, a.h, a.q, true)));
+// Forward workspace: [Wo^T [h][staged_transpose_ld(q)], when the output
+// projection runs on the large-tile engine with both operands k-contiguous]
+// [that projection's k-split partials]; 256 bytes at least, so that 0
+// keeps meaning an invalid shape.
+struct FlashFwdWs {
+  bool wot;
+  size_t tail_off, total;
+};
+
+FlashFwdWs flash_fwd_layout(const AttnDims& a, int dtype) {
+  FlashFwdWs w{};
+  w.wot = planned_gemm_stages(dtype, a.T, a.h, a.q);
+  w.tail_off = w.wot ? a256((size_t)(a.h * staged_transpose_ld(a.q)) * 2) : 0;
+  w.total = std::max<size_t>(256, w.tail_off + a256(planned_gemm_tail_bytes(dtype, a.T, a.h, a.q, w.wot)));
+  return w;
 }
+
+size_t flash_fwd_ws(const AttnDims& a, int dtype) { return flash_fwd_layout(a, dtype).total; }
 
 // Backward workspace: [D fp32 Z s][dO 16-bit T q][column partials of dQKV
 // fp32 [T/256][3q]][k-split partials of the projections' plain-store GEMMs].
@@ -79,9 +92,21 @@ int flash_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, cons
   f.out = static_cast<uint16_t*>(O);
   f.one_bits = dtype == TPMLP_BF16 ? 0x3F80u : 0x3C00u;  // 1.0
   ATTN_HIP(flash::launch_fwd<S>(f, st));
-  // Yp = O Wo: P = O [T,q] k-contiguous, Q = Wo [q,h] n-contiguous
-  ATTN_HIP(planned_gemm(dtype, true, false, a.T, a.h, a.q, O, a.q, Wo, a.h, Yp, a.h, nullptr,
-                        static_cast<float*>(ws), ws_bytes, st));
+  // Yp = O Wo: P = O [T,q] k-contiguous; Q = Wo [q,h] is n-contiguous, so
+  // where the large-tile engine runs it a transposed copy Wo^T [h][q] is
+  // staged first (3 MB at the 2.4B shape), which lets it take the 320-wide
+  // tiles (one wave of 256 x 320 there, against 1.25 of 256 x 256)
+  const FlashFwdWs w = flash_fwd_layout(a, dtype);
+  char* wsb = static_cast<char*>(ws);
+  if (w.wot) {
+    const int64_t ldt = staged_transpose_ld(a.q);
+    ATTN_HIP(staged_transpose(Wo, wsb, a.q, a.h, st));
+    ATTN_HIP(planned_gemm(dtype, true, true, a.T, a.h, a.q, O, a.q, wsb, ldt, Yp, a.h, nullptr,
+                          reinterpret_cast<float*>(wsb + w.tail_off), ws_bytes - w.tail_off, st));
+  } else {
+    ATTN_HIP(planned_gemm(dtype, true, false, a.T, a.h, a.q, O, a.q, Wo, a.h, Yp, a.h, nullptr,
+                          reinterpret_cast<float*>(wsb), ws_bytes, st));
+  }
   return TPMLP_OK;
 }
 
