@@ -378,12 +378,18 @@ hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStr
   return hipGetLastError();
 }
 
-// Does a GEMM of this shape run on the direct-to-LDS engine once all its
-// operands are k-contiguous? (Then staging transposed copies pays off.)
+// Does staging k-contiguous copies of a GEMM's mn-contiguous operands pay
+// off? Only where the copies buy the 256 x 320 tiles: with both operands
+// k-contiguous the planner picks them, and that tile reads k-contiguous
+// operands only. Where it would take 256 x 256 tiles anyway, the direct-load
+// engine reads an mn-contiguous operand in place with transposing LDS reads,
+// and on MI355X that cost less than the copies (the 7B shard's step, whose
+// 4096-wide GEMMs all take 256 x 256 tiles: 1.68 ms in place against
+// 1.77 ms staged; the 2.4B and h=10240 shards, whose GEMMs take the 320-wide
+// tiles, ran 18-22 % and 13 % slower in place).
 inline bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
   if (dtype == TPMLP_F32 || M <= 0 || N <= 0 || K <= 0) return false;
-  const Engine e = pick_engine(M, N, K, false, true);
-  return e == Engine::Dma256 || e == Engine::Dma320;
+  return pick_engine(M, N, K, false, true) == Engine::Dma320;
 }
 
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }

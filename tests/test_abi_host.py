@@ -117,20 +117,18 @@ def test_workspace_bytes(lib):
     # ... and the forward stages A_i^T and B_i^T, rows padded likewise (Yp:
     # 2048 tiles of 256 x 320, no tail)
     assert fws(16384, 10240, 10240, 2) == 2 * 10240 * (10240 + 256) * 2
-    # h = 8192 (TP = 4 of a 32768-wide FFN): Yp and dXp have 64 x 32 tiles,
-    # dB and dA 32 x 32 = 1024: no tails
-    t8 = 8192 * (16384 + 256) * 2
-    assert fws(16384, 8192, 8192, 2) == 2 * 8192 * (8192 + 256) * 2
-    assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240 + 4 * t8
-    # ... its weight gradients (12 x 3 = 36 tiles, K = 4096) and dXp (16 x 3 = 48 tiles, K = 3072) are
-    # launches of less than half a wave with long reductions: direct-load engine on staged copies of H, dY,
-    # X and dZ, every tile split into 4 k-ranges (at most 4 below K = 8192; the largest partials, dXp's,
+    # h = 8192 (TP = 4 of a 32768-wide FFN): 8192 is no multiple of 320, so every GEMM takes 256 x 256 tiles
+    # with k-contiguous copies too; nothing is staged (the mn-contiguous operands are read in place: Yp and
+    # dXp have 64 x 32 tiles, dB and dA 32 x 32 = 1024, no tails), only the db1 partials remain
+    assert fws(16384, 8192, 8192, 2) == 0
+    assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240
+    # ... GPT-2-small: 256 x 256 tiles everywhere, so nothing staged either; its weight gradients (12 x 3 = 36
+    # tiles, K = 4096) and dXp (16 x 3 = 48 tiles, K = 3072) are launches of less than half a wave with long
+    # reductions: every tile split into 4 k-ranges (at most 4 below K = 8192; the largest partials, dXp's,
     # size the shared room)
-    t2 = lambda rows: rows * (4096 + 256) * 2
-    assert ws(4096, 768, 3072, 1) == part2 + 2 * t2(3072) + 2 * t2(768) + 48 * 4 * 256 * 256 * 4
-    # ... and its forward stages A_i^T (first GEMM: 192 tiles) and B_i^T (second GEMM: 48 tiles, K = 3072,
-    # split into 4 k-ranges)
-    assert fws(4096, 768, 3072, 1) == 3072 * (768 + 256) * 2 + 768 * (3072 + 256) * 2 + 48 * 4 * 256 * 256 * 4
+    assert ws(4096, 768, 3072, 1) == part2 + 48 * 4 * 256 * 256 * 4
+    # ... and its forward's second GEMM (48 tiles, K = 3072) is split the same way
+    assert fws(4096, 768, 3072, 1) == 48 * 4 * 256 * 256 * 4
     # small shapes and fp32 stage nothing
     assert ws(520, 264, 392, 1) == ws(520, 264, 392, 1, MINIMAL)
     assert fws(520, 264, 392, 1) == 0 and fws(64, 128, 256, 0) == 0
@@ -144,14 +142,15 @@ def test_workspace_bytes(lib):
 
 
 def test_k_split_tail_workspace_full_shard(lib, plan):
-    """With 256 x 256 tiles forced, dB and dA of the h = 10240 shard have
-    40 x 40 = 1600 tiles: six full waves and 64 tiles left, each split into
-    4 k-ranges of fp32 partials; dXp (2560 tiles) splits nothing."""
+    """With 256 x 256 tiles forced, nothing is staged (the copies would not
+    buy the 320-wide tile): dB and dA of the h = 10240 shard read H, dY, X
+    and dZ in place, 40 x 40 = 1600 tiles: six full waves and 64 tiles
+    left, each split into 4 k-ranges of fp32 partials; dXp (2560 tiles)
+    splits nothing."""
     ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
     plan(3, 0)
     part = (16384 // 256) * 10240 * 4
-    t = 10240 * (16384 + 256) * 2
-    assert ws() == part + 4 * t + 64 * 4 * 256 * 256 * 4
+    assert ws() == part + 64 * 4 * 256 * 256 * 4
 
 
 def test_k_split_tail_workspace(lib, plan):
@@ -160,7 +159,8 @@ def test_k_split_tail_workspace(lib, plan):
     ws = lambda T, h, f: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)), 0)
     fws = lambda T, h, f: lib.tp_mlp_fwd_workspace_bytes(ctypes.byref(_shape(T, h, f, 2)))
     plan(3, 0)
-    base, fbase = ws(520, 264, 392), fws(520, 264, 392)
+    # 256 x 256 tiles forced: nothing staged; the partials follow the db1 partials at a 256-byte boundary
+    base, fbase = (ws(520, 264, 392) + 255) // 256 * 256, fws(520, 264, 392)
     short = fws(520, 264, 200)
     tile = 256 * 256 * 4
     # 3 CUs: dB and dA have 2 x 2 tiles, one left over, split into
