@@ -27,8 +27,15 @@
 // operand of that product takes the same slot order from a row-major tile in
 // LDS with two transposing reads (ds_read_b64_tr_b16, frag_cols): the sum
 // over k does not depend on the order, and no value moves between lanes.
-// Lanes l and l + 32 hold the same row: the forward exchanges the running
-// maximum between them once per key block and the running sums at the end.
+// Lanes l and l + 32 hold the same row: the forward exchanges the block
+// maximum between them once per 32-key fragment and the running sums at the
+// end.
+//
+// Workgroups of eight waves: four row groups of 32 rows, each in two halves
+// (waves g and g + 4) that take alternate 64-row blocks of the loop and add
+// their partial results through LDS at the end, in a fixed order. The
+// longest row block's chain of dependent blocks, which sets a causal
+// launch's time, is then half as long.
 #pragma once
 
 #include <hip/hip_runtime.h>
