@@ -9,8 +9,12 @@ seeded synthetic tensors resident in HBM before timing starts.
 Prints one JSON line: whole-step TFLOP/s (GEMM flops 12 T h f per step over
 wall-clock time between device synchronizations), the fraction of the dense
 16-bit MFMA peak, the dominant kernel's roofline (its algorithmic flops over
-its average duration from HIP events recorded on the launch stream), and the
-float64 CPU oracle timed on a bounded token sample of the same workload.
+its average duration from HIP events recorded on the launch stream around it
+in the timed steps), and the float64 CPU oracle timed on a bounded token
+sample of the same workload. The per-kernel breakdown (kernel_ms and the
+step medians) comes from as many untimed steps with every step boundary
+recorded: an event record between two kernels idles the stream for a few
+microseconds, so the timed steps record only the two they need.
 """
 import argparse
 import json
@@ -252,6 +256,10 @@ def attention_rate(tpmlp, dev, reps=10, cpu=True):
     kw = dict(batch=b, heads=n, causal=cfg.causal)
 
     def measure(fwd, bwd):
+        """(forward ms, backward ms, forward + backward ms): the split from
+        events around each call, the sum from one event pair around reps
+        back-to-back calls (an event record idles the stream for a few
+        microseconds, which the split's intervals include)."""
         for _ in range(2):
             fwd()
             bwd()
@@ -264,31 +272,41 @@ def attention_rate(tpmlp, dev, reps=10, cpu=True):
             bwd()
             ev[r][2].record()
         torch.cuda.synchronize()
-        return (sum(x[0].elapsed_time(x[1]) for x in ev) / reps, sum(x[1].elapsed_time(x[2]) for x in ev) / reps)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for r in range(reps):
+            fwd()
+            bwd()
+        g1.record()
+        torch.cuda.synchronize()
+        return (sum(x[0].elapsed_time(x[1]) for x in ev) / reps, sum(x[1].elapsed_time(x[2]) for x in ev) / reps,
+                g0.elapsed_time(g1) / reps)
 
     ffws = u8(tpmlp.tp_attn_flash_fwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
     fbws = u8(tpmlp.tp_attn_flash_bwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
-    f_ms, b_ms = measure(lambda: tpmlp.tp_attn_flash_fwd(X, Wqkv, bqkv, Wo, QKV, LSE, O, Yp, ffws, **kw),
+    f_ms, b_ms, fb_ms = measure(lambda: tpmlp.tp_attn_flash_fwd(X, Wqkv, bqkv, Wo, QKV, LSE, O, Yp, ffws, **kw),
                          lambda: tpmlp.tp_attn_flash_bwd(dY, X, Wqkv, Wo, QKV, LSE, O, dQKV, dXp, dWqkv, dbqkv, dWo,
                                                          fbws, **kw))
     del ffws, fbws
     P = e(Z, s, s)
     mfws = u8(tpmlp.tp_attn_fwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
     mbws = u8(tpmlp.tp_attn_bwd_workspace_bytes(b, s, h, n, d, code, cfg.causal))
-    mf_ms, mb_ms = measure(lambda: tpmlp.tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, mfws, **kw),
+    mf_ms, mb_ms, mfb_ms = measure(lambda: tpmlp.tp_attn_fwd(X, Wqkv, bqkv, Wo, QKV, P, O, Yp, mfws, **kw),
                            lambda: tpmlp.tp_attn_bwd(dY, X, Wqkv, Wo, QKV, P, O, dQKV, dXp, dWqkv, dbqkv, dWo, mbws,
                                                      **kw))
     del P, mfws, mbws
     flops_f = 2.0 * T * h * 3 * q + 2.0 * T * q * h + 2 * 2.0 * Z * s * s * d * (0.5 if cfg.causal else 1.0)
-    rate = lambda fm, bm: 3 * flops_f / ((fm + bm) * 1e-3) / 1e12
+    rate = lambda ms: 3 * flops_f / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
-    tflops, m_tflops = rate(f_ms, b_ms), rate(mf_ms, mb_ms)
+    tflops, m_tflops = rate(fb_ms), rate(mfb_ms)
     out = {"workload": f"{cfg.name}: one TP={cfg.tp} rank's attention of hidden {h}, {cfg.heads} heads of width {d} "
                        f"({n} on this rank), micro-batch {b} x seq {s}, causal, {cfg.dtype}",
            "path": "fused (tp_attn_flash_fwd + tp_attn_flash_bwd)",
-           "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tflops, 2), "peak": peak,
+           "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "fwd_bwd_ms": round(fb_ms, 4),
+           "tflops": round(tflops, 2), "peak": peak,
            "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "bound": "mfma",
-           "materialized": {"fwd_ms": round(mf_ms, 4), "bwd_ms": round(mb_ms, 4), "tflops": round(m_tflops, 2),
+           "materialized": {"fwd_ms": round(mf_ms, 4), "bwd_ms": round(mb_ms, 4), "fwd_bwd_ms": round(mfb_ms, 4),
+                            "tflops": round(m_tflops, 2),
                             "frac": round(m_tflops / peak, 4)},
            "cpu_baseline": None}
     if cpu:  # forward, then a backward that recomputes the forward: 4 x the forward's work
@@ -398,18 +416,18 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(FWD_STEPS) + 1)] for _ in range(K)]
     bwd_steps = (["rTA", "rF1"] + BWD_STEPS) if args.recompute else BWD_STEPS
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bwd_steps) + 1)] for _ in range(K)]
-    log(f"timing {K} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    nf, nb = len(FWD_STEPS) + 1, len(bwd_steps) + 1
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    # Per-step breakdown (kernel_ms, the medians): K untimed steps with an event
+    # at every step boundary. Each event record idles the stream for a few
+    # microseconds, so the timed region below records only two per step.
+    fev = [[mk() for _ in range(nf)] for _ in range(K)]
+    bev = [[mk() for _ in range(nb)] for _ in range(K)]
+    log(f"breakdown: {K} steps with every step boundary recorded")
     for k in range(K):
         step(fev[k], bev[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log("timed region done")
-
     per = {n: 0.0 for n in FWD_STEPS + bwd_steps}
     for k in range(K):
         for i, n in enumerate(FWD_STEPS):
@@ -417,18 +435,48 @@ def main():
         for i, n in enumerate(bwd_steps):
             per[n] += bev[k][i].elapsed_time(bev[k][i + 1])
     per = {n: v / K for n, v in per.items()}
-    gpu_ms = fev[0][0].elapsed_time(bev[K - 1][len(bwd_steps)]) / K
-    fwd_each = [fev[k][0].elapsed_time(fev[k][len(FWD_STEPS)]) for k in range(K)]
-    bwd_each = [bev[k][0].elapsed_time(bev[k][len(bwd_steps)]) for k in range(K)]
+    fwd_each = [fev[k][0].elapsed_time(fev[k][nf - 1]) for k in range(K)]
+    bwd_each = [bev[k][0].elapsed_time(bev[k][nb - 1]) for k in range(K)]
     step_each = sorted(a + b for a, b in zip(fwd_each, bwd_each))
     med = lambda v: sorted(v)[len(v) // 2]
+    dom = max(GEMM_STEPS, key=lambda n: per[n])
+
+    # Timed region: K steps; the events are the dominant GEMM's two step
+    # boundaries (for the roofline) and one pair around the whole region. All
+    # are created (recorded once) before the clock starts.
+    in_fwd = dom in FWD_STEPS
+    di = (FWD_STEPS if in_fwd else bwd_steps).index(dom)
+    ta, tb = [mk() for _ in range(K)], [mk() for _ in range(K)]
+    g0, g1 = mk(), mk()
+    for ev in ta + tb + [g0, g1]:
+        ev.record()
+    torch.cuda.synchronize()
+
+    def bracket(k):
+        arr = [None] * (nf if in_fwd else nb)
+        arr[di], arr[di + 1] = ta[k], tb[k]
+        return arr
+
+    log(f"timing {K} steps ({dom} bracketed)")
+    t0 = time.perf_counter()
+    g0.record()
+    for k in range(K):
+        if in_fwd:
+            step(bracket(k), None)
+        else:
+            step(None, bracket(k))
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+    gpu_ms = g0.elapsed_time(g1) / K
+    dom_ms = sum(ta[k].elapsed_time(tb[k]) for k in range(K)) / K
     ms = wall / K * 1e3
     flops = 12.0 * T * h * f
     value = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     gemm_flops = 2.0 * T * h * f
-    dom = max(GEMM_STEPS, key=lambda n: per[n])
-    achieved = gemm_flops / (per[dom] * 1e-3) / 1e12
+    achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
 
     reduce_line = None if args.no_reduce else reduce_partials_rate(tpmlp, Yp, cfg, dev)
     attn_line = None if args.no_attn else attention_rate(tpmlp, dev, cpu=not args.no_cpu_baseline)

@@ -170,6 +170,9 @@ size_t tp_mlp_workspace_bytes(const tpmlp_shape* shape, unsigned flags);
  *           B_i transpose (TB), second GEMM (F2). A transpose that does not
  *           run leaves its two events back to back (TB never runs with
  *           TPMLP_LAYOUT_B_T: B_i^T is already k-contiguous for F2).
+ *           A NULL entry is skipped (each record between two kernels
+ *           costs the stream a few microseconds of idle time). The same
+ *           holds for the events of every entry point below.
  */
 int tp_mlp_fwd(const tpmlp_shape* shape,
                const void* X, const void* A, const void* b1, const void* B,

@@ -167,7 +167,9 @@ def _events(events):
         return None
     arr = (ctypes.c_void_p * len(events))()
     for i, e in enumerate(events):
-        if hasattr(e, "cuda_event"):
+        if e is None:  # a NULL entry: that point is not recorded
+            arr[i] = None
+        elif hasattr(e, "cuda_event"):
             if not e.cuda_event:  # torch creates its HIP event on first record
                 e.record()
             arr[i] = e.cuda_event

@@ -352,8 +352,11 @@ inline int check_buffers(const Span* in, int n_in, const bool* in_required, cons
   return TPMLP_OK;
 }
 
+// Records events[i] on st; a NULL array or a NULL entry records nothing (an
+// event record between two kernels idles the GPU for a few microseconds, so
+// callers that time one step ask for only the points they use).
 inline int record(void* const* events, int i, hipStream_t st) {
-  if (!events) return TPMLP_OK;
+  if (!events || !events[i]) return TPMLP_OK;
   return hipEventRecord(static_cast<hipEvent_t>(events[i]), st) == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP;
 }
 

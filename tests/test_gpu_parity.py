@@ -275,6 +275,21 @@ def test_events_bracket_each_step(gpu_lib):
             assert a.elapsed_time(b) >= 0.0
 
 
+def test_null_event_entries_are_skipped(gpu_lib):
+    """Only the non-NULL entries are recorded: here B1's two boundaries and
+    F1's, the way bench.py brackets one GEMM per step."""
+    import torch
+    inp = synth.draw_inputs(512, 256, 512, "bf16", seed=7)
+    X, A, b1, B, dY = device_inputs(inp)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    fe, be = [None, mk(), mk(), None, None], [mk(), mk()] + [None] * 8
+    Z, H, Yp = gpu_lib.fwd(X, A, b1, B, events=fe)
+    got = gpu_lib.bwd(dY, X, A, B, Z, H, events=be)
+    torch.cuda.synchronize()
+    assert fe[1].elapsed_time(fe[2]) > 0.0 and be[0].elapsed_time(be[1]) > 0.0
+    compare({"Z": Z, "H": H, "Yp": Yp, **got}, _oracle_shard(inp), TOL["bf16"])
+
+
 # ----------------------------------------------- GeLU epilogue grids ----
 
 def _grid_inputs(dtype, n):
