@@ -114,6 +114,8 @@ inline int check_spans(const Span2* in, int n_in, const Span2* out, int n_out) {
 // query t, D[z][t] = sum_e dO[t][e] O[t][e] over the head's d columns (fp32,
 // in e order). In exact arithmetic D = sum_k P[t][k] dP[t][k], since
 // dP = dO V^T and O = P V; it is the term the softmax's backward subtracts.
+// The loads of four 8-column chunks of each operand are issued before their
+// products are added (in e order), so a thread has eight in flight.
 template <class S>
 __global__ __launch_bounds__(256) void softmax_rowdot_kernel(const typename S::T* __restrict__ dO,
                                                              const typename S::T* __restrict__ O, float* __restrict__ D,
@@ -125,15 +127,26 @@ __global__ __launch_bounds__(256) void softmax_rowdot_kernel(const typename S::T
   const typename S::T* a = dO + t * q + (int64_t)j * d;
   const typename S::T* o = O + t * q + (int64_t)j * d;
   float acc = 0.0f;
-  for (int e = 0; e < d; e += 8) {
-    const uint4 wa = *reinterpret_cast<const uint4*>(a + e), wo = *reinterpret_cast<const uint4*>(o + e);
+  auto add = [&](const uint4& wa, const uint4& wo) {
     const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w}, uo[4] = {wo.x, wo.y, wo.z, wo.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       acc += S::to_f((typename S::T)(ua[k] & 0xffffu)) * S::to_f((typename S::T)(uo[k] & 0xffffu));
       acc += S::to_f((typename S::T)(ua[k] >> 16)) * S::to_f((typename S::T)(uo[k] >> 16));
     }
+  };
+  int e = 0;
+  for (; e + 32 <= d; e += 32) {
+    uint4 wa[4], wo[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      wa[c] = *reinterpret_cast<const uint4*>(a + e + 8 * c);
+      wo[c] = *reinterpret_cast<const uint4*>(o + e + 8 * c);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) add(wa[c], wo[c]);
   }
+  for (; e < d; e += 8) add(*reinterpret_cast<const uint4*>(a + e), *reinterpret_cast<const uint4*>(o + e));
   const int64_t b = t / s, pos = t % s;
   D[((b * heads) + j) * s + pos] = acc;
 }

@@ -89,12 +89,25 @@ inline int subwave_parts(int64_t ntile, int64_t K) {
   return parts;
 }
 
-// Cost of a k-split sub-wave launch in whole waves of its work items times
-// the work of one item.
+// Cost of a k-split sub-wave launch: whole waves of its work items times the
+// multiply-adds of one item, plus kPartialCost per fp32 partial element
+// (written by the GEMM, read back by the finish). The weight is a fit to
+// MI355X timings of such launches (e.g. 8192 x 640 x 2560: 256 x 320 tiles in
+// four ranges, 50 us, against 256 x 256 tiles in two, 43 us; the tile work
+// alone ranks them the other way).
+constexpr int64_t kPartialCost = 7;
 inline int64_t subwave_cost(int64_t M, int64_t N, int64_t K, int bm, int bn) {
   const int64_t ntile = ceil_div(M, bm) * ceil_div(N, bn);
   const int parts = subwave_parts(ntile, K);
-  return ceil_div(ntile * parts, kCUs) * bm * bn * ceil_div(K, parts);
+  const int64_t partials = parts > 1 ? ntile * parts * bm * bn : 0;
+  return ceil_div(ntile * parts, kCUs) * bm * bn * ceil_div(K, parts) + kPartialCost * partials;
+}
+
+// A launch of 16 .. kCUs / 2 tiles of 256 x 256 with a reduction of at least
+// kSubWaveSplitK: plan_tail splits it into k-ranges.
+inline bool subwave_split_candidate(int64_t M, int64_t N, int64_t K) {
+  const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+  return t256 >= 16 && t256 <= kCUs / 2 && K >= kSubWaveSplitK;
 }
 
 // Tile choice for the 16-bit engines. Large tiles (256x256) once they give
@@ -119,7 +132,7 @@ inline Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc)
     default: break;
   }
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-  const bool split_candidate = t256 >= 16 && t256 <= kCUs / 2 && K >= kSubWaveSplitK;
+  const bool split_candidate = subwave_split_candidate(M, N, K);
   if (t256 < kDmaMinTiles && !split_candidate) return Engine::Mfma128;
   if (!dma_fits) return Engine::Mfma256;
   if (kc && split_candidate)  // the k-split's work items decide which tile fills the chip better
@@ -382,16 +395,21 @@ hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStr
 }
 
 // Does staging k-contiguous copies of a GEMM's mn-contiguous operands pay
-// off? Only where the copies buy the 256 x 320 tiles: with both operands
-// k-contiguous the planner picks them, and that tile reads k-contiguous
-// operands only. Where it would take 256 x 256 tiles anyway, the direct-load
-// engine reads an mn-contiguous operand in place with transposing LDS reads,
-// and on MI355X that cost less than the copies (the 7B shard's step, whose
-// 4096-wide GEMMs all take 256 x 256 tiles: 1.68 ms in place against
-// 1.77 ms staged; the 2.4B and h=10240 shards, whose GEMMs take the 320-wide
-// tiles, ran 18-22 % and 13 % slower in place).
+// off? Only where the copies buy the 256 x 320 tiles for a launch of a wave
+// or more: with both operands k-contiguous the planner picks them, and that
+// tile reads k-contiguous operands only. Where it would take 256 x 256 tiles
+// anyway, the direct-load engine reads an mn-contiguous operand in place
+// with transposing LDS reads, and on MI355X that cost less than the copies
+// (the 7B shard's step, whose 4096-wide GEMMs all take 256 x 256 tiles:
+// 1.68 ms in place against 1.77 ms staged; the 2.4B and h=10240 shards,
+// whose GEMMs take the 320-wide tiles, ran 18-22 % and 13 % slower in
+// place). A k-split sub-wave launch is not staged either: its copies scale
+// with the long reduction while its tiles do not (the 2.4B shard's weight
+// gradients, 2560 x 2560 x 8192: 123 us in place against 133 us for the two
+// copies and the 320-wide GEMM).
 inline bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
   if (dtype == TPMLP_F32 || M <= 0 || N <= 0 || K <= 0) return false;
+  if (subwave_split_candidate(M, N, K)) return false;
   return pick_engine(M, N, K, false, true) == Engine::Dma320;
 }
 

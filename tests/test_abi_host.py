@@ -363,10 +363,11 @@ def test_attention_workspace_sizes_and_validation(lib):
     Z = 32 * 2048 * 2048
     assert fws(big) == Z * 4
     # D fp32 [32][2048], dS bf16, dO [8192, 640], column partials [8192 / 256][1920] fp32, then the k-split
-    # partials of the projections, sized by the largest: dO = dY Wo^T is 32 x 2 tiles of 256 x 320 (less than
-    # half a wave, K = 2560), each split into 4 k-ranges (dWo: 3 x 10 tiles of 256 x 256, K = 8192, in 8 ranges;
-    # dWqkv: 10 x 8 in 3; dXp: one full wave of 256 x 320, no split)
-    ks = max(64 * 4 * 256 * 320 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
+    # partials of the projections, sized by the largest: dO = dY Wo^T is 32 x 3 tiles of 256 x 256 (less than
+    # half a wave, K = 2560), each split into 2 k-ranges (the 256 x 320 tiles' 64 x 4 ranges write more partials
+    # than the tile work saves), dWo: 3 x 10 tiles of 256 x 256, K = 8192, in 8 ranges; dWqkv: 10 x 8 in 3;
+    # dXp: one full wave of 256 x 320, no split
+    ks = max(96 * 2 * 256 * 256 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
     assert bws(big) == 32 * 2048 * 4 + Z * 2 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
     assert fws(sh(4, 2048, 2560, 8, 80, 0)) == 0          # fp32 storage is not supported
     assert fws(sh(4, 2044, 2560, 8, 80, 2)) == 0          # seq not a multiple of 8
@@ -408,7 +409,7 @@ def test_flash_attention_workspace_sizes_and_validation(lib):
     assert fws(big) == 2560 * (640 + 256) * 2
     assert fws(sh(1, 16, 16, 1, 8, 2)) == 256           # small: no staging, the 256-byte minimum
     # the materialized layout without dS: D, dO, column partials, then the same k-split room
-    ks = max(64 * 4 * 256 * 320 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
+    ks = max(96 * 2 * 256 * 256 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
     assert bws(big) == 32 * 2048 * 4 + 8192 * 640 * 2 + 32 * 1920 * 4 + ks
     assert bws(big) == lib.tp_attn_bwd_workspace_bytes(ctypes.byref(big)) - 32 * 2048 * 2048 * 2
     # no sequence cap: 65536 tokens of one sequence
