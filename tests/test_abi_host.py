@@ -129,6 +129,12 @@ def test_workspace_bytes(lib):
     assert ws(4096, 768, 3072, 1) == part2 + 48 * 4 * 256 * 256 * 4
     # ... and its forward's second GEMM (48 tiles, K = 3072) is split the same way
     assert fws(4096, 768, 3072, 1) == 48 * 4 * 256 * 256 * 4
+    # the 2.4B shard (T = 8192, h = f = 2560): the forward's GEMMs are one full wave of 256 x 320 tiles, so A_i^T
+    # and B_i^T are staged; dB and dA (2560 x 2560, K = 8192) are launches of less than half a wave that the
+    # k-split spreads: they read H, dY, X and dZ in place on 10 x 10 tiles of 256 x 256 in 2 k-ranges (copies
+    # of [2560][8192] operands would cost more than the 320-wide tile saves); dXp is a full wave, no split
+    assert fws(8192, 2560, 2560, 2) == 2 * 2560 * (2560 + 256) * 2
+    assert ws(8192, 2560, 2560, 2) == 32 * 2560 * 4 + 100 * 2 * 256 * 256 * 4
     # small shapes and fp32 stage nothing
     assert ws(520, 264, 392, 1) == ws(520, 264, 392, 1, MINIMAL)
     assert fws(520, 264, 392, 1) == 0 and fws(64, 128, 256, 0) == 0
