@@ -142,7 +142,9 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
   float* const tail = room ? reinterpret_cast<float*>(wsb + w.tail_off) : nullptr;
   const size_t tcap = room ? w.tail_bytes : 0;
 
-  const EpiGeluGrad<S> epi_b1{(const T*)Z, (T*)dZ, part, f};
+  // Z streams through B1's epilogue once; from the MALL's 256 MiB on it is
+  // read with non-temporal loads
+  const EpiGeluGrad<S> epi_b1{(const T*)Z, (T*)dZ, part, f, Tn * f * (int64_t)sizeof(T) >= (int64_t(256) << 20)};
 
   TPMLP_TRY(record(ev, 0, st));
   // B1: dZ = (dY B_i^T) * gelu'(Z), plus per-tile column sums; Q[k][n] = B_i[n][k] is k-contiguous.
