@@ -447,9 +447,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     static_for<0, FM>([&](auto i) { fa[i] = pa.template read<i, KS>(smem); });
     static_for<0, FN>([&](auto j) { fb[j] = qa.template read<j, KS>(smem); });
   };
+  // Column-major over the wave's fragments: consecutive MFMAs share their B
+  // fragment (measured on MI355X with the reads interleaved as below: about
+  // 1.5 % faster than row-major on 16384 x 10240 x 10240).
   auto mfmas = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN]) __attribute__((always_inline)) {
-    static_for<0, FM>([&](auto i) {
-      static_for<0, FN>([&](auto j) { acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]); });
+    static_for<0, FN>([&](auto j) {
+      static_for<0, FM>([&](auto i) { acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]); });
     });
   };
   constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
@@ -488,11 +491,11 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     //
     // Software pipeline, pinned with scheduling constraints (left alone, the
     // compiler sinks each fragment read to just before its first MFMA and
-    // exposes the full LDS latency on every read): substep s issues all
-    // reads of substep s+1, then its own MFMAs. After the barrier, the
-    // direct loads that refill the freed stage and the reads of the next
-    // tile's first substep are interleaved one by one with the MFMAs of the
-    // last substep.
+    // exposes the full LDS latency on every read): the reads of substep s+1
+    // are interleaved one by one with the MFMAs of substep s (one read after
+    // each of the first MFMAs). After the barrier, the direct loads that
+    // refill the freed stage and the reads of the next tile's first substep
+    // are interleaved the same way with the MFMAs of the last substep.
     if (cur.nk > 0) {
       wait_vmcnt<(ST - 1) * LOADS>();  // k-tile 0 has landed
       barrier_lds();
@@ -509,14 +512,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           static_for<0, NKS - 2>([&](auto ks) {
             if constexpr (ks % 2 == 0) {
               read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
-              sched_fence();
               mfmas(fa0, fb0);
             } else {
               read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
-              sched_fence();
               mfmas(fa1, fb1);
             }
-            sched_fence();
+            sched_interleave<FM * FN, 0, DSR>();
           });
           read_frags(fa1, fb1, std::integral_constant<int, NKS - 1>{});  // NKS even: substep NKS-1 in set 1
           // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight.
@@ -538,14 +539,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           static_for<0, NKS - 1>([&](auto ks) {
             if constexpr (ks % 2 == 0) {
               read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
-              sched_fence();
               mfmas(fa0, fb0);
             } else {
               read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
-              sched_fence();
               mfmas(fa1, fb1);
             }
-            sched_fence();
+            sched_interleave<FM * FN, 0, DSR>();
           });
           wait_vmcnt<(ST - 2) * LOADS>();
           barrier_lds();
