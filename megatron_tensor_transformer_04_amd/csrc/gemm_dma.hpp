@@ -53,8 +53,8 @@
 // filled the texture unit's queues and stalled the MFMAs interleaved with
 // them (measured on MI355X with the SQ_VMEM_TA_*_FIFO_FULL counters).
 // Scheduling constraints hold this order (the compiler's own schedule
-// serialises each read with its first use), and after the barrier the
-// loads and reads are interleaved with the MFMAs. Workgroups are
+// serialises each read with its first use); the reads and, after the
+// barrier, the loads are interleaved one by one with the MFMAs. Workgroups are
 // persistent (see gemm_dma_kernel): the next output tile's k-tile 0 is
 // issued before the current tile's epilogue.
 //
