@@ -192,7 +192,7 @@ def _layout(b_transposed: bool) -> int:
 
 
 # tile names of tp_mlp_debug_plan (TPMLP_PLAN_* in include/tp_mlp.h)
-PLAN_TILES = {None: 0, "auto": 0, 128: 1, "128": 1, 256: 2, "256": 2, "dma256": 3, "dma320": 4}
+PLAN_TILES = {None: 0, "auto": 0, 128: 1, "128": 1, 256: 2, "256": 2, "dma256": 3, "dma320": 4, "dma320m32": 5}
 
 
 def tp_mlp_debug_plan(tile=None, tail_cus: int = 0) -> None:

@@ -15,13 +15,20 @@
 //   [P stage 0][Q stage 0] .. [P stage S-1][Q stage S-1]
 //   KC tile: [rows][BK], rows of BK/8 16-byte chunks; chunk c of row r sits
 //            at c ^ sk(r): sk(r) = (r & 7) ^ ((r >> 3) & 1) for BK = 64,
-//            ((r >> 1) ^ (r >> 3)) & 3 for BK = 32.
+//            ((r >> 1) ^ (r >> 3)) & 3 for BK = 32; in the 16x16 form
+//            (below) rot(r & 7) ^ (4 ((r >> 3) & 1)), rot = the three bits
+//            rotated right by one.
 //   MC tile: [BK][R], k-rows of R/16 32-byte units; unit u of k-row k sits
 //            at u ^ sm(k), sm(k) = (k & 3) ^ ((k & 3) << 1) (mod 8).
 // A fragment read by 8 or 16 consecutive lanes (KC, ds_read_b128) and by 16
 // or 32 consecutive lanes (MC, ds_read_b64_tr_b16) touches distinct banks
 // under either swizzle, and both depend only on the lane, so every fragment
-// of a wave is addressed as a per-lane base register plus an immediate.
+// of a wave is addressed as a per-lane base register plus an immediate. The
+// 16x16 form's reads (16 consecutive rows, one chunk each) meet in the
+// banks under sk: rows r and r + 2 are 64 banks apart, so the eight rows of
+// one parity need eight distinct chunks, which rot(r & 7) ^ 4 ((r >> 3) & 1)
+// gives and (r & 7) ^ ((r >> 3) & 1) does not (measured on MI355X: about
+// 250x fewer LDS bank-conflict cycles, 1.5x the read rate).
 //
 // A direct LDS load writes the 16 bytes of lane l at offset 16 l of a 1 KB
 // block, so the swizzle is applied on the global side: lane l fetches the
@@ -31,9 +38,20 @@
 // l % 32 and the eight k values 8 (l / 32) .. 8 (l / 32) + 7, and holds the
 // results C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15. A fragment
 // comes from a KC tile with one ds_read_b128 and from an MC tile with two
-// ds_read_b64_tr_b16 transposing reads. (The 16x16x32 form is avoided: the
-// compiler does not accumulate it in place, and copies every accumulator
-// once per use.)
+// ds_read_b64_tr_b16 transposing reads.
+//
+// The 16x16 form (DmaTile MF16; KC operands, BK = 64, a plain or bias + GeLU
+// store): v_mfma_f32_16x16x32_{bf16,f16}, lane l supplies row / column l % 16
+// and k values 8 (l / 16) .. + 7 of a 32-wide substep and holds
+// C[4 (l / 16) + r][l % 16], r = 0..3. Same tiles, same k order per
+// element (on MI355X the outputs of 16384 x 10240 x 10240 matched the 32x32
+// form's bit for bit); the chip holds a higher clock under this form (1.56
+// against 1.40 GHz under the profiler with 256 x 320 tiles, for 2.6 % less
+// time in plain runs). Its fragments fill more registers per flop (a 64 x
+// 160 wave tile: 40 of 16x16 against 10 of 32x32, the same accumulator
+// bytes but 14 reads of 16 B per 32-wide substep instead of 7 per 16), so
+// one set of fragment registers serves both substeps: each is refilled as
+// soon as its last MFMA of the substep has issued (see the k-loop).
 //
 // Pipeline. Within one output tile, k-tile t lives in stage (t + s0) % S
 // and is consumed in BK/16 substeps (fragments double-buffered in
@@ -76,14 +94,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // OCC_: workgroups per CU the tile is built for (their waves share each
-// SIMD's registers and the CU's LDS).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1>
+// SIMD's registers and the CU's LDS). MF16_: the 16x16x32 MFMA form (see
+// the header comment; k-contiguous operands, 64-deep k-tiles).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1, bool MF16_ = false>
 struct DmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
+  static constexpr bool MF16 = MF16_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M_ * WAVES_N_;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int FRAG = MF16 ? 16 : 32;  // fragment edge
+  static constexpr int FM = WTM / FRAG, FN = WTN / FRAG;
   static constexpr int LDS_P = BM * BK * 2, LDS_Q = BN * BK * 2;  // one stage of P / Q
   static constexpr int STG = LDS_P + LDS_Q;                       // one stage (P, then Q)
   static constexpr int LDS_BYTES = STAGES * STG;
@@ -96,6 +117,7 @@ struct DmaTile {
   static_assert(STAGES >= 2, "at least two stages");
   static_assert(BK == 32 || BK == 64, "k-tiles of 32 or 64 (an even number of 16-wide substeps)");
   static_assert(BK == 32 || WAVES % 2 == 0, "64-deep KC tiles need an even number of waves");
+  static_assert(!MF16 || (BK == 64 && LP + LQ <= FN - 1), "16x16 form: two substeps, loads fit the columns");
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS is 160 KB per CU");
   static constexpr int WAVES_PER_SIMD = WAVES * OCC / 4;
   static constexpr int PER_XCD = 32 * OCC;  // workgroups in flight per XCD
@@ -141,6 +163,24 @@ __device__ __forceinline__ void sched_interleave() {
   sched_fence();
 }
 
+// The 16x16 form's substep (see the k-loop): NB - 1 columns of FMA MFMAs,
+// each followed by one VMEM read (the first VM columns) and one DS read,
+// then the last column one MFMA and one DS read at a time, then one DS read.
+template <int NB, int FMA, int VM>
+__device__ __forceinline__ void sched_rolling() {
+  static_for<0, NB - 1>([&](auto j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, FMA, 0);
+    if constexpr (j < VM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  });
+  static_for<0, FMA>([&](auto i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  });
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  sched_fence();
+}
+
 // Opaque copies: the compiler can neither hoist out of a loop nor merge what
 // is computed from the result. The constraints are AMDGPU register classes
 // (v: VGPR, s: SGPR), so the statements exist in the device pass only.
@@ -160,8 +200,12 @@ __device__ __forceinline__ int opaque_s(int x) {
 // Offsets beyond every buffer's num_records: the load returns zeros.
 constexpr uint32_t kOobOffset = 0x80000000u;
 
-template <int BK>
+template <int BK, bool MF16 = false>
 __device__ __forceinline__ int dsk(int r) {
+  if constexpr (MF16) {  // BK = 64: the low three row bits rotated right, bit 2 flipped on odd 8-row groups
+    const int lo = r & 7;
+    return (((lo & 1) << 2) | (lo >> 1)) ^ (((r >> 3) & 1) << 2);
+  }
   if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
@@ -223,12 +267,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, in
 // Source of the 16 bytes that lane `lane` writes in 1 KB block `blk` of an
 // operand tile: element offset from the tile origin at k = 0 (`rel`), the
 // tile-local row (KC) or column (MC) index `mn`, and the k offset `kk`.
-template <bool KC, int R, int BK>
+template <bool KC, int R, int BK, bool MF16 = false>
 __device__ __forceinline__ void dma_slot(int blk, int lane, int64_t ld, int64_t& rel, int& mn, int& kk) {
   if constexpr (KC) {
     constexpr int CH = BK / 8;                // 16-byte chunks per row
     const int r = blk * (64 / CH) + lane / CH;  // 1024 / (2 BK) rows per block
-    const int kc = (lane % CH) ^ dsk<BK>(r);
+    const int kc = (lane % CH) ^ dsk<BK, MF16>(r);
     mn = r;
     kk = kc * 8;
     rel = (int64_t)r * ld + kk;
@@ -307,6 +351,30 @@ struct FragAddr {
   }
 };
 
+// Per-lane LDS byte offsets of a wave's 16x16x32 fragments (KC tiles with
+// the MF16 swizzle, BK = 64): NF fragments of 16 rows, the first at tile row
+// `first`. Lane l reads row first + 16 i + (l & 15), 16-byte chunk
+// 4 ks + (l >> 4) of k-substep ks (32 wide).
+template <int NF>
+struct FragAddr16 {
+  static constexpr int BK = 64, NB = 2;
+  uint32_t base[NB];
+  __device__ __forceinline__ void init(int lane, int region, int first) {
+    const int r = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks)
+      base[ks] = (uint32_t)(region + (first + r) * (2 * BK) + (((4 * ks + (lane >> 4)) ^ dsk<BK, true>(r)) << 4));
+  }
+  __device__ __forceinline__ void advance(uint32_t delta) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) base[i] += delta;
+  }
+  template <int I, int KS>
+  __device__ __forceinline__ u32x4 read(const char* lds) const {
+    return *reinterpret_cast<const u32x4*>(lds + base[KS] + I * 16 * (2 * BK));
+  }
+};
+
 // One workgroup per CU, each looping over work items v = blockIdx.x,
 // blockIdx.x + gridDim.x, ... (nwork items: the tiles, with the tail tiles
 // split into k-ranges, see TailSplit). Between two items the first k-tile
@@ -325,6 +393,9 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   static_assert(!SLICED_P || P_KC, "row slices of a k-contiguous P only");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES, STG = Cfg::STG;
+  constexpr bool M16 = Cfg::MF16;
+  static_assert(!M16 || (P_KC && Q_KC && !Epi::kInput && !Epi::kColSum && !Epi::kDirectF32),
+                "16x16 form: k-contiguous operands, a plain or bias + GeLU store");
   static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
                 "an mn-contiguous operand needs a power-of-two tile extent (swizzle, loads per k-row)");
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
@@ -361,40 +432,58 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   };
   // Buffer resources of an item's operand tiles, based at the tile origin
   // with num_records = the operand's extent from there, so any offset past
-  // the tensor reads zeros.
+  // the tensor reads zeros. The 16x16 form also ends them at the matrix's
+  // last row (its loads carry no per-row check).
   auto p_rsrc = [&](const Item& it) __attribute__((always_inline)) {
     if constexpr (SLICED_P) {
       const int64_t sl = it.m0 / xs.rows, r0 = it.m0 - sl * xs.rows;
-      return uniform_rsrc(xs.p[sl] + r0 * P.ld, (xs.rows - r0) * P.ld * 2);
+      const int64_t rows = M16 ? min(xs.rows - r0, sh.M - it.m0) : xs.rows - r0;
+      return uniform_rsrc(xs.p[sl] + r0 * P.ld, rows * P.ld * 2);
     } else {
       const int64_t base = P_KC ? it.m0 * P.ld : it.m0;
-      return uniform_rsrc(P.ptr + base, (p_extent - base) * 2);
+      return uniform_rsrc(P.ptr + base, (M16 ? min(p_extent - base, (sh.M - it.m0) * P.ld) : p_extent - base) * 2);
     }
   };
   auto q_rsrc = [&](const Item& it) __attribute__((always_inline)) {
     const int64_t base = Q_KC ? it.n0 * Q.ld : it.n0;
-    return uniform_rsrc(Q.ptr + base, (q_extent - base) * 2);
+    return uniform_rsrc(Q.ptr + base, (M16 ? min(q_extent - base, (sh.N - it.n0) * Q.ld) : q_extent - base) * 2);
   };
 
   // Per-lane byte offsets from the tile origin at k = 0; rows / columns
   // outside the matrix get kOobOffset. The k advance of each tile goes in
   // the instruction's scalar offset, so the K loop does no per-lane address
   // arithmetic. pk0 / qk0: the k offset (within a tile) of load 0's chunk
-  // (the same for every item); load c's is that plus dma_kstep<>(c).
+  // (the same for every item); load c's is that plus dma_kstep<>(c). The
+  // 16x16 form keeps load 0's offset only (registers are short there): load
+  // c's rows are c * WAVES * 8 rows further on, with the same chunk (the
+  // swizzle depends on the row mod 16), and rows past the matrix fall
+  // outside the buffer resource.
+  constexpr int NPV = M16 ? 1 : LP, NQV = M16 ? 1 : LQ;
   int pk0 = 0, qk0 = 0;
-  auto offsets = [&](const Item& it, uint32_t(&pv)[LP], uint32_t(&qv)[LQ]) __attribute__((always_inline)) {
+  auto offsets = [&](const Item& it, uint32_t(&pv)[NPV], uint32_t(&qv)[NQV]) __attribute__((always_inline)) {
     // Recomputed per item from an opaque copy of the lane index: hoisting
     // the item-independent 64-bit parts out of the item loop would keep
     // them live across the K loop.
     const int ln = opaque_v(lane);
-    static_for<0, LP>([&](auto c) {
+    if constexpr (M16) {
+      int64_t rel;
+      int mn, kk;
+      dma_slot<true, BM, BK, true>(wave, ln, P.ld, rel, mn, kk);
+      pv[0] = (uint32_t)rel * 2u;
+      pk0 = kk;
+      dma_slot<true, BN, BK, true>(wave, ln, Q.ld, rel, mn, kk);
+      qv[0] = (uint32_t)rel * 2u;
+      qk0 = kk;
+      return;
+    }
+    static_for<0, NPV>([&](auto c) {
       int64_t rel;
       int mn, kk;
       dma_slot<P_KC, BM, BK>(c * Cfg::WAVES + wave, ln, P.ld, rel, mn, kk);
       pv[c] = it.m0 + mn < sh.M ? (uint32_t)rel * 2u : kOobOffset;
       if constexpr (c == 0) pk0 = kk;
     });
-    static_for<0, LQ>([&](auto c) {
+    static_for<0, NQV>([&](auto c) {
       int64_t rel;
       int mn, kk;
       dma_slot<Q_KC, BN, BK>(c * Cfg::WAVES + wave, ln, Q.ld, rel, mn, kk);
@@ -413,7 +502,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // (t >= nk) is all kOobOffset and fills its stage with zeros that nothing
   // reads, which keeps the loop body free of branches.
   auto issue_tile = [&](const Item& it, __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs,
-                        const uint32_t(&pv)[LP], const uint32_t(&qv)[LQ], int t, int stage, auto part_c)
+                        const uint32_t(&pv)[NPV], const uint32_t(&qv)[NQV], int t, int stage, auto part_c)
       __attribute__((always_inline)) {
     constexpr int PART = decltype(part_c)::value;
     const int krem = it.kspan - t * BK;  // k extent left from this tile on
@@ -421,6 +510,26 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const int psoff = __builtin_amdgcn_readfirstlane((int)((P_KC ? k0 : k0 * P.ld) * 2));
     const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
     char* const sp = smem + stage * STG;
+    if constexpr (M16) {
+      // load 0's offset, or kOobOffset past the k-range (then every load's
+      // offset stays beyond num_records); made opaque so that the per-load
+      // sums are formed here, not kept in registers across the loop
+      constexpr int RSTEP = Cfg::WAVES * 8;
+      const uint32_t pb = (uint32_t)opaque_v((int)(pk0 < krem ? pv[0] : kOobOffset));
+      const uint32_t qb = (uint32_t)opaque_v((int)(qk0 < krem ? qv[0] : kOobOffset));
+      const uint32_t pstep = (uint32_t)(RSTEP * P.ld * 2), qstep = (uint32_t)(RSTEP * Q.ld * 2);
+      static_for<0, LP>([&](auto c) {
+        if constexpr (PART == 2 || (PART == 0) == (c < FIRST))
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + (c * Cfg::WAVES + wave) * 1024), 16,
+                                                   pb + (uint32_t)c * pstep, psoff, 0, 0);
+      });
+      static_for<0, LQ>([&](auto c) {
+        if constexpr (PART == 2 || (PART == 0) == (LP + c < FIRST))
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(sp + Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024),
+                                                   16, qb + (uint32_t)c * qstep, qsoff, 0, 0);
+      });
+      return;
+    }
     static_for<0, LP>([&](auto c) {
       if constexpr (PART == 2 || (PART == 0) == (c < FIRST)) {
         const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
@@ -438,9 +547,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   };
   constexpr auto kAll = std::integral_constant<int, 2>{};
 
-  FragAddr<P_KC, BM, BK, FM> pa;
-  FragAddr<Q_KC, BN, BK, FN> qa;
-  f32x16 acc[FM][FN];
+  std::conditional_t<M16, FragAddr16<FM>, FragAddr<P_KC, BM, BK, FM>> pa;
+  std::conditional_t<M16, FragAddr16<FN>, FragAddr<Q_KC, BN, BK, FN>> qa;
+  using AccT = std::conditional_t<M16, f32x4, f32x16>;
+  AccT acc[FM][FN];
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto read_frags = [&](u32x4(&fa)[FM], u32x4(&fb)[FN], auto ks_c) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks_c)::value;
@@ -451,9 +561,11 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // fragment (measured on MI355X with the reads interleaved as below: about
   // 1.5 % faster than row-major on 16384 x 10240 x 10240).
   auto mfmas = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN]) __attribute__((always_inline)) {
-    static_for<0, FN>([&](auto j) {
-      static_for<0, FM>([&](auto i) { acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]); });
-    });
+    if constexpr (!M16) {
+      static_for<0, FN>([&](auto j) {
+        static_for<0, FM>([&](auto i) { acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]); });
+      });
+    }
   };
   constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
   // DS read instructions per substep (a transposing read moves half a
@@ -467,7 +579,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   int s0 = 0;  // stage of the current item's k-tile 0
   {
     const Item first = decode(v);
-    uint32_t pv[LP], qv[LQ];
+    uint32_t pv[NPV], qv[NQV];
     offsets(first, pv, qv);
     issue_tile(first, p_rsrc(first), q_rsrc(first), pv, qv, 0, 0, kAll);
   }
@@ -478,10 +590,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     lane = opaque_v(lane);
     const Item cur = decode(opaque_s(v));
     const __amdgpu_buffer_rsrc_t prs = p_rsrc(cur), qrs = q_rsrc(cur);
-    uint32_t pv[LP], qv[LQ];
+    uint32_t pv[NPV], qv[NQV];
     offsets(cur, pv, qv);
     static_for<1, ST>([&](auto t) { issue_tile(cur, prs, qrs, pv, qv, t, (t + s0) % ST, kAll); });
-    static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
+    static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = AccT{}; }); });
     pa.init(lane, s0 * STG, wm * Cfg::WTM);
     qa.init(lane, s0 * STG + Cfg::LDS_P, wn * Cfg::WTN);
 
@@ -503,7 +615,36 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       for (int t = 0; t < cur.nk; ++t) {
         const int st_t = (t + s0) % ST;
         const bool wrap = st_t == ST - 1;  // tile t+1 sits in stage 0
-        if constexpr (NKS >= 4) {
+        if constexpr (M16) {
+          // Two 32-wide substeps on one set of fragment registers: each B
+          // fragment is refilled with the next substep's once its column of
+          // MFMAs has issued, each A fragment once its last MFMA (in the
+          // last column) has. Substep 0, then the barrier (this wave's reads
+          // of tile t are all issued), then substep 1 with the loads that
+          // refill the stage, one per column, and the reads of tile t+1.
+          static_for<0, FN>([&](auto j) {
+            static_for<0, FM>([&](auto i) {
+              acc[i][j] = S::mfma16x16x32(fa0[i], fb0[j], acc[i][j]);
+              if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 1>(smem);
+            });
+            fb0[j] = qa.template read<j, 1>(smem);
+          });
+          sched_rolling<FN, FM, 0>();
+          wait_vmcnt<(ST - 2) * LOADS>();
+          barrier_lds();
+          sched_fence();
+          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, kAll);
+          pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          static_for<0, FN>([&](auto j) {
+            static_for<0, FM>([&](auto i) {
+              acc[i][j] = S::mfma16x16x32(fa0[i], fb0[j], acc[i][j]);
+              if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 0>(smem);
+            });
+            fb0[j] = qa.template read<j, 0>(smem);
+          });
+          sched_rolling<FN, FM, LOADS>();
+        } else if constexpr (NKS >= 4) {
           // Substeps 0 .. NKS-3, then the reads of the last substep; with
           // those, this wave is done with stage st_t and the barrier comes
           // one substep before the end of the tile: the loads that refill
@@ -571,7 +712,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const bool has_next = v_next < nwork;
     if (has_next) {
       const Item nxt = decode(opaque_s(v_next));
-      uint32_t pv2[LP], qv2[LQ];
+      uint32_t pv2[NPV], qv2[NQV];
       offsets(nxt, pv2, qv2);
       const __amdgpu_buffer_rsrc_t prs2 = p_rsrc(nxt), qrs2 = q_rsrc(nxt);
       static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST, kAll); });
@@ -605,7 +746,18 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       // One k-range of a tail tile: the raw fp32 partial sums, in place of
       // the epilogue (tail_finish_kernel applies it).
       float* pt = tail.partial + ((int64_t)(done.tile - tail.full) * tail.parts + done.part) * (BM * BN);
-      static_for<0, FM>([&](auto i) {
+      if constexpr (M16) {
+        // lane l holds C[4 (l / 16) + r][l % 16] of each 16x16 fragment
+        static_for<0, FM>([&](auto i) {
+          static_for<0, FN>([&](auto j) {
+            const int c = wn * Cfg::WTN + j * 16 + (lane & 15);
+            static_for<0, 4>([&](auto r) {
+              const int row = wm * Cfg::WTM + i * 16 + 4 * (lane >> 4) + r;
+              pt[row * BN + c] = acc[i][j][(int)r];
+            });
+          });
+        });
+      } else static_for<0, FM>([&](auto i) {
         static_for<0, FN>([&](auto j) {
           const int c = wn * Cfg::WTN + j * 32 + (lane & 31);
           static_for<0, 16>([&](auto r) {
@@ -613,6 +765,58 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
             pt[row * BN + c] = acc[i][j][(int)r];
           });
         });
+      });
+    } else if constexpr (M16) {
+      // The 16x16 form's epilogue: per fragment row of the wave's tile (16
+      // rows), each output is rounded into a private block of stage s_epi
+      // (lane l holds C[4 (l / 16) + r][l % 16] of each fragment), read back
+      // as 16-byte row chunks and stored non-temporally (as below). A second
+      // output reuses the block once the first is stored, its fp32 values
+      // held in the accumulators meanwhile.
+      barrier_lds();
+      char* const epi_lds = smem + s_epi * STG;
+      constexpr int CPR = Cfg::WTN / 8;      // 16-byte chunks per staged row
+      constexpr int RS = Cfg::WTN * 2 + 16;  // staged row stride (bytes)
+      constexpr int HB = 16, BLK = HB * RS;
+      constexpr int PASSES = (HB * CPR + 63) / 64;
+      constexpr bool PART = PASSES * 64 != HB * CPR;
+      static_assert(Cfg::WAVES * BLK <= STG, "staging fits in one stage");
+      char* const stg = epi_lds + wave * BLK;
+      const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
+      auto store_block = [&](typename S::T* out, int64_t mb) __attribute__((always_inline)) {
+        static_for<0, PASSES>([&](auto p) {
+          const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
+          if (PART && p == PASSES - 1 && q >= HB * CPR) return;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(stg + row * RS + c8 * 16);
+          if (mb + row < sh.M && nw + c8 * 8 < sh.N)
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + (mb + row) * epi.ld + nw + c8 * 8));
+        });
+      };
+      static_for<0, FM>([&](auto i) {
+        const int64_t mb = mw + i * 16;
+        static_for<0, FN>([&](auto j) {
+          const int64_t n = nw + j * 16 + (lane & 15);
+          const float colp = n < sh.N ? epi.colparam(n) : 0.0f;
+          static_for<0, 4>([&](auto r) {
+            float o[2];
+            epi.eval(acc[i][j][(int)r], colp, 0.0f, o);
+            *reinterpret_cast<typename S::T*>(stg + (4 * (lane >> 4) + r) * RS + (j * 16 + (lane & 15)) * 2) =
+                S::from_f(o[0]);
+            if constexpr (Epi::kOuts == 2) acc[i][j][(int)r] = o[1];
+          });
+        });
+        if (epi.output(0)) store_block(epi.output(0), mb);
+        if constexpr (Epi::kOuts == 2) {
+          if (epi.output(1)) {
+            static_for<0, FN>([&](auto j) {
+              static_for<0, 4>([&](auto r) {
+                *reinterpret_cast<typename S::T*>(stg + (4 * (lane >> 4) + r) * RS + (j * 16 + (lane & 15)) * 2) =
+                    S::from_f(acc[i][j][(int)r]);
+              });
+            });
+            store_block(epi.output(1), mb);
+          }
+        }
       });
     } else {
       // Epilogue, one block of 32, 16 or 8 rows of the wave's tile at a

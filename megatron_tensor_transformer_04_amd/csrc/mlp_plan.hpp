@@ -34,6 +34,17 @@ using CfgD256 = DmaTile<256, 256, 2, 4, 64, 2>;
 // through L2 and LDS than 256 x 256; k-contiguous operands only (the
 // mn-contiguous LDS swizzle assumes a power-of-two row of units).
 using CfgD320 = DmaTile<256, 320, 4, 2, 64, 2>;
+// The same tiles on the 16x16x32 MFMA form, for the epilogues it supports
+// (a plain or bias + GeLU store) and row pitches whose per-load offsets stay
+// below 2^31.
+using CfgD320x16 = DmaTile<256, 320, 4, 2, 64, 2, 1, true>;
+template <class Epi>
+inline constexpr bool kMf16Epi = !Epi::kInput && !Epi::kColSum && !Epi::kDirectF32;
+constexpr int64_t kMf16MaxLd = (int64_t(1) << 31) / (2 * CfgD320x16::BM);
+inline std::atomic<bool> g_plan_mf16{true};
+inline bool use_mf16(int64_t ldp, int64_t ldq) {
+  return g_plan_mf16.load(std::memory_order_relaxed) && ldp < kMf16MaxLd && ldq < kMf16MaxLd;
+}
 
 struct Plan {
   Engine eng;
@@ -128,7 +139,8 @@ inline Engine pick_engine(int64_t M, int64_t N, int64_t K, bool gelu_p, bool kc)
     case TPMLP_PLAN_REG128: return Engine::Mfma128;
     case TPMLP_PLAN_REG256: return Engine::Mfma256;
     case TPMLP_PLAN_DMA256: return dma_fits ? Engine::Dma256 : Engine::Mfma256;
-    case TPMLP_PLAN_DMA320: return !dma_fits ? Engine::Mfma256 : kc ? Engine::Dma320 : Engine::Dma256;
+    case TPMLP_PLAN_DMA320:
+    case TPMLP_PLAN_DMA320_M32: return !dma_fits ? Engine::Mfma256 : kc ? Engine::Dma320 : Engine::Dma256;
     default: break;
   }
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
@@ -255,6 +267,8 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
           TailSplit tail = plan_tail(pl, K, Epi::kTailSplit && tail_ws != nullptr);
           if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
           tail.partial = tail_ws;
+          if constexpr (kMf16Epi<Epi>)
+            if (use_mf16(ldp, ldq)) return launch_dma<CfgD320x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
           return launch_dma<CfgD320, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
         }
         break;
@@ -290,8 +304,14 @@ hipError_t run_gemm_sliced(int dtype, int64_t M, int64_t N, int64_t K, const Row
     switch (pl.eng) {
       case Engine::Dma256: return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
       case Engine::Dma320:  // planned for k-contiguous Q only
-        if constexpr (QK) return launch_dma<CfgD320, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
-        else return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
+        if constexpr (QK) {
+          if constexpr (kMf16Epi<Epi>)
+            if (use_mf16(ldp, ldq))
+              return launch_dma<CfgD320x16, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
+          return launch_dma<CfgD320, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
+        } else {
+          return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
+        }
       case Engine::Mfma256: launch_mfma<Cfg256, S, true, QK, false, Epi, true>(sh, nullptr, ldp, q, ldq, epi, st, xs); break;
       default: launch_mfma<Cfg128, S, true, QK, false, Epi, true>(sh, nullptr, ldp, q, ldq, epi, st, xs); break;
     }

@@ -399,8 +399,9 @@ int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* con
 }
 
 int tp_mlp_debug_plan(int tile, int tail_cus) {
-  if (tile < TPMLP_PLAN_AUTO || tile > TPMLP_PLAN_DMA320 || tail_cus < 0 || tail_cus > 4096) return TPMLP_ERR_SHAPE;
+  if (tile < TPMLP_PLAN_AUTO || tile > TPMLP_PLAN_DMA320_M32 || tail_cus < 0 || tail_cus > 4096) return TPMLP_ERR_SHAPE;
   g_plan_tile.store(tile, std::memory_order_relaxed);
+  g_plan_mf16.store(tile != TPMLP_PLAN_DMA320_M32, std::memory_order_relaxed);
   g_plan_cus.store(tail_cus, std::memory_order_relaxed);
   return TPMLP_OK;
 }

@@ -470,7 +470,7 @@ def test_debug_plan_rejects_out_of_range_values(lib):
     ws = lambda: lib.tp_mlp_workspace_bytes(ctypes.byref(_shape(16384, 10240, 10240, 2)), 0)
     base = ws()
     assert lib.tp_mlp_debug_plan(-1, 0) == shape_err
-    assert lib.tp_mlp_debug_plan(_header_define("TPMLP_PLAN_DMA320") + 1, 0) == shape_err
+    assert lib.tp_mlp_debug_plan(_header_define("TPMLP_PLAN_DMA320_M32") + 1, 0) == shape_err
     assert lib.tp_mlp_debug_plan(0, -1) == shape_err
     assert lib.tp_mlp_debug_plan(0, 4097) == shape_err
     assert ws() == base

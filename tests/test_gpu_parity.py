@@ -44,7 +44,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("tile", [128, 256, "dma256", "dma320"], indirect=True)
+@pytest.mark.parametrize("tile", [128, 256, "dma256", "dma320", "dma320m32"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,h,f", RAGGED)
 def test_ragged_shapes_16bit(gpu_lib, tile, dtype, T, h, f):
@@ -68,7 +68,7 @@ def test_operands_read_in_place(gpu_lib, tile, dtype, T, h, f):
     compare(got, ref, TOL[dtype])
 
 
-@pytest.mark.parametrize("tile", ["dma256", "dma320"], indirect=True)
+@pytest.mark.parametrize("tile", ["dma256", "dma320", "dma320m32"], indirect=True)
 @pytest.mark.parametrize("cus", [3, 4, 5])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,h,f", [(520, 264, 392), (1000, 264, 392)])
@@ -217,7 +217,8 @@ FULL_WAVE = (4352, 5440, 5440)
 @pytest.mark.parametrize("tile,cus,shape", [(128, None, None), (256, None, None), ("dma256", None, None),
                                             ("dma256", 4, None), ("dma320", None, None), ("dma320", 2, None),
                                             (None, None, FULL_WAVE), ("dma256", None, FULL_WAVE),
-                                            ("dma320", None, FULL_WAVE)],
+                                            ("dma320", None, FULL_WAVE), ("dma320m32", None, FULL_WAVE),
+                                            ("dma320m32", 2, None)],
                          indirect=["tile"])
 def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, shape):
     """Each output lives between two poisoned guard regions, which must

@@ -32,7 +32,7 @@ def _bits(t):
 # a 256-row tile (the planner falls back to the register-staged engines,
 # which map each row to its slice), ragged and single slices
 SHAPES = [(8192, 1024, 2560, 4, None), (7800, 1024, 2560, 2, None), (1024, 264, 392, 4, "dma256"),
-          (1024, 264, 392, 2, "dma320"), (520, 264, 392, 4, None), (264, 136, 200, 3, None),
+          (1024, 264, 392, 2, "dma320"), (1024, 264, 392, 2, "dma320m32"), (520, 264, 392, 4, None), (264, 136, 200, 3, None),
           (96, 64, 128, 1, None), (4096, 512, 768, 16, 256)]
 
 
