@@ -117,7 +117,12 @@ struct DmaTile {
   static_assert(STAGES >= 2, "at least two stages");
   static_assert(BK == 32 || BK == 64, "k-tiles of 32 or 64 (an even number of 16-wide substeps)");
   static_assert(BK == 32 || WAVES % 2 == 0, "64-deep KC tiles need an even number of waves");
-  static_assert(!MF16 || (BK == 64 && LP + LQ <= FN - 1), "16x16 form: two substeps, loads fit the columns");
+  // 16x16 form: one set of fragment registers refilled as it is consumed
+  // (ROLLED, see the k-loop) where two sets and the accumulators would pass
+  // 224 of the 256 registers a lane has at two waves per SIMD.
+  static constexpr bool ROLLED = MF16 && (FM + FN) * 2 * 4 + FM * FN * 4 > 224;
+  static_assert(!MF16 || BK == 64, "16x16 form: two 32-wide substeps per k-tile");
+  static_assert(!ROLLED || LP + LQ <= FN - 1, "rolled 16x16 form: one load per column");
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS is 160 KB per CU");
   static constexpr int WAVES_PER_SIMD = WAVES * OCC / 4;
   static constexpr int PER_XCD = 32 * OCC;  // workgroups in flight per XCD
@@ -394,8 +399,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES, STG = Cfg::STG;
   constexpr bool M16 = Cfg::MF16;
-  static_assert(!M16 || (P_KC && Q_KC && !Epi::kInput && !Epi::kColSum && !Epi::kDirectF32),
-                "16x16 form: k-contiguous operands, a plain or bias + GeLU store");
+  static_assert(!M16 || (P_KC && Q_KC && !Epi::kDirectF32), "16x16 form: k-contiguous operands, a tile-wise epilogue");
   static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
                 "an mn-contiguous operand needs a power-of-two tile extent (swizzle, loads per k-row)");
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
@@ -561,13 +565,14 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // fragment (measured on MI355X with the reads interleaved as below: about
   // 1.5 % faster than row-major on 16384 x 10240 x 10240).
   auto mfmas = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN]) __attribute__((always_inline)) {
-    if constexpr (!M16) {
-      static_for<0, FN>([&](auto j) {
-        static_for<0, FM>([&](auto i) { acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]); });
+    static_for<0, FN>([&](auto j) {
+      static_for<0, FM>([&](auto i) {
+        if constexpr (M16) acc[i][j] = S::mfma16x16x32(fa[i], fb[j], acc[i][j]);
+        else acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]);
       });
-    }
+    });
   };
-  constexpr int NKS = BK / 16;  // 16-wide substeps per k-tile
+  constexpr int NKS = BK / (M16 ? 32 : 16);  // substeps per k-tile
   // DS read instructions per substep (a transposing read moves half a
   // fragment).
   constexpr int DSR = (P_KC ? 1 : 2) * FM + (Q_KC ? 1 : 2) * FN;
@@ -615,7 +620,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       for (int t = 0; t < cur.nk; ++t) {
         const int st_t = (t + s0) % ST;
         const bool wrap = st_t == ST - 1;  // tile t+1 sits in stage 0
-        if constexpr (M16) {
+        if constexpr (Cfg::ROLLED) {
           // Two 32-wide substeps on one set of fragment registers: each B
           // fragment is refilled with the next substep's once its column of
           // MFMAs has issued, each A fragment once its last MFMA (in the
@@ -768,11 +773,14 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       });
     } else if constexpr (M16) {
       // The 16x16 form's epilogue: per fragment row of the wave's tile (16
-      // rows), each output is rounded into a private block of stage s_epi
-      // (lane l holds C[4 (l / 16) + r][l % 16] of each fragment), read back
-      // as 16-byte row chunks and stored non-temporally (as below). A second
-      // output reuses the block once the first is stored, its fp32 values
-      // held in the accumulators meanwhile.
+      // rows) through a private block of stage s_epi, as below: the input
+      // (if any) lands there as 16-byte row chunks and comes back per lane
+      // with one transposing read per fragment (lane l holds
+      // C[4 (l / 16) + r][l % 16], r = 0..3, of each fragment: four rows of
+      // a column); each output is rounded into the block, read back as
+      // 16-byte row chunks and stored non-temporally. A second output reuses
+      // the block once the first is stored, its fp32 values held in the
+      // accumulators meanwhile.
       barrier_lds();
       char* const epi_lds = smem + s_epi * STG;
       constexpr int CPR = Cfg::WTN / 8;      // 16-byte chunks per staged row
@@ -783,6 +791,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       static_assert(Cfg::WAVES * BLK <= STG, "staging fits in one stage");
       char* const stg = epi_lds + wave * BLK;
       const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
+      const int G = lane >> 4, jj = lane & 15;
       auto store_block = [&](typename S::T* out, int64_t mb) __attribute__((always_inline)) {
         static_for<0, PASSES>([&](auto p) {
           const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
@@ -792,16 +801,43 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
             __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + (mb + row) * epi.ld + nw + c8 * 8));
         });
       };
+      float cs[FN];
+      static_for<0, FN>([&](auto j) { cs[j] = 0.0f; });
       static_for<0, FM>([&](auto i) {
         const int64_t mb = mw + i * 16;
+        if constexpr (Epi::kInput) {
+          static_for<0, PASSES>([&](auto p) {
+            const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
+            if (PART && p == PASSES - 1 && q >= HB * CPR) return;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (mb + row < sh.M && nw + c8 * 8 < sh.N) {
+              const u32x4* src = reinterpret_cast<const u32x4*>(epi.input() + (mb + row) * epi.ld + nw + c8 * 8);
+              x = epi.stream ? __builtin_nontemporal_load(src) : *src;
+            }
+            *reinterpret_cast<u32x4*>(stg + row * RS + c8 * 16) = x;
+          });
+        }
         static_for<0, FN>([&](auto j) {
-          const int64_t n = nw + j * 16 + (lane & 15);
-          const float colp = n < sh.N ? epi.colparam(n) : 0.0f;
+          const int64_t n = nw + j * 16 + jj;
+          const bool n_ok = n < sh.N;
+          const float colp = n_ok ? epi.colparam(n) : 0.0f;
+          float in[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (Epi::kInput) {
+            // the 16 lanes of group G supply rows 4 G + jj / 4, four columns
+            // from 4 (jj % 4) each; lane jj gets column jj's four rows
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(stg + (4 * G + (jj >> 2)) * RS + (j * 16 + (jj & 3) * 4) * 2));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) in[r] = S::to_f((typename S::T)(uint16_t)x[r]);
+          }
           static_for<0, 4>([&](auto r) {
             float o[2];
-            epi.eval(acc[i][j][(int)r], colp, 0.0f, o);
-            *reinterpret_cast<typename S::T*>(stg + (4 * (lane >> 4) + r) * RS + (j * 16 + (lane & 15)) * 2) =
-                S::from_f(o[0]);
+            const float c = epi.eval(acc[i][j][(int)r], colp, in[(int)r], o);
+            if constexpr (Epi::kColSum) {
+              if (n_ok && mb + 4 * G + r < sh.M) cs[j] += c;
+            }
+            *reinterpret_cast<typename S::T*>(stg + (4 * G + r) * RS + (j * 16 + jj) * 2) = S::from_f(o[0]);
             if constexpr (Epi::kOuts == 2) acc[i][j][(int)r] = o[1];
           });
         });
@@ -810,7 +846,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           if (epi.output(1)) {
             static_for<0, FN>([&](auto j) {
               static_for<0, 4>([&](auto r) {
-                *reinterpret_cast<typename S::T*>(stg + (4 * (lane >> 4) + r) * RS + (j * 16 + (lane & 15)) * 2) =
+                *reinterpret_cast<typename S::T*>(stg + (4 * G + r) * RS + (j * 16 + jj) * 2) =
                     S::from_f(acc[i][j][(int)r]);
               });
             });
@@ -818,6 +854,24 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           }
         }
       });
+      if constexpr (Epi::kColSum) {
+        // Column sums of this tile, in a fixed order: the four lane groups
+        // (pairwise), then the waves along M.
+        __syncthreads();
+        float* red = reinterpret_cast<float*>(epi_lds);  // [WAVES_M][BN]
+        static_for<0, FN>([&](auto j) {
+          cs[j] += __shfl_xor(cs[j], 16);
+          cs[j] += __shfl_xor(cs[j], 32);
+        });
+        if (lane < 16) static_for<0, FN>([&](auto j) { red[wm * BN + wn * Cfg::WTN + j * 16 + lane] = cs[j]; });
+        __syncthreads();
+        for (int c = tid; c < BN; c += Cfg::THREADS) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int w = 0; w < Cfg::WAVES_M; ++w) sum += red[w * BN + c];
+          if (n0 + c < sh.N) epi.colsum(done.tm, n0 + c, sum);
+        }
+      }
     } else {
       // Epilogue, one block of 32, 16 or 8 rows of the wave's tile at a
       // time, staged through a private region of stage s_epi so that global

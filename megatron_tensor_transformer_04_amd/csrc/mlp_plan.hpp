@@ -34,12 +34,14 @@ using CfgD256 = DmaTile<256, 256, 2, 4, 64, 2>;
 // through L2 and LDS than 256 x 256; k-contiguous operands only (the
 // mn-contiguous LDS swizzle assumes a power-of-two row of units).
 using CfgD320 = DmaTile<256, 320, 4, 2, 64, 2>;
-// The same tiles on the 16x16x32 MFMA form, for the epilogues it supports
-// (a plain or bias + GeLU store) and row pitches whose per-load offsets stay
-// below 2^31.
+// The direct-load tiles on the 16x16x32 MFMA form (see gemm_dma.hpp), taken
+// where both operands are k-contiguous, the epilogue is tile-wise (not the
+// fp32 read-modify-write) and the row pitches keep every load's offset below
+// 2^31.
 using CfgD320x16 = DmaTile<256, 320, 4, 2, 64, 2, 1, true>;
+using CfgD256x16 = DmaTile<256, 256, 2, 4, 64, 2, 1, true>;
 template <class Epi>
-inline constexpr bool kMf16Epi = !Epi::kInput && !Epi::kColSum && !Epi::kDirectF32;
+inline constexpr bool kMf16Epi = !Epi::kDirectF32;
 constexpr int64_t kMf16MaxLd = (int64_t(1) << 31) / (2 * CfgD320x16::BM);
 inline std::atomic<bool> g_plan_mf16{true};
 inline bool use_mf16(int64_t ldp, int64_t ldq) {
@@ -259,6 +261,8 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
           TailSplit tail = plan_tail(pl, K, Epi::kTailSplit && tail_ws != nullptr);
           if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
           tail.partial = tail_ws;
+          if constexpr (PK && QK && kMf16Epi<Epi>)
+            if (use_mf16(ldp, ldq)) return launch_dma<CfgD256x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
           return launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
         }
         break;
@@ -302,7 +306,11 @@ hipError_t run_gemm_sliced(int dtype, int64_t M, int64_t N, int64_t K, const Row
     return hipErrorInvalidValue;  // the fp32 path reads dense operands only
   } else {
     switch (pl.eng) {
-      case Engine::Dma256: return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
+      case Engine::Dma256:
+        if constexpr (QK && kMf16Epi<Epi>)
+          if (use_mf16(ldp, ldq))
+            return launch_dma<CfgD256x16, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
+        return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
       case Engine::Dma320:  // planned for k-contiguous Q only
         if constexpr (QK) {
           if constexpr (kMf16Epi<Epi>)
