@@ -379,8 +379,8 @@ int tp_mlp_reduce_partials(const tpmlp_shape* shape, int nparts, const void* con
  *             (direct-load 256x320 where both operands are k-contiguous,
  *             256x256 elsewhere), TPMLP_PLAN_DMA320_M32 (as DMA320, with
  *             every direct-load tile on the 32x32x16 MFMA form; otherwise
- *             tiles whose operands are both k-contiguous run on the
- *             16x16x32 form). A forced direct-load engine still yields
+ *             they run on the 16x16x32 form, except under the fp32
+ *             main-gradient accumulation). A forced direct-load engine still yields
  *             to the register-staged 256x256 one where an operand exceeds
  *             its 32-bit offsets or GeLU is applied on load.
  *   tail_cus  CU count of the k-split plan, 1 .. 4096; 0 = the chip's 256.

@@ -19,7 +19,8 @@
 //            (below) rot(r & 7) ^ (4 ((r >> 3) & 1)), rot = the three bits
 //            rotated right by one.
 //   MC tile: [BK][R], k-rows of R/16 32-byte units; unit u of k-row k sits
-//            at u ^ sm(k), sm(k) = (k & 3) ^ ((k & 3) << 1) (mod 8).
+//            at u ^ sm(k), sm(k) = (k & 3) ^ ((k & 3) << 1) (mod 8), in the
+//            16x16 form sm(k) ^ 4 ((k >> 3) & 1).
 // A fragment read by 8 or 16 consecutive lanes (KC, ds_read_b128) and by 16
 // or 32 consecutive lanes (MC, ds_read_b64_tr_b16) touches distinct banks
 // under either swizzle, and both depend only on the lane, so every fragment
@@ -215,7 +216,11 @@ __device__ __forceinline__ int dsk(int r) {
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-__device__ __forceinline__ int dsm(int k) { return ((k & 3) ^ ((k & 3) << 1)) & 7; }
+template <bool MF16 = false>
+__device__ __forceinline__ int dsm(int k) {
+  const int s = ((k & 3) ^ ((k & 3) << 1)) & 7;
+  return MF16 ? s ^ (((k >> 3) & 1) << 2) : s;  // 16x16 form: k-row bit 3 flips bit 2
+}
 
 // Workgroup -> work order for kernels that run one workgroup per CU. The
 // hardware hands workgroup b to XCD b % 8, and each XCD has its own L2;
@@ -284,7 +289,7 @@ __device__ __forceinline__ void dma_slot(int blk, int lane, int64_t ld, int64_t&
   } else {
     const int o = blk * 1024 + lane * 16;
     const int kr = o / (R * 2), w = o % (R * 2);
-    const int u = (w >> 5) ^ dsm(kr);
+    const int u = (w >> 5) ^ dsm<MF16>(kr);
     const int c8 = 2 * u + ((w >> 4) & 1);
     mn = c8 * 8;
     kk = kr;
@@ -380,6 +385,45 @@ struct FragAddr16 {
   }
 };
 
+// The same for an MC tile [BK][R] (16x16 form swizzle): NF fragments of 16
+// columns, the first at tile column `first` (a multiple of 16). Lanes 16 G
+// .. 16 G + 15 read 32-byte unit first/16 + i, k-rows 32 ks + 8 G + 4 hh +
+// (l % 16) / 4 (hh = 0, 1: two transposing reads), 8-byte piece l % 4: lane
+// l gets column l % 16's eight k values 32 ks + 8 G .. + 7. Bits 0, 1 and 3
+// of the k-row pick the unit's place, so the 32 lanes of groups 0 and 1
+// touch 8 distinct places (all 64 banks).
+template <int R, int NF>
+struct FragAddrMC16 {
+  static constexpr int NB = NF;
+  uint32_t base[NB];
+  __device__ __forceinline__ void init(int lane, int region, int first) {
+    const int G = lane >> 4, j = lane & 15;
+    const int kr = 8 * G + (j >> 2);
+    const int u0 = first >> 4;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      base[i] = (uint32_t)(region + kr * (R * 2) + (((u0 + i) ^ dsm<true>(kr)) << 5) + ((j & 3) << 3));
+  }
+  __device__ __forceinline__ void advance(uint32_t delta) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) base[i] += delta;
+  }
+  template <int I, int KS>
+  __device__ __forceinline__ u32x4 read(const char* lds) const {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    u32x4 out;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const i16x4 v =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + base[I] + (KS * 32 + hh * 4) * (R * 2)));
+      const u32x2 w = __builtin_bit_cast(u32x2, v);
+      out[2 * hh] = w[0];
+      out[2 * hh + 1] = w[1];
+    }
+    return out;
+  }
+};
+
 // One workgroup per CU, each looping over work items v = blockIdx.x,
 // blockIdx.x + gridDim.x, ... (nwork items: the tiles, with the tail tiles
 // split into k-ranges, see TailSplit). Between two items the first k-tile
@@ -399,7 +443,8 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES, STG = Cfg::STG;
   constexpr bool M16 = Cfg::MF16;
-  static_assert(!M16 || (P_KC && Q_KC && !Epi::kDirectF32), "16x16 form: k-contiguous operands, a tile-wise epilogue");
+  static_assert(!M16 || !Epi::kDirectF32, "16x16 form: a tile-wise epilogue");
+  static_assert(!Cfg::ROLLED || (P_KC && Q_KC), "rolled 16x16 form: k-contiguous operands");
   static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
                 "an mn-contiguous operand needs a power-of-two tile extent (swizzle, loads per k-row)");
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
@@ -445,12 +490,14 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       return uniform_rsrc(xs.p[sl] + r0 * P.ld, rows * P.ld * 2);
     } else {
       const int64_t base = P_KC ? it.m0 * P.ld : it.m0;
-      return uniform_rsrc(P.ptr + base, (M16 ? min(p_extent - base, (sh.M - it.m0) * P.ld) : p_extent - base) * 2);
+      return uniform_rsrc(P.ptr + base,
+                          (M16 && P_KC ? min(p_extent - base, (sh.M - it.m0) * P.ld) : p_extent - base) * 2);
     }
   };
   auto q_rsrc = [&](const Item& it) __attribute__((always_inline)) {
     const int64_t base = Q_KC ? it.n0 * Q.ld : it.n0;
-    return uniform_rsrc(Q.ptr + base, (M16 ? min(q_extent - base, (sh.N - it.n0) * Q.ld) : q_extent - base) * 2);
+    return uniform_rsrc(Q.ptr + base,
+                        (M16 && Q_KC ? min(q_extent - base, (sh.N - it.n0) * Q.ld) : q_extent - base) * 2);
   };
 
   // Per-lane byte offsets from the tile origin at k = 0; rows / columns
@@ -459,9 +506,13 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // arithmetic. pk0 / qk0: the k offset (within a tile) of load 0's chunk
   // (the same for every item); load c's is that plus dma_kstep<>(c). The
   // 16x16 form keeps load 0's offset only (registers are short there): load
-  // c's rows are c * WAVES * 8 rows further on, with the same chunk (the
-  // swizzle depends on the row mod 16), and rows past the matrix fall
-  // outside the buffer resource.
+  // c's source is a fixed stride further on (KC: c * WAVES * 8 rows, with
+  // the same chunk, as the swizzle depends on the row mod 16; MC: the
+  // k-rows of dma_kstep<>(c), a multiple of 16, with the same columns). A KC
+  // tile's rows past the matrix fall outside its buffer resource; an MC
+  // tile's columns past the matrix read whatever lies there (inside the
+  // buffer) or zeros (past it), and feed only output columns or rows past
+  // the matrix, which no epilogue stores or sums.
   constexpr int NPV = M16 ? 1 : LP, NQV = M16 ? 1 : LQ;
   int pk0 = 0, qk0 = 0;
   auto offsets = [&](const Item& it, uint32_t(&pv)[NPV], uint32_t(&qv)[NQV]) __attribute__((always_inline)) {
@@ -472,10 +523,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     if constexpr (M16) {
       int64_t rel;
       int mn, kk;
-      dma_slot<true, BM, BK, true>(wave, ln, P.ld, rel, mn, kk);
+      dma_slot<P_KC, BM, BK, true>(wave, ln, P.ld, rel, mn, kk);
       pv[0] = (uint32_t)rel * 2u;
       pk0 = kk;
-      dma_slot<true, BN, BK, true>(wave, ln, Q.ld, rel, mn, kk);
+      dma_slot<Q_KC, BN, BK, true>(wave, ln, Q.ld, rel, mn, kk);
       qv[0] = (uint32_t)rel * 2u;
       qk0 = kk;
       return;
@@ -515,22 +566,26 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
     char* const sp = smem + stage * STG;
     if constexpr (M16) {
-      // load 0's offset, or kOobOffset past the k-range (then every load's
-      // offset stays beyond num_records); made opaque so that the per-load
-      // sums are formed here, not kept in registers across the loop
-      constexpr int RSTEP = Cfg::WAVES * 8;
-      const uint32_t pb = (uint32_t)opaque_v((int)(pk0 < krem ? pv[0] : kOobOffset));
-      const uint32_t qb = (uint32_t)opaque_v((int)(qk0 < krem ? qv[0] : kOobOffset));
-      const uint32_t pstep = (uint32_t)(RSTEP * P.ld * 2), qstep = (uint32_t)(RSTEP * Q.ld * 2);
+      // Load c's offset from load 0's (made opaque, so that the per-load
+      // sums are formed here rather than kept in registers across the loop).
+      // KC: all loads share load 0's k chunk, so one check against the
+      // k-range selects kOobOffset for all (kOobOffset + c * step stays past
+      // num_records); MC: load c's k-row is checked on its own.
+      auto one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t base, int k0c, int soff, bool kc, int64_t ld, int R,
+                     int lds_off, auto c) __attribute__((always_inline)) {
+        const int kstep = kc ? 0 : c * Cfg::WAVES * (1024 / (2 * R));
+        const uint32_t step = kc ? (uint32_t)(Cfg::WAVES * 8 * ld * 2) : (uint32_t)(kstep * ld * 2);
+        const uint32_t off = kc ? base + (uint32_t)c * step : (k0c + kstep < krem ? base + step : kOobOffset);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sp + lds_off + (c * Cfg::WAVES + wave) * 1024), 16,
+                                                 off, soff, 0, 0);
+      };
+      const uint32_t pb = (uint32_t)opaque_v((int)(!P_KC || pk0 < krem ? pv[0] : kOobOffset));
+      const uint32_t qb = (uint32_t)opaque_v((int)(!Q_KC || qk0 < krem ? qv[0] : kOobOffset));
       static_for<0, LP>([&](auto c) {
-        if constexpr (PART == 2 || (PART == 0) == (c < FIRST))
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + (c * Cfg::WAVES + wave) * 1024), 16,
-                                                   pb + (uint32_t)c * pstep, psoff, 0, 0);
+        if constexpr (PART == 2 || (PART == 0) == (c < FIRST)) one(prs, pb, pk0, psoff, P_KC, P.ld, BM, 0, c);
       });
       static_for<0, LQ>([&](auto c) {
-        if constexpr (PART == 2 || (PART == 0) == (LP + c < FIRST))
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(sp + Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024),
-                                                   16, qb + (uint32_t)c * qstep, qsoff, 0, 0);
+        if constexpr (PART == 2 || (PART == 0) == (LP + c < FIRST)) one(qrs, qb, qk0, qsoff, Q_KC, Q.ld, BN, Cfg::LDS_P, c);
       });
       return;
     }
@@ -551,8 +606,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   };
   constexpr auto kAll = std::integral_constant<int, 2>{};
 
-  std::conditional_t<M16, FragAddr16<FM>, FragAddr<P_KC, BM, BK, FM>> pa;
-  std::conditional_t<M16, FragAddr16<FN>, FragAddr<Q_KC, BN, BK, FN>> qa;
+  std::conditional_t<M16, std::conditional_t<P_KC, FragAddr16<FM>, FragAddrMC16<BM, FM>>, FragAddr<P_KC, BM, BK, FM>>
+      pa;
+  std::conditional_t<M16, std::conditional_t<Q_KC, FragAddr16<FN>, FragAddrMC16<BN, FN>>, FragAddr<Q_KC, BN, BK, FN>>
+      qa;
   using AccT = std::conditional_t<M16, f32x4, f32x16>;
   AccT acc[FM][FN];
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];

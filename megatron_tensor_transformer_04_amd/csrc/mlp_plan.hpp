@@ -34,19 +34,6 @@ using CfgD256 = DmaTile<256, 256, 2, 4, 64, 2>;
 // through L2 and LDS than 256 x 256; k-contiguous operands only (the
 // mn-contiguous LDS swizzle assumes a power-of-two row of units).
 using CfgD320 = DmaTile<256, 320, 4, 2, 64, 2>;
-// The direct-load tiles on the 16x16x32 MFMA form (see gemm_dma.hpp), taken
-// where both operands are k-contiguous, the epilogue is tile-wise (not the
-// fp32 read-modify-write) and the row pitches keep every load's offset below
-// 2^31.
-using CfgD320x16 = DmaTile<256, 320, 4, 2, 64, 2, 1, true>;
-using CfgD256x16 = DmaTile<256, 256, 2, 4, 64, 2, 1, true>;
-template <class Epi>
-inline constexpr bool kMf16Epi = !Epi::kDirectF32;
-constexpr int64_t kMf16MaxLd = (int64_t(1) << 31) / (2 * CfgD320x16::BM);
-inline std::atomic<bool> g_plan_mf16{true};
-inline bool use_mf16(int64_t ldp, int64_t ldq) {
-  return g_plan_mf16.load(std::memory_order_relaxed) && ldp < kMf16MaxLd && ldq < kMf16MaxLd;
-}
 
 struct Plan {
   Engine eng;
@@ -71,6 +58,27 @@ inline int64_t staged_ld(int64_t R) { return R + kStagePad; }
 
 // CUs of an MI355X: one wave of 256 x 256 tiles.
 constexpr int kCUs = 256;
+
+// The direct-load tiles on the 16x16x32 MFMA form (see gemm_dma.hpp), taken
+// where the epilogue is tile-wise (not the fp32 read-modify-write) and the
+// row pitches keep every load's offset below 2^31 (256 x 320 tiles only
+// come with k-contiguous operands). With an mn-contiguous operand only in
+// launches of at least one tile per CU: the form gains through the clock
+// the chip holds under full load, and a launch that leaves CUs idle runs
+// at a higher clock on either form, where the 16x16 one's doubled
+// transposing reads cost more (measured on MI355X: 7B shard, 16 x 16
+// tiles, dA 236 -> 230 us; 2.4B shard, 10 x 10 tiles split in two k-ranges,
+// 126 -> 135 us).
+using CfgD320x16 = DmaTile<256, 320, 4, 2, 64, 2, 1, true>;
+using CfgD256x16 = DmaTile<256, 256, 2, 4, 64, 2, 1, true>;
+template <class Epi>
+inline constexpr bool kMf16Epi = !Epi::kDirectF32;
+constexpr int64_t kMf16MaxLd = (int64_t(1) << 31) / (2 * CfgD320x16::BM);
+inline std::atomic<bool> g_plan_mf16{true};
+inline bool use_mf16(int64_t ldp, int64_t ldq, bool kc, int64_t ntile) {
+  return g_plan_mf16.load(std::memory_order_relaxed) && ldp < kMf16MaxLd && ldq < kMf16MaxLd &&
+         (kc || ntile >= kCUs);
+}
 
 // Tile work of a launch counted in whole waves over the CUs (a last partial
 // wave costs as much as a full one).
@@ -261,8 +269,9 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
           TailSplit tail = plan_tail(pl, K, Epi::kTailSplit && tail_ws != nullptr);
           if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
           tail.partial = tail_ws;
-          if constexpr (PK && QK && kMf16Epi<Epi>)
-            if (use_mf16(ldp, ldq)) return launch_dma<CfgD256x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
+          if constexpr (kMf16Epi<Epi>)
+            if (use_mf16(ldp, ldq, PK && QK, (int64_t)pl.tiles_m * pl.tiles_n))
+              return launch_dma<CfgD256x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
           return launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
         }
         break;
@@ -272,7 +281,7 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
           if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
           tail.partial = tail_ws;
           if constexpr (kMf16Epi<Epi>)
-            if (use_mf16(ldp, ldq)) return launch_dma<CfgD320x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
+            if (use_mf16(ldp, ldq, true, 0)) return launch_dma<CfgD320x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
           return launch_dma<CfgD320, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
         }
         break;
@@ -307,14 +316,14 @@ hipError_t run_gemm_sliced(int dtype, int64_t M, int64_t N, int64_t K, const Row
   } else {
     switch (pl.eng) {
       case Engine::Dma256:
-        if constexpr (QK && kMf16Epi<Epi>)
-          if (use_mf16(ldp, ldq))
+        if constexpr (kMf16Epi<Epi>)
+          if (use_mf16(ldp, ldq, QK, (int64_t)pl.tiles_m * pl.tiles_n))
             return launch_dma<CfgD256x16, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
         return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
       case Engine::Dma320:  // planned for k-contiguous Q only
         if constexpr (QK) {
           if constexpr (kMf16Epi<Epi>)
-            if (use_mf16(ldp, ldq))
+            if (use_mf16(ldp, ldq, true, 0))
               return launch_dma<CfgD320x16, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
           return launch_dma<CfgD320, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
         } else {

@@ -57,10 +57,12 @@ def test_ragged_shapes_16bit(gpu_lib, tile, dtype, T, h, f):
 
 @pytest.mark.parametrize("tile", ["dma256"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,h,f", [(200, 136, 264), (520, 264, 392)])
+@pytest.mark.parametrize("T,h,f", [(200, 136, 264), (520, 264, 392), (4352, 5440, 5440)])
 def test_operands_read_in_place(gpu_lib, tile, dtype, T, h, f):
     """Minimal workspaces: the large-tile engine reads the mn-contiguous
-    operands in place (transposing LDS reads) instead of staged copies."""
+    operands in place (transposing LDS reads) instead of staged copies. The
+    last shape has more than one wave of 256 x 256 tiles, where those
+    launches run on the 16x16x32 MFMA form."""
     print(f"case in-place dtype={dtype} T={T} h={h} f={f}", flush=True)
     inp = synth.draw_inputs(T, h, f, dtype, seed=T + 3 * f, sigma_dy=1.0)
     ref = _oracle_shard(inp)
