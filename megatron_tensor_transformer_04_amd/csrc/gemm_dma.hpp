@@ -764,6 +764,47 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     // Drain this wave's loads of the tiles past the end (they write LDS).
     wait_vmcnt<0>();
 
+    // 16x16 form with an epilogue input: the input's first 16-row block is
+    // requested now, ahead of the next item's loads, so that waiting for it
+    // does not wait for them (vector-memory operations complete in order);
+    // each later block is requested before the current block's arithmetic
+    // and stores (see the epilogue), into the fragment registers the K loop
+    // has released. The epilogue's loads and stores are buffer operations
+    // without branches: rows past the matrix lie beyond the buffer
+    // resource (which starts at the tile's first row), chunks past the last
+    // column take kOobOffset. Branches around them would leave the compiler
+    // unable to count the operations in flight, and every wait for a block
+    // would then wait for the previous block's stores as well.
+    constexpr int E_CPR = Cfg::WTN / 8, E_HB = 16, E_PASSES = (E_HB * E_CPR + 63) / 64;
+    constexpr bool E_PART = E_PASSES * 64 != E_HB * E_CPR;
+    u32x4 zin[M16 && Epi::kInput ? E_PASSES : 1];
+    // byte offset of 16-byte chunk c8 of row `row` (both relative to the
+    // wave's tile) in a tensor of the epilogue's pitch, rows from the tile's
+    // first on; kOobOffset past the last column
+    auto e_off = [&](const Item& it, int row, int c8) __attribute__((always_inline)) {
+      const int64_t n = it.n0 + wn * Cfg::WTN + c8 * 8;
+      return n < sh.N ? (uint32_t)(((int64_t)(wm * Cfg::WTM + row) * epi.ld + n) * 2) : kOobOffset;
+    };
+    auto e_rsrc = [&](const Item& it, const void* t) __attribute__((always_inline)) {
+      return uniform_rsrc(t ? static_cast<const char*>(t) + it.m0 * epi.ld * 2 : nullptr,
+                          t ? (sh.M - it.m0) * epi.ld * 2 : 0);
+    };
+    auto load_input = [&](const Item& it, int rb) __attribute__((always_inline)) {  // rows rb .. rb + 15
+      if constexpr (M16 && Epi::kInput) {
+        const __amdgpu_buffer_rsrc_t rs = e_rsrc(it, epi.input());
+        auto go = [&](auto aux) __attribute__((always_inline)) {
+          static_for<0, E_PASSES>([&](auto p) {
+            const int q = lane + 64 * p, row = q / E_CPR, c8 = q % E_CPR;
+            if (E_PART && p == E_PASSES - 1 && q >= E_HB * E_CPR) return;
+            zin[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, e_off(it, rb + row, c8), 0, decltype(aux)::value);
+          });
+        };
+        if (epi.stream) go(std::integral_constant<int, 2>{});  // non-temporal
+        else go(std::integral_constant<int, 0>{});
+      }
+    };
+    load_input(cur, 0);
+
     // Stages: the next item's k-tile 0 goes to the stage after the last
     // tile this item issued (free: its last reader passed a barrier above,
     // and this wave's own loads into it have drained); the epilogue stages
@@ -772,7 +813,18 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const int s_epi = (cur.nk + s0 + ST - 1) % ST;
     const int v_next = v + (int)gridDim.x;
     const bool has_next = v_next < nwork;
-    if (has_next) {
+    if constexpr (M16 && Epi::kInput) {
+      // Without a branch (so that the compiler counts these loads when it
+      // waits for the input block requested above): past the last item,
+      // empty buffer resources make them fill stage s_next with zeros that
+      // nothing reads, and the loads drain before the workgroup ends.
+      const Item nxt = decode(opaque_s(has_next ? v_next : v));
+      uint32_t pv2[NPV], qv2[NQV];
+      offsets(nxt, pv2, qv2);
+      const __amdgpu_buffer_rsrc_t none = uniform_rsrc(nullptr, 0);
+      const __amdgpu_buffer_rsrc_t prs2 = has_next ? p_rsrc(nxt) : none, qrs2 = has_next ? q_rsrc(nxt) : none;
+      static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST, kAll); });
+    } else if (has_next) {
       const Item nxt = decode(opaque_s(v_next));
       uint32_t pv2[NPV], qv2[NQV];
       offsets(nxt, pv2, qv2);
@@ -831,8 +883,9 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     } else if constexpr (M16) {
       // The 16x16 form's epilogue: per fragment row of the wave's tile (16
       // rows) through a private block of stage s_epi, as below: the input
-      // (if any) lands there as 16-byte row chunks and comes back per lane
-      // with one transposing read per fragment (lane l holds
+      // (if any, requested one block ahead) lands there as 16-byte row
+      // chunks and comes back per lane with one transposing read per
+      // fragment (lane l holds
       // C[4 (l / 16) + r][l % 16], r = 0..3, of each fragment: four rows of
       // a column); each output is rounded into the block, read back as
       // 16-byte row chunks and stored non-temporally. A second output reuses
@@ -849,13 +902,13 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       char* const stg = epi_lds + wave * BLK;
       const int64_t mw = m0 + wm * Cfg::WTM, nw = n0 + wn * Cfg::WTN;
       const int G = lane >> 4, jj = lane & 15;
-      auto store_block = [&](typename S::T* out, int64_t mb) __attribute__((always_inline)) {
+      auto store_block = [&](typename S::T* out, int i) __attribute__((always_inline)) {  // fragment row i
+        const __amdgpu_buffer_rsrc_t rs = e_rsrc(done, out);
         static_for<0, PASSES>([&](auto p) {
           const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
           if (PART && p == PASSES - 1 && q >= HB * CPR) return;
           const u32x4 x = *reinterpret_cast<const u32x4*>(stg + row * RS + c8 * 16);
-          if (mb + row < sh.M && nw + c8 * 8 < sh.N)
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + (mb + row) * epi.ld + nw + c8 * 8));
+          __builtin_amdgcn_raw_buffer_store_b128(x, rs, e_off(done, 16 * i + row, c8), 0, 2);  // non-temporal
         });
       };
       float cs[FN];
@@ -863,16 +916,13 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       static_for<0, FM>([&](auto i) {
         const int64_t mb = mw + i * 16;
         if constexpr (Epi::kInput) {
+          static_assert(E_PASSES == PASSES && E_CPR == CPR && E_HB == HB, "one block layout");
           static_for<0, PASSES>([&](auto p) {
             const int q = lane + 64 * p, row = q / CPR, c8 = q % CPR;
             if (PART && p == PASSES - 1 && q >= HB * CPR) return;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (mb + row < sh.M && nw + c8 * 8 < sh.N) {
-              const u32x4* src = reinterpret_cast<const u32x4*>(epi.input() + (mb + row) * epi.ld + nw + c8 * 8);
-              x = epi.stream ? __builtin_nontemporal_load(src) : *src;
-            }
-            *reinterpret_cast<u32x4*>(stg + row * RS + c8 * 16) = x;
+            *reinterpret_cast<u32x4*>(stg + row * RS + c8 * 16) = zin[p];
           });
+          if constexpr (i + 1 < FM) load_input(done, 16 * (i + 1));
         }
         static_for<0, FN>([&](auto j) {
           const int64_t n = nw + j * 16 + jj;
@@ -880,13 +930,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           const float colp = n_ok ? epi.colparam(n) : 0.0f;
           float in[4] = {0.f, 0.f, 0.f, 0.f};
           if constexpr (Epi::kInput) {
-            // the 16 lanes of group G supply rows 4 G + jj / 4, four columns
-            // from 4 (jj % 4) each; lane jj gets column jj's four rows
-            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(stg + (4 * G + (jj >> 2)) * RS + (j * 16 + (jj & 3) * 4) * 2));
+            // rows 4 G + r of column j * 16 + jj: four 16-bit reads (a
+            // transposing read here made the compiler wait for every
+            // direct-to-LDS load in flight first, the next item's included)
+            const char* const pz = stg + 4 * G * RS + (j * 16 + jj) * 2;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) in[r] = S::to_f((typename S::T)(uint16_t)x[r]);
+            for (int r = 0; r < 4; ++r) in[r] = S::to_f(*reinterpret_cast<const typename S::T*>(pz + r * RS));
           }
           static_for<0, 4>([&](auto r) {
             float o[2];
@@ -898,7 +947,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
             if constexpr (Epi::kOuts == 2) acc[i][j][(int)r] = o[1];
           });
         });
-        if (epi.output(0)) store_block(epi.output(0), mb);
+        store_block(epi.output(0), i);  // a null output: an empty resource, every store dropped
         if constexpr (Epi::kOuts == 2) {
           if (epi.output(1)) {
             static_for<0, FN>([&](auto j) {
@@ -907,21 +956,22 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
                     S::from_f(acc[i][j][(int)r]);
               });
             });
-            store_block(epi.output(1), mb);
+            store_block(epi.output(1), i);
           }
         }
       });
       if constexpr (Epi::kColSum) {
         // Column sums of this tile, in a fixed order: the four lane groups
-        // (pairwise), then the waves along M.
-        __syncthreads();
+        // (pairwise), then the waves along M. LDS-only barriers: the
+        // outputs' stores may still be in flight.
+        barrier_lds();
         float* red = reinterpret_cast<float*>(epi_lds);  // [WAVES_M][BN]
         static_for<0, FN>([&](auto j) {
           cs[j] += __shfl_xor(cs[j], 16);
           cs[j] += __shfl_xor(cs[j], 32);
         });
         if (lane < 16) static_for<0, FN>([&](auto j) { red[wm * BN + wn * Cfg::WTN + j * 16 + lane] = cs[j]; });
-        __syncthreads();
+        barrier_lds();
         for (int c = tid; c < BN; c += Cfg::THREADS) {
           float sum = 0.0f;
 #pragma unroll
@@ -1039,7 +1089,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
         }
       }
     }
-    if (!has_next) break;
+    if (!has_next) {
+      if constexpr (M16 && Epi::kInput) wait_vmcnt<0>();  // the loads into stage s_next above
+      break;
+    }
     // Every wave is done with stage s_epi before the next item loads it.
     barrier_lds();
     v = v_next;
