@@ -17,6 +17,11 @@
 //   const T* input() / T* output(k) / int64_t ld   those tensors (an output
 //                                                  may be null: not kept);
 //   float colparam(int64_t n)                      a per-column value;
+//   static constexpr bool kColParam                whether it has one other
+//                                                  than 0, and then
+//   const T* colvec()                              the 16-bit vector it is
+//                                                  read from (colparam(n) =
+//                                                  colvec()[n]);
 //   float eval(float acc, float colp, float in, float (&o)[2])
 //                                                  the fp32 outputs before
 //                                                  rounding, and the value
@@ -37,9 +42,11 @@ struct EpiStore {
   static constexpr bool kInput = false;
   static constexpr bool kTailSplit = true;  // a plain store: k-split tail tiles may finish it elsewhere
   static constexpr bool kDirectF32 = false;
+  static constexpr bool kColParam = false;
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int) const { return out; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
+  __device__ __forceinline__ const typename S::T* colvec() const { return nullptr; }
   __device__ __forceinline__ float eval(float acc, float, float, float (&o)[2]) const {
     o[0] = acc;
     return 0.0f;
@@ -66,9 +73,11 @@ struct EpiBiasGelu {
   static constexpr bool kInput = false;
   static constexpr bool kTailSplit = false;
   static constexpr bool kDirectF32 = false;
+  static constexpr bool kColParam = true;
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int k) const { return k ? h : z; }
   __device__ __forceinline__ float colparam(int64_t n) const { return S::to_f(bias[n]); }
+  __device__ __forceinline__ const typename S::T* colvec() const { return bias; }
   __device__ __forceinline__ float eval(float acc, float colp, float, float (&o)[2]) const {
     const float v = acc + colp;
     o[0] = v;
@@ -104,9 +113,11 @@ struct EpiGeluGrad {
   static constexpr bool kInput = true;
   static constexpr bool kTailSplit = false;
   static constexpr bool kDirectF32 = false;
+  static constexpr bool kColParam = false;
   __device__ __forceinline__ const typename S::T* input() const { return zin; }
   __device__ __forceinline__ typename S::T* output(int) const { return dz; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
+  __device__ __forceinline__ const typename S::T* colvec() const { return nullptr; }
   __device__ __forceinline__ float eval(float acc, float, float zv, float (&o)[2]) const {
     const float d = acc * gelu_tanh_grad(zv);
     o[0] = d;
@@ -140,9 +151,11 @@ struct EpiAccumF32 {
   static constexpr bool kInput = false;
   static constexpr bool kTailSplit = false;
   static constexpr bool kDirectF32 = true;
+  static constexpr bool kColParam = false;
   __device__ __forceinline__ const typename S::T* input() const { return nullptr; }
   __device__ __forceinline__ typename S::T* output(int) const { return nullptr; }
   __device__ __forceinline__ float colparam(int64_t) const { return 0.0f; }
+  __device__ __forceinline__ const typename S::T* colvec() const { return nullptr; }
   __device__ __forceinline__ float eval(float acc, float, float, float (&o)[2]) const {
     o[0] = acc;
     return 0.0f;
@@ -167,6 +180,7 @@ struct EpiTransposed {
   static constexpr bool kInput = false;
   static constexpr bool kTailSplit = false;
   static constexpr bool kDirectF32 = false;
+  static constexpr bool kColParam = false;
   __device__ __forceinline__ float apply(int64_t m, int64_t n, float acc) const { return inner.apply(n, m, acc); }
   __device__ __forceinline__ void colsum(int, int64_t, float) const {}
 };

@@ -804,6 +804,18 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       }
     };
     load_input(cur, 0);
+    // The per-column parameters of the wave's columns (the bias), the same
+    // for every fragment row: requested here too, branch-free (past the
+    // last column: kOobOffset, a zero).
+    float colp[M16 && Epi::kColParam ? FN : 1];
+    if constexpr (M16 && Epi::kColParam) {
+      const __amdgpu_buffer_rsrc_t crs = uniform_rsrc(epi.colvec(), sh.N * 2);
+      static_for<0, FN>([&](auto j) {
+        const int64_t n = cur.n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
+        const uint16_t u = __builtin_amdgcn_raw_buffer_load_b16(crs, n < sh.N ? (uint32_t)(n * 2) : kOobOffset, 0, 0);
+        colp[j] = S::to_f((typename S::T)u);
+      });
+    }
 
     // Stages: the next item's k-tile 0 goes to the stage after the last
     // tile this item issued (free: its last reader passed a barrier above,
@@ -813,9 +825,9 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const int s_epi = (cur.nk + s0 + ST - 1) % ST;
     const int v_next = v + (int)gridDim.x;
     const bool has_next = v_next < nwork;
-    if constexpr (M16 && Epi::kInput) {
+    if constexpr (M16 && (Epi::kInput || Epi::kColParam)) {
       // Without a branch (so that the compiler counts these loads when it
-      // waits for the input block requested above): past the last item,
+      // waits for the data requested above): past the last item,
       // empty buffer resources make them fill stage s_next with zeros that
       // nothing reads, and the loads drain before the workgroup ends.
       const Item nxt = decode(opaque_s(has_next ? v_next : v));
@@ -927,7 +939,6 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
         static_for<0, FN>([&](auto j) {
           const int64_t n = nw + j * 16 + jj;
           const bool n_ok = n < sh.N;
-          const float colp = n_ok ? epi.colparam(n) : 0.0f;
           float in[4] = {0.f, 0.f, 0.f, 0.f};
           if constexpr (Epi::kInput) {
             // rows 4 G + r of column j * 16 + jj: four 16-bit reads (a
@@ -939,7 +950,8 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           }
           static_for<0, 4>([&](auto r) {
             float o[2];
-            const float c = epi.eval(acc[i][j][(int)r], colp, in[(int)r], o);
+            const float c = epi.eval(acc[i][j][(int)r], Epi::kColParam ? colp[Epi::kColParam ? (int)j : 0] : 0.0f,
+                                     in[(int)r], o);
             if constexpr (Epi::kColSum) {
               if (n_ok && mb + 4 * G + r < sh.M) cs[j] += c;
             }
@@ -1090,7 +1102,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       }
     }
     if (!has_next) {
-      if constexpr (M16 && Epi::kInput) wait_vmcnt<0>();  // the loads into stage s_next above
+      if constexpr (M16 && (Epi::kInput || Epi::kColParam)) wait_vmcnt<0>();  // the loads into stage s_next above
       break;
     }
     // Every wave is done with stage s_epi before the next item loads it.
