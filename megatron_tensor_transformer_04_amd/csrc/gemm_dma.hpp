@@ -581,11 +581,14 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       };
       const uint32_t pb = (uint32_t)opaque_v((int)(!P_KC || pk0 < krem ? pv[0] : kOobOffset));
       const uint32_t qb = (uint32_t)opaque_v((int)(!Q_KC || qk0 < krem ? qv[0] : kOobOffset));
+      // PART >= 3: load PART - 3 alone (P's loads, then Q's)
       static_for<0, LP>([&](auto c) {
-        if constexpr (PART == 2 || (PART == 0) == (c < FIRST)) one(prs, pb, pk0, psoff, P_KC, P.ld, BM, 0, c);
+        if constexpr (PART == 2 || (PART < 2 && (PART == 0) == (c < FIRST)) || PART == 3 + c)
+          one(prs, pb, pk0, psoff, P_KC, P.ld, BM, 0, c);
       });
       static_for<0, LQ>([&](auto c) {
-        if constexpr (PART == 2 || (PART == 0) == (LP + c < FIRST)) one(qrs, qb, qk0, qsoff, Q_KC, Q.ld, BN, Cfg::LDS_P, c);
+        if constexpr (PART == 2 || (PART < 2 && (PART == 0) == (LP + c < FIRST)) || PART == 3 + LP + c)
+          one(qrs, qb, qk0, qsoff, Q_KC, Q.ld, BN, Cfg::LDS_P, c);
       });
       return;
     }
@@ -695,14 +698,17 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           wait_vmcnt<(ST - 2) * LOADS>();
           barrier_lds();
           sched_fence();
-          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, kAll);
           pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
           qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
+          // the loads that refill stage st_t, one after each column's MFMAs
+          // (written in that order: left to the scheduler they bunched up
+          // behind the first two columns)
           static_for<0, FN>([&](auto j) {
             static_for<0, FM>([&](auto i) {
               acc[i][j] = S::mfma16x16x32(fa0[i], fb0[j], acc[i][j]);
               if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 0>(smem);
             });
+            if constexpr (j < LOADS) issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, std::integral_constant<int, 3 + j>{});
             fb0[j] = qa.template read<j, 0>(smem);
           });
           sched_rolling<FN, FM, LOADS>();
