@@ -11,8 +11,8 @@
 // p[m*ld + k], Q[k][n] at q[n*ld + k]) or mn-contiguous ("MC": P[m][k] at
 // p[k*ld + m], Q[k][n] at q[k*ld + n]).
 //
-// LDS is a ring of STAGES k-tiles (BK deep), each stage P's tile then Q's:
-//   [P stage 0][Q stage 0] .. [P stage S-1][Q stage S-1]
+// LDS holds two stages of one k-tile (BK deep) each, P's tile then Q's,
+// each stage its own array: [P stage 0][Q stage 0], [P stage 1][Q stage 1].
 //   KC tile: [rows][BK], rows of BK/8 16-byte chunks; chunk c of row r sits
 //            at c ^ sk(r): sk(r) = (r & 7) ^ ((r >> 3) & 1) for BK = 64,
 //            ((r >> 1) ^ (r >> 3)) & 3 for BK = 32; in the 16x16 form
@@ -54,19 +54,20 @@
 // one set of fragment registers serves both substeps: each is refilled as
 // soon as its last MFMA of the substep has issued (see the k-loop).
 //
-// Pipeline. Within one output tile, k-tile t lives in stage (t + s0) % S
-// and is consumed in BK/16 substeps (fragments double-buffered in
-// registers). Tiles 0..S-1 are issued first; iteration t (BK = 64, four
+// Pipeline. Within one output tile, k-tile t lives in stage t % 2 (tiles
+// run in pairs, so that each access names its stage's array at compile
+// time) and is consumed in BK/16 substeps (fragments double-buffered in
+// registers). Tiles 0 and 1 are issued first; iteration t (BK = 64, four
 // substeps) then does
 //   read frags (t, 1)        | MFMAs (t, 0)
 //   read frags (t, 2)        | MFMAs (t, 1)
 //   read frags (t, 3)
 //   -- wait until tile t+1 has landed (later tiles may still be in flight),
-//      barrier: every wave is done with stage t % S --
-//   first half of the loads of tile t+S into stage t % S | MFMAs (t, 2)
+//      barrier: every wave is done with stage t % 2 --
+//   first half of the loads of tile t+2 into stage t % 2 | MFMAs (t, 2)
 //   rest of those loads, read frags (t+1, 0)              | MFMAs (t, 3)
-// so LDS reads overlap MFMAs and a tile's global loads have about S-1
-// iterations of MFMA work to land. Placing the barrier one substep before
+// so LDS reads overlap MFMAs and a tile's global loads have about one
+// iteration of MFMA work to land. Placing the barrier one substep before
 // the end of the tile spreads each wave's loads over 20 MFMAs instead of
 // 10: issued in one burst after the barrier, the loads of all eight waves
 // filled the texture unit's queues and stalled the MFMAs interleaved with
@@ -306,8 +307,8 @@ __host__ __device__ constexpr int dma_kstep(int c) {
   return KC ? 0 : c * WAVES * (1024 / (2 * R));
 }
 
-// Per-lane LDS byte offsets of a wave's MFMA fragments (relative to the LDS
-// base; they start in stage 0 and step through the ring). NF fragments of
+// Per-lane LDS byte offsets of a wave's MFMA fragments (relative to a
+// stage's array; every stage uses the same offsets). NF fragments of
 // 32 rows (KC) or 32 columns (MC), the first at tile row / column `first`
 // (a multiple of 32).
 template <bool KC, int R, int BK, int NF>
@@ -334,13 +335,13 @@ struct FragAddr {
     }
   }
 
-  // Move every base by `delta` bytes (to the next stage of the ring).
+
+  // Fragment I for k-substep KS (16 wide) of the stage the bases point at.
+  // Move every base by `delta` bytes (to the other stage of one array).
   __device__ __forceinline__ void advance(uint32_t delta) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) base[i] += delta;
   }
-
-  // Fragment I for k-substep KS (16 wide) of the stage the bases point at.
   template <int I, int KS>
   __device__ __forceinline__ u32x4 read(const char* lds) const {
     if constexpr (KC) {
@@ -375,6 +376,7 @@ struct FragAddr16 {
     for (int ks = 0; ks < NB; ++ks)
       base[ks] = (uint32_t)(region + (first + r) * (2 * BK) + (((4 * ks + (lane >> 4)) ^ dsk<BK, true>(r)) << 4));
   }
+  // Move every base by `delta` bytes (to the other stage of one array).
   __device__ __forceinline__ void advance(uint32_t delta) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) base[i] += delta;
@@ -404,6 +406,7 @@ struct FragAddrMC16 {
     for (int i = 0; i < NB; ++i)
       base[i] = (uint32_t)(region + kr * (R * 2) + (((u0 + i) ^ dsm<true>(kr)) << 5) + ((j & 3) << 3));
   }
+  // Move every base by `delta` bytes (to the other stage of one array).
   __device__ __forceinline__ void advance(uint32_t delta) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) base[i] += delta;
@@ -447,7 +450,25 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   static_assert(!Cfg::ROLLED || (P_KC && Q_KC), "rolled 16x16 form: k-contiguous operands");
   static_assert((P_KC || (BM & (BM - 1)) == 0) && (Q_KC || (BN & (BN - 1)) == 0),
                 "an mn-contiguous operand needs a power-of-two tile extent (swizzle, loads per k-row)");
-  __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
+  // The two stages are two LDS arrays, and every access names its array at
+  // compile time (the k-loop runs tiles in pairs, tile t in stage t % 2):
+  // the compiler then knows that a transposing fragment read of one stage
+  // does not read what the direct loads in flight are writing into the
+  // other. Through one array indexed at run time it waited for every
+  // direct load in flight before each such read (the full load latency in
+  // every k-tile of an mn-contiguous operand; ordinary LDS reads are not
+  // affected).
+  // Kernels without an mn-contiguous operand (no transposing reads) keep one
+  // array, with the fragment offsets moved between the stages each tile:
+  // two arrays cost them a second set of fragment address registers
+  // (offsets past the 16-bit immediate), and their 16x16 forms spilled.
+  static_assert(ST == 2, "two stages");
+  constexpr bool TWO = !(P_KC && Q_KC) && !M16;
+  static_assert(!(M16 && !(P_KC && Q_KC)), "the 16x16 form reads k-contiguous operands");
+  __shared__ __attribute__((aligned(1024))) char ldsA[TWO ? STG : ST * STG];
+  __shared__ __attribute__((aligned(1024))) char ldsB[TWO ? STG : 16];
+  char* const lds0 = ldsA;
+  char* const lds1 = TWO ? ldsB : ldsA + STG;
 
   const int tid = threadIdx.x;
   int lane = tid & 63;  // made opaque at the top of every work item (see below)
@@ -552,19 +573,18 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   constexpr int FIRST = (LOADS + 1) / 2;  // loads in the first half (see the k-loop)
   // Direct loads of k-tile t of item `it` into stage `stage`: all of them
   // (PART 2), or the first FIRST (PART 0) or the rest (PART 1) in P-then-Q
-  // order. On a K-tail tile, chunks at or beyond the item's k-range take
+  // order, or load PART - 3 alone (PART >= 3). On a K-tail tile, chunks at or beyond the item's k-range take
   // kOobOffset (one 32-bit compare per load); a tile past the end
   // (t >= nk) is all kOobOffset and fills its stage with zeros that nothing
   // reads, which keeps the loop body free of branches.
   auto issue_tile = [&](const Item& it, __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs,
-                        const uint32_t(&pv)[NPV], const uint32_t(&qv)[NQV], int t, int stage, auto part_c)
+                        const uint32_t(&pv)[NPV], const uint32_t(&qv)[NQV], int t, char* const sp, auto part_c)
       __attribute__((always_inline)) {
     constexpr int PART = decltype(part_c)::value;
     const int krem = it.kspan - t * BK;  // k extent left from this tile on
     const int64_t k0 = krem > 0 ? it.kbeg + (int64_t)t * BK : 0;
     const int psoff = __builtin_amdgcn_readfirstlane((int)((P_KC ? k0 : k0 * P.ld) * 2));
     const int qsoff = __builtin_amdgcn_readfirstlane((int)((Q_KC ? k0 : k0 * Q.ld) * 2));
-    char* const sp = smem + stage * STG;
     if constexpr (M16) {
       // Load c's offset from load 0's (made opaque, so that the per-load
       // sums are formed here rather than kept in registers across the loop).
@@ -593,14 +613,14 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       return;
     }
     static_for<0, LP>([&](auto c) {
-      if constexpr (PART == 2 || (PART == 0) == (c < FIRST)) {
+      if constexpr (PART == 2 || (PART < 2 && (PART == 0) == (c < FIRST)) || PART == 3 + c) {
         const uint32_t off = pk0 + dma_kstep<P_KC, BM, Cfg::WAVES>(c) < krem ? pv[c] : kOobOffset;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + (c * Cfg::WAVES + wave) * 1024), 16, off,
                                                  psoff, 0, 0);
       }
     });
     static_for<0, LQ>([&](auto c) {
-      if constexpr (PART == 2 || (PART == 0) == (LP + c < FIRST)) {
+      if constexpr (PART == 2 || (PART < 2 && (PART == 0) == (LP + c < FIRST)) || PART == 3 + LP + c) {
         const uint32_t off = qk0 + dma_kstep<Q_KC, BN, Cfg::WAVES>(c) < krem ? qv[c] : kOobOffset;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             qrs, (lds_void*)(sp + Cfg::LDS_P + (c * Cfg::WAVES + wave) * 1024), 16, off, qsoff, 0, 0);
@@ -616,10 +636,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   using AccT = std::conditional_t<M16, f32x4, f32x16>;
   AccT acc[FM][FN];
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  auto read_frags = [&](u32x4(&fa)[FM], u32x4(&fb)[FN], auto ks_c) __attribute__((always_inline)) {
+  auto read_frags = [&](u32x4(&fa)[FM], u32x4(&fb)[FN], auto ks_c, const char* lds) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks_c)::value;
-    static_for<0, FM>([&](auto i) { fa[i] = pa.template read<i, KS>(smem); });
-    static_for<0, FN>([&](auto j) { fb[j] = qa.template read<j, KS>(smem); });
+    static_for<0, FM>([&](auto i) { fa[i] = pa.template read<i, KS>(lds); });
+    static_for<0, FN>([&](auto j) { fb[j] = qa.template read<j, KS>(lds); });
   };
   // Column-major over the wave's fragments: consecutive MFMAs share their B
   // fragment (measured on MI355X with the reads interleaved as below: about
@@ -632,6 +652,25 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       });
     });
   };
+  // One substep's MFMAs (column-major) with, after MFMA k, the direct load
+  // L0 + k (k < NL) and the read of fragment k of substep KS into the other
+  // set (k < FM + FN, A fragments first; none if KS < 0), in that program
+  // order. The scheduling constraints alone did not keep the loads apart:
+  // the compiler moved them all next to the barrier.
+  auto mfmas_then = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN], u32x4(&na)[FM], u32x4(&nb)[FN], auto ks_c,
+                        const char* lds, auto l0_c, auto nl_c, auto load) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks_c)::value, L0 = decltype(l0_c)::value, NL = decltype(nl_c)::value;
+    static_for<0, FN>([&](auto j) {
+      static_for<0, FM>([&](auto i) {
+        if constexpr (M16) acc[i][j] = S::mfma16x16x32(fa[i], fb[j], acc[i][j]);
+        else acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        constexpr int k = j * FM + i;
+        if constexpr (k < NL) load(std::integral_constant<int, 3 + L0 + k>{});
+        if constexpr (KS >= 0 && k < FM) na[k] = pa.template read<k, KS>(lds);
+        else if constexpr (KS >= 0 && k >= FM && k < FM + FN) nb[k - FM] = qa.template read<k - FM, KS>(lds);
+      });
+    });
+  };
   constexpr int NKS = BK / (M16 ? 32 : 16);  // substeps per k-tile
   // DS read instructions per substep (a transposing read moves half a
   // fragment).
@@ -640,13 +679,13 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // Work item state is decoded again where it is needed rather than kept
   // live across the K loop (scalar registers are the scarce resource);
   // opaque_s() hides the work index from common-subexpression elimination.
+  // Every item starts in stage 0: its tile count is rounded up to even.
   int v = blockIdx.x;
-  int s0 = 0;  // stage of the current item's k-tile 0
   {
     const Item first = decode(v);
     uint32_t pv[NPV], qv[NQV];
     offsets(first, pv, qv);
-    issue_tile(first, p_rsrc(first), q_rsrc(first), pv, qv, 0, 0, kAll);
+    issue_tile(first, p_rsrc(first), q_rsrc(first), pv, qv, 0, lds0, kAll);
   }
   while (true) {
     // Everything derived from the lane index is recomputed per item: hoisted
@@ -657,10 +696,10 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     const __amdgpu_buffer_rsrc_t prs = p_rsrc(cur), qrs = q_rsrc(cur);
     uint32_t pv[NPV], qv[NQV];
     offsets(cur, pv, qv);
-    static_for<1, ST>([&](auto t) { issue_tile(cur, prs, qrs, pv, qv, t, (t + s0) % ST, kAll); });
+    issue_tile(cur, prs, qrs, pv, qv, 1, lds1, kAll);
     static_for<0, FM>([&](auto i) { static_for<0, FN>([&](auto j) { acc[i][j] = AccT{}; }); });
-    pa.init(lane, s0 * STG, wm * Cfg::WTM);
-    qa.init(lane, s0 * STG + Cfg::LDS_P, wn * Cfg::WTN);
+    pa.init(lane, 0, wm * Cfg::WTM);  // offsets within a stage
+    qa.init(lane, Cfg::LDS_P, wn * Cfg::WTN);
 
     // One straight-line loop body: no branch at all, so the accumulators
     // keep their registers. The last iterations load and read stages
@@ -676,10 +715,20 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     if (cur.nk > 0) {
       wait_vmcnt<(ST - 1) * LOADS>();  // k-tile 0 has landed
       barrier_lds();
-      read_frags(fa0, fb0, std::integral_constant<int, 0>{});
-      for (int t = 0; t < cur.nk; ++t) {
-        const int st_t = (t + s0) % ST;
-        const bool wrap = st_t == ST - 1;  // tile t+1 sits in stage 0
+      read_frags(fa0, fb0, std::integral_constant<int, 0>{}, TWO ? lds0 : ldsA);
+      // k-tile t, in stage cs; tile t+1 is in stage ns, and tile t+2 goes
+      // into cs once every wave has read tile t
+      auto tile = [&](int t, char* const cs_, char* const ns_, uint32_t delta) __attribute__((always_inline)) {
+        // fragment reads: the stage's array (two arrays), or the one array
+        // with the offsets moved to tile t+1's stage after the barrier
+        const char* const cs = TWO ? cs_ : ldsA;
+        const char* const ns = TWO ? ns_ : ldsA;
+        auto to_next = [&]() __attribute__((always_inline)) {
+          if constexpr (!TWO) {
+            pa.advance(delta);
+            qa.advance(delta);
+          }
+        };
         if constexpr (Cfg::ROLLED) {
           // Two 32-wide substeps on one set of fragment registers: each B
           // fragment is refilled with the next substep's once its column of
@@ -690,67 +739,69 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           static_for<0, FN>([&](auto j) {
             static_for<0, FM>([&](auto i) {
               acc[i][j] = S::mfma16x16x32(fa0[i], fb0[j], acc[i][j]);
-              if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 1>(smem);
+              if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 1>(cs);
             });
-            fb0[j] = qa.template read<j, 1>(smem);
+            fb0[j] = qa.template read<j, 1>(cs);
           });
           sched_rolling<FN, FM, 0>();
           wait_vmcnt<(ST - 2) * LOADS>();
           barrier_lds();
           sched_fence();
-          pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-          qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-          // the loads that refill stage st_t, one after each column's MFMAs
+          to_next();
+          // the loads that refill stage cs, one after each column's MFMAs
           // (written in that order: left to the scheduler they bunched up
           // behind the first two columns)
           static_for<0, FN>([&](auto j) {
             static_for<0, FM>([&](auto i) {
               acc[i][j] = S::mfma16x16x32(fa0[i], fb0[j], acc[i][j]);
-              if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 0>(smem);
+              if constexpr (j == FN - 1) fa0[i] = pa.template read<i, 0>(ns);
             });
-            if constexpr (j < LOADS) issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, std::integral_constant<int, 3 + j>{});
-            fb0[j] = qa.template read<j, 0>(smem);
+            if constexpr (j < LOADS) issue_tile(cur, prs, qrs, pv, qv, t + ST, cs_, std::integral_constant<int, 3 + j>{});
+            fb0[j] = qa.template read<j, 0>(ns);
           });
           sched_rolling<FN, FM, LOADS>();
         } else if constexpr (NKS >= 4) {
           // Substeps 0 .. NKS-3, then the reads of the last substep; with
-          // those, this wave is done with stage st_t and the barrier comes
+          // those, this wave is done with stage cs and the barrier comes
           // one substep before the end of the tile: the loads that refill
           // the stage are spread over the last two substeps' MFMAs (half
           // each) instead of all landing on the texture unit at once.
           static_for<0, NKS - 2>([&](auto ks) {
             if constexpr (ks % 2 == 0) {
-              read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+              read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{}, cs);
               mfmas(fa0, fb0);
             } else {
-              read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+              read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{}, cs);
               mfmas(fa1, fb1);
             }
             sched_interleave<FM * FN, 0, DSR>();
           });
-          read_frags(fa1, fb1, std::integral_constant<int, NKS - 1>{});  // NKS even: substep NKS-1 in set 1
+          read_frags(fa1, fb1, std::integral_constant<int, NKS - 1>{}, cs);  // NKS even: substep NKS-1 in set 1
           // Tile t+1 must have landed; tiles t+2 .. t+S-1 stay in flight.
           // The barrier also orders every wave's reads of tile t's stage
           // before the loads that refill it.
           wait_vmcnt<(ST - 2) * LOADS>();
           barrier_lds();
           sched_fence();
-          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, std::integral_constant<int, 0>{});
-          mfmas(fa0, fb0);  // substep NKS-2
+          to_next();
+          auto load = [&](auto part) __attribute__((always_inline)) {
+            issue_tile(cur, prs, qrs, pv, qv, t + ST, cs_, part);
+          };
+          // substep NKS-2 with the first FIRST loads
+          mfmas_then(fa0, fb0, fa0, fb0, std::integral_constant<int, -1>{}, ns, std::integral_constant<int, 0>{},
+                     std::integral_constant<int, FIRST>{}, load);
           sched_interleave<FM * FN, FIRST, 0>();
-          pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-          qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, std::integral_constant<int, 1>{});
-          read_frags(fa0, fb0, std::integral_constant<int, 0>{});
-          mfmas(fa1, fb1);  // substep NKS-1
+          // substep NKS-1 with the rest of the loads and tile t+1's first reads
+          mfmas_then(fa1, fb1, fa0, fb0, std::integral_constant<int, 0>{}, ns, std::integral_constant<int, FIRST>{},
+                     std::integral_constant<int, LOADS - FIRST>{}, load);
           sched_interleave<FM * FN, LOADS - FIRST, DSR>();
         } else {
           static_for<0, NKS - 1>([&](auto ks) {
             if constexpr (ks % 2 == 0) {
-              read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{});
+              read_frags(fa1, fb1, std::integral_constant<int, ks + 1>{}, cs);
               mfmas(fa0, fb0);
             } else {
-              read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{});
+              read_frags(fa0, fb0, std::integral_constant<int, ks + 1>{}, cs);
               mfmas(fa1, fb1);
             }
             sched_interleave<FM * FN, 0, DSR>();
@@ -758,12 +809,29 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
           wait_vmcnt<(ST - 2) * LOADS>();
           barrier_lds();
           sched_fence();
-          issue_tile(cur, prs, qrs, pv, qv, t + ST, st_t, kAll);
-          pa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-          qa.advance(wrap ? (uint32_t)(-(ST - 1) * STG) : (uint32_t)STG);
-          read_frags(fa0, fb0, std::integral_constant<int, 0>{});
-          mfmas(fa1, fb1);  // NKS is even: the last substep's fragments are in set 1
+          to_next();
+          // NKS is even: the last substep's fragments are in set 1; the
+          // loads and tile t+1's first reads go after its MFMAs
+          mfmas_then(fa1, fb1, fa0, fb0, std::integral_constant<int, 0>{}, ns, std::integral_constant<int, 0>{},
+                     std::integral_constant<int, LOADS>{}, [&](auto part) __attribute__((always_inline)) {
+                       issue_tile(cur, prs, qrs, pv, qv, t + ST, cs_, part);
+                     });
           sched_interleave<FM * FN, LOADS, DSR>();
+        }
+      };
+      // An even number of tiles (an odd count runs one more tile past the
+      // end: its stage holds zeros, which add nothing); with two arrays in
+      // pairs, so that each names its stage at compile time.
+      if constexpr (TWO) {
+        for (int t = 0; t < cur.nk; t += 2) {
+          tile(t, lds0, lds1, (uint32_t)STG);
+          tile(t + 1, lds1, lds0, (uint32_t)-STG);
+        }
+      } else {
+        const int nk_run = (cur.nk + 1) & ~1;
+        for (int t = 0; t < nk_run; ++t) {
+          const bool odd = t & 1;
+          tile(t, odd ? lds1 : lds0, odd ? lds0 : lds1, odd ? (uint32_t)-STG : (uint32_t)STG);
         }
       }
     }
@@ -823,31 +891,30 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       });
     }
 
-    // Stages: the next item's k-tile 0 goes to the stage after the last
-    // tile this item issued (free: its last reader passed a barrier above,
-    // and this wave's own loads into it have drained); the epilogue stages
-    // its output through the stage the next item's k-tile ST-1 will use.
-    const int s_next = (cur.nk + s0) % ST;
-    const int s_epi = (cur.nk + s0 + ST - 1) % ST;
+    // Stages: the loop ran an even number of tiles, so the next item's
+    // k-tile 0 goes to stage 0 (free: its last reader, of a tile past the
+    // end whose data nothing uses, may still be reading; this wave's own
+    // loads into it have drained) and the epilogue stages its output
+    // through stage 1, which the next item's k-tile 1 will use.
     const int v_next = v + (int)gridDim.x;
     const bool has_next = v_next < nwork;
     if constexpr (M16 && (Epi::kInput || Epi::kColParam)) {
       // Without a branch (so that the compiler counts these loads when it
       // waits for the data requested above): past the last item,
-      // empty buffer resources make them fill stage s_next with zeros that
+      // empty buffer resources make them fill stage 0 with zeros that
       // nothing reads, and the loads drain before the workgroup ends.
       const Item nxt = decode(opaque_s(has_next ? v_next : v));
       uint32_t pv2[NPV], qv2[NQV];
       offsets(nxt, pv2, qv2);
       const __amdgpu_buffer_rsrc_t none = uniform_rsrc(nullptr, 0);
       const __amdgpu_buffer_rsrc_t prs2 = has_next ? p_rsrc(nxt) : none, qrs2 = has_next ? q_rsrc(nxt) : none;
-      static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST, kAll); });
+      issue_tile(nxt, prs2, qrs2, pv2, qv2, 0, lds0, kAll);
     } else if (has_next) {
       const Item nxt = decode(opaque_s(v_next));
       uint32_t pv2[NPV], qv2[NQV];
       offsets(nxt, pv2, qv2);
       const __amdgpu_buffer_rsrc_t prs2 = p_rsrc(nxt), qrs2 = q_rsrc(nxt);
-      static_for<0, ST - 1>([&](auto t) { issue_tile(nxt, prs2, qrs2, pv2, qv2, t, (t + s_next) % ST, kAll); });
+      issue_tile(nxt, prs2, qrs2, pv2, qv2, 0, lds0, kAll);
     }
 
     const Item done = decode(opaque_s(v));
@@ -900,7 +967,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       });
     } else if constexpr (M16) {
       // The 16x16 form's epilogue: per fragment row of the wave's tile (16
-      // rows) through a private block of stage s_epi, as below: the input
+      // rows) through a private block of stage 1, as below: the input
       // (if any, requested one block ahead) lands there as 16-byte row
       // chunks and comes back per lane with one transposing read per
       // fragment (lane l holds
@@ -910,7 +977,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       // the block once the first is stored, its fp32 values held in the
       // accumulators meanwhile.
       barrier_lds();
-      char* const epi_lds = smem + s_epi * STG;
+      char* const epi_lds = lds1;
       constexpr int CPR = Cfg::WTN / 8;      // 16-byte chunks per staged row
       constexpr int RS = Cfg::WTN * 2 + 16;  // staged row stride (bytes)
       constexpr int HB = 16, BLK = HB * RS;
@@ -999,7 +1066,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       }
     } else {
       // Epilogue, one block of 32, 16 or 8 rows of the wave's tile at a
-      // time, staged through a private region of stage s_epi so that global
+      // time, staged through a private region of stage 1 so that global
       // memory sees whole 16-byte row chunks. The outputs are written with
       // non-temporal stores: no later access of this launch reads them, and
       // when every workgroup finishes a tile at once a burst of ordinary
@@ -1020,7 +1087,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       // fragment, r = 0..15. The barrier first makes sure no wave still
       // reads fragments of that stage.
       barrier_lds();
-      char* const epi_lds = smem + s_epi * STG;
+      char* const epi_lds = lds1;
       constexpr int CPR = Cfg::WTN / 8;      // 16-byte chunks per staged row
       constexpr int RS = Cfg::WTN * 2 + 16;  // staged row stride (bytes)
       // Rows per staged block: as many (32, 16 or 8) as fit in one stage.
@@ -1108,13 +1175,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       }
     }
     if (!has_next) {
-      if constexpr (M16 && (Epi::kInput || Epi::kColParam)) wait_vmcnt<0>();  // the loads into stage s_next above
+      if constexpr (M16 && (Epi::kInput || Epi::kColParam)) wait_vmcnt<0>();  // the loads into stage 0 above
       break;
     }
     // Every wave is done with stage s_epi before the next item loads it.
     barrier_lds();
     v = v_next;
-    s0 = s_next;
   }
 }
 

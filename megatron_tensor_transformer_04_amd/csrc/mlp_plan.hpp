@@ -75,9 +75,8 @@ template <class Epi>
 inline constexpr bool kMf16Epi = !Epi::kDirectF32;
 constexpr int64_t kMf16MaxLd = (int64_t(1) << 31) / (2 * CfgD320x16::BM);
 inline std::atomic<bool> g_plan_mf16{true};
-inline bool use_mf16(int64_t ldp, int64_t ldq, bool kc, int64_t ntile) {
-  return g_plan_mf16.load(std::memory_order_relaxed) && ldp < kMf16MaxLd && ldq < kMf16MaxLd &&
-         (kc || ntile >= kCUs);
+inline bool use_mf16(int64_t ldp, int64_t ldq, bool kc, int64_t) {
+  return g_plan_mf16.load(std::memory_order_relaxed) && ldp < kMf16MaxLd && ldq < kMf16MaxLd && kc;
 }
 
 // Tile work of a launch counted in whole waves over the CUs (a last partial
@@ -269,8 +268,8 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
           TailSplit tail = plan_tail(pl, K, Epi::kTailSplit && tail_ws != nullptr);
           if (tail_bytes(tail, pl) > tail_cap) tail = TailSplit{pl.tiles_m * pl.tiles_n, 1, K, nullptr};
           tail.partial = tail_ws;
-          if constexpr (kMf16Epi<Epi>)
-            if (use_mf16(ldp, ldq, PK && QK, (int64_t)pl.tiles_m * pl.tiles_n))
+          if constexpr (kMf16Epi<Epi> && PK && QK)
+            if (use_mf16(ldp, ldq, true, (int64_t)pl.tiles_m * pl.tiles_n))
               return launch_dma<CfgD256x16, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
           return launch_dma<CfgD256, S, PK, QK>(sh, p, ldp, q, ldq, epi, tail, st);
         }
@@ -316,8 +315,8 @@ hipError_t run_gemm_sliced(int dtype, int64_t M, int64_t N, int64_t K, const Row
   } else {
     switch (pl.eng) {
       case Engine::Dma256:
-        if constexpr (kMf16Epi<Epi>)
-          if (use_mf16(ldp, ldq, QK, (int64_t)pl.tiles_m * pl.tiles_n))
+        if constexpr (kMf16Epi<Epi> && QK)
+          if (use_mf16(ldp, ldq, true, (int64_t)pl.tiles_m * pl.tiles_n))
             return launch_dma<CfgD256x16, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
         return launch_dma<CfgD256, S, true, QK, Epi, true>(sh, nullptr, ldp, q, ldq, epi, none, st, xs);
       case Engine::Dma320:  // planned for k-contiguous Q only
