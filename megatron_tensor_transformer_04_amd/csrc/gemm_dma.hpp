@@ -156,14 +156,16 @@ __device__ __forceinline__ void barrier_lds() {
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // The region just ended issues MF MFMAs, VM vector-memory reads and DS DS
-// reads: order them as MFMA, VMEM, DS, DS.., MFMA, VMEM, DS.. (one VMEM and
-// up to ceil(DS / MF) DS reads after each MFMA) and close the region.
+// reads: order them as MFMA, VMEM, DS, DS.., MFMA, DS.. (one VMEM after every
+// MF / VM-th MFMA, up to ceil(DS / MF) DS reads after each) and close the
+// region.
 template <int MF, int VM, int DS>
 __device__ __forceinline__ void sched_interleave() {
   constexpr int DPER = (DS + MF - 1) / MF;
+  constexpr int VS = VM > 0 && MF / VM > 1 ? MF / VM : 1;  // MFMAs per VMEM read
   static_for<0, MF>([&](auto i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (i < VM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if constexpr (i % VS == 0 && i / VS < VM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     constexpr int d = DS - i * DPER < DPER ? DS - i * DPER : DPER;
     if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
   });
@@ -466,9 +468,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   constexpr bool TWO = !(P_KC && Q_KC) && !M16;
   static_assert(!(M16 && !(P_KC && Q_KC)), "the 16x16 form reads k-contiguous operands");
   __shared__ __attribute__((aligned(1024))) char ldsA[TWO ? STG : ST * STG];
-  __shared__ __attribute__((aligned(1024))) char ldsB[TWO ? STG : 16];
+  char* lds1 = ldsA + STG;
+  if constexpr (TWO) {
+    __shared__ __attribute__((aligned(1024))) char ldsB[STG];
+    lds1 = ldsB;
+  }
   char* const lds0 = ldsA;
-  char* const lds1 = TWO ? ldsB : ldsA + STG;
 
   const int tid = threadIdx.x;
   int lane = tid & 63;  // made opaque at the top of every work item (see below)
@@ -652,11 +657,12 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       });
     });
   };
-  // One substep's MFMAs (column-major) with, after MFMA k, the direct load
-  // L0 + k (k < NL) and the read of fragment k of substep KS into the other
-  // set (k < FM + FN, A fragments first; none if KS < 0), in that program
-  // order. The scheduling constraints alone did not keep the loads apart:
-  // the compiler moved them all next to the barrier.
+  // One substep's MFMAs (column-major) with, after MFMA k, a direct load
+  // (loads L0 .. L0 + NL - 1, one after every (FM FN) / NL-th MFMA) and the
+  // read of fragment k of substep KS into the other set (k < FM + FN, A
+  // fragments first; none if KS < 0), in that program order. The
+  // scheduling constraints alone did not keep the loads apart: the
+  // compiler moved them all next to the barrier.
   auto mfmas_then = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN], u32x4(&na)[FM], u32x4(&nb)[FN], auto ks_c,
                         const char* lds, auto l0_c, auto nl_c, auto load) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks_c)::value, L0 = decltype(l0_c)::value, NL = decltype(nl_c)::value;
@@ -665,7 +671,8 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
         if constexpr (M16) acc[i][j] = S::mfma16x16x32(fa[i], fb[j], acc[i][j]);
         else acc[i][j] = S::mfma32x32x16(fa[i], fb[j], acc[i][j]);
         constexpr int k = j * FM + i;
-        if constexpr (k < NL) load(std::integral_constant<int, 3 + L0 + k>{});
+        constexpr int LS = NL > 0 && FM * FN / NL > 1 ? FM * FN / NL : 1;
+        if constexpr (k % LS == 0 && k / LS < NL) load(std::integral_constant<int, 3 + L0 + k / LS>{});
         if constexpr (KS >= 0 && k < FM) na[k] = pa.template read<k, KS>(lds);
         else if constexpr (KS >= 0 && k >= FM && k < FM + FN) nb[k - FM] = qa.template read<k - FM, KS>(lds);
       });
