@@ -436,11 +436,14 @@ hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStr
 // tile reads k-contiguous operands only. Where it would take 256 x 256 tiles
 // anyway, the direct-load engine reads an mn-contiguous operand in place
 // with transposing LDS reads, and on MI355X that cost less than the copies
-// (the 7B shard's step, whose 4096-wide GEMMs all take 256 x 256 tiles:
-// 1.68 ms in place against 1.77 ms staged; the 2.4B and h=10240 shards,
-// whose GEMMs take the 320-wide tiles, ran 18-22 % and 13 % slower in
-// place). A k-split sub-wave launch is not staged either: its copies scale
-// with the long reduction while its tiles do not (the 2.4B shard's weight
+// (the 7B shard's 4096 x 4096 x 8192 weight gradient: 204 us in place
+// against 233 us for the two copies and the GEMM; 8192 x 4096 x 4096 with
+// one mn-contiguous operand: 208 against 204 us). Where the copies buy the
+// 320-wide tiles they win or tie: at h=10240, 16384 x 10240 x 10240 with
+// one such operand 2.57 ms in place against 2.39 ms for its copy and the
+// GEMM, a 10240 x 10240 x 16384 weight gradient 2.61 against 2.63 ms. A
+// k-split sub-wave launch is not staged either: its copies scale with the
+// long reduction while its tiles do not (the 2.4B shard's weight
 // gradients, 2560 x 2560 x 8192: 123 us in place against 133 us for the two
 // copies and the 320-wide GEMM).
 inline bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
