@@ -155,10 +155,14 @@ def reduce_partials_rate(tpmlp, Yp, cfg, dev, reps=10):
 OTHER_CONFIGS = ("gpt2_small", "gpt_2p4b", "gpt_7b")
 
 
-def config_rate(tpmlp, name, dev, steps=10, warmup=3):
+def config_rate(tpmlp, name, dev, steps=20, warmup_s=0.1):
     """Whole-step rate of another MLP workload (default launch configuration:
     staged workspaces, H and dZ kept), timed with HIP events on the launch
-    stream; reported beside the main workload, whose line this is."""
+    stream; reported beside the main workload, whose line this is. Run
+    before the main workload, after untimed steps for about warmup_s of GPU
+    time (the main workload runs that long, warm-up and breakdown pass,
+    before its timed steps), so that neither starts at the clock the other
+    leaves the chip at."""
     import torch
     import synth
     from synth.device import device_inputs
@@ -178,8 +182,13 @@ def config_rate(tpmlp, name, dev, steps=10, warmup=3):
         tpmlp.tp_mlp_fwd(X, A, b1, B, Z, H, Yp, fws)
         tpmlp.tp_mlp_bwd(dY, X, A, B, Z, H, dZ, dXp, dA, dB, db1, ws)
 
-    for _ in range(warmup):
-        step()
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warmup_s:
+            break
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -227,7 +236,7 @@ def attention_cpu_baseline(inp, cfg, flops_per_call, target_s=8.0, max_calls=4):
                       f"{dt:.1f} s"}
 
 
-def attention_rate(tpmlp, dev, reps=10, cpu=True):
+def attention_rate(tpmlp, dev, reps=10):
     """Forward + backward of one TP rank's attention share of the 2.4B model
     (8 of 32 heads of width 80, 4 sequences of 2048 tokens, bf16, causal),
     timed with HIP events on the launch stream, through the fused path
@@ -309,9 +318,20 @@ def attention_rate(tpmlp, dev, reps=10, cpu=True):
                             "tflops": round(m_tflops, 2),
                             "frac": round(m_tflops / peak, 4)},
            "cpu_baseline": None}
-    if cpu:  # forward, then a backward that recomputes the forward: 4 x the forward's work
-        out["cpu_baseline"] = attention_cpu_baseline(inp, cfg, 4 * flops_f)
     return out
+
+
+def attention_cpu(out):
+    """The attention line's cpu_baseline: the float64 oracle on the same
+    shard (forward, then a backward that recomputes the forward: 4 x the
+    forward's work)."""
+    import synth
+    cfg = synth.get_attn_config("attn_2p4b")
+    b, s, h, n, d = cfg.micro_batch, cfg.seq_len, cfg.hidden, cfg.heads_shard, cfg.head_dim
+    inp = synth.draw_attn_inputs(b, s, h, n, d, cfg.dtype, seed=cfg.seed, sigma_dy=cfg.sigma_dy)
+    T, q, Z = b * s, n * d, b * n
+    flops_f = 2.0 * T * h * 3 * q + 2.0 * T * q * h + 2 * 2.0 * Z * s * s * d * (0.5 if cfg.causal else 1.0)
+    out["cpu_baseline"] = attention_cpu_baseline(inp, cfg, 4 * flops_f)
 
 
 def main():
@@ -410,6 +430,16 @@ def main():
         log(f"copy probe: {n} bytes read and written by one copy kernel")
         del src, dst
 
+    # The other MLP workloads and the attention shard first: each measured
+    # from its own warm-up rather than right after the main workload's run
+    # (whose power draw sets the clock the chip settles at). Their CPU
+    # baselines come after the main timing.
+    other = None
+    if not args.no_configs and not (args.main_grad or args.recompute or bt):
+        other = {n: config_rate(tpmlp, n, dev) for n in OTHER_CONFIGS if n != cfg.name}
+    attn_line = None if args.no_attn else attention_rate(tpmlp, dev)
+    torch.cuda.synchronize()
+
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
@@ -479,10 +509,8 @@ def main():
     achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
 
     reduce_line = None if args.no_reduce else reduce_partials_rate(tpmlp, Yp, cfg, dev)
-    attn_line = None if args.no_attn else attention_rate(tpmlp, dev, cpu=not args.no_cpu_baseline)
-    other = None
-    if not args.no_configs and not (args.main_grad or args.recompute or bt):
-        other = {n: config_rate(tpmlp, n, dev) for n in OTHER_CONFIGS if n != cfg.name}
+    if attn_line is not None and not args.no_cpu_baseline:
+        attention_cpu(attn_line)
 
     result = {
         "metric": METRIC,
