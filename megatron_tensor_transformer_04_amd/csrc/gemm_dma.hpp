@@ -888,11 +888,11 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     // The per-column parameters of the wave's columns (the bias), the same
     // for every fragment row: requested here too, branch-free (past the
     // last column: kOobOffset, a zero).
-    float colp[M16 && Epi::kColParam ? FN : 1];
-    if constexpr (M16 && Epi::kColParam) {
+    float colp[Epi::kColParam ? FN : 1];
+    if constexpr (Epi::kColParam) {
       const __amdgpu_buffer_rsrc_t crs = uniform_rsrc(epi.colvec(), sh.N * 2);
       static_for<0, FN>([&](auto j) {
-        const int64_t n = cur.n0 + wn * Cfg::WTN + j * 16 + (lane & 15);
+        const int64_t n = cur.n0 + wn * Cfg::WTN + j * Cfg::FRAG + (lane & (Cfg::FRAG - 1));
         const uint16_t u = __builtin_amdgcn_raw_buffer_load_b16(crs, n < sh.N ? (uint32_t)(n * 2) : kOobOffset, 0, 0);
         colp[j] = S::to_f((typename S::T)u);
       });
@@ -905,7 +905,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     // through stage 1, which the next item's k-tile 1 will use.
     const int v_next = v + (int)gridDim.x;
     const bool has_next = v_next < nwork;
-    if constexpr (M16 && (Epi::kInput || Epi::kColParam)) {
+    if constexpr ((M16 && Epi::kInput) || Epi::kColParam) {
       // Without a branch (so that the compiler counts these loads when it
       // waits for the data requested above): past the last item,
       // empty buffer resources make them fill stage 0 with zeros that
@@ -1129,7 +1129,6 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
         static_for<0, FN>([&](auto j) {
           const int64_t n = nw + j * 32 + (lane & 31);
           const bool n_ok = n < sh.N;
-          const float colp = n_ok ? epi.colparam(n) : 0.0f;
           static_for<0, HB / 8>([&](auto g) {
             float in[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (Epi::kInput) {
@@ -1143,7 +1142,8 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
             static_for<0, 4>([&](auto rr) {
               const int row = 8 * g + 4 * (lane >> 5) + rr;  // within the block
               float o[2];
-              const float c = epi.eval(acc[i][j][4 * (g0 + g) + rr], colp, in[rr], o);
+              const float c = epi.eval(acc[i][j][4 * (g0 + g) + rr],
+                                       Epi::kColParam ? colp[Epi::kColParam ? (int)j : 0] : 0.0f, in[rr], o);
               if (n_ok && mb + row < sh.M) cs[j] += c;
               static_for<0, Epi::kOuts>([&](auto k) {
                 *reinterpret_cast<typename S::T*>(stg + k * BLK + row * RS + (j * 32 + (lane & 31)) * 2) =
@@ -1182,7 +1182,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       }
     }
     if (!has_next) {
-      if constexpr (M16 && (Epi::kInput || Epi::kColParam)) wait_vmcnt<0>();  // the loads into stage 0 above
+      if constexpr ((M16 && Epi::kInput) || Epi::kColParam) wait_vmcnt<0>();  // the loads into stage 0 above
       break;
     }
     // Every wave is done with stage s_epi before the next item loads it.
