@@ -431,25 +431,39 @@ hipError_t run_transpose(const void* in, void* out, int64_t R, int64_t C, hipStr
 }
 
 // Does staging k-contiguous copies of a GEMM's mn-contiguous operands pay
-// off? Only where the copies buy the 256 x 320 tiles for a launch of a wave
-// or more: with both operands k-contiguous the planner picks them, and that
-// tile reads k-contiguous operands only. Where it would take 256 x 256 tiles
-// anyway, the direct-load engine reads an mn-contiguous operand in place
-// with transposing LDS reads, and on MI355X that cost less than the copies
-// (the 7B shard's 4096 x 4096 x 8192 weight gradient: 204 us in place
-// against 233 us for the two copies and the GEMM; 8192 x 4096 x 4096 with
-// one mn-contiguous operand: 208 against 204 us). Where the copies buy the
-// 320-wide tiles they win or tie: at h=10240, 16384 x 10240 x 10240 with
-// one such operand 2.57 ms in place against 2.39 ms for its copy and the
-// GEMM, a 10240 x 10240 x 16384 weight gradient 2.61 against 2.63 ms. A
-// k-split sub-wave launch is not staged either: its copies scale with the
-// long reduction while its tiles do not (the 2.4B shard's weight
-// gradients, 2560 x 2560 x 8192: 123 us in place against 133 us for the two
-// copies and the 320-wide GEMM).
+// off? For the weight gradients (both operands [rows][T]) only where the
+// copies buy the 256 x 320 tiles for a launch of a wave or more: with both
+// operands k-contiguous the planner picks them, and that tile reads
+// k-contiguous operands only. Where they would take 256 x 256 tiles anyway,
+// the direct-load engine reads the operands in place with transposing LDS
+// reads, and on MI355X that cost less than the two copies (the 7B shard's
+// 4096 x 4096 x 8192 weight gradient: 204 us in place against 233 us for
+// the copies and the GEMM). Where the copies buy the 320-wide tiles they
+// win or tie: at h=10240, 16384 x 10240 x 10240 with one such operand
+// 2.57 ms in place against 2.39 ms for its copy and the GEMM, a 10240 x
+// 10240 x 16384 weight gradient 2.61 against 2.63 ms. A k-split sub-wave
+// launch is not staged either: its copies scale with the long reduction
+// while its tiles do not (the 2.4B shard's weight gradients, 2560 x 2560 x
+// 8192: 123 us in place against 133 us for the two copies and the
+// 320-wide GEMM). A forward weight is copied on more occasions
+// (stages_weight).
 inline bool stages(int dtype, int64_t M, int64_t N, int64_t K) {
   if (dtype == TPMLP_F32 || M <= 0 || N <= 0 || K <= 0) return false;
   if (subwave_split_candidate(M, N, K)) return false;
   return pick_engine(M, N, K, false, true) == Engine::Dma320;
+}
+
+// A GEMM whose one mn-contiguous operand is a weight ([h][f] or [f][h], far
+// smaller than the token-long operands): staged as stages() says, and also
+// where it takes 256 x 256 tiles on the direct-load engine, since there the
+// copy buys the 16x16 MFMA form, which reads k-contiguous operands only.
+// Measured on MI355X, the 7B shard's forward (8192 x 4096 x 4096, fp16):
+// the first GEMM 225 us plus a 10 us copy against 250 us in place, the
+// second 212 plus 11 against 234 us.
+inline bool stages_weight(int dtype, int64_t M, int64_t N, int64_t K) {
+  if (stages(dtype, M, N, K)) return true;
+  if (dtype == TPMLP_F32 || M <= 0 || N <= 0 || K <= 0 || subwave_split_candidate(M, N, K)) return false;
+  return pick_engine(M, N, K, false, true) == Engine::Dma256 && staged_ld(K) < kMf16MaxLd;
 }
 
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -465,9 +479,9 @@ inline FwdWs fwd_ws(const tpmlp_shape& s) {
   FwdWs w{};
   const size_t e = elt_size(s.dtype);
   const size_t at_b = (size_t)(s.ffn_shard * staged_ld(s.hidden)) * e, bt_b = (size_t)(s.hidden * staged_ld(s.ffn_shard)) * e;
-  w.at = stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
+  w.at = stages_weight(s.dtype, s.tokens, s.ffn_shard, s.hidden);
   // B_i^T given (b_t): already the k-contiguous operand of F2, nothing to stage
-  w.bt = !b_t(s) && stages(s.dtype, s.tokens, s.hidden, s.ffn_shard);
+  w.bt = !b_t(s) && stages_weight(s.dtype, s.tokens, s.hidden, s.ffn_shard);
   w.at_off = 0;
   w.bt_off = w.at ? align256(at_b) : 0;
   w.tail_off = w.bt_off + (w.bt ? align256(bt_b) : 0);
@@ -513,7 +527,7 @@ inline BwdWs bwd_ws(const tpmlp_shape& s, bool dz_in_ws) {
     w.dzt_off = at + th;
     at += th + tf;
   }
-  w.stage_b1 = b_t(s) && stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
+  w.stage_b1 = b_t(s) && stages_weight(s.dtype, s.tokens, s.ffn_shard, s.hidden);
   if (w.stage_b1) {
     w.bs_off = at;
     at += align256((size_t)(s.ffn_shard * staged_ld(s.hidden)) * e);
@@ -540,7 +554,7 @@ struct RcWs {
 inline RcWs rc_ws(const tpmlp_shape& s) {
   RcWs r{};
   const size_t e = elt_size(s.dtype);
-  r.at = stages(s.dtype, s.tokens, s.ffn_shard, s.hidden);
+  r.at = stages_weight(s.dtype, s.tokens, s.ffn_shard, s.hidden);
   r.at_off = align256((size_t)(s.tokens * s.ffn_shard) * e);
   r.bytes = r.at_off + (r.at ? align256((size_t)(s.ffn_shard * staged_ld(s.hidden)) * e) : 0);
   return r;

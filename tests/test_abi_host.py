@@ -118,17 +118,19 @@ def test_workspace_bytes(lib):
     # 2048 tiles of 256 x 320, no tail)
     assert fws(16384, 10240, 10240, 2) == 2 * 10240 * (10240 + 256) * 2
     # h = 8192 (TP = 4 of a 32768-wide FFN): 8192 is no multiple of 320, so every GEMM takes 256 x 256 tiles
-    # with k-contiguous copies too; nothing is staged (the mn-contiguous operands are read in place: Yp and
-    # dXp have 64 x 32 tiles, dB and dA 32 x 32 = 1024, no tails), only the db1 partials remain
-    assert fws(16384, 8192, 8192, 2) == 0
+    # with k-contiguous copies too. The forward still stages A_i^T and B_i^T (the copies buy the 16x16 MFMA
+    # form); the weight gradients read H, dY, X and dZ in place (Yp and dXp have 64 x 32 tiles, dB and dA
+    # 32 x 32 = 1024, no tails), so only the db1 partials remain in the backward's workspace
+    assert fws(16384, 8192, 8192, 2) == 2 * 8192 * (8192 + 256) * 2
     assert ws(16384, 8192, 8192, 2) == part * 8192 // 10240
-    # ... GPT-2-small: 256 x 256 tiles everywhere, so nothing staged either; its weight gradients (12 x 3 = 36
-    # tiles, K = 4096) and dXp (16 x 3 = 48 tiles, K = 3072) are launches of less than half a wave with long
-    # reductions: every tile split into 4 k-ranges (at most 4 below K = 8192; the largest partials, dXp's,
-    # size the shared room)
+    # ... GPT-2-small: 256 x 256 tiles everywhere; its weight gradients (12 x 3 = 36 tiles, K = 4096) and dXp
+    # (16 x 3 = 48 tiles, K = 3072) are launches of less than half a wave with long reductions, read in place:
+    # every tile split into 4 k-ranges (at most 4 below K = 8192; the largest partials, dXp's, size the
+    # shared room)
     assert ws(4096, 768, 3072, 1) == part2 + 48 * 4 * 256 * 256 * 4
-    # ... and its forward's second GEMM (48 tiles, K = 3072) is split the same way
-    assert fws(4096, 768, 3072, 1) == 48 * 4 * 256 * 256 * 4
+    # ... its forward stages A_i^T [3072][768 + 256] for the first GEMM (16 x 12 = 192 tiles), not B_i^T: the
+    # second GEMM (48 tiles, K = 3072) is split the same way and reads B_i in place
+    assert fws(4096, 768, 3072, 1) == 3072 * (768 + 256) * 2 + 48 * 4 * 256 * 256 * 4
     # the 2.4B shard (T = 8192, h = f = 2560): the forward's GEMMs are one full wave of 256 x 320 tiles, so A_i^T
     # and B_i^T are staged; dB and dA (2560 x 2560, K = 8192) are launches of less than half a wave that the
     # k-split spreads: they read H, dY, X and dZ in place on 10 x 10 tiles of 256 x 256 in 2 k-ranges (copies
