@@ -267,6 +267,17 @@ struct TailSplit {
   float* partial;
 };
 
+// The second GEMM of a paired launch (gemm_dma_kernel's PAIR form): its
+// operands and epilogue; shape, pitches and layout are the first one's.
+// tiles: the tile count of each GEMM.
+template <class Epi>
+struct PairGemm {
+  const uint16_t* p;
+  const uint16_t* q;
+  Epi epi;
+  int tiles;
+};
+
 // Raw buffer resource (stride 0) over `bytes` bytes at `p`, built from
 // wave-uniform values so that it lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int64_t bytes) {
@@ -439,12 +450,21 @@ struct FragAddrMC16 {
 // SLICED_P: P (k-contiguous) is read from the row slices xs; every slice
 // holds a whole number of BM-row tiles (the host checks), so each work
 // item's P tile lies in one slice and gets that slice's buffer resource.
-template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi, bool SLICED_P = false>
+//
+// PAIR: two GEMMs of one shape, pitches and epilogue type in one launch
+// (work items g2.tiles .. 2 g2.tiles - 1 are the second one's tiles, with
+// g2's operands and epilogue), unsplit. Two launches of at most half a
+// wave each then fill the CUs together, without the k-split's partials.
+template <class Cfg, class S, bool P_KC, bool Q_KC, class Epi, bool SLICED_P = false, bool PAIR = false>
 __global__ __launch_bounds__(Cfg::THREADS)
 __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD)))
-void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi,
-                     TailSplit tail, int nwork, RowSlices xs) {
+void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64_t q_extent, Epi epi_first,
+                     TailSplit tail, int nwork, RowSlices xs, PairGemm<Epi> g2) {
   static_assert(!SLICED_P || P_KC, "row slices of a k-contiguous P only");
+  static_assert(!(PAIR && SLICED_P), "a paired launch reads dense operands");
+  // The epilogue of the item being finished (the second GEMM's for its
+  // items in a paired launch).
+  Epi epi = epi_first;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LP = Cfg::LP, LQ = Cfg::LQ;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, ST = Cfg::STAGES, STG = Cfg::STG;
   constexpr bool M16 = Cfg::MF16;
@@ -483,13 +503,19 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
   // A work item: its output tile and k-range.
   struct Item {
     int tile, part;  // part >= 0: a k-range of a tail tile
+    bool second;     // a tile of the second GEMM of a paired launch
     int tm, tn;
     int64_t m0, n0, kbeg;
     int kspan, nk;
   };
   auto decode = [&](int v) __attribute__((always_inline)) {
     Item it;
-    const int w = map_work<Cfg::PER_XCD>(v, nwork);
+    int w = map_work<Cfg::PER_XCD>(v, nwork);
+    it.second = false;
+    if constexpr (PAIR) {
+      it.second = w >= g2.tiles;
+      if (it.second) w -= g2.tiles;
+    }
     it.tile = w;
     it.part = -1;
     if (w >= tail.full) {
@@ -516,13 +542,15 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
       return uniform_rsrc(xs.p[sl] + r0 * P.ld, rows * P.ld * 2);
     } else {
       const int64_t base = P_KC ? it.m0 * P.ld : it.m0;
-      return uniform_rsrc(P.ptr + base,
+      const uint16_t* const ptr = PAIR && it.second ? g2.p : P.ptr;
+      return uniform_rsrc(ptr + base,
                           (M16 && P_KC ? min(p_extent - base, (sh.M - it.m0) * P.ld) : p_extent - base) * 2);
     }
   };
   auto q_rsrc = [&](const Item& it) __attribute__((always_inline)) {
     const int64_t base = Q_KC ? it.n0 * Q.ld : it.n0;
-    return uniform_rsrc(Q.ptr + base,
+    const uint16_t* const ptr = PAIR && it.second ? g2.q : Q.ptr;
+    return uniform_rsrc(ptr + base,
                         (M16 && Q_KC ? min(q_extent - base, (sh.N - it.n0) * Q.ld) : q_extent - base) * 2);
   };
 
@@ -844,6 +872,7 @@ void gemm_dma_kernel(GemmShape sh, Operand P, int64_t p_extent, Operand Q, int64
     }
     // Drain this wave's loads of the tiles past the end (they write LDS).
     wait_vmcnt<0>();
+    if constexpr (PAIR) epi = cur.second ? g2.epi : epi_first;
 
     // 16x16 form with an epilogue input: the input's first 16-row block is
     // requested now, ahead of the next item's loads, so that waiting for it

@@ -166,52 +166,67 @@ int bwd_impl(const tpmlp_shape& s, const void* dY, const void* X, const void* A,
     TPMLP_HIP(hipGetLastError());
   }
   TPMLP_TRY(record(ev, 2, st));
-  // TH, TdY + B2: dB = H^T dY. Staged: P = H^T [f,T] (gelu(Z)^T when H is
-  // not kept) and Q[k][n] = dY^T[n][k], both k-contiguous. In place: both
-  // operands mn-contiguous (and gelu applied to Z on load without H).
-  if (room && w.stage_b2) {
-    if (H)
-      TPMLP_HIP((run_transpose<S, false>(H, wsb + w.ht_off, Tn, f, st)));
-    else
-      TPMLP_HIP((run_transpose<S, true>(Z, wsb + w.ht_off, Tn, f, st)));
+  // B2 + B3 paired: with f = h, dB = H^T dY and dA = X^T dZ have one shape
+  // and pitches; where each alone would be a launch of at most half a wave
+  // (split into k-ranges), they run as one launch, unsplit (pair_fits).
+  // Their events then bracket both in B2's interval; B3's is empty.
+  const bool paired = !bt && H && f == h && !(room && (w.stage_b2 || w.stage_b3)) &&
+                      pair_fits(s.dtype, f, h, Tn, false);
+  if (paired) {
     TPMLP_TRY(record(ev, 3, st));
-    TPMLP_HIP((run_transpose<S, false>(dY, wsb + w.dyt_off, Tn, h, st)));
     TPMLP_TRY(record(ev, 4, st));
-    if (bt)  // dB^T = dY^T H: the same staged operands, swapped
-      TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.dyt_off, staged_ld(Tn), wsb + w.ht_off,
-                                                staged_ld(Tn), epi_dB(), st, tail, tcap)));
-    else
-      TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, staged_ld(Tn), wsb + w.dyt_off,
-                                                staged_ld(Tn), epi_dB(), st, tail, tcap)));
+    TPMLP_HIP((run_gemm_pair<S, false, false>(f, h, Tn, H, dY, epi_dB(), X, dZ, epi_dA(), f, h, st)));
+    TPMLP_TRY(record(ev, 5, st));
+    TPMLP_TRY(record(ev, 6, st));
+    TPMLP_TRY(record(ev, 7, st));
   } else {
-    TPMLP_TRY(record(ev, 3, st));
-    TPMLP_TRY(record(ev, 4, st));
-    if (bt && H)  // dB^T [h,f] = dY^T H: P[m][k] = dY[k][m], Q[k][n] = H[k][n]
-      TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, dY, h, H, f, epi_dB(), st, tail, tcap)));
-    else if (bt)  // gelu applies to P only: compute H^T dY with gelu(Z) on load, store it transposed
-      TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h,
-                                                 EpiTransposed<decltype(epi_dB())>{epi_dB()}, st)));
-    else if (H)
+    // TH, TdY + B2: dB = H^T dY. Staged: P = H^T [f,T] (gelu(Z)^T when H is
+    // not kept) and Q[k][n] = dY^T[n][k], both k-contiguous. In place: both
+    // operands mn-contiguous (and gelu applied to Z on load without H).
+    if (room && w.stage_b2) {
+      if (H)
+        TPMLP_HIP((run_transpose<S, false>(H, wsb + w.ht_off, Tn, f, st)));
+      else
+        TPMLP_HIP((run_transpose<S, true>(Z, wsb + w.ht_off, Tn, f, st)));
+      TPMLP_TRY(record(ev, 3, st));
+      TPMLP_HIP((run_transpose<S, false>(dY, wsb + w.dyt_off, Tn, h, st)));
+      TPMLP_TRY(record(ev, 4, st));
+      if (bt)  // dB^T = dY^T H: the same staged operands, swapped
+        TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.dyt_off, staged_ld(Tn), wsb + w.ht_off,
+                                                  staged_ld(Tn), epi_dB(), st, tail, tcap)));
+      else
+        TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, f, h, Tn, wsb + w.ht_off, staged_ld(Tn), wsb + w.dyt_off,
+                                                  staged_ld(Tn), epi_dB(), st, tail, tcap)));
+    } else {
+      TPMLP_TRY(record(ev, 3, st));
+      TPMLP_TRY(record(ev, 4, st));
+      if (bt && H)  // dB^T [h,f] = dY^T H: P[m][k] = dY[k][m], Q[k][n] = H[k][n]
+        TPMLP_HIP((run_gemm<S, false, false, false>(s.dtype, h, f, Tn, dY, h, H, f, epi_dB(), st, tail, tcap)));
+      else if (bt)  // gelu applies to P only: compute H^T dY with gelu(Z) on load, store it transposed
+        TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h,
+                                                   EpiTransposed<decltype(epi_dB())>{epi_dB()}, st)));
+      else if (H)
+        TPMLP_HIP(
+            (run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, epi_dB(), st, tail, tcap)));
+      else
+        TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, epi_dB(), st)));
+    }
+    TPMLP_TRY(record(ev, 5, st));
+    // TX, TdZ + B3: dA = X^T dZ. Staged: P = X^T [h,T], Q[k][n] = dZ^T[n][k].
+    if (room && w.stage_b3) {
+      TPMLP_HIP((run_transpose<S, false>(X, wsb + w.xt_off, Tn, h, st)));
+      TPMLP_TRY(record(ev, 6, st));
+      TPMLP_HIP((run_transpose<S, false>(dZ, wsb + w.dzt_off, Tn, f, st)));
+      TPMLP_TRY(record(ev, 7, st));
+      TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, staged_ld(Tn), wsb + w.dzt_off,
+                                                staged_ld(Tn),
+                                                epi_dA(), st, tail, tcap)));
+    } else {
+      TPMLP_TRY(record(ev, 6, st));
+      TPMLP_TRY(record(ev, 7, st));
       TPMLP_HIP(
-          (run_gemm<S, false, false, false>(s.dtype, f, h, Tn, H, f, dY, h, epi_dB(), st, tail, tcap)));
-    else
-      TPMLP_HIP((run_gemm<S, false, false, true>(s.dtype, f, h, Tn, Z, f, dY, h, epi_dB(), st)));
-  }
-  TPMLP_TRY(record(ev, 5, st));
-  // TX, TdZ + B3: dA = X^T dZ. Staged: P = X^T [h,T], Q[k][n] = dZ^T[n][k].
-  if (room && w.stage_b3) {
-    TPMLP_HIP((run_transpose<S, false>(X, wsb + w.xt_off, Tn, h, st)));
-    TPMLP_TRY(record(ev, 6, st));
-    TPMLP_HIP((run_transpose<S, false>(dZ, wsb + w.dzt_off, Tn, f, st)));
-    TPMLP_TRY(record(ev, 7, st));
-    TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, h, f, Tn, wsb + w.xt_off, staged_ld(Tn), wsb + w.dzt_off,
-                                              staged_ld(Tn),
-                                              epi_dA(), st, tail, tcap)));
-  } else {
-    TPMLP_TRY(record(ev, 6, st));
-    TPMLP_TRY(record(ev, 7, st));
-    TPMLP_HIP(
-        (run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, epi_dA(), st, tail, tcap)));
+          (run_gemm<S, false, false, false>(s.dtype, h, f, Tn, X, h, dZ, f, epi_dA(), st, tail, tcap)));
+    }
   }
   TPMLP_TRY(record(ev, 8, st));
   // B4: dXp = dZ A_i^T; Q[k=f][n=h] = A_i[n][k] is k-contiguous

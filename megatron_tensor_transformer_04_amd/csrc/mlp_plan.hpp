@@ -231,7 +231,8 @@ hipError_t launch_dma(const GemmShape& sh, const void* p, int64_t ldp, const voi
   // operand extents in elements: rows (KC) or k-rows (MC) times the pitch
   hipLaunchKernelGGL((gemm_dma_kernel<Cfg, S, PK, QK, Epi, SL>), dim3(nblk), dim3(Cfg::THREADS), 0, st, sh,
                      Operand{static_cast<const uint16_t*>(p), ldp}, (PK ? sh.M : sh.K) * ldp,
-                     Operand{static_cast<const uint16_t*>(q), ldq}, (QK ? sh.N : sh.K) * ldq, epi, tail, nwork, xs);
+                     Operand{static_cast<const uint16_t*>(q), ldq}, (QK ? sh.N : sh.K) * ldq, epi, tail, nwork, xs,
+                     PairGemm<Epi>{nullptr, nullptr, epi, 0});
   if constexpr (Epi::kTailSplit) {
     if (tail.parts > 1) {
       const int ntail = ntile - tail.full;
@@ -289,6 +290,44 @@ hipError_t run_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void* p, i
     }
   }
   return hipGetLastError();
+}
+
+// Two GEMMs of one shape, pitches and layout (the weight gradients dB and
+// dA of a shard with f = h), each alone a launch of at most half a wave of
+// 256 x 256 tiles, which plan_tail would split into k-ranges with fp32
+// partials and a finishing pass: launched as one, their tiles fill up to a
+// wave side by side, each over the whole reduction. Where the planner puts
+// such a GEMM on the direct-load engine's 256 x 256 tiles and two of them
+// fit in one wave of the CUs (the CU count that tp_mlp_debug_plan may
+// replace, as for plan_tail).
+inline bool pair_fits(int dtype, int64_t M, int64_t N, int64_t K, bool kc) {
+  if (dtype == TPMLP_F32 || M <= 0 || N <= 0 || K <= 0) return false;
+  const Plan pl = plan_gemm(dtype, M, N, K, false, kc);
+  const int forced = g_plan_cus.load(std::memory_order_relaxed);
+  const int cus = forced > 0 ? forced : kCUs;
+  return pl.eng == Engine::Dma256 && 2 * pl.tiles_m * pl.tiles_n <= cus;
+}
+
+// C1 = P1 Q1 through epi1 and C2 = P2 Q2 through epi2 in one launch, where
+// pair_fits (the caller checks); 256 x 256 tiles on the 32x32 MFMA form.
+template <class S, bool PK, bool QK, class Epi>
+hipError_t run_gemm_pair(int64_t M, int64_t N, int64_t K, const void* p1, const void* q1, const Epi& epi1,
+                         const void* p2, const void* q2, const Epi& epi2, int64_t ldp, int64_t ldq,
+                         hipStream_t st) {
+  if constexpr (std::is_same_v<S, StoreF32>) {
+    return hipErrorInvalidValue;  // pair_fits is false for fp32
+  } else {
+    using Cfg = CfgD256;
+    const int tm = (int)ceil_div(M, Cfg::BM), tn = (int)ceil_div(N, Cfg::BN), ntile = tm * tn;
+    const GemmShape sh{M, N, K, tm, tn, 1, K};
+    const int nwork = 2 * ntile;
+    hipLaunchKernelGGL((gemm_dma_kernel<Cfg, S, PK, QK, Epi, false, true>), dim3(std::min(nwork, kCUs * Cfg::OCC)),
+                       dim3(Cfg::THREADS), 0, st, sh, Operand{static_cast<const uint16_t*>(p1), ldp},
+                       (PK ? M : K) * ldp, Operand{static_cast<const uint16_t*>(q1), ldq}, (QK ? N : K) * ldq, epi1,
+                       TailSplit{ntile, 1, K, nullptr}, nwork, RowSlices{},
+                       PairGemm<Epi>{static_cast<const uint16_t*>(p2), static_cast<const uint16_t*>(q2), epi2, ntile});
+    return hipGetLastError();
+  }
 }
 
 // run_gemm with P (k-contiguous, [M][K]) read from row slices xs (see

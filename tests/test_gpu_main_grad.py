@@ -55,8 +55,9 @@ def _err(new, old, ref):
 
 @pytest.mark.parametrize("tile", [128, 256, "dma256", "dma320"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,h,f", [(200, 136, 264), (520, 264, 392), (8, 8, 8)])
+@pytest.mark.parametrize("T,h,f", [(200, 136, 264), (520, 264, 392), (8, 8, 8), (2048, 1024, 1024)])
 def test_main_grad_accumulates(gpu_lib, tile, dtype, T, h, f):
+    # 2048 x 1024 x 1024 (f = h): dB and dA as one paired launch on the direct-load tiles
     print(f"case main-grad tile={tile} dtype={dtype} T={T} h={h} f={f}", flush=True)
     inp = synth.draw_inputs(T, h, f, dtype, seed=T + 2 * h + f, sigma_dy=1.0)
     ref = oracle.shard_backward(inp.X, inp.A, inp.b1, inp.B, inp.dY)

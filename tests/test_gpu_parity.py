@@ -214,13 +214,17 @@ def test_deterministic_bitwise(gpu_lib):
 # the planner splits into k-ranges. It runs the XCD renumbering of full
 # waves (map_work) as well as the plain order of the last wave.
 FULL_WAVE = (4352, 5440, 5440)
+# f = h with few tiles and a long reduction: dB and dA run as one paired
+# launch (16 + 16 or 25 + 25 tiles of 256 x 256), unsplit
+PAIRED, PAIRED_RAGGED = (2048, 1024, 1024), (2056, 1032, 1032)
 
 
 @pytest.mark.parametrize("tile,cus,shape", [(128, None, None), (256, None, None), ("dma256", None, None),
                                             ("dma256", 4, None), ("dma320", None, None), ("dma320", 2, None),
                                             (None, None, FULL_WAVE), ("dma256", None, FULL_WAVE),
                                             ("dma320", None, FULL_WAVE), ("dma320m32", None, FULL_WAVE),
-                                            ("dma320m32", 2, None)],
+                                            ("dma320m32", 2, None), (None, None, PAIRED),
+                                            (None, None, PAIRED_RAGGED), ("dma256", None, PAIRED)],
                          indirect=["tile"])
 def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, shape):
     """Each output lives between two poisoned guard regions, which must
@@ -228,7 +232,7 @@ def test_outputs_leave_neighbouring_memory_untouched(gpu_lib, tile, cus, shape):
     must be overwritten (the poison value may not remain) and match the
     oracle (cus: k-split tails planned as if the chip had that many CUs, so
     that the partials use the workspace; FULL_WAVE: launches of more than
-    one full wave of work items)."""
+    one full wave of work items; PAIRED: dB and dA from one launch)."""
     import torch
     if cus is not None:
         gpu_lib.tp_mlp_debug_plan(tile, cus)
@@ -348,12 +352,13 @@ def test_epilogue_rounding_is_nearest_even(gpu_lib, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,h,f,keep_dz", [(2048, 1024, 1024, True), (2056, 1032, 1048, False)])
+@pytest.mark.parametrize("T,h,f,keep_dz", [(2048, 1024, 1040, True), (2056, 1032, 1048, False)])
 def test_sub_wave_k_split(gpu_lib, dtype, T, h, f, keep_dz):
     """Weight gradients with few output tiles and a long reduction (T >= 2048
-    tokens): 16-25 tiles of 256 x 256, every tile split into 4 k-ranges
+    tokens): 20-25 tiles of 256 x 256, every tile split into 4 k-ranges
     whose fp32 partials are summed in a fixed order (the ragged case ends in
-    a short last range). Against the oracle, and bitwise run to run."""
+    a short last range). f != h, so dB and dA are not paired. Against the
+    oracle, and bitwise run to run."""
     import torch
     print(f"case sub-wave k-split dtype={dtype} T={T} h={h} f={f}", flush=True)
     inp = synth.draw_inputs(T, h, f, dtype, seed=T + f, sigma_dy=1.0)
@@ -363,3 +368,25 @@ def test_sub_wave_k_split(gpu_lib, dtype, T, h, f, keep_dz):
     again = run_shard(gpu_lib, *dev, keep_dz=keep_dz)
     for k in ("dA", "dB", "dXp", "db1"):
         assert torch.equal(out[k], again[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,h,f,keep_dz", [PAIRED + (True,), PAIRED_RAGGED + (False,)])
+@pytest.mark.parametrize("tile", [None, "dma256"], indirect=True)
+def test_paired_weight_gradients(gpu_lib, tile, dtype, T, h, f, keep_dz):
+    """f = h, few output tiles, a long reduction: dB = H^T dY and dA = X^T dZ
+    run as one launch of 2 x 16 (or 2 x 25, ragged) tiles of 256 x 256, each
+    tile over the whole reduction. Against the oracle, bitwise run to run,
+    and with H not kept (gelu(Z) applied on load: not paired) against the
+    same oracle."""
+    import torch
+    print(f"case paired dB/dA tile={tile} dtype={dtype} T={T} h={h} f={f}", flush=True)
+    inp = synth.draw_inputs(T, h, f, dtype, seed=T + 3 * f, sigma_dy=1.0)
+    dev = device_inputs(inp)
+    ref = _oracle_shard(inp)
+    out = run_shard(gpu_lib, *dev, keep_dz=keep_dz)
+    compare(out, ref, TOL[dtype])
+    again = run_shard(gpu_lib, *dev, keep_dz=keep_dz)
+    for k in ("dA", "dB", "dXp", "db1"):
+        assert torch.equal(out[k], again[k]), k
+    compare(run_shard(gpu_lib, *dev, keep_h=False, keep_dz=keep_dz), ref, TOL[dtype])
