@@ -87,22 +87,40 @@ typedef enum {
 /*
  * Shape of one rank's share: X [tokens, hidden], A_i [hidden, ffn_shard].
  *
- * layout: 0, or TPMLP_LAYOUT_B_T. With TPMLP_LAYOUT_B_T the second weight is
+ * layout: 0, or an OR of TPMLP_LAYOUT_B_T and TPMLP_LAYOUT_WEIGHTS_STAGED.
+ * With TPMLP_LAYOUT_B_T the second weight is
  * passed as B_i^T [hidden, ffn_shard] (row-major), i.e. in the [out, in]
  * order of a linear layer's weight, and its gradient dB (or dB_main) is
  * written in that same [hidden, ffn_shard] order; every other tensor is as
  * described above. The pages fix only which dimension of the second weight
  * is split (its input rows), not the order in which a rank stores its block.
+ *
+ * TPMLP_LAYOUT_WEIGHTS_STAGED (read by tp_mlp_fwd and tp_mlp_fwd_sp; every
+ * other call ignores it): the caller vouches that the forward workspace
+ * `ws` already holds the k-contiguous copies of the weights that an earlier
+ * tp_mlp_fwd or tp_mlp_fwd_sp call wrote there, with the same shape and
+ * B_T bit, the same A_i and B_i contents, and the same ws pointer with
+ * ws_bytes at least tp_mlp_fwd_workspace_bytes. The call then skips those
+ * copies (the TA and TB transposes; their events are recorded back to
+ * back) and reads the ones in the workspace. This serves gradient
+ * accumulation over micro-batches ("Training GPT-2 with Megatron-LM",
+ * section 4.3): the weights change only at the optimizer step, so the
+ * first micro-batch's copies serve the rest. The library cannot check the
+ * promise: with stale copies the results are those of the weights that
+ * were copied. The rest of the workspace (k-split partial sums) is
+ * rewritten by every call as before.
+ *
  * Any other bit set is TPMLP_ERR_SHAPE. A zero-initialised struct (e.g.
  * {tokens, hidden, ffn_shard, dtype}) is the default layout.
  */
 #define TPMLP_LAYOUT_B_T 1
+#define TPMLP_LAYOUT_WEIGHTS_STAGED 2
 typedef struct {
   int64_t tokens;
   int64_t hidden;
   int64_t ffn_shard;
   int32_t dtype;  /* tpmlp_dtype */
-  int32_t layout; /* 0 or TPMLP_LAYOUT_B_T */
+  int32_t layout; /* 0, or TPMLP_LAYOUT_B_T | TPMLP_LAYOUT_WEIGHTS_STAGED */
 } tpmlp_shape;
 
 /* TPMLP_ABI_VERSION of the built library. */

@@ -45,6 +45,7 @@ class TpMlpError(RuntimeError):
 
 
 TPMLP_LAYOUT_B_T = 1   # B passed as B_i^T [hidden, ffn_shard] (dB returned in that order)
+TPMLP_LAYOUT_WEIGHTS_STAGED = 2  # the forward workspace already holds the weight copies (tp_mlp_fwd*)
 
 
 class tpmlp_shape(ctypes.Structure):
@@ -187,8 +188,8 @@ def shape_of(tokens: int, hidden: int, ffn_shard: int, dtype: int, layout: int =
     return tpmlp_shape(tokens, hidden, ffn_shard, dtype, layout)
 
 
-def _layout(b_transposed: bool) -> int:
-    return TPMLP_LAYOUT_B_T if b_transposed else 0
+def _layout(b_transposed: bool, weights_staged: bool = False) -> int:
+    return (TPMLP_LAYOUT_B_T if b_transposed else 0) | (TPMLP_LAYOUT_WEIGHTS_STAGED if weights_staged else 0)
 
 
 # tile names of tp_mlp_debug_plan (TPMLP_PLAN_* in include/tp_mlp.h)
@@ -242,21 +243,25 @@ def _nbytes(ws):
     return 0 if ws is None else ws.numel() * ws.element_size()
 
 
-def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_transposed=False) -> None:
-    """Forward of one TP rank into caller-allocated Z, H (or None) and Yp."""
-    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed))
+def tp_mlp_fwd(X, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_transposed=False,
+               weights_staged=False) -> None:
+    """Forward of one TP rank into caller-allocated Z, H (or None) and Yp.
+    weights_staged: `ws` already holds the weight copies of an earlier
+    forward with the same weights and workspace (TPMLP_LAYOUT_WEIGHTS_STAGED)."""
+    s = shape_of(X.shape[0], X.shape[1], A.shape[1], _dtype_code(X), _layout(b_transposed, weights_staged))
     ev = _events(events)
     _check(load().tp_mlp_fwd(ctypes.byref(s), _ptr(X), _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),
                              _ptr(ws), _nbytes(ws), _stream(stream), ev))
 
 
-def tp_mlp_fwd_sp(X_slices, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_transposed=False) -> None:
+def tp_mlp_fwd_sp(X_slices, A, b1, B, Z, H, Yp, ws=None, *, stream=None, events=None, b_transposed=False,
+                  weights_staged=False) -> None:
     """Forward of one TP rank under sequence parallelism: X given as equal
     token-row slices (a list of [T/n, hidden] device tensors, one per rank),
     read in place by the first GEMM instead of an all-gathered copy."""
     n = len(X_slices)
     T = sum(x.shape[0] for x in X_slices)
-    s = shape_of(T, X_slices[0].shape[1], A.shape[1], _dtype_code(X_slices[0]), _layout(b_transposed))
+    s = shape_of(T, X_slices[0].shape[1], A.shape[1], _dtype_code(X_slices[0]), _layout(b_transposed, weights_staged))
     arr = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in X_slices])
     ev = _events(events)
     _check(load().tp_mlp_fwd_sp(ctypes.byref(s), n, arr, _ptr(A), _ptr(b1), _ptr(B), _ptr(Z), _ptr(H), _ptr(Yp),

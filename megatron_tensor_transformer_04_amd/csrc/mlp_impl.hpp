@@ -70,8 +70,11 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
   TPMLP_TRY(record(ev, 0, st));
   // TA + F1: Z = X A_i + b1 (and H = gelu(Z)); P = X [T,h] k-contiguous,
   // Q = A_i [h,f] (n-contiguous), or its transpose A_i^T [f,h] (k-contiguous)
+  // With TPMLP_LAYOUT_WEIGHTS_STAGED the copies of A_i and B_i are already in
+  // the workspace (written by an earlier call from the same weights).
+  const bool have_copies = weights_staged(s);
   if (room && w.at) {
-    TPMLP_HIP((run_transpose<S, false>(A, wsb + w.at_off, h, f, st)));
+    if (!have_copies) TPMLP_HIP((run_transpose<S, false>(A, wsb + w.at_off, h, f, st)));
     TPMLP_TRY(record(ev, 1, st));
     const EpiBiasGelu<S> epi{(const T*)b1, (T*)Z, (T*)H, f};
     if (xs)
@@ -102,7 +105,7 @@ int fwd_impl(const tpmlp_shape& s, const void* X, const void* A, const void* b1,
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_HIP((run_gemm<S, true, false, true>(s.dtype, Tn, h, f, Z, f, B, h, EpiStore<S>{(T*)Yp, h}, st)));
   } else if (room && w.bt) {
-    TPMLP_HIP((run_transpose<S, false>(B, wsb + w.bt_off, f, h, st)));
+    if (!have_copies) TPMLP_HIP((run_transpose<S, false>(B, wsb + w.bt_off, f, h, st)));
     TPMLP_TRY(record(ev, 3, st));
     TPMLP_HIP((run_gemm<S, true, true, false>(s.dtype, Tn, h, f, H, f, wsb + w.bt_off, staged_ld(f),
                                               EpiStore<S>{(T*)Yp, h},

@@ -401,12 +401,14 @@ inline int check_shape(const tpmlp_shape* s) {
   for (int64_t v : d) {
     if (v % mult) return TPMLP_ERR_ALIGN;
   }
-  if (s->layout & ~TPMLP_LAYOUT_B_T) return TPMLP_ERR_SHAPE;
+  if (s->layout & ~(TPMLP_LAYOUT_B_T | TPMLP_LAYOUT_WEIGHTS_STAGED)) return TPMLP_ERR_SHAPE;
   return TPMLP_OK;
 }
 
 // The second weight arrives as B_i^T [h][f] (and dB leaves as [h][f]).
 inline bool b_t(const tpmlp_shape& s) { return (s.layout & TPMLP_LAYOUT_B_T) != 0; }
+// The forward workspace already holds the weight copies (the caller's promise).
+inline bool weights_staged(const tpmlp_shape& s) { return (s.layout & TPMLP_LAYOUT_WEIGHTS_STAGED) != 0; }
 
 struct Span {
   const void* p;

@@ -350,12 +350,16 @@ def test_b_transposed_layout_workspace_and_validation(lib):
     assert fws(1) == 10240 * (10240 + 256) * 2
     assert ws(1) == ws(0) + 10240 * (10240 + 256) * 2
     assert ws(1, MINIMAL) == ws(0, MINIMAL)
-    assert ws(2) == 0 and fws(4) == 0 and ws(-1) == 0
+    assert ws(4) == 0 and fws(4) == 0 and ws(-1) == 0
+    # TPMLP_LAYOUT_WEIGHTS_STAGED (the forward reuses the weight copies already in its workspace) changes no size
+    assert _header_define("TPMLP_LAYOUT_WEIGHTS_STAGED") == tpmlp.TPMLP_LAYOUT_WEIGHTS_STAGED == 2
+    assert fws(2) == fws(0) and fws(3) == fws(1)
+    assert ws(2) == ws(0) and ws(3) == ws(1) and ws(2, MINIMAL) == ws(0, MINIMAL)
     # small shapes stage nothing in either layout
     small = lambda layout: tpmlp_shape(520, 264, 392, 1, layout)
     assert lib.tp_mlp_workspace_bytes(ctypes.byref(small(1)), 0) == lib.tp_mlp_workspace_bytes(
         ctypes.byref(small(0)), 0)
-    bad = tpmlp_shape(64, 128, 256, 2, 2)
+    bad = tpmlp_shape(64, 128, 256, 2, 4)
     assert lib.tp_mlp_fwd(ctypes.byref(bad), *([None] * 7), None, 0, None, None) == 2  # TPMLP_ERR_SHAPE
 
 

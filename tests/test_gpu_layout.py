@@ -150,3 +150,51 @@ def test_b_transposed_full_size_h10240_sampled(gpu_lib):
     _check("db1[cols]", to_host(out["db1"].index_select(0, ci)), rc["db1"], tol, errs)
     _check("dB^T[:,cols]", to_host(out["dB"].index_select(1, ci)).T, rc["dB"], tol, errs)
     print("errors", errs, flush=True)
+
+
+@pytest.mark.parametrize("dtype,T,h,f,b_transposed,b_staged", [
+    ("bf16", 8192, 2560, 2560, False, True),    # 2.4B shard: A_i^T and B_i^T copied
+    ("bf16", 8192, 2560, 2560, True, False),    # B_i^T passed: only A_i^T copied
+    ("f16", 4096, 768, 3072, False, False),     # GPT-2-small: A_i^T copied, the second GEMM reads B_i in place
+])
+def test_weights_staged_reuses_the_copies(gpu_lib, dtype, T, h, f, b_transposed, b_staged):
+    """TPMLP_LAYOUT_WEIGHTS_STAGED: a forward over new tokens that reuses the
+    weight copies an earlier forward left in its workspace equals a plain
+    forward bit for bit (also with X given as row slices); and with other
+    weights passed, the copied ones are used: the copies are really skipped."""
+    import torch
+    print(f"case weights staged dtype={dtype} T={T} h={h} f={f} b_t={b_transposed}", flush=True)
+    first = synth.draw_inputs(T, h, f, dtype, seed=31)
+    second = synth.draw_inputs(T, h, f, dtype, seed=32)
+    X, A, b1, B, _ = device_inputs(first)
+    X2 = device_inputs(second)[0]
+    if b_transposed:
+        B = B.t().contiguous()
+    nfws = gpu_lib.tp_mlp_fwd_workspace_bytes(T, h, f, gpu_lib.TPMLP_F16 if dtype == "f16" else gpu_lib.TPMLP_BF16,
+                                              gpu_lib.TPMLP_LAYOUT_B_T if b_transposed else 0)
+    assert nfws > 0
+    ws, fresh = (torch.empty((nfws,), dtype=torch.uint8, device="cuda") for _ in range(2))
+    new = lambda: tuple(torch.empty((T, n), dtype=X.dtype, device="cuda") for n in (f, f, h))
+
+    def fwd(x, a, b, w, staged, out):
+        gpu_lib.tp_mlp_fwd(x, a, b1, b, *out, w, b_transposed=b_transposed, weights_staged=staged)
+        torch.cuda.synchronize()
+        return out
+
+    fwd(X, A, B, ws, False, new())                      # writes the copies into ws
+    ref = fwd(X2, A, B, fresh, False, new())
+    got = fwd(X2, A, B, ws, True, new())
+    for name, r, g in zip(("Z", "H", "Yp"), ref, got):
+        assert torch.equal(r.view(torch.int16), g.view(torch.int16)), name
+    sliced = new()
+    gpu_lib.tp_mlp_fwd_sp(list(X2.chunk(4)), A, b1, B, *sliced, ws, b_transposed=b_transposed, weights_staged=True)
+    torch.cuda.synchronize()
+    for name, r, g in zip(("Z", "H", "Yp"), ref, sliced):
+        assert torch.equal(r.view(torch.int16), g.view(torch.int16)), name
+    # zero weights passed with the flag: the copies of A_i (and B_i where it is copied) still hold the first ones
+    Z0, H0, Yp0 = fwd(X2, torch.zeros_like(A), torch.zeros_like(B), ws, True, new())
+    assert torch.equal(Z0.view(torch.int16), ref[0].view(torch.int16))
+    if b_staged:
+        assert torch.equal(Yp0.view(torch.int16), ref[2].view(torch.int16))
+    else:
+        assert not torch.any(Yp0)
