@@ -342,6 +342,9 @@ def main():
     ap.add_argument("--config", default="gpt_h10240")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="skip the extra steps timed with the weight copies reused (profiled runs, so that every "
+                         "step in the trace is a headline step)")
     ap.add_argument("--main-grad", action="store_true",
                     help="run the backward as tp_mlp_bwd_main_grad (dA, dB, db1 added to fp32 main gradients)")
     ap.add_argument("--recompute", action="store_true",
@@ -513,7 +516,7 @@ def main():
     # forward reusing the weight copies that the steps above left in its
     # workspace (TPMLP_LAYOUT_WEIGHTS_STAGED).
     reuse_ms = None
-    if not args.recompute:
+    if not (args.recompute or args.no_reuse):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(K):
