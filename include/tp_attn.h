@@ -137,8 +137,10 @@ int tp_attn_bwd(const tpattn_shape* shape,
  * Workspace bytes (0 on an invalid shape):
  *   forward:  a transposed copy of Wo (when the output projection runs on
  *             the large-tile engine, which then reads both operands
- *             k-contiguous) and the projection's k-split partials, 256 at
- *             least;
+ *             k-contiguous), a transposed copy of Wqkv (when the QKV
+ *             projection runs on that engine's 256 x 256 tiles, whose
+ *             16x16 MFMA form reads k-contiguous operands only) and the
+ *             output projection's k-split partials, 256 at least;
  *   backward: fp32 row terms rowsum(dO * O) [batch*heads][seq], dO [T, q],
  *             fp32 per-256-row column partials of dQKV for dbqkv, and fp32
  *             k-split partials of the projections' GEMMs.

@@ -27,6 +27,9 @@ size_t planned_gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K, bool 
 // both operands are k-contiguous (so that staging a transposed copy of an
 // mn-contiguous operand pays off)?
 bool planned_gemm_stages(int dtype, int64_t M, int64_t N, int64_t K);
+// The same for a GEMM whose mn-contiguous operand is a weight, which is
+// also copied where the copy buys the 16x16 MFMA form (256 x 256 tiles).
+bool planned_gemm_stages_weight(int dtype, int64_t M, int64_t N, int64_t K);
 
 // out[c][r] = in[r][c] for a dense 16-bit [R][C] matrix; out has row pitch
 // staged_transpose_ld(R) (R plus padding that spreads its rows over the L2

@@ -22,17 +22,21 @@ using namespace attn;
 
 // Forward workspace: [Wo^T [h][staged_transpose_ld(q)], when the output
 // projection runs on the large-tile engine with both operands k-contiguous]
-// [that projection's k-split partials]; 256 bytes at least, so that 0
-// keeps meaning an invalid shape.
+// [Wqkv^T [3q][staged_transpose_ld(h)], when the k-contiguous copy pays for
+// the QKV projection (planned_gemm_stages_weight)] [the output
+// projection's k-split partials]; 256 bytes at least, so that 0 keeps
+// meaning an invalid shape.
 struct FlashFwdWs {
-  bool wot;
-  size_t tail_off, total;
+  bool wot, wqkvt;
+  size_t wqkvt_off, tail_off, total;
 };
 
 FlashFwdWs flash_fwd_layout(const AttnDims& a, int dtype) {
   FlashFwdWs w{};
   w.wot = planned_gemm_stages(dtype, a.T, a.h, a.q);
-  w.tail_off = w.wot ? a256((size_t)(a.h * staged_transpose_ld(a.q)) * 2) : 0;
+  w.wqkvt = planned_gemm_stages_weight(dtype, a.T, 3 * a.q, a.h);
+  w.wqkvt_off = w.wot ? a256((size_t)(a.h * staged_transpose_ld(a.q)) * 2) : 0;
+  w.tail_off = w.wqkvt_off + (w.wqkvt ? a256((size_t)(3 * a.q * staged_transpose_ld(a.h)) * 2) : 0);
   w.total = std::max<size_t>(256, w.tail_off + a256(planned_gemm_tail_bytes(dtype, a.T, a.h, a.q, w.wot)));
   return w;
 }
@@ -85,8 +89,19 @@ int flash_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, cons
                    const void* Wo, void* QKV, void* LSE, void* O, void* Yp, void* ws, size_t ws_bytes,
                    hipStream_t st) {
   const int64_t T3 = 3 * a.q;
-  // QKV = X Wqkv + bqkv: P = X [T,h] k-contiguous, Q = Wqkv [h,3q] n-contiguous
-  ATTN_HIP(planned_gemm(dtype, true, false, a.T, T3, a.h, X, a.h, Wqkv, T3, QKV, T3, bqkv, nullptr, 0, st));
+  const FlashFwdWs w = flash_fwd_layout(a, dtype);
+  char* wsb = static_cast<char*>(ws);
+  // QKV = X Wqkv + bqkv: P = X [T,h] k-contiguous, Q = Wqkv [h,3q]
+  // n-contiguous, or its copy Wqkv^T [3q][h] (k-contiguous) where that pays
+  // (the 16x16 MFMA form reads k-contiguous operands only)
+  if (w.wqkvt) {
+    const int64_t ldt = staged_transpose_ld(a.h);
+    ATTN_HIP(staged_transpose(Wqkv, wsb + w.wqkvt_off, a.h, T3, st));
+    ATTN_HIP(planned_gemm(dtype, true, true, a.T, T3, a.h, X, a.h, wsb + w.wqkvt_off, ldt, QKV, T3, bqkv, nullptr,
+                          0, st));
+  } else {
+    ATTN_HIP(planned_gemm(dtype, true, false, a.T, T3, a.h, X, a.h, Wqkv, T3, QKV, T3, bqkv, nullptr, 0, st));
+  }
   flash::Args f = core_args(a, causal, QKV);
   f.lse = static_cast<float*>(LSE);
   f.out = static_cast<uint16_t*>(O);
@@ -96,8 +111,6 @@ int flash_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, cons
   // where the large-tile engine runs it a transposed copy Wo^T [h][q] is
   // staged first (3 MB at the 2.4B shape), which lets it take the 320-wide
   // tiles (one wave of 256 x 320 there, against 1.25 of 256 x 256)
-  const FlashFwdWs w = flash_fwd_layout(a, dtype);
-  char* wsb = static_cast<char*>(ws);
   if (w.wot) {
     const int64_t ldt = staged_transpose_ld(a.q);
     ATTN_HIP(staged_transpose(Wo, wsb, a.q, a.h, st));
@@ -105,7 +118,7 @@ int flash_fwd_impl(const AttnDims& a, int dtype, int causal, const void* X, cons
                           reinterpret_cast<float*>(wsb + w.tail_off), ws_bytes - w.tail_off, st));
   } else {
     ATTN_HIP(planned_gemm(dtype, true, false, a.T, a.h, a.q, O, a.q, Wo, a.h, Yp, a.h, nullptr,
-                          reinterpret_cast<float*>(wsb), ws_bytes, st));
+                          reinterpret_cast<float*>(wsb + w.tail_off), ws_bytes - w.tail_off, st));
   }
   return TPMLP_OK;
 }

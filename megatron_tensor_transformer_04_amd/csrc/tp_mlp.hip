@@ -79,6 +79,10 @@ size_t planned_gemm_tail_bytes(int dtype, int64_t M, int64_t N, int64_t K, bool 
 
 bool planned_gemm_stages(int dtype, int64_t M, int64_t N, int64_t K) { return stages(dtype, M, N, K); }
 
+bool planned_gemm_stages_weight(int dtype, int64_t M, int64_t N, int64_t K) {
+  return stages_weight(dtype, M, N, K);
+}
+
 hipError_t staged_transpose(const void* in, void* out, int64_t R, int64_t C, hipStream_t st) {
   // the transpose moves 16-bit values: the storage type only names them
   return run_transpose<StoreBF16, false>(in, out, R, C, st);

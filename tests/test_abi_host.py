@@ -417,8 +417,9 @@ def test_flash_attention_workspace_sizes_and_validation(lib):
     bws = lambda s: lib.tp_attn_flash_bwd_workspace_bytes(ctypes.byref(s))
     big = sh(4, 2048, 2560, 8, 80, 2)
     # Yp = O Wo runs on 256 x 320 tiles from a staged Wo^T [2560][640 + 256] (32 x 8 tiles, one wave, K = 640:
-    # no k-split)
-    assert fws(big) == 2560 * (640 + 256) * 2
+    # no k-split); QKV = X Wqkv (32 x 8 tiles of 256 x 256, 1920 being no multiple of 320) from a staged
+    # Wqkv^T [1920][2560 + 256]
+    assert fws(big) == 2560 * (640 + 256) * 2 + 1920 * (2560 + 256) * 2
     assert fws(sh(1, 16, 16, 1, 8, 2)) == 256           # small: no staging, the 256-byte minimum
     # the materialized layout without dS: D, dO, column partials, then the same k-split room
     ks = max(96 * 2 * 256 * 256 * 4, 30 * 8 * 256 * 256 * 4, 80 * 3 * 256 * 256 * 4)
