@@ -146,7 +146,8 @@ const char* tp_mlp_status_string(int status);
  * computed as up to four k-ranges whose fp32 sums are added in a fixed
  * order (results stay deterministic, but differ in the last bits from an
  * unsplit run). Only plain-store GEMMs (the second forward GEMM, dB, dA,
- * dXp) split, and only with the full workspace.
+ * dXp) split, and only with the full workspace; dB and dA do not where
+ * tp_mlp_bwd runs them as one launch (see there).
  *
  * tp_mlp_workspace_bytes: bytes for tp_mlp_bwd. Flags:
  *   TPMLP_WS_DZ       room for dZ_i as well, for callers that pass dZ = NULL;
@@ -252,6 +253,13 @@ int tp_mlp_fwd_sp(const tpmlp_shape* shape, int nslices, const void* const* X_sl
  *           two events back to back. With TPMLP_LAYOUT_B_T and the staged
  *           workspace, B1's interval also holds a transpose of B_i^T into
  *           the workspace, from which the dZ GEMM reads B_i k-contiguous.
+ *           Where dB and dA run as one launch (below), B2's interval holds
+ *           both and B3's two events are back to back.
+ * dB and dA as one launch: with ffn_shard == hidden, H_i kept, the default
+ * layout and operands read in place, the two weight-gradient GEMMs have one
+ * shape; where each alone would fill at most half of the compute units,
+ * they run as one launch of both GEMMs' output tiles, each over the whole
+ * token reduction (no k-split partials for them).
  */
 int tp_mlp_bwd(const tpmlp_shape* shape,
                const void* dY, const void* X, const void* A, const void* B,
